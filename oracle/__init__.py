@@ -1,0 +1,306 @@
+"""CPU oracle for the Lynx hierarchical split-stream quantizer.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the CPU-baseline
+leg of the benchmark are the only callers.  The GPU library never imports,
+links or calls this package, and the two share no code.
+
+The arithmetic lives in ``lynx_oracle.c`` (plain C, binary32 with one
+rounding per operation, compander decision and attention in binary64); this
+module only compiles it with gcc and marshals numpy arrays through ctypes.
+It follows "Lynx: Progressive Speculative Quantization for accelerating KV
+Transfer in Long-Context Inference", Section 4.1, Algorithm 1 and Eq. (3)-(4),
+and the reading notes "Lynx 阅读笔记", section "具体算例" (worked example).
+
+Pins of every function (tests/test_oracle_*.py) hold it to what the pages and
+the mathematics fix; see the docstring of each wrapper for its pin.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "lynx_oracle.c")
+_LIB = os.path.join(_HERE, "liblynx_oracle.so")
+
+# Plain scalar build: no FMA contraction, no fast-math, SSE binary32.
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+          "-fno-fast-math", "-fno-unsafe-math-optimizations", "-Wall"]
+
+_lock = threading.Lock()
+_lib = None
+
+P_DEFAULT, C_DEFAULT, H_DEFAULT = 256, 32, 128
+
+
+def build(force: bool = True) -> str:
+    """Compile lynx_oracle.c into liblynx_oracle.so with gcc."""
+    if not force and os.path.exists(_LIB) and \
+            os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    subprocess.check_call(["gcc", *CFLAGS, "-o", tmp, _SRC, "-lm"])
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB) or \
+                    os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build()
+            L = ctypes.CDLL(_LIB)
+            i64, i32, f32, f64 = (ctypes.c_int64, ctypes.c_int, ctypes.c_float,
+                                  ctypes.c_double)
+            vp = ctypes.c_void_p
+            L.oracle_code.restype = i32
+            L.oracle_code.argtypes = [f32, f32, f32]
+            L.oracle_code_real.restype = f64
+            L.oracle_code_real.argtypes = [f32, f32, f32]
+            L.oracle_level.restype = f32
+            L.oracle_level.argtypes = [i32, f32, f32]
+            L.oracle_split.restype = None
+            L.oracle_split.argtypes = [i32, i32, ctypes.POINTER(i32),
+                                       ctypes.POINTER(i32), ctypes.POINTER(i32)]
+            L.oracle_unsplit.restype = i32
+            L.oracle_unsplit.argtypes = [ctypes.c_uint, i32, ctypes.c_uint,
+                                         ctypes.POINTER(i32)]
+            L.oracle_quantize_block_ex.restype = i32
+            L.oracle_quantize_block_ex.argtypes = [
+                vp, i64, i32, i32, i32, f32, f32, f32, vp, vp, vp, vp, vp, vp,
+                vp, vp, vp, vp, vp]
+            L.oracle_dequant_block.restype = i32
+            L.oracle_dequant_block.argtypes = [
+                vp, vp, vp, vp, vp, vp, i32, i32, i32, f32, f32, f32, vp, i64]
+            L.oracle_quantize.restype = i32
+            L.oracle_quantize.argtypes = [
+                vp, i64, i64, i64, i64, i64, i32, i32, i32, f32, f32, f32,
+                i64, i64, i64, vp, vp, vp, vp, vp, vp]
+            L.oracle_dequant.restype = i32
+            L.oracle_dequant.argtypes = [
+                vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, i32,
+                f32, f32, f32, i64, i64, i64, vp]
+            L.oracle_attention.restype = i32
+            L.oracle_attention.argtypes = [
+                vp, vp, vp, i32, i32, i32, i32, i64, f64, i32, i32, i32, vp]
+            _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray | None):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"] or a.ndim == 0
+    return a.ctypes.data
+
+
+# ---------------------------------------------------------------- scalars --
+
+def code(x_abs: float, alpha: float = 255.0, code_scale: float = 127.0) -> int:
+    """Round(Eq. (3)) of one binary32 magnitude, before the 120 clip."""
+    return lib().oracle_code(x_abs, alpha, code_scale)
+
+
+def code_real(x_abs: float, alpha: float = 255.0, code_scale: float = 127.0) -> float:
+    """Y of Eq. (3) in binary64 (used to measure rounding margins)."""
+    return lib().oracle_code_real(x_abs, alpha, code_scale)
+
+
+def level(k: int, alpha: float = 255.0, code_scale: float = 127.0) -> float:
+    """Reconstruction magnitude of code k (inverse of Eq. (3))."""
+    return lib().oracle_level(k, alpha, code_scale)
+
+
+def split(code_c: int, sign: int):
+    """Algorithm 1 Stage 4 on one clipped code: returns (V_mag, Q_res, Q_anc)."""
+    v, r, a = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    lib().oracle_split(code_c, sign, ctypes.byref(v), ctypes.byref(r),
+                       ctypes.byref(a))
+    return v.value, r.value, a.value
+
+
+def unsplit(anchor_nibble: int, residual_nibble: int | None):
+    """Decoder side of Stage 4: (code, sign) from the nibbles."""
+    s = ctypes.c_int()
+    c = lib().oracle_unsplit(anchor_nibble, residual_nibble is not None,
+                             residual_nibble or 0, ctypes.byref(s))
+    return c, s.value
+
+
+# ------------------------------------------------------------ page blocks --
+
+class BlockResult:
+    """Outputs of one oracle page block (plus optional intermediates)."""
+
+    def __init__(self, H, P, C):
+        nch = P // C
+        self.anchor = np.zeros((P, H // 2), np.uint8)
+        self.residual = np.zeros((P, H // 2), np.uint8)
+        self.gamma_min = np.zeros(H, np.float32)
+        self.gamma_scale = np.zeros(H, np.float32)
+        self.mu = np.zeros((nch, H), np.float32)
+        self.sigma = np.zeros((nch, H), np.float32)
+        self.xn = np.zeros((H, P), np.float32)
+        self.xcent = np.zeros((H, P), np.float32)
+        self.xfinal = np.zeros((H, P), np.float32)
+        self.code_raw = np.zeros((H, P), np.int32)
+        self.sign = np.zeros((H, P), np.int8)
+
+
+def quantize_block(x_bf16: np.ndarray, alpha=255.0, eps=1e-6, code_scale=127.0,
+                   C=C_DEFAULT) -> BlockResult:
+    """Quantize one page block given token-major as uint16 bf16 bits [P][H]."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    P, H = x.shape
+    r = BlockResult(H, P, C)
+    rc = lib().oracle_quantize_block_ex(
+        _ptr(x), H, H, P, C, alpha, eps, code_scale, _ptr(r.anchor),
+        _ptr(r.residual), _ptr(r.gamma_min), _ptr(r.gamma_scale), _ptr(r.mu),
+        _ptr(r.sigma), _ptr(r.xn), _ptr(r.xcent), _ptr(r.xfinal),
+        _ptr(r.code_raw), _ptr(r.sign))
+    if rc:
+        raise ValueError("oracle_quantize_block_ex rejected the block")
+    return r
+
+
+def dequant_block(r: BlockResult, full: bool, alpha=255.0, eps=1e-6,
+                  code_scale=127.0, C=C_DEFAULT) -> np.ndarray:
+    """Reconstruct a block from its codes: anchor-only or anchor + residual."""
+    P, Hh = r.anchor.shape
+    H = Hh * 2
+    out = np.zeros((P, H), np.uint16)
+    rc = lib().oracle_dequant_block(
+        _ptr(r.anchor), _ptr(r.residual) if full else None, _ptr(r.gamma_min),
+        _ptr(r.gamma_scale), _ptr(r.mu), _ptr(r.sigma), H, P, C, alpha, eps,
+        code_scale, _ptr(out), H)
+    if rc:
+        raise ValueError("oracle_dequant_block rejected the block")
+    return out
+
+
+# ---------------------------------------------------------------- tensors --
+
+class Codes:
+    """Oracle outputs for a KV set of num_tensors [T][Ch] tensors."""
+
+    def __init__(self, nblocks, H=H_DEFAULT, P=P_DEFAULT, C=C_DEFAULT):
+        self.nblocks = nblocks
+        self.anchor = np.zeros((nblocks, P, H // 2), np.uint8)
+        self.residual = np.zeros((nblocks, P, H // 2), np.uint8)
+        self.gamma_min = np.zeros((nblocks, H), np.float32)
+        self.gamma_scale = np.zeros((nblocks, H), np.float32)
+        self.mu = np.zeros((nblocks, P // C, H), np.float32)
+        self.sigma = np.zeros((nblocks, P // C, H), np.float32)
+
+
+def _ranges(n, parts):
+    parts = max(1, min(parts, n))
+    step = (n + parts - 1) // parts
+    return [(b, min(n, b + step)) for b in range(0, n, step)]
+
+
+def quantize(kv: np.ndarray, alpha=255.0, eps=1e-6, code_scale=127.0,
+             H=H_DEFAULT, P=P_DEFAULT, C=C_DEFAULT, threads=1,
+             blocks: tuple[int, int] | None = None) -> Codes:
+    """Quantize kv (uint16 bf16 bits, shape [num_tensors, T, Ch]).
+
+    ``blocks=(b0, b1)`` restricts the work (and the returned arrays) to page
+    blocks b0..b1-1 of the global block order.  ``threads`` splits the block
+    range over Python threads (the C call releases the GIL).
+    """
+    kv = np.ascontiguousarray(kv, dtype=np.uint16)
+    nt, T, Ch = kv.shape
+    nblocks = nt * (T // P) * (Ch // H)
+    b0, b1 = blocks if blocks is not None else (0, nblocks)
+    out = Codes(b1 - b0, H, P, C)
+    L = lib()
+
+    def run(r):
+        lo, hi = r
+        rc = L.oracle_quantize(
+            _ptr(kv), nt, T * Ch, T, Ch, Ch, H, P, C, alpha, eps, code_scale,
+            lo, hi, b0, _ptr(out.anchor), _ptr(out.residual),
+            _ptr(out.gamma_min), _ptr(out.gamma_scale), _ptr(out.mu),
+            _ptr(out.sigma))
+        if rc:
+            raise ValueError("oracle_quantize rejected the arguments")
+
+    ranges = [(lo + b0, hi + b0) for lo, hi in _ranges(b1 - b0, threads)]
+    if len(ranges) == 1:
+        run(ranges[0])
+    else:
+        with ThreadPoolExecutor(len(ranges)) as ex:
+            list(ex.map(run, ranges))
+    return out
+
+
+def dequant(codes: Codes, shape, full: bool, alpha=255.0, eps=1e-6,
+            code_scale=127.0, H=H_DEFAULT, P=P_DEFAULT, C=C_DEFAULT, threads=1,
+            blocks: tuple[int, int] | None = None) -> np.ndarray:
+    """Reconstruct bf16 bits [num_tensors, T, Ch] from codes.
+
+    With ``blocks=(b0, b1)`` the codes hold blocks b0..b1-1 only and only
+    those blocks of the output are written (the rest stays zero).
+    """
+    nt, T, Ch = shape
+    nblocks = nt * (T // P) * (Ch // H)
+    b0, b1 = blocks if blocks is not None else (0, nblocks)
+    assert codes.nblocks == b1 - b0
+    out = np.zeros((nt, T, Ch), np.uint16)
+    L = lib()
+
+    def run(r):
+        lo, hi = r
+        rc = L.oracle_dequant(
+            _ptr(codes.anchor), _ptr(codes.residual) if full else None,
+            _ptr(codes.gamma_min), _ptr(codes.gamma_scale), _ptr(codes.mu),
+            _ptr(codes.sigma), nt, T * Ch, T, Ch, Ch, H, P, C, alpha, eps,
+            code_scale, lo, hi, b0, _ptr(out))
+        if rc:
+            raise ValueError("oracle_dequant rejected the arguments")
+
+    ranges = [(lo + b0, hi + b0) for lo, hi in _ranges(b1 - b0, threads)]
+    if len(ranges) == 1:
+        run(ranges[0])
+    else:
+        with ThreadPoolExecutor(len(ranges)) as ex:
+            list(ex.map(run, ranges))
+    return out
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+              causal_tail: bool, threads=1) -> np.ndarray:
+    """softmax(q k^T * scale) v in binary64 over bf16 bits.
+
+    q: [t_q, n_qh, d], k / v: [ctx, n_kvh, d] (uint16 bf16 bits).
+    Returns float64 [t_q, n_qh, d].
+    """
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    t_q, n_qh, d = q.shape
+    ctx, n_kvh, _ = k.shape
+    out = np.zeros((t_q, n_qh, d), np.float64)
+    L = lib()
+
+    def run(r):
+        lo, hi = r
+        rc = L.oracle_attention(_ptr(q), _ptr(k), _ptr(v), t_q, n_qh, n_kvh, d,
+                                ctx, scale, int(causal_tail), lo, hi, _ptr(out))
+        if rc:
+            raise ValueError("oracle_attention rejected the arguments")
+
+    ranges = _ranges(n_qh, threads)
+    if len(ranges) == 1:
+        run(ranges[0])
+    else:
+        with ThreadPoolExecutor(len(ranges)) as ex:
+            list(ex.map(run, ranges))
+    return out

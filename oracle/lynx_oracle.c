@@ -1,0 +1,464 @@
+/*
+ * Lynx hierarchical split-stream quantizer: CPU ORACLE.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this file's library.  The GPU
+ * library never links, includes or calls anything here, and this file shares
+ * no code, header, table or constant generator with it.
+ *
+ * Source: "Lynx: Progressive Speculative Quantization for accelerating KV
+ * Transfer in Long-Context Inference" (Han et al.), Section 4.1,
+ * Algorithm 1 "Lynx Hierarchical Quantization (Vectorized)", Eq. (3) and
+ * Eq. (4); the reading notes "Lynx 阅读笔记" (Zhongzhu Zhou), section
+ * "具体算例" (worked example) for the inverse and the anchor-only level.
+ *
+ * Arithmetic: IEEE-754 binary32 with round-to-nearest-even for every step
+ * of Algorithm 1, one rounding per operation (built with -ffp-contract=off,
+ * no fast-math).  The compander decision (Eq. 3 followed by Round) is taken
+ * in binary64, which decides the real-arithmetic rounding of Y exactly for
+ * every binary32 input (the test suite pins the margin).  Attention is
+ * evaluated in binary64.
+ *
+ * Readings of points the pages leave open (each one is listed with its
+ * reason in the design notes of the repository):
+ *   - axis=1 of X in R^{H x P} is the token axis: statistics are per channel;
+ *   - one epsilon for both stages;
+ *   - gamma_min is canonicalised with "+ 0.0f" (turns -0 into +0);
+ *   - the 32-token mean is a balanced pairwise tree sum, then / C;
+ *   - S = Sign(X_cent), with +0 and -0 counted as non-negative;
+ *   - Round is round-half-up of the real value Y;
+ *   - the integer code is clipped at 120 so that the anchor magnitude
+ *     (I + 7) >> 4 fits a 4-bit two's-complement nibble;
+ *   - anchor-only reconstruction uses code V << 4;
+ *   - the exact inverse of Eq. (3) is ((1 + alpha)^(I / 127) - 1) / alpha;
+ *   - denormalisation is the literal inverse of lines "X_final" then
+ *     "X <- (X - gamma_min) / (gamma_scale + eps)", four roundings, then
+ *     bf16 round-to-nearest-even;
+ *   - nibble packing: token-major rows, byte k of a row holds channel 2k in
+ *     its low nibble and channel 2k+1 in its high nibble.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_EINVAL -1
+
+/* ---------------------------------------------------------------- bf16 -- */
+
+static float bf16_to_f32(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Round-to-nearest-even from binary32 to bfloat16 on the bit pattern. */
+static uint16_t f32_to_bf16_rne(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7fffffffu) > 0x7f800000u) /* NaN: keep it a quiet NaN */
+        return (uint16_t)((u >> 16) | 0x0040u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+/* ------------------------------------------------------- Eq. (3), Round -- */
+
+/* Integer code of one magnitude |X_final| (Algorithm 1, Stage 3):
+ *   Y = code_scale * ln(1 + alpha*|x|) / ln(1 + alpha),  I = Round(Y),
+ * with Round taken as round-half-up of the real value.  alpha*|x| is an
+ * exact binary64 product of two binary32 values. */
+int oracle_code(float x_abs, float alpha, float code_scale)
+{
+    double y = (double)code_scale * log1p((double)alpha * (double)x_abs) /
+               log1p((double)alpha);
+    double fl = floor(y);
+    int i = (int)fl;
+    if (y - fl >= 0.5)
+        i += 1;
+    return i;
+}
+
+/* The same Y as a binary64 value, for tests that measure the distance of Y
+ * to the rounding boundaries. */
+double oracle_code_real(float x_abs, float alpha, float code_scale)
+{
+    return (double)code_scale * log1p((double)alpha * (double)x_abs) /
+           log1p((double)alpha);
+}
+
+/* Largest code whose anchor magnitude (I + 7) >> 4 still fits the 4-bit
+ * two's-complement anchor nibble (0..7 for either sign). */
+#define ORACLE_CODE_MAX 120
+
+/* Reconstruction level of code k, the inverse of Eq. (3)
+ * (|x^| grows as (1 + alpha)^(y / 127), Eq. (4)):
+ *   L[k] = ((1 + alpha)^(k / code_scale) - 1) / alpha,
+ * evaluated in binary64 and rounded once to binary32. */
+float oracle_level(int k, float alpha, float code_scale)
+{
+    double e = ((double)k / (double)code_scale) * log1p((double)alpha);
+    return (float)(expm1(e) / (double)alpha);
+}
+
+/* ------------------------------------------------------------ Stage 4 -- */
+
+/* Split-stream construction of one clipped code I (0..120) with sign S
+ * (Algorithm 1, Stage 4):
+ *   I_bias = I + 7;  V_mag = I_bias >> 4;  V_recon = V_mag << 4;
+ *   Q_res = V_recon - I;  Q_anc = V_mag * S + min(S, 0). */
+void oracle_split(int code, int sign, int *v_mag, int *q_res, int *q_anc)
+{
+    int i_bias = code + 7;
+    int v = i_bias >> 4;
+    int v_recon = v << 4;
+    *v_mag = v;
+    *q_res = v_recon - code;
+    *q_anc = v * sign + (sign < 0 ? sign : 0);
+}
+
+/* Inverse of the split: the code that the decoder rebuilds from an anchor
+ * nibble alone (V << 4) or from anchor and residual ((V << 4) - Q_res),
+ * plus the sign carried by the anchor.  Codes below 0 (only reachable with
+ * a residual the quantizer never writes) are clamped to 0. */
+static int sext4(unsigned nib)
+{
+    nib &= 0xfu;
+    return (nib & 0x8u) ? (int)nib - 16 : (int)nib;
+}
+
+int oracle_unsplit(unsigned anc_nib, int have_res, unsigned res_nib, int *sign)
+{
+    int a = sext4(anc_nib);
+    int s = a < 0 ? -1 : 1;
+    int v = a < 0 ? -a - 1 : a;
+    int code = v << 4;
+    if (have_res)
+        code -= sext4(res_nib);
+    if (code < 0)
+        code = 0;
+    *sign = s;
+    return code;
+}
+
+/* ------------------------------------------------------------- Stage 2 -- */
+
+/* Balanced pairwise tree sum of n (a power of two) values:
+ * sum(a[0..n)) = sum(a[0..n/2)) + sum(a[n/2..n)). */
+static float tree_sum(const float *a, int n)
+{
+    if (n == 1)
+        return a[0];
+    return tree_sum(a, n / 2) + tree_sum(a + n / 2, n / 2);
+}
+
+static int is_pow2(int n) { return n > 0 && (n & (n - 1)) == 0; }
+
+/* ------------------------------------------------------- one page block -- */
+
+/*
+ * Quantize one page block X in R^{H x P} stored token-major: element
+ * (channel c, token t) is x[t * row_stride + c] (bfloat16 bits).
+ *
+ * Outputs (all caller-owned):
+ *   anchor, residual : P rows of H/2 bytes (packed nibbles, see header);
+ *   gamma_min, gamma_scale : H floats;
+ *   mu, sigma : (P/C) x H floats, chunk-major ([chunk][channel]).
+ * Optional intermediates (NULL to skip), each H x P, channel-major
+ * ([c * P + t]):
+ *   xn (Stage 1 output), xcent, xfinal (Stage 2), code_raw (Round(Y) before
+ *   the clip), sign (+1 / -1).
+ */
+int oracle_quantize_block_ex(const uint16_t *x, int64_t row_stride, int H,
+                             int P, int C, float alpha, float eps,
+                             float code_scale, uint8_t *anchor,
+                             uint8_t *residual, float *gamma_min,
+                             float *gamma_scale, float *mu, float *sigma,
+                             float *xn_out, float *xcent_out,
+                             float *xfinal_out, int32_t *code_raw_out,
+                             int8_t *sign_out)
+{
+    if (H <= 0 || (H & 1) || P <= 0 || !is_pow2(C) || P % C)
+        return ORACLE_EINVAL;
+    const int nchunk = P / C;
+    float *xn = (float *)malloc(sizeof(float) * (size_t)P);
+    float *xc = (float *)malloc(sizeof(float) * (size_t)P);
+    int8_t *qa = (int8_t *)malloc((size_t)H * (size_t)P);
+    int8_t *qr = (int8_t *)malloc((size_t)H * (size_t)P);
+    if (!xn || !xc || !qa || !qr) {
+        free(xn); free(xc); free(qa); free(qr);
+        return ORACLE_EINVAL;
+    }
+
+    for (int c = 0; c < H; ++c) {
+        /* Stage 1: per-channel, page-level normalisation. */
+        float mn = bf16_to_f32(x[c]);
+        float mx = mn;
+        for (int t = 1; t < P; ++t) {
+            float v = bf16_to_f32(x[(int64_t)t * row_stride + c]);
+            if (v < mn) mn = v;
+            if (v > mx) mx = v;
+        }
+        mn = mn + 0.0f;
+        float gscale = mx - mn;
+        float d1 = gscale + eps;
+        gamma_min[c] = mn;
+        gamma_scale[c] = gscale;
+        for (int t = 0; t < P; ++t) {
+            float v = bf16_to_f32(x[(int64_t)t * row_stride + c]);
+            float num = v - mn;
+            xn[t] = num / d1;
+        }
+
+        /* Stage 2: per-channel, chunk-wise isolation. */
+        for (int j = 0; j < nchunk; ++j) {
+            const float *blk = xn + j * C;
+            float m = tree_sum(blk, C) / (float)C;
+            float sg = 0.0f;
+            for (int i = 0; i < C; ++i) {
+                xc[j * C + i] = blk[i] - m;
+                float a = fabsf(xc[j * C + i]);
+                if (a > sg) sg = a;
+            }
+            mu[j * H + c] = m;
+            sigma[j * H + c] = sg;
+            float d2 = sg + eps;
+
+            /* Stages 3 and 4 for every element of the chunk. */
+            for (int i = 0; i < C; ++i) {
+                int t = j * C + i;
+                float xf = xc[t] / d2;
+                int code = oracle_code(fabsf(xf), alpha, code_scale);
+                int s = xc[t] < 0.0f ? -1 : 1;
+                int code_c = code < ORACLE_CODE_MAX ? code : ORACLE_CODE_MAX;
+                int v, q_res, q_anc;
+                oracle_split(code_c, s, &v, &q_res, &q_anc);
+                qa[(size_t)t * H + c] = (int8_t)q_anc;
+                qr[(size_t)t * H + c] = (int8_t)q_res;
+                if (xfinal_out) xfinal_out[(size_t)c * P + t] = xf;
+                if (code_raw_out) code_raw_out[(size_t)c * P + t] = code;
+                if (sign_out) sign_out[(size_t)c * P + t] = (int8_t)s;
+            }
+        }
+        if (xn_out)
+            memcpy(xn_out + (size_t)c * P, xn, sizeof(float) * (size_t)P);
+        if (xcent_out)
+            memcpy(xcent_out + (size_t)c * P, xc, sizeof(float) * (size_t)P);
+    }
+
+    /* Packing: two's-complement nibbles, even channel in the low nibble. */
+    for (int t = 0; t < P; ++t) {
+        for (int k = 0; k < H / 2; ++k) {
+            unsigned a0 = (unsigned)qa[(size_t)t * H + 2 * k] & 0xfu;
+            unsigned a1 = (unsigned)qa[(size_t)t * H + 2 * k + 1] & 0xfu;
+            unsigned r0 = (unsigned)qr[(size_t)t * H + 2 * k] & 0xfu;
+            unsigned r1 = (unsigned)qr[(size_t)t * H + 2 * k + 1] & 0xfu;
+            anchor[(size_t)t * (H / 2) + k] = (uint8_t)(a0 | (a1 << 4));
+            residual[(size_t)t * (H / 2) + k] = (uint8_t)(r0 | (r1 << 4));
+        }
+    }
+    free(xn); free(xc); free(qa); free(qr);
+    return ORACLE_OK;
+}
+
+/*
+ * Dequantize one page block.  residual == NULL gives the anchor-only
+ * (draft) reconstruction; otherwise anchor + residual (verification
+ * precision).  out is token-major bf16 with row stride out_row_stride.
+ *   x^_f = S * L[code];  x^_n = x^_f * (sigma + eps) + mu;
+ *   x^ = x^_n * (gamma_scale + eps) + gamma_min;  out = bf16_rne(x^).
+ */
+int oracle_dequant_block(const uint8_t *anchor, const uint8_t *residual,
+                         const float *gamma_min, const float *gamma_scale,
+                         const float *mu, const float *sigma, int H, int P,
+                         int C, float alpha, float eps, float code_scale,
+                         uint16_t *out, int64_t out_row_stride)
+{
+    if (H <= 0 || (H & 1) || P <= 0 || C <= 0 || P % C)
+        return ORACLE_EINVAL;
+    float lut[128];
+    for (int k = 0; k < 128; ++k)
+        lut[k] = oracle_level(k, alpha, code_scale);
+    for (int t = 0; t < P; ++t) {
+        int j = t / C;
+        for (int c = 0; c < H; ++c) {
+            unsigned ab = anchor[(size_t)t * (H / 2) + c / 2];
+            unsigned an = (c & 1) ? (ab >> 4) : (ab & 0xfu);
+            unsigned rn = 0;
+            if (residual) {
+                unsigned rb = residual[(size_t)t * (H / 2) + c / 2];
+                rn = (c & 1) ? (rb >> 4) : (rb & 0xfu);
+            }
+            int s;
+            int code = oracle_unsplit(an, residual != NULL, rn, &s);
+            float m = lut[code];
+            float xf = s < 0 ? -m : m;
+            float d2 = sigma[j * H + c] + eps;
+            float d1 = gamma_scale[c] + eps;
+            float t1 = xf * d2;
+            float xnv = t1 + mu[j * H + c];
+            float t2 = xnv * d1;
+            float xv = t2 + gamma_min[c];
+            out[(int64_t)t * out_row_stride + c] = f32_to_bf16_rne(xv);
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------- whole tensors -- */
+
+/*
+ * A KV set is num_tensors token-major tensors [T][Ch] (tensor k starts at
+ * element k * tensor_stride, token rows row_stride elements apart).  It is
+ * cut into page blocks of H channels x P tokens, numbered
+ *   b = ((tensor * (T / P)) + page) * (Ch / H) + channel_group.
+ * Only blocks [block_begin, block_end) are computed (so several threads
+ * can share one call's outputs).  The code and metadata arrays hold blocks
+ * from out_first_block on: block b's anchor and residual are bytes
+ * [(b - out_first_block) * P * H / 2, ...), its gamma_* floats
+ * [(b - out_first_block) * H, ...), its mu / sigma floats
+ * [(b - out_first_block) * (P/C) * H, ...).
+ */
+static int block_geometry(int64_t b, int64_t T, int64_t Ch, int H, int P,
+                          int64_t *tensor, int64_t *page, int64_t *group)
+{
+    int64_t groups = Ch / H, pages = T / P;
+    *group = b % groups;
+    *page = (b / groups) % pages;
+    *tensor = b / (groups * pages);
+    return 0;
+}
+
+int oracle_quantize(const uint16_t *kv, int64_t num_tensors,
+                    int64_t tensor_stride, int64_t T, int64_t Ch,
+                    int64_t row_stride, int H, int P, int C, float alpha,
+                    float eps, float code_scale, int64_t block_begin,
+                    int64_t block_end, int64_t out_first_block,
+                    uint8_t *anchor, uint8_t *residual,
+                    float *gamma_min, float *gamma_scale, float *mu,
+                    float *sigma)
+{
+    if (T % P || Ch % H || num_tensors < 0)
+        return ORACLE_EINVAL;
+    const int64_t nblocks = num_tensors * (T / P) * (Ch / H);
+    if (block_begin < 0 || block_end > nblocks || block_begin > block_end ||
+        out_first_block > block_begin)
+        return ORACLE_EINVAL;
+    const int64_t code_bytes = (int64_t)P * H / 2;
+    const int64_t chunk_meta = (int64_t)(P / C) * H;
+    for (int64_t b = block_begin; b < block_end; ++b) {
+        int64_t tensor, page, group;
+        block_geometry(b, T, Ch, H, P, &tensor, &page, &group);
+        const uint16_t *x = kv + tensor * tensor_stride +
+                            page * P * row_stride + group * H;
+        const int64_t o = b - out_first_block;
+        int rc = oracle_quantize_block_ex(
+            x, row_stride, H, P, C, alpha, eps, code_scale,
+            anchor + o * code_bytes, residual + o * code_bytes,
+            gamma_min + o * H, gamma_scale + o * H, mu + o * chunk_meta,
+            sigma + o * chunk_meta, NULL, NULL, NULL, NULL, NULL);
+        if (rc)
+            return rc;
+    }
+    return ORACLE_OK;
+}
+
+int oracle_dequant(const uint8_t *anchor, const uint8_t *residual,
+                   const float *gamma_min, const float *gamma_scale,
+                   const float *mu, const float *sigma, int64_t num_tensors,
+                   int64_t tensor_stride, int64_t T, int64_t Ch,
+                   int64_t row_stride, int H, int P, int C, float alpha,
+                   float eps, float code_scale, int64_t block_begin,
+                   int64_t block_end, int64_t in_first_block, uint16_t *out)
+{
+    if (T % P || Ch % H || num_tensors < 0)
+        return ORACLE_EINVAL;
+    const int64_t nblocks = num_tensors * (T / P) * (Ch / H);
+    if (block_begin < 0 || block_end > nblocks || block_begin > block_end ||
+        in_first_block > block_begin)
+        return ORACLE_EINVAL;
+    const int64_t code_bytes = (int64_t)P * H / 2;
+    const int64_t chunk_meta = (int64_t)(P / C) * H;
+    for (int64_t b = block_begin; b < block_end; ++b) {
+        int64_t tensor, page, group;
+        block_geometry(b, T, Ch, H, P, &tensor, &page, &group);
+        uint16_t *o = out + tensor * tensor_stride + page * P * row_stride +
+                      group * H;
+        const int64_t i = b - in_first_block;
+        int rc = oracle_dequant_block(
+            anchor + i * code_bytes, residual ? residual + i * code_bytes : NULL,
+            gamma_min + i * H, gamma_scale + i * H, mu + i * chunk_meta,
+            sigma + i * chunk_meta, H, P, C, alpha, eps, code_scale, o,
+            row_stride);
+        if (rc)
+            return rc;
+    }
+    return ORACLE_OK;
+}
+
+/* ----------------------------------------------------------- attention -- */
+
+/*
+ * Scaled dot-product attention O = softmax(Q K^T * scale) V (Lynx paper,
+ * Section 2.1) over reconstructed bf16 K^, V^, in binary64.
+ *   q   : [t_q][n_qh][d] bf16,   k, v : [ctx][n_kvh][d] bf16 (token-major),
+ *   out : [t_q][n_qh][d] binary64.
+ * Query head h reads KV head h / (n_qh / n_kvh) (grouped-query attention).
+ * With causal_tail set, the t_q queries are the last t_q positions of the
+ * context and query row r sees positions 0 .. ctx - t_q + r.
+ * Only query heads [h_begin, h_end) are computed.
+ */
+int oracle_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                     int t_q, int n_qh, int n_kvh, int d, int64_t ctx,
+                     double scale, int causal_tail, int h_begin, int h_end,
+                     double *out)
+{
+    if (t_q <= 0 || n_qh <= 0 || n_kvh <= 0 || n_qh % n_kvh || d <= 0 ||
+        ctx <= 0 || (causal_tail && ctx < t_q))
+        return ORACLE_EINVAL;
+    const int group = n_qh / n_kvh;
+    double *s = (double *)malloc(sizeof(double) * (size_t)ctx);
+    double *qv = (double *)malloc(sizeof(double) * (size_t)d);
+    if (!s || !qv) {
+        free(s); free(qv);
+        return ORACLE_EINVAL;
+    }
+    for (int r = 0; r < t_q; ++r) {
+        int64_t visible = causal_tail ? ctx - t_q + r + 1 : ctx;
+        for (int h = h_begin; h < h_end; ++h) {
+            int kh = h / group;
+            for (int i = 0; i < d; ++i)
+                qv[i] = bf16_to_f32(q[((size_t)r * n_qh + h) * d + i]);
+            double mx = -INFINITY;
+            for (int64_t p = 0; p < visible; ++p) {
+                const uint16_t *kr = k + ((size_t)p * n_kvh + kh) * d;
+                double acc = 0.0;
+                for (int i = 0; i < d; ++i)
+                    acc += qv[i] * (double)bf16_to_f32(kr[i]);
+                s[p] = acc * scale;
+                if (s[p] > mx) mx = s[p];
+            }
+            double den = 0.0;
+            for (int64_t p = 0; p < visible; ++p) {
+                s[p] = exp(s[p] - mx);
+                den += s[p];
+            }
+            double *o = out + ((size_t)r * n_qh + h) * d;
+            for (int i = 0; i < d; ++i)
+                o[i] = 0.0;
+            for (int64_t p = 0; p < visible; ++p) {
+                const uint16_t *vr = v + ((size_t)p * n_kvh + kh) * d;
+                double w = s[p] / den;
+                for (int i = 0; i < d; ++i)
+                    o[i] += w * (double)bf16_to_f32(vr[i]);
+            }
+        }
+    }
+    free(s);
+    free(qv);
+    return ORACLE_OK;
+}
