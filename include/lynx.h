@@ -1,0 +1,193 @@
+/*
+ * lynx.h: C ABI of the MI355X (gfx950) Lynx split-stream KV codec.
+ *
+ * The operations are those of "Lynx: Progressive Speculative Quantization
+ * for accelerating KV Transfer in Long-Context Inference" (Han et al.):
+ *   - lynx_quantize_pages: Section 4.1, Algorithm 1 (Stages 1-4) and
+ *     Eq. (3) on every page block of a KV set, producing the Anchor stream,
+ *     the Residual stream and the metadata {gamma_min, gamma_scale, mu,
+ *     sigma} (Section 4.2, prefill workflow: the quantization kernel turns
+ *     each KV object into Q_anc, Q_res and the metadata);
+ *   - lynx_dequant_anchor: the anchor phase of the decode workflow
+ *     (Section 4.2, Figure 7(b)): approximate KV from Q_anc and metadata;
+ *   - lynx_dequant_full: the residual phase (Section 4.2, Figure 7(c)):
+ *     Q_res combined with the stored metadata refines the KV to Q_full;
+ *   - lynx_page_stats / lynx_block_stats: Stage 1 and Stage 2 statistics of
+ *     Algorithm 1 on their own (the same arithmetic as the fused quantize).
+ *
+ * Terms
+ *   KV set      num_tensors token-major bf16 tensors [num_tokens][num_channels]
+ *               (e.g. layers x {K, V}); tensor k starts tensor_stride elements
+ *               after tensor k-1, token rows are row_stride elements apart.
+ *   page block  X in R^{H x P}: H = 128 consecutive channels (one KV head)
+ *               x P = 256 consecutive tokens of one tensor; chunk = C = 32
+ *               consecutive tokens of one channel inside a page block.
+ *   block index b = ((tensor * (num_tokens / P)) + page) * (num_channels / H)
+ *               + head.  Every per-block output below is stored at block b.
+ *
+ * Stream and metadata layouts (all outputs are plain device buffers)
+ *   anchor      uint8 [nblocks][P][H/2]: per token row, byte k holds the
+ *               4-bit two's-complement anchor of channel 2k in its low
+ *               nibble and of channel 2k+1 in its high nibble.  16384 bytes
+ *               per block, blocks back to back: one contiguous stream.
+ *   residual    uint8 [nblocks][P][H/2], same nibble layout, 4-bit signed
+ *               residual (code = (anchor magnitude << 4) - residual).
+ *   gamma_min, gamma_scale   float32 [nblocks][H]
+ *   mu, sigma               float32 [nblocks][P/C][H]
+ *
+ * Numerics: binary32 with one IEEE round-to-nearest-even rounding per step
+ * of Algorithm 1 (no contraction); the compander code is the exact
+ * real-arithmetic rounding (half-up) of Eq. (3) applied to the binary32
+ * X_final, clipped at 120 so the anchor fits 4 bits; reconstruction is
+ * ((S * L[code]) * (sigma + eps) + mu) * (gamma_scale + eps) + gamma_min with
+ * L[k] = ((1 + alpha)^(k / code_scale) - 1) / alpha rounded to binary32, then
+ * bf16 round-to-nearest-even.  Anchor-only uses code = anchor magnitude << 4.
+ * Results are deterministic and independent of launch geometry.
+ * Non-finite inputs, and channels whose max - min overflows binary32, give
+ * unspecified (but in-bounds) outputs.
+ *
+ * Ownership and errors: the caller allocates and owns every buffer; the
+ * library allocates no device memory and keeps no device state (its only
+ * state is a host-side cache of the compander tables, keyed by the
+ * parameters and guarded by a mutex).  Every call validates its arguments
+ * before launching anything and returns a status code; on an error nothing
+ * is launched and no output is written.  Successful calls are asynchronous
+ * on `stream` (NULL = the default stream): results are visible once the
+ * stream is synchronised.  Device pointers must be 16-byte aligned, row and
+ * tensor strides multiples of 8 elements.
+ */
+#ifndef LYNX_H
+#define LYNX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define LYNX_OK 0
+#define LYNX_EINVAL (-1) /* null pointer, negative size, bad parameter     */
+#define LYNX_ESHAPE (-2) /* tokens % 256, channels % 128, stride or align   */
+#define LYNX_EHIP (-3)   /* a HIP call or launch failed (see status string) */
+
+/* Geometry fixed by the GPU kernels. */
+#define LYNX_PAGE_TOKENS 256
+#define LYNX_CHUNK_TOKENS 32
+#define LYNX_BLOCK_CHANNELS 128
+
+/* Method parameters (Algorithm 1 and Eq. (3)).  alpha > 0 controls the
+ * skew of the alpha-law (default 255); eps > 0 is added to both scales
+ * (default 1e-6); code_scale is the 2^7 - 1 = 127 of Eq. (3) (120 is also
+ * accepted: then no code needs the clip).  page_tokens, chunk_tokens and
+ * block_channels must be 256, 32 and 128. */
+typedef struct lynx_params {
+    float alpha;
+    float eps;
+    float code_scale;
+    int32_t page_tokens;
+    int32_t chunk_tokens;
+    int32_t block_channels;
+} lynx_params;
+
+/* Shape of a KV set (element strides, bf16 elements). */
+typedef struct lynx_kv_shape {
+    int64_t num_tensors;
+    int64_t tensor_stride;
+    int64_t num_tokens;
+    int64_t num_channels;
+    int64_t row_stride;
+} lynx_kv_shape;
+
+/* Device pointers to the four metadata arrays (layouts above). */
+typedef struct lynx_meta {
+    float *gamma_min;
+    float *gamma_scale;
+    float *mu;
+    float *sigma;
+} lynx_meta;
+
+/* Fills *p with alpha = 255, eps = 1e-6, code_scale = 127, P = 256,
+ * C = 32, H = 128. */
+void lynx_default_params(lynx_params *p);
+
+/* Number of page blocks of a shape, or a negative status if the shape is
+ * invalid. */
+int64_t lynx_num_blocks(const lynx_kv_shape *shape);
+
+/* Bytes of one stream (anchor or residual) and number of floats of each
+ * metadata array, for a shape; 0 if the shape is invalid. */
+size_t lynx_stream_bytes(const lynx_kv_shape *shape);
+size_t lynx_gamma_floats(const lynx_kv_shape *shape);
+size_t lynx_chunk_floats(const lynx_kv_shape *shape);
+
+/* Eq. (1) of the paper (Section 2.2): Size_KV = K_factor * L * D *
+ * N_layers * Precision bytes (K_factor 2 for K and V, 1 for MLA; D = heads
+ * x head dimension; precision in bytes).  0 on overflow or bad input. */
+uint64_t lynx_kv_bytes(int64_t k_factor, int64_t seq_len, int64_t hidden,
+                       int64_t layers, int64_t precision_bytes);
+
+/* The 128 compander thresholds the kernels use for `params` (NULL =
+ * defaults): thr[k], k = 1..120, is the smallest binary32 magnitude whose
+ * Eq. (3) value reaches k - 1/2 (so code(|x|) = #{k : |x| >= thr[k]});
+ * thr[0] = 0 and thr[k] = +inf for codes the clip at 120 removes.  Host
+ * only, no GPU needed.  Returns LYNX_EINVAL for bad parameters. */
+int lynx_compander_thresholds(const lynx_params *params, float *thr128);
+
+/* Human-readable text for a status code, or the last HIP error text of the
+ * calling thread for LYNX_EHIP. */
+const char *lynx_status_string(int status);
+
+/*
+ * Algorithm 1 on every page block of the KV set `kv` (bf16, layout given
+ * by `shape`): writes anchor, residual (nblocks * 16384 bytes each) and the
+ * four metadata arrays.  `params` NULL means the defaults.
+ */
+int lynx_quantize_pages(const void *kv, const lynx_kv_shape *shape,
+                        const lynx_params *params, uint8_t *anchor,
+                        uint8_t *residual, lynx_meta meta, hipStream_t stream);
+
+/*
+ * Anchor phase: rebuilds every page block from the anchor stream and the
+ * metadata (code = anchor magnitude << 4) into `out` (bf16, layout given by
+ * `shape`; the shape's strides describe `out`).  meta.* are only read.
+ */
+int lynx_dequant_anchor(const uint8_t *anchor, lynx_meta meta,
+                        const lynx_kv_shape *shape, const lynx_params *params,
+                        void *out, hipStream_t stream);
+
+/*
+ * Residual phase: rebuilds every page block at the verification precision
+ * from anchor + residual and the metadata into `out`.
+ */
+int lynx_dequant_full(const uint8_t *anchor, const uint8_t *residual,
+                      lynx_meta meta, const lynx_kv_shape *shape,
+                      const lynx_params *params, void *out,
+                      hipStream_t stream);
+
+/*
+ * Algorithm 1 Stage 1 alone: gamma_min (canonical +0 for a zero minimum)
+ * and gamma_scale = max - gamma_min of every channel of every page block.
+ */
+int lynx_page_stats(const void *kv, const lynx_kv_shape *shape,
+                    const lynx_params *params, float *gamma_min,
+                    float *gamma_scale, hipStream_t stream);
+
+/*
+ * Algorithm 1 Stage 2 statistics alone, given the Stage 1 statistics
+ * (read from gamma_min / gamma_scale): mu (balanced pairwise tree mean of
+ * the 32 normalised values) and sigma = max |X - mu| of every chunk.
+ */
+int lynx_block_stats(const void *kv, const lynx_kv_shape *shape,
+                     const lynx_params *params, const float *gamma_min,
+                     const float *gamma_scale, float *mu, float *sigma,
+                     hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LYNX_H */

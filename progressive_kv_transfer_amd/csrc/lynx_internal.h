@@ -1,0 +1,64 @@
+// Internal declarations shared by the host API and the gfx950 kernels of
+// liblynx.so.  Not part of the public ABI (include/lynx.h is).
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace lynx {
+
+constexpr int kPage = 256;      // P: tokens per page block
+constexpr int kChunk = 32;      // C: tokens per chunk
+constexpr int kHead = 128;      // H: channels per page block
+constexpr int kChunks = kPage / kChunk;
+constexpr int kCodeMax = 120;   // largest code whose anchor fits 4 bits
+constexpr int kMaxBuckets = 1536;
+
+// Compander tables, built once per (alpha, code_scale) on the host and
+// passed by value as a kernel argument.
+//
+// thr[k] (k = 1..120) is the smallest binary32 x >= 0 whose Eq. (3) value
+// Y(x) reaches k - 1/2, i.e. the code of |x| is #{k : |x| >= thr[k]};
+// thr[0] = 0 and thr[121..127] = +inf (the clip at 120).
+//
+// Bucket index of a magnitude m is bits(m) >> shift, clamped to
+// [bucket_lo, bucket_lo + nbuckets - 1]; every bucket holds at most one
+// threshold, so code(m) = bucket_code[i] + (m >= thr[bucket_code[i] + 1]).
+struct QuantTab {
+    float thr[128];
+    uint8_t bucket_code[kMaxBuckets];
+    int32_t bucket_lo;
+    int32_t nbuckets;
+    int32_t shift;
+    float eps;
+};
+
+// Reconstruction levels L[k] = ((1 + alpha)^(k / code_scale) - 1) / alpha.
+struct DequantTab {
+    float level[128];
+    float eps;
+};
+
+// Geometry of one launch: a KV set cut into page blocks.
+struct Geometry {
+    int64_t tensor_stride;  // elements
+    int64_t row_stride;     // elements
+    int32_t pages;          // pages per tensor
+    int32_t heads;          // 128-channel groups per tensor
+    int64_t nblocks;        // blocks in this launch
+    int64_t block0;         // global index of the launch's first block
+};
+
+enum StatsMode : int { kModeQuantize = 0, kModePageStats = 1, kModeBlockStats = 2 };
+
+hipError_t launch_quantize(const uint16_t *kv, const Geometry &g, const QuantTab &tab,
+                           uint8_t *anchor, uint8_t *residual, float *gmin, float *gscale,
+                           float *mu, float *sigma, int mode, hipStream_t stream);
+
+hipError_t launch_dequant(const uint8_t *anchor, const uint8_t *residual, const float *gmin,
+                          const float *gscale, const float *mu, const float *sigma,
+                          const Geometry &g, const DequantTab &tab, uint16_t *out,
+                          hipStream_t stream);
+
+}  // namespace lynx

@@ -1,0 +1,238 @@
+"""Thin Python binding of liblynx.so (include/lynx.h).
+
+Same names as the C ABI; this module only marshals torch tensors (device
+memory) and the current torch stream into the C calls.  All arithmetic runs
+in the library's HIP kernels.  If liblynx.so is missing or cannot be loaded
+every call raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblynx.so")
+
+PAGE_TOKENS = 256
+CHUNK_TOKENS = 32
+BLOCK_CHANNELS = 128
+STATUS = {0: "LYNX_OK", -1: "LYNX_EINVAL", -2: "LYNX_ESHAPE", -3: "LYNX_EHIP"}
+
+
+class LynxError(RuntimeError):
+    def __init__(self, fn, status, text):
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({text})")
+        self.status = status
+
+
+class lynx_params(ctypes.Structure):
+    _fields_ = [("alpha", ctypes.c_float), ("eps", ctypes.c_float),
+                ("code_scale", ctypes.c_float), ("page_tokens", ctypes.c_int32),
+                ("chunk_tokens", ctypes.c_int32), ("block_channels", ctypes.c_int32)]
+
+
+class lynx_kv_shape(ctypes.Structure):
+    _fields_ = [("num_tensors", ctypes.c_int64), ("tensor_stride", ctypes.c_int64),
+                ("num_tokens", ctypes.c_int64), ("num_channels", ctypes.c_int64),
+                ("row_stride", ctypes.c_int64)]
+
+
+class lynx_meta(ctypes.Structure):
+    _fields_ = [("gamma_min", ctypes.c_void_p), ("gamma_scale", ctypes.c_void_p),
+                ("mu", ctypes.c_void_p), ("sigma", ctypes.c_void_p)]
+
+
+# Every symbol include/lynx.h declares.
+EXPORTS = ["lynx_default_params", "lynx_num_blocks", "lynx_stream_bytes",
+           "lynx_gamma_floats", "lynx_chunk_floats", "lynx_kv_bytes",
+           "lynx_status_string", "lynx_compander_thresholds", "lynx_quantize_pages", "lynx_dequant_anchor",
+           "lynx_dequant_full", "lynx_page_stats", "lynx_block_stats"]
+
+_lib = None
+
+
+def lib():
+    """Load liblynx.so (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built: run "
+                "`python -m progressive_kv_transfer_amd.build` (no CPU fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        P = ctypes.POINTER
+        L.lynx_default_params.argtypes = [P(lynx_params)]
+        L.lynx_default_params.restype = None
+        L.lynx_num_blocks.argtypes = [P(lynx_kv_shape)]
+        L.lynx_num_blocks.restype = i64
+        for f in ("lynx_stream_bytes", "lynx_gamma_floats", "lynx_chunk_floats"):
+            getattr(L, f).argtypes = [P(lynx_kv_shape)]
+            getattr(L, f).restype = ctypes.c_size_t
+        L.lynx_kv_bytes.argtypes = [i64] * 5
+        L.lynx_kv_bytes.restype = ctypes.c_uint64
+        L.lynx_compander_thresholds.argtypes = [P(lynx_params), vp]
+        L.lynx_compander_thresholds.restype = i32
+        L.lynx_status_string.argtypes = [i32]
+        L.lynx_status_string.restype = ctypes.c_char_p
+        L.lynx_quantize_pages.argtypes = [vp, P(lynx_kv_shape), P(lynx_params), vp, vp,
+                                          lynx_meta, vp]
+        L.lynx_dequant_anchor.argtypes = [vp, lynx_meta, P(lynx_kv_shape), P(lynx_params),
+                                          vp, vp]
+        L.lynx_dequant_full.argtypes = [vp, vp, lynx_meta, P(lynx_kv_shape),
+                                        P(lynx_params), vp, vp]
+        L.lynx_page_stats.argtypes = [vp, P(lynx_kv_shape), P(lynx_params), vp, vp, vp]
+        L.lynx_block_stats.argtypes = [vp, P(lynx_kv_shape), P(lynx_params), vp, vp, vp,
+                                       vp, vp]
+        for f in ("lynx_quantize_pages", "lynx_dequant_anchor", "lynx_dequant_full",
+                  "lynx_page_stats", "lynx_block_stats"):
+            getattr(L, f).restype = i32
+        _lib = L
+    return _lib
+
+
+def _check(fn, rc):
+    if rc != 0:
+        raise LynxError(fn, rc, lib().lynx_status_string(rc).decode())
+
+
+def params(alpha=255.0, eps=1e-6, code_scale=127.0) -> lynx_params:
+    p = lynx_params()
+    lib().lynx_default_params(ctypes.byref(p))
+    p.alpha, p.eps, p.code_scale = alpha, eps, code_scale
+    return p
+
+
+def shape_of(kv: torch.Tensor) -> lynx_kv_shape:
+    """lynx_kv_shape of a [num_tensors, T, Ch] (or [T, Ch]) tensor view."""
+    if kv.dim() == 2:
+        kv = kv.unsqueeze(0)
+    if kv.dim() != 3 or kv.stride(2) != 1:
+        raise ValueError("KV must be [num_tensors, tokens, channels] with unit channel stride")
+    s = lynx_kv_shape()
+    s.num_tensors, s.num_tokens, s.num_channels = kv.shape
+    s.tensor_stride, s.row_stride = kv.stride(0), kv.stride(1)
+    return s
+
+
+def kv_bytes(k_factor, seq_len, hidden, layers, precision_bytes) -> int:
+    """Eq. (1) of the paper through the library."""
+    return lib().lynx_kv_bytes(k_factor, seq_len, hidden, layers, precision_bytes)
+
+
+def compander_thresholds(p: lynx_params | None = None):
+    """The 128 binary32 thresholds of lynx_compander_thresholds (host only)."""
+    import numpy as np
+    out = np.zeros(128, np.float32)
+    _check("lynx_compander_thresholds", lib().lynx_compander_thresholds(
+        ctypes.byref(p) if p else None, out.ctypes.data))
+    return out
+
+
+def num_blocks(shape: lynx_kv_shape) -> int:
+    n = lib().lynx_num_blocks(ctypes.byref(shape))
+    if n < 0:
+        _check("lynx_num_blocks", int(n))
+    return int(n)
+
+
+@dataclass
+class Codes:
+    """Device buffers of one quantized KV set (layouts of include/lynx.h)."""
+    anchor: torch.Tensor       # uint8 [nblocks, 256, 64]
+    residual: torch.Tensor     # uint8 [nblocks, 256, 64]
+    gamma_min: torch.Tensor    # float32 [nblocks, 128]
+    gamma_scale: torch.Tensor  # float32 [nblocks, 128]
+    mu: torch.Tensor           # float32 [nblocks, 8, 128]
+    sigma: torch.Tensor        # float32 [nblocks, 8, 128]
+
+    def meta(self) -> lynx_meta:
+        m = lynx_meta()
+        m.gamma_min, m.gamma_scale = self.gamma_min.data_ptr(), self.gamma_scale.data_ptr()
+        m.mu, m.sigma = self.mu.data_ptr(), self.sigma.data_ptr()
+        return m
+
+
+def alloc_codes(nblocks: int, device) -> Codes:
+    u8 = dict(dtype=torch.uint8, device=device)
+    f32 = dict(dtype=torch.float32, device=device)
+    return Codes(torch.empty((nblocks, PAGE_TOKENS, BLOCK_CHANNELS // 2), **u8),
+                 torch.empty((nblocks, PAGE_TOKENS, BLOCK_CHANNELS // 2), **u8),
+                 torch.empty((nblocks, BLOCK_CHANNELS), **f32),
+                 torch.empty((nblocks, BLOCK_CHANNELS), **f32),
+                 torch.empty((nblocks, PAGE_TOKENS // CHUNK_TOKENS, BLOCK_CHANNELS), **f32),
+                 torch.empty((nblocks, PAGE_TOKENS // CHUNK_TOKENS, BLOCK_CHANNELS), **f32))
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("lynx calls take device tensors")
+
+
+def quantize_pages(kv: torch.Tensor, p: lynx_params | None = None,
+                   out: Codes | None = None, stream=None) -> Codes:
+    """lynx_quantize_pages on a bf16 [num_tensors, T, Ch] device tensor."""
+    _require_cuda(kv)
+    if kv.dtype != torch.bfloat16:
+        raise ValueError("KV must be bfloat16")
+    sh = shape_of(kv)
+    nb = num_blocks(sh)
+    codes = out if out is not None else alloc_codes(nb, kv.device)
+    _check("lynx_quantize_pages", lib().lynx_quantize_pages(
+        kv.data_ptr(), ctypes.byref(sh), ctypes.byref(p) if p else None,
+        codes.anchor.data_ptr(), codes.residual.data_ptr(), codes.meta(), _stream(stream)))
+    return codes
+
+
+def dequant_anchor(codes: Codes, out: torch.Tensor, p: lynx_params | None = None,
+                   stream=None) -> torch.Tensor:
+    """lynx_dequant_anchor into a bf16 [num_tensors, T, Ch] device tensor."""
+    _require_cuda(out)
+    sh = shape_of(out)
+    _check("lynx_dequant_anchor", lib().lynx_dequant_anchor(
+        codes.anchor.data_ptr(), codes.meta(), ctypes.byref(sh),
+        ctypes.byref(p) if p else None, out.data_ptr(), _stream(stream)))
+    return out
+
+
+def dequant_full(codes: Codes, out: torch.Tensor, p: lynx_params | None = None,
+                 stream=None) -> torch.Tensor:
+    """lynx_dequant_full into a bf16 [num_tensors, T, Ch] device tensor."""
+    _require_cuda(out)
+    sh = shape_of(out)
+    _check("lynx_dequant_full", lib().lynx_dequant_full(
+        codes.anchor.data_ptr(), codes.residual.data_ptr(), codes.meta(), ctypes.byref(sh),
+        ctypes.byref(p) if p else None, out.data_ptr(), _stream(stream)))
+    return out
+
+
+def page_stats(kv: torch.Tensor, gamma_min: torch.Tensor, gamma_scale: torch.Tensor,
+               p: lynx_params | None = None, stream=None):
+    """lynx_page_stats (Stage 1 statistics only)."""
+    _require_cuda(kv, gamma_min, gamma_scale)
+    sh = shape_of(kv)
+    _check("lynx_page_stats", lib().lynx_page_stats(
+        kv.data_ptr(), ctypes.byref(sh), ctypes.byref(p) if p else None,
+        gamma_min.data_ptr(), gamma_scale.data_ptr(), _stream(stream)))
+
+
+def block_stats(kv: torch.Tensor, gamma_min: torch.Tensor, gamma_scale: torch.Tensor,
+                mu: torch.Tensor, sigma: torch.Tensor, p: lynx_params | None = None,
+                stream=None):
+    """lynx_block_stats (Stage 2 statistics given Stage 1's)."""
+    _require_cuda(kv, gamma_min, gamma_scale, mu, sigma)
+    sh = shape_of(kv)
+    _check("lynx_block_stats", lib().lynx_block_stats(
+        kv.data_ptr(), ctypes.byref(sh), ctypes.byref(p) if p else None,
+        gamma_min.data_ptr(), gamma_scale.data_ptr(), mu.data_ptr(), sigma.data_ptr(),
+        _stream(stream)))

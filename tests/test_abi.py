@@ -1,0 +1,181 @@
+"""CPU tests of the C ABI (no GPU): the library loads and exports every
+symbol include/lynx.h declares, the host helpers, the compander threshold
+table against the oracle's decision, and argument errors that are rejected
+before any launch."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from progressive_kv_transfer_amd import lynx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lynx.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lynx_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = declared_symbols()
+    assert names == sorted(lynx.EXPORTS)
+    L = lynx.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", lynx.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (lynx_[a-z0-9_]+)", out))
+    assert set(names) <= exported
+
+
+def test_kv_bytes_eq1_worked_example():
+    """Eq. (1) with the paper's Qwen3-235B-A22B example (footnote 4):
+    2 x 94 x 131072 x (4 x 128) x 2 bytes = 23.5 GiB."""
+    import json
+    g = json.load(open(os.path.join(ROOT, "tests", "golden",
+                                    "kv_size_qwen3_235b_128k.json")))
+    n = lynx.kv_bytes(g["k_factor"], g["tokens"], g["kv_heads"] * g["head_dim"],
+                      g["layers"], g["precision_bytes"])
+    assert n == g["bytes"]
+    assert n / 2**30 == g["printed_gb"]
+    # Qwen-32B-shaped KV at 16K: 64 layers x 8 heads x 128 -> 4 GiB
+    assert lynx.kv_bytes(2, 16384, 1024, 64, 2) == 2**32
+    assert lynx.kv_bytes(1, 10, 10, 10, 2) == 2000  # MLA: K_factor 1
+    assert lynx.kv_bytes(-1, 1, 1, 1, 1) == 0
+    assert lynx.kv_bytes(2**40, 2**40, 1, 1, 1) == 0  # overflow
+
+
+def test_size_helpers_and_metadata_overhead():
+    """Stream and metadata sizes; the reading notes' metadata count of
+    2304 scalars (9 KB fp32) per 128 x 256 page."""
+    import json
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "metadata_overhead.json")))
+    s = lynx.lynx_kv_shape(num_tensors=128, tensor_stride=16384 * 1024,
+                           num_tokens=16384, num_channels=1024, row_stride=1024)
+    L = lynx.lib()
+    nb = lynx.num_blocks(s)
+    assert nb == 128 * 64 * 8
+    assert L.lynx_stream_bytes(ctypes.byref(s)) == nb * 16384
+    per_block = (L.lynx_gamma_floats(ctypes.byref(s)) * 2 +
+                 L.lynx_chunk_floats(ctypes.byref(s)) * 2) // nb
+    assert per_block == g["scalars"]
+    assert per_block * 4 == g["bytes_fp32"]
+
+
+@pytest.mark.parametrize("alpha,code_scale", [(255.0, 127.0), (100.0, 127.0),
+                                              (255.0, 120.0)])
+def test_compander_thresholds_match_oracle_decision(alpha, code_scale):
+    """Every threshold of the kernels' table is exactly the point where the
+    oracle's Eq. (3) code steps: code(thr[k]) >= k > code(pred(thr[k]))."""
+    thr = lynx.compander_thresholds(lynx.params(alpha=alpha, code_scale=code_scale))
+    assert thr[0] == 0.0
+    for k in range(1, 128):
+        t = float(thr[k])
+        if k > 120:
+            assert np.isinf(t)
+            continue
+        if np.isinf(t):
+            assert oracle.code(1.0, alpha, code_scale) < k
+            continue
+        prev = float(np.nextafter(np.float32(t), np.float32(0)))
+        assert oracle.code(t, alpha, code_scale) >= k
+        assert oracle.code(prev, alpha, code_scale) < k
+
+
+def _shape(nt=1, T=256, Ch=128, rs=None, ts=None):
+    rs = Ch if rs is None else rs
+    ts = T * rs if ts is None else ts
+    return lynx.lynx_kv_shape(num_tensors=nt, tensor_stride=ts, num_tokens=T,
+                              num_channels=Ch, row_stride=rs)
+
+
+FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced
+
+
+def _meta(ptr=FAKE):
+    m = lynx.lynx_meta()
+    m.gamma_min = m.gamma_scale = m.mu = m.sigma = ptr
+    return m
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("tokens", -2), ("channels", -2), ("row_stride", -2), ("row_stride_small", -2),
+    ("tensor_stride", -2), ("negative", -1), ("alpha", -1), ("alpha_nan", -1),
+    ("eps", -1), ("page", -1), ("chunk", -1), ("null_kv", -1), ("null_anchor", -1),
+    ("misaligned", -2), ("code_scale", -1)])
+def test_quantize_argument_errors(case, expect):
+    """Every malformed call returns its status before launching anything."""
+    L = lynx.lib()
+    s = _shape()
+    p = lynx.params()
+    kv, anc, res, meta = FAKE, FAKE, FAKE, _meta()
+    if case == "tokens":
+        s = _shape(T=300)
+    elif case == "channels":
+        s = _shape(Ch=192)
+    elif case == "row_stride":
+        s = _shape(rs=132)
+    elif case == "row_stride_small":
+        s = _shape(rs=64)
+    elif case == "tensor_stride":
+        s = _shape(nt=2, ts=1000)
+    elif case == "negative":
+        s = _shape(nt=-1)
+    elif case == "alpha":
+        p.alpha = 0.0
+    elif case == "alpha_nan":
+        p.alpha = float("nan")
+    elif case == "eps":
+        p.eps = 0.5
+    elif case == "page":
+        p.page_tokens = 128
+    elif case == "chunk":
+        p.chunk_tokens = 16
+    elif case == "code_scale":
+        p.code_scale = 200.0
+    elif case == "null_kv":
+        kv = None
+    elif case == "null_anchor":
+        anc = None
+    elif case == "misaligned":
+        kv = FAKE + 2
+    rc = L.lynx_quantize_pages(kv, ctypes.byref(s), ctypes.byref(p), anc, res, meta, None)
+    assert rc == expect
+    assert L.lynx_status_string(rc).decode()
+
+
+def test_dequant_and_stats_argument_errors():
+    L = lynx.lib()
+    s = _shape()
+    p = lynx.params()
+    assert L.lynx_dequant_full(FAKE, None, _meta(), ctypes.byref(s), None, FAKE, None) == -1
+    assert L.lynx_dequant_anchor(None, _meta(), ctypes.byref(s), None, FAKE, None) == -1
+    assert L.lynx_dequant_anchor(FAKE, _meta(None), ctypes.byref(s), None, FAKE, None) == -1
+    assert L.lynx_dequant_anchor(FAKE, _meta(), ctypes.byref(_shape(T=100)), None, FAKE,
+                                 None) == -2
+    assert L.lynx_dequant_full(FAKE, FAKE + 8, _meta(), ctypes.byref(s), None, FAKE,
+                               None) == -2
+    assert L.lynx_page_stats(FAKE, ctypes.byref(s), ctypes.byref(p), None, FAKE, None) == -1
+    assert L.lynx_block_stats(FAKE, ctypes.byref(s), None, FAKE, FAKE, None, FAKE,
+                              None) == -1
+    bad = lynx.params(eps=0.0)
+    assert L.lynx_page_stats(FAKE, ctypes.byref(s), ctypes.byref(bad), FAKE, FAKE,
+                             None) == -1
+
+
+def test_empty_shapes_are_no_ops():
+    """Zero tensors / tokens / channels: nothing to do, OK without touching
+    any pointer."""
+    L = lynx.lib()
+    for s in (_shape(nt=0), _shape(T=0), _shape(Ch=0, rs=0)):
+        assert L.lynx_quantize_pages(None, ctypes.byref(s), None, None, None, _meta(None),
+                                     None) == 0
+        assert L.lynx_dequant_anchor(None, _meta(None), ctypes.byref(s), None, None,
+                                     None) == 0
