@@ -1,0 +1,237 @@
+"""Benchmark of the Lynx split-stream KV codec on one MI355X.
+
+One step = the whole hot path over the Qwen-32B-shaped KV set at 16K
+context (64 layers x {K, V} x 16384 tokens x 1024 channels, bf16, 4 GiB,
+seeded synthetic values, resident in HBM before timing):
+    quantize + split (lynx_quantize_pages)
+ -> anchor-only reconstruction (lynx_dequant_anchor)
+ -> anchor + residual reconstruction (lynx_dequant_full)
+
+Prints ONE JSON line.  value = bf16 KV bytes through the whole path per
+second (2 bytes x elements / step time).  Per-kernel times come from HIP
+events recorded on the launch stream around every launch of the timed
+steps; `roofline` reports the dominant kernel's algorithmic bytes per launch
+over its average launch time against the 8 TB/s HBM peak.  `cpu_baseline`
+times the CPU oracle (test infrastructure, never tuned) on a bounded sample
+of the same workload on this host.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --profile-run      # a few steps only, for rocprofv3
+    python bench.py --copy-probe       # plain 1 GiB copy, PMC scale factor
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "quantize+split and dequant GB/s of bf16 KV (1 GPU) + % of HBM peak"
+WORKLOAD = "qwen32b_16k"
+
+# Algorithmic HBM bytes per bf16 element (one page block of 32768 elements
+# moves 64 KiB of bf16, 16 KiB per 4-bit stream and 9 KiB of metadata).
+BYTES_PER_ELEM = {
+    "quantize": 2.0 + 0.5 + 0.5 + 0.28125,
+    "dequant_anchor": 0.5 + 0.28125 + 2.0,
+    "dequant_full": 0.5 + 0.5 + 0.28125 + 2.0,
+}
+KERNEL_SYMBOL = {
+    "quantize": "quant_kernel<0>",
+    "dequant_anchor": "dequant_kernel<false>",
+    "dequant_full": "dequant_kernel<true>",
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qwen32b_16k.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("lynx_quant.hip", "lynx_dequant.hip", "lynx_internal.h"):
+        with open(os.path.join(ROOT, "progressive_kv_transfer_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str):
+    """Measured HBM bytes per launch from the committed PMC summary, or
+    None if absent or taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def cpu_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def run_cpu_baseline(cfg, kv_dev, budget_s: float):
+    """Oracle quantize + both dequants, tensor by tensor, until ~budget_s."""
+    import oracle
+    from progressive_kv_transfer_amd import kvgen
+
+    th = cpu_threads()
+    oracle.lib()
+    done, elems, t_total = 0, 0, 0.0
+    while done < kv_dev.shape[0]:
+        xb = kvgen.bf16_bits(kv_dev[done:done + 1])
+        t0 = time.perf_counter()
+        c = oracle.quantize(xb, threads=th)
+        oracle.dequant(c, xb.shape, False, threads=th)
+        oracle.dequant(c, xb.shape, True, threads=th)
+        t_total += time.perf_counter() - t0
+        done += 1
+        elems += xb.size
+        if t_total >= budget_s:
+            break
+    gbps = 2.0 * elems / t_total / 1e9
+    return {"value": round(gbps, 4), "unit": "GB/s", "cores": th, "kind": "oracle",
+            "sample": (f"first {done} of {kv_dev.shape[0]} tensors (K/V of layers "
+                       f"0..{(done - 1) // 2}) of {cfg.name}: {elems} elements, "
+                       f"{t_total:.1f} s wall, quantize + anchor dequant + full dequant")}
+
+
+def copy_probe():
+    """A plain device copy of known size, for scaling PMC byte counters."""
+    import torch
+    n = 1 << 29  # 1 GiB of int16
+    a = torch.ones(n, dtype=torch.int16, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": 2 * n, "copy_probe_bytes_written": 2 * n}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--profile-run", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one MI355X: the codec's page blocks are independent and "
+              "this build runs on a single GPU only (--gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_probe:
+        copy_probe()
+        return
+    if args.profile_run:
+        args.steps, args.warmup, args.no_cpu_baseline = 3, 1, True
+
+    import torch
+    from progressive_kv_transfer_amd import kvgen, lynx
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    lynx.lib()
+    cfg = kvgen.CONFIGS[WORKLOAD]
+    dev = "cuda"
+    kv = cfg.make(dev)
+    n_elem = kv.numel()
+    nb = n_elem // (256 * 128)
+    codes = lynx.alloc_codes(nb, dev)
+    out_a = torch.empty_like(kv)
+    out_f = torch.empty_like(kv)
+    p = lynx.params()
+    stream = torch.cuda.current_stream()
+
+    names = ["quantize", "dequant_anchor", "dequant_full"]
+
+    def step(evs=None):
+        if evs:
+            evs[0].record(stream)
+        lynx.quantize_pages(kv, p, out=codes, stream=stream)
+        if evs:
+            evs[1].record(stream)
+        lynx.dequant_anchor(codes, out_a, p, stream=stream)
+        if evs:
+            evs[2].record(stream)
+        lynx.dequant_full(codes, out_f, p, stream=stream)
+        if evs:
+            evs[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per = {n: [] for n in names}
+    for ev in events:
+        for i, n in enumerate(names):
+            per[n].append(ev[i].elapsed_time(ev[i + 1]))
+    kern = {}
+    for n in names:
+        ms = sum(per[n]) / len(per[n])
+        algo = BYTES_PER_ELEM[n] * n_elem / (ms * 1e-3) / 1e9
+        kern[n] = {"ms": round(ms, 4), "bf16_GBps": round(2.0 * n_elem / (ms * 1e-3) / 1e9, 1),
+                   "algo_GBps": round(algo, 1), "hbm_frac": round(algo / HBM_PEAK_GBPS, 4)}
+    ms_step = wall / args.steps * 1e3
+    value = 2.0 * n_elem / (wall / args.steps) / 1e9
+    dom = max(names, key=lambda n: kern[n]["ms"])
+    achieved = kern[dom]["algo_GBps"]
+    traffic = load_traffic(dom)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded per-channel Laplacian KV with x100 outlier channels and "
+                "x20 bursts, bf16)",
+        "config": {"workload": WORKLOAD, "layers": cfg.layers, "tensors": cfg.num_tensors,
+                   "tokens": cfg.num_tokens, "channels": cfg.num_channels,
+                   "page_tokens": 256, "chunk_tokens": 32, "head_channels": 128,
+                   "alpha": 255.0, "eps": 1e-6, "code_scale": 127.0,
+                   "kv_bf16_bytes": 2 * n_elem, "step": "quantize+anchor_dequant+full_dequant"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None if traffic is None else int(traffic),
+                     "algorithmic_bytes_per_launch": int(BYTES_PER_ELEM[dom] * n_elem)},
+        "kernels": kern,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = run_cpu_baseline(cfg, kv, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
