@@ -18,6 +18,7 @@ of the same workload on this host.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --profile-run      # a few steps only, for rocprofv3
     python bench.py --copy-probe       # plain 1 GiB copy, PMC scale factor
+    python bench.py --hbm-probe        # timed copy / read / write bandwidths
 """
 from __future__ import annotations
 
@@ -107,8 +108,10 @@ def run_cpu_baseline(cfg, kv_dev, budget_s: float):
                        f"{t_total:.1f} s wall, quantize + anchor dequant + full dequant")}
 
 
-def copy_probe():
-    """A plain device copy of known size, for scaling PMC byte counters."""
+def copy_probe(timed: bool = False):
+    """A plain device copy of 1 GiB (PMC byte-counter scale factor); with
+    `timed`, also the achieved copy, read-only and write-only bandwidths on
+    4 GiB buffers (a practical streaming ceiling beside the 8 TB/s peak)."""
     import torch
     n = 1 << 29  # 1 GiB of int16
     a = torch.ones(n, dtype=torch.int16, device="cuda")
@@ -116,7 +119,31 @@ def copy_probe():
     for _ in range(3):
         b.copy_(a)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_probe_bytes_read": 2 * n, "copy_probe_bytes_written": 2 * n}))
+    out = {"copy_probe_bytes_read": 2 * n, "copy_probe_bytes_written": 2 * n}
+    if timed:
+        del a, b
+        m = 1 << 31  # 4 GiB of int16
+        a = torch.ones(m, dtype=torch.int16, device="cuda")
+        b = torch.empty_like(a)
+
+        def timeit(fn, reps=10):
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps * 1e-3
+
+        t = timeit(lambda: b.copy_(a))
+        out["copy_GBps"] = round(2 * 2 * m / t / 1e9, 1)
+        t = timeit(lambda: torch.sum(a, dtype=torch.int64))
+        out["read_GBps"] = round(2 * m / t / 1e9, 1)
+        t = timeit(lambda: b.fill_(3))
+        out["write_GBps"] = round(2 * m / t / 1e9, 1)
+    print(json.dumps(out))
 
 
 def main():
@@ -128,14 +155,15 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--profile-run", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--hbm-probe", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one MI355X: the codec's page blocks are independent and "
               "this build runs on a single GPU only (--gpus 1).", file=sys.stderr)
         sys.exit(2)
-    if args.copy_probe:
-        copy_probe()
+    if args.copy_probe or args.hbm_probe:
+        copy_probe(timed=args.hbm_probe)
         return
     if args.profile_run:
         args.steps, args.warmup, args.no_cpu_baseline = 3, 1, True

@@ -26,11 +26,13 @@
  *               + head.  Every per-block output below is stored at block b.
  *
  * Stream and metadata layouts (all outputs are plain device buffers)
- *   anchor      uint8 [nblocks][P][H/2]: per token row, byte k holds the
+ *   anchor      uint8 [nblocks][P/C][H/2][C], chunk-tiled: byte
+ *               [b][j][k][i] holds token 32 j + i of channel pair k, the
  *               4-bit two's-complement anchor of channel 2k in its low
  *               nibble and of channel 2k+1 in its high nibble.  16384 bytes
- *               per block, blocks back to back: one contiguous stream.
- *   residual    uint8 [nblocks][P][H/2], same nibble layout, 4-bit signed
+ *               per block, each chunk one 2048-byte tile, blocks back to
+ *               back: one contiguous stream.
+ *   residual    uint8 [nblocks][P/C][H/2][C], same layout, 4-bit signed
  *               residual (code = (anchor magnitude << 4) - residual).
  *   gamma_min, gamma_scale   float32 [nblocks][H]
  *   mu, sigma               float32 [nblocks][P/C][H]

@@ -141,8 +141,9 @@ class BlockResult:
 
     def __init__(self, H, P, C):
         nch = P // C
-        self.anchor = np.zeros((P, H // 2), np.uint8)
-        self.residual = np.zeros((P, H // 2), np.uint8)
+        # chunk-tiled streams: [chunk][channel pair][token of the chunk]
+        self.anchor = np.zeros((nch, H // 2, C), np.uint8)
+        self.residual = np.zeros((nch, H // 2, C), np.uint8)
         self.gamma_min = np.zeros(H, np.float32)
         self.gamma_scale = np.zeros(H, np.float32)
         self.mu = np.zeros((nch, H), np.float32)
@@ -173,8 +174,8 @@ def quantize_block(x_bf16: np.ndarray, alpha=255.0, eps=1e-6, code_scale=127.0,
 def dequant_block(r: BlockResult, full: bool, alpha=255.0, eps=1e-6,
                   code_scale=127.0, C=C_DEFAULT) -> np.ndarray:
     """Reconstruct a block from its codes: anchor-only or anchor + residual."""
-    P, Hh = r.anchor.shape
-    H = Hh * 2
+    nch, Hh, C = r.anchor.shape
+    P, H = nch * C, Hh * 2
     out = np.zeros((P, H), np.uint16)
     rc = lib().oracle_dequant_block(
         _ptr(r.anchor), _ptr(r.residual) if full else None, _ptr(r.gamma_min),
@@ -192,8 +193,8 @@ class Codes:
 
     def __init__(self, nblocks, H=H_DEFAULT, P=P_DEFAULT, C=C_DEFAULT):
         self.nblocks = nblocks
-        self.anchor = np.zeros((nblocks, P, H // 2), np.uint8)
-        self.residual = np.zeros((nblocks, P, H // 2), np.uint8)
+        self.anchor = np.zeros((nblocks, P // C, H // 2, C), np.uint8)
+        self.residual = np.zeros((nblocks, P // C, H // 2, C), np.uint8)
         self.gamma_min = np.zeros((nblocks, H), np.float32)
         self.gamma_scale = np.zeros((nblocks, H), np.float32)
         self.mu = np.zeros((nblocks, P // C, H), np.float32)

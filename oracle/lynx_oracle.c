@@ -34,8 +34,10 @@
  *   - denormalisation is the literal inverse of lines "X_final" then
  *     "X <- (X - gamma_min) / (gamma_scale + eps)", four roundings, then
  *     bf16 round-to-nearest-even;
- *   - nibble packing: token-major rows, byte k of a row holds channel 2k in
- *     its low nibble and channel 2k+1 in its high nibble.
+ *   - nibble packing: two channels per byte (channel 2k in the low nibble,
+ *     2k+1 in the high nibble), one byte per token; bytes are chunk-tiled,
+ *     [chunk j][channel pair k][token i of the chunk], so every chunk of a
+ *     page block is one contiguous (H/2) x C byte tile.
  */
 #include <math.h>
 #include <stdint.h>
@@ -165,7 +167,8 @@ static int is_pow2(int n) { return n > 0 && (n & (n - 1)) == 0; }
  * (channel c, token t) is x[t * row_stride + c] (bfloat16 bits).
  *
  * Outputs (all caller-owned):
- *   anchor, residual : P rows of H/2 bytes (packed nibbles, see header);
+ *   anchor, residual : P * H / 2 bytes each (packed nibbles, chunk-tiled,
+ *                      see header);
  *   gamma_min, gamma_scale : H floats;
  *   mu, sigma : (P/C) x H floats, chunk-major ([chunk][channel]).
  * Optional intermediates (NULL to skip), each H x P, channel-major
@@ -250,15 +253,19 @@ int oracle_quantize_block_ex(const uint16_t *x, int64_t row_stride, int H,
             memcpy(xcent_out + (size_t)c * P, xc, sizeof(float) * (size_t)P);
     }
 
-    /* Packing: two's-complement nibbles, even channel in the low nibble. */
+    /* Packing: two's-complement nibbles, even channel in the low nibble,
+     * chunk-tiled: for chunk j, channel pair k, token i of the chunk, the
+     * byte sits at j * (H / 2) * C + k * C + i. */
     for (int t = 0; t < P; ++t) {
+        const int j = t / C, i = t % C;
         for (int k = 0; k < H / 2; ++k) {
             unsigned a0 = (unsigned)qa[(size_t)t * H + 2 * k] & 0xfu;
             unsigned a1 = (unsigned)qa[(size_t)t * H + 2 * k + 1] & 0xfu;
             unsigned r0 = (unsigned)qr[(size_t)t * H + 2 * k] & 0xfu;
             unsigned r1 = (unsigned)qr[(size_t)t * H + 2 * k + 1] & 0xfu;
-            anchor[(size_t)t * (H / 2) + k] = (uint8_t)(a0 | (a1 << 4));
-            residual[(size_t)t * (H / 2) + k] = (uint8_t)(r0 | (r1 << 4));
+            size_t off = ((size_t)j * (H / 2) + k) * C + i;
+            anchor[off] = (uint8_t)(a0 | (a1 << 4));
+            residual[off] = (uint8_t)(r0 | (r1 << 4));
         }
     }
     free(xn); free(xc); free(qa); free(qr);
@@ -286,11 +293,12 @@ int oracle_dequant_block(const uint8_t *anchor, const uint8_t *residual,
     for (int t = 0; t < P; ++t) {
         int j = t / C;
         for (int c = 0; c < H; ++c) {
-            unsigned ab = anchor[(size_t)t * (H / 2) + c / 2];
+            size_t off = ((size_t)j * (H / 2) + c / 2) * C + (t % C);
+            unsigned ab = anchor[off];
             unsigned an = (c & 1) ? (ab >> 4) : (ab & 0xfu);
             unsigned rn = 0;
             if (residual) {
-                unsigned rb = residual[(size_t)t * (H / 2) + c / 2];
+                unsigned rb = residual[off];
                 rn = (c & 1) ? (rb >> 4) : (rb & 0xfu);
             }
             int s;

@@ -45,6 +45,8 @@ def build(verbose: bool = False, isa_dir: str | None = None) -> str:
     With ``isa_dir`` the gfx950 assembly of each device source is also
     written there (for instruction counts)."""
     tmp = tempfile.mkdtemp(prefix="lynx_build_")
+    if isa_dir:
+        isa_dir = os.path.abspath(isa_dir)
     try:
         objs = []
         for src in DEVICE_SOURCES:

@@ -12,10 +12,12 @@
 // four binary32 roundings, then bf16 round-to-nearest-even
 // (v_cvt_pk_bf16_f32).
 //
-// Lane mapping as in the quantize kernel: wave w = chunk w, lane 16 s + g
-// owns channels 8g..8g+7 of tokens 32w + 8s .. +7, so every lane needs the
-// metadata of 8 channels of one chunk only and writes 16-byte row pieces
-// that 16 lanes join into one 256-byte row.
+// Lane mapping: wave w = chunk w, lane 16 s + g owns channels 8g..8g+7 of
+// tokens 32w + 8s .. +7, so every lane needs the metadata of 8 channels of
+// one chunk only and writes 16-byte row pieces that 16 lanes join into one
+// 256-byte row.  Its codes are four 8-byte runs of the chunk-tiled streams
+// (one per channel pair); the 64 lanes of a wave read each 128-byte line of
+// the chunk's tile completely.
 #include "lynx_internal.h"
 
 namespace lynx {
@@ -24,6 +26,7 @@ namespace {
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
     f32x2 v = {lo, hi};
@@ -40,7 +43,7 @@ __global__ __launch_bounds__(512) void dequant_kernel(
     constexpr int kLut = FULL ? 256 : 16;
     __shared__ float s_lut[kLut];
 
-    const int64_t b = g.block0 + blockIdx.x;
+    const int64_t b = g.block0 + __builtin_amdgcn_workgroup_id_x();
     const int head = (int)(b % g.heads);
     const int64_t tp = b / g.heads;
     const int page = (int)(tp % g.pages);
@@ -48,21 +51,23 @@ __global__ __launch_bounds__(512) void dequant_kernel(
     uint16_t *obase =
         out + tensor * g.tensor_stride + (int64_t)page * kPage * g.row_stride + head * kHead;
 
-    const int tid = threadIdx.x;
+    const int tid = (int)__builtin_amdgcn_workitem_id_x();
     const int wave = tid >> 6;
     const int lane = tid & 63;
     const int cg = lane & 15;
     const int s = lane >> 4;
     const int tok0 = wave * kChunk + s * 8;
 
-    const uint32_t *anc = (const uint32_t *)(anchor + b * (kPage * kHead / 2));
-    const uint32_t *res = (const uint32_t *)(residual + b * (kPage * kHead / 2));
-    uint32_t A[8], R[8];
+    // Chunk-tiled streams: the 8 bytes of channel pair 4 cg + k for tokens
+    // 32 wave + 8 s .. + 7 sit at [chunk wave][pair][8 s].
+    const int64_t coff = b * (kPage * kHead / 2) + wave * (kHead / 2 * kChunk) +
+                         (4 * cg) * kChunk + 8 * s;
+    u32x2 A[4], R[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        A[i] = __builtin_nontemporal_load(anc + (tok0 + i) * (kHead / 8) + cg);
+    for (int k = 0; k < 4; ++k) {
+        A[k] = __builtin_nontemporal_load((const u32x2 *)(anchor + coff + k * kChunk));
         if (FULL)
-            R[i] = __builtin_nontemporal_load(res + (tok0 + i) * (kHead / 8) + cg);
+            R[k] = __builtin_nontemporal_load((const u32x2 *)(residual + coff + k * kChunk));
     }
     const float4 *gm4 = (const float4 *)(gmin + b * kHead + cg * 8);
     const float4 *gs4 = (const float4 *)(gscale + b * kHead + cg * 8);
@@ -97,22 +102,30 @@ __global__ __launch_bounds__(512) void dequant_kernel(
     }
     __syncthreads();
 
+    // idx[i][e]: table index of token i, channel e of the lane's 8.
+    uint32_t ev[4][2], od[4][2];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            // byte i of ev / od = (anchor nibble) | (residual nibble << 4)
+            // of channel 2k / 2k+1 at token 4h + i.
+            if (FULL) {
+                ev[k][h] = (A[k][h] & 0x0f0f0f0fu) | ((R[k][h] << 4) & 0xf0f0f0f0u);
+                od[k][h] = ((A[k][h] >> 4) & 0x0f0f0f0fu) | (R[k][h] & 0xf0f0f0f0u);
+            } else {
+                ev[k][h] = A[k][h] & 0x0f0f0f0fu;
+                od[k][h] = (A[k][h] >> 4) & 0x0f0f0f0fu;
+            }
+        }
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         uint32_t idx[8];
-        if (FULL) {
-            // byte j of ev / od = (anchor nibble) | (residual nibble << 4) of
-            // channel 2j / 2j+1.
-            uint32_t ev = (A[i] & 0x0f0f0f0fu) | ((R[i] << 4) & 0xf0f0f0f0u);
-            uint32_t od = ((A[i] >> 4) & 0x0f0f0f0fu) | (R[i] & 0xf0f0f0f0u);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                idx[2 * j] = (ev >> (8 * j)) & 0xffu;
-                idx[2 * j + 1] = (od >> (8 * j)) & 0xffu;
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) idx[e] = (A[i] >> (4 * e)) & 0xfu;
+        for (int k = 0; k < 4; ++k) {
+            idx[2 * k] = (ev[k][i >> 2] >> (8 * (i & 3))) & 0xffu;
+            idx[2 * k + 1] = (od[k][i >> 2] >> (8 * (i & 3))) & 0xffu;
         }
         float y[8];
 #pragma unroll

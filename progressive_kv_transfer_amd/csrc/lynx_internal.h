@@ -48,8 +48,12 @@ struct Geometry {
     int32_t heads;          // 128-channel groups per tensor
     int64_t nblocks;        // blocks in this launch
     int64_t block0;         // global index of the launch's first block
+    int64_t grid_wgs;       // workgroups of a persistent launch
 };
 
+// Block and lane indices come from the amdgcn intrinsics: the kernels are
+// built with IEEE mode off, so the device library's index helpers (built
+// with it on) would not be inlined.
 enum StatsMode : int { kModeQuantize = 0, kModePageStats = 1, kModeBlockStats = 2 };
 
 hipError_t launch_quantize(const uint16_t *kv, const Geometry &g, const QuantTab &tab,

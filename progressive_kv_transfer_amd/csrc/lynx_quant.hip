@@ -8,13 +8,16 @@
 // The same kernel body, cut short, gives the Stage 1 and Stage 2
 // statistics on their own.
 //
-// Workgroup = 512 lanes = 8 wave64s.  Wave w owns chunk w (tokens
-// 32w..32w+31); inside a wave, lane = 16 s + g owns channels 8g..8g+7 of
-// tokens 32w + 8s .. 32w + 8s + 7.  Every token row of the block is 256
-// contiguous bytes, so each 16-byte load of a row group is one fully used
-// 256-byte segment per 16 lanes.  Reductions over the 4 lanes of a chunk use
-// v_permlane16_swap / v_permlane32_swap (no LDS); the 8 waves of a page meet
-// once in LDS.
+// Each lane owns one whole 32-token chunk of a channel pair (64 values), so
+// the chunk mean and max |X - mu| need no cross-lane traffic and every
+// per-channel cost is spread over 32 tokens.  A workgroup of 256 lanes
+// covers half a page block (64 channels x 256 tokens); its lanes meet once
+// in LDS for the page minimum / maximum.  Rows are read with buffer loads
+// (scalar row offsets): 32 lanes x 4 bytes = one 128-byte line per row.
+// The anchor and residual bytes of a lane are 32 contiguous bytes of the
+// chunk-tiled stream layout, so a workgroup writes whole cache lines that no
+// other workgroup touches.  Workgroups are persistent (grid = resident
+// workgroups) and build the compander table in LDS once.
 //
 // Arithmetic is binary32 with one rounding per operation (built with
 // -ffp-contract=off).  The two divisions of Algorithm 1 use
@@ -30,6 +33,7 @@ namespace lynx {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -41,280 +45,294 @@ __device__ __forceinline__ float div_fast(float a, float d, float r) {
     return __builtin_fmaf(e, r, q);
 }
 
-// Pairwise combination across lane rows: after permlane16_swap with both
-// operands = v, the pair holds (row 2k, row 2k+1) of v; after
-// permlane32_swap it holds (lanes 0-31, lanes 32-63).
-struct Pair {
-    float a, b;
-};
-__device__ __forceinline__ Pair swap16(float v) {
-    auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return {__uint_as_float(p[0]), __uint_as_float(p[1])};
-}
-__device__ __forceinline__ Pair swap32(float v) {
-    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return {__uint_as_float(p[0]), __uint_as_float(p[1])};
-}
-
 constexpr float kTiny100 = 0x1p-100f;
 constexpr float kTiny125 = 0x1p-125f;
 constexpr float kHuge125 = 0x1p125f;
 constexpr float kMuTiny = 0x1p-74f;
 
+// Lane tile: 2 channels x 32 tokens, i.e. one whole chunk of a channel
+// pair.  A work unit is half a page block (64 channels x 256 tokens;
+// statistics are per channel, so the halves are independent); unit u is
+// half (u & 1) of block block0 + (u >> 1).  A workgroup (4 wave64s) walks
+// units u = workgroup, workgroup + grid, ... so the compander table is
+// built once per workgroup.
+constexpr int kHalf = kHead / 2;        // channels per unit
+constexpr int kPairs = kHalf / 2;       // channel pairs per unit (lanes per chunk)
+constexpr int kThreads = kPairs * kChunks;  // 256
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, 0x7fffffff,
+                                             0x00020000);
+}
+
 template <int MODE>
-__global__ __launch_bounds__(512) void quant_kernel(const uint16_t *__restrict__ kv, Geometry g,
-                                                    const QuantTab tab,
-                                                    uint8_t *__restrict__ anchor,
-                                                    uint8_t *__restrict__ residual,
-                                                    float *__restrict__ gmin_io,
-                                                    float *__restrict__ gscale_io,
-                                                    float *__restrict__ mu_out,
-                                                    float *__restrict__ sigma_out) {
-    __shared__ float s_min[kChunks][kHead];
-    __shared__ float s_max[kChunks][kHead];
-    __shared__ float4 s_ch[kHead];  // gamma_min, d1, r1, slow flag
-    __shared__ uint2 s_tab[MODE == kModeQuantize ? kMaxBuckets : 1];
+__global__ __launch_bounds__(kThreads) void quant_kernel(
+    const uint16_t *__restrict__ kv, Geometry g, const QuantTab tab,
+    uint8_t *__restrict__ anchor, uint8_t *__restrict__ residual, float *__restrict__ gmin_io,
+    float *__restrict__ gscale_io, float *__restrict__ mu_out, float *__restrict__ sigma_out) {
+    __shared__ float2 s_min[kChunks][kPairs];
+    __shared__ float2 s_max[kChunks][kPairs];
+    __shared__ float4 s_ch[kHalf];  // gamma_min, d1, r1, slow flag
+    __shared__ u32x2 s_tab[MODE == kModeQuantize ? kMaxBuckets : 1];
 
-    const int64_t b = g.block0 + blockIdx.x;
-    const int head = (int)(b % g.heads);
-    const int64_t tp = b / g.heads;
-    const int page = (int)(tp % g.pages);
-    const int64_t tensor = tp / g.pages;
-    const uint16_t *base =
-        kv + tensor * g.tensor_stride + (int64_t)page * kPage * g.row_stride + head * kHead;
+    const int tid = (int)__builtin_amdgcn_workitem_id_x();
+    const int p = tid & (kPairs - 1);  // channel pair: channels 2p, 2p+1 of the unit
+    const int j = tid / kPairs;        // chunk: tokens 32 j .. 32 j + 31
 
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6;
-    const int lane = tid & 63;
-    const int cg = lane & 15;
-    const int s = lane >> 4;
-    const int tok0 = wave * kChunk + s * 8;
-
-    // ---- load 8 token rows x 8 channels (16 B per row) ------------------
-    u32x4 raw[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        raw[i] = __builtin_nontemporal_load(
-            (const u32x4 *)(base + (int64_t)(tok0 + i) * g.row_stride + cg * 8));
-
-    // Compander table into LDS while the loads are in flight.
+    // Compander table into LDS, once per workgroup.
     if (MODE == kModeQuantize) {
-        for (int i = tid; i < tab.nbuckets; i += 512) {
+        for (int i = tid; i < tab.nbuckets; i += kThreads) {
             uint32_t c = tab.bucket_code[i];
-            s_tab[i] = make_uint2(__float_as_uint(tab.thr[c + 1]), c + 7u);
+            s_tab[i] = u32x2{__float_as_uint(tab.thr[c + 1]), c + 7u};
         }
     }
+    typedef __attribute__((address_space(3))) const u32x2 lds_u32x2;
+    const float mag_lo = __uint_as_float((uint32_t)tab.bucket_lo << tab.shift);
+    const uint32_t sh = (uint32_t)tab.shift;
+    const uint32_t tab_base = (uint32_t)(uintptr_t)(lds_u32x2 *)s_tab -
+                              (uint32_t)tab.bucket_lo * (uint32_t)sizeof(u32x2);
+    const uint32_t row_bytes = (uint32_t)g.row_stride * 2u;
+    const int64_t nunits = 2 * g.nblocks;
 
-    float x[8][8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            x[i][2 * k] = bf16_lo(raw[i][k]);
-            x[i][2 * k + 1] = bf16_hi(raw[i][k]);
-        }
-    }
+    for (int64_t u = __builtin_amdgcn_workgroup_id_x(); u < nunits;
+         u += g.grid_wgs) {
+        const int64_t b = g.block0 + (u >> 1);
+        const int half = (int)(u & 1);
+        const int head = (int)(b % g.heads);
+        const int64_t tp = b / g.heads;
+        const int page = (int)(tp % g.pages);
+        const int64_t tensor = tp / g.pages;
+        const uint16_t *base = kv + tensor * g.tensor_stride +
+                               (int64_t)page * kPage * g.row_stride + head * kHead +
+                               half * kHalf;
+        const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(base);
+        const int64_t meta0 = b * kHead + half * kHalf;
+        const int64_t cmeta0 = b * (kChunks * kHead) + j * kHead + half * kHalf;
 
-    // ---- phase 1: page statistics --------------------------------------
-    if (MODE != kModeBlockStats) {
-        float mn[8], mx[8];
+        // ---- load 32 token rows x 2 channels (4 B per row) ---------------
+        const uint32_t voff = (uint32_t)(j * kChunk) * row_bytes + (uint32_t)p * 4u;
+        uint32_t raw[kChunk];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            mn[e] = x[0][e];
-            mx[e] = x[0][e];
+        for (int i = 0; i < kChunk; ++i)
+            raw[i] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, voff, i * row_bytes, 0);
+        float x[kChunk][2];
 #pragma unroll
-            for (int i = 1; i < 8; ++i) {
-                mn[e] = fminf(mn[e], x[i][e]);
-                mx[e] = fmaxf(mx[e], x[i][e]);
-            }
-            Pair p = swap16(mn[e]);
-            mn[e] = fminf(p.a, p.b);
-            p = swap32(mn[e]);
-            mn[e] = fminf(p.a, p.b);
-            p = swap16(mx[e]);
-            mx[e] = fmaxf(p.a, p.b);
-            p = swap32(mx[e]);
-            mx[e] = fmaxf(p.a, p.b);
+        for (int i = 0; i < kChunk; ++i) {
+            x[i][0] = bf16_lo(raw[i]);
+            x[i][1] = bf16_hi(raw[i]);
         }
-        if (s == 0) {
+
+        // ---- phase 1: page statistics ------------------------------------
+        if (MODE != kModeBlockStats) {
+            float mn[2], mx[2];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                s_min[wave][cg * 8 + e] = mn[e];
-                s_max[wave][cg * 8 + e] = mx[e];
+            for (int e = 0; e < 2; ++e) {
+                mn[e] = x[0][e];
+                mx[e] = x[0][e];
+#pragma unroll
+                for (int i = 1; i < kChunk; ++i) {
+                    mn[e] = fminf(mn[e], x[i][e]);
+                    mx[e] = fmaxf(mx[e], x[i][e]);
+                }
             }
+            s_min[j][p] = make_float2(mn[0], mn[1]);
+            s_max[j][p] = make_float2(mx[0], mx[1]);
         }
         __syncthreads();
-    }
-    if (tid < kHead) {
-        float gmin, gsc;
-        if (MODE == kModeBlockStats) {
-            gmin = gmin_io[b * kHead + tid];
-            gsc = gscale_io[b * kHead + tid];
-        } else {
-            float a = s_min[0][tid], m = s_max[0][tid];
+        if (tid < kHalf) {
+            float gmin, gsc;
+            if (MODE == kModeBlockStats) {
+                gmin = gmin_io[meta0 + tid];
+                gsc = gscale_io[meta0 + tid];
+            } else {
+                const float *mn = (const float *)&s_min[0][0] + tid;
+                const float *mx = (const float *)&s_max[0][0] + tid;
+                float a = mn[0], m = mx[0];
 #pragma unroll
-            for (int w = 1; w < kChunks; ++w) {
-                a = fminf(a, s_min[w][tid]);
-                m = fmaxf(m, s_max[w][tid]);
+                for (int w = 1; w < kChunks; ++w) {
+                    a = fminf(a, mn[w * kHalf]);
+                    m = fmaxf(m, mx[w * kHalf]);
+                }
+                gmin = a + 0.0f;  // canonical +0 for a zero minimum
+                gsc = m - gmin;
+                gmin_io[meta0 + tid] = gmin;
+                gscale_io[meta0 + tid] = gsc;
             }
-            gmin = a + 0.0f;  // canonical +0 for a zero minimum
-            gsc = m - gmin;
-            gmin_io[b * kHead + tid] = gmin;
-            gscale_io[b * kHead + tid] = gsc;
+            float d1 = gsc + tab.eps;
+            float r1 = __fdiv_rn(1.0f, d1);
+            // Every nonzero x - gamma_min of a bf16 channel is at least
+            // 2^-9 |gamma_min|; the fast division needs it above the bound.
+            bool fast = gmin != 0.0f &&
+                        fabsf(gmin) * 0x1p-9f >= fmaxf(kTiny100, d1 * kTiny125) &&
+                        d1 < kHuge125;
+            s_ch[tid] = make_float4(gmin, d1, r1, fast ? 0.0f : 1.0f);
         }
-        float d1 = gsc + tab.eps;
-        float r1 = __fdiv_rn(1.0f, d1);
-        // Every nonzero x - gamma_min of a bf16 channel is at least
-        // 2^-9 |gamma_min|; the fast division needs it above the bound.
-        bool fast = gmin != 0.0f && fabsf(gmin) * 0x1p-9f >= fmaxf(kTiny100, d1 * kTiny125) &&
-                    d1 < kHuge125;
-        s_ch[tid] = make_float4(gmin, d1, r1, fast ? 0.0f : 1.0f);
-    }
-    if (MODE == kModePageStats)
-        return;
-    __syncthreads();
-
-    // ---- phase 2: normalise, chunk mean and max |X - mu| ----------------
-    float gmin[8], d1[8], r1[8];
-    bool slow1 = false;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        float4 c = s_ch[cg * 8 + e];
-        gmin[e] = c.x;
-        d1[e] = c.y;
-        r1[e] = c.z;
-        slow1 |= c.w != 0.0f;
-    }
-    if (!slow1) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[i][e] = div_fast(x[i][e] - gmin[e], d1[e], r1[e]);
-    } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[i][e] = __fdiv_rn(x[i][e] - gmin[e], d1[e]);
-    }
-
-    float mu[8], sg[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        // balanced tree: tokens 8s..8s+7 in-lane, then rows, then halves
-        float s8 = ((x[0][e] + x[1][e]) + (x[2][e] + x[3][e])) +
-                   ((x[4][e] + x[5][e]) + (x[6][e] + x[7][e]));
-        Pair p = swap16(s8);
-        float s16 = p.a + p.b;
-        p = swap32(s16);
-        float s32 = p.a + p.b;
-        mu[e] = s32 * 0.03125f;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        float m = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            x[i][e] = x[i][e] - mu[e];
-            m = fmaxf(m, fabsf(x[i][e]));
+        if (MODE == kModePageStats) {
+            __syncthreads();  // s_min is rewritten by the next unit
+            continue;
         }
-        Pair p = swap16(m);
-        m = fmaxf(p.a, p.b);
-        p = swap32(m);
-        sg[e] = fmaxf(p.a, p.b);
-    }
-    if (s == 0) {
-        float4 *mo = (float4 *)(mu_out + b * (kChunks * kHead) + wave * kHead + cg * 8);
-        float4 *so = (float4 *)(sigma_out + b * (kChunks * kHead) + wave * kHead + cg * 8);
-        mo[0] = make_float4(mu[0], mu[1], mu[2], mu[3]);
-        mo[1] = make_float4(mu[4], mu[5], mu[6], mu[7]);
-        so[0] = make_float4(sg[0], sg[1], sg[2], sg[3]);
-        so[1] = make_float4(sg[4], sg[5], sg[6], sg[7]);
-    }
-    if (MODE == kModeBlockStats)
-        return;
+        __syncthreads();
 
-    // ---- phase 3: scale, compand, split, pack ---------------------------
-    float d2[8], r2[8];
-    bool slow2 = false;
+        // ---- phase 2: normalise, chunk mean and max |X - mu| -------------
+        {
+            const float4 c0 = s_ch[2 * p], c1 = s_ch[2 * p + 1];
+            const float gm[2] = {c0.x, c1.x}, d1[2] = {c0.y, c1.y}, r1[2] = {c0.z, c1.z};
+            if (c0.w == 0.0f && c1.w == 0.0f) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        d2[e] = sg[e] + tab.eps;
-        r2[e] = __fdiv_rn(1.0f, d2[e]);
-        slow2 |= mu[e] > 0.0f && mu[e] < kMuTiny;
-    }
-    if (slow2) {
-        // IEEE quotient; + 0 turns a -0 quotient into +0 so that the sign
-        // bit below is exactly [X_cent < 0].
+                for (int i = 0; i < kChunk; ++i)
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+                    for (int e = 0; e < 2; ++e) x[i][e] = div_fast(x[i][e] - gm[e], d1[e], r1[e]);
+            } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[i][e] = __fdiv_rn(x[i][e], d2[e]) + 0.0f;
-    } else {
+                for (int i = 0; i < kChunk; ++i)
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[i][e] = div_fast(x[i][e], d2[e], r2[e]);
-    }
-    __syncthreads();  // s_tab complete
-
-    const uint32_t lo = (uint32_t)tab.bucket_lo;
-    const uint32_t hi = lo + (uint32_t)tab.nbuckets - 1u;
-    const uint32_t sh = (uint32_t)tab.shift;
-    uint32_t *anc = (uint32_t *)(anchor + b * (kPage * kHead / 2));
-    uint32_t *res = (uint32_t *)(residual + b * (kPage * kHead / 2));
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        uint32_t J[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            uint32_t mag = __float_as_uint(x[i][e]) & 0x7fffffffu;
-            uint32_t idx = mag >> sh;
-            idx = idx < lo ? lo : (idx > hi ? hi : idx);
-            uint2 ent = s_tab[idx - lo];
-            // J = code + 7: high nibble = anchor magnitude (code + 7) >> 4,
-            // low nibble ^ 7 = residual (-code) mod 16.
-            J[e] = ent.y + (mag >= ent.x ? 1u : 0u);
+                    for (int e = 0; e < 2; ++e) x[i][e] = __fdiv_rn(x[i][e] - gm[e], d1[e]);
+            }
         }
-        uint32_t w_even = J[0] | (J[2] << 8) | (J[4] << 16) | (J[6] << 24);
-        uint32_t w_odd = J[1] | (J[3] << 8) | (J[5] << 16) | (J[7] << 24);
-        uint32_t a = ((w_even >> 4) & 0x0f0f0f0fu) | (w_odd & 0xf0f0f0f0u);
-        uint32_t r = ((w_even & 0x0f0f0f0fu) | ((w_odd << 4) & 0xf0f0f0f0u)) ^ 0x77777777u;
-        // Sign bits of the 8 quotients replicated to bytes (v_perm
-        // selectors 9 and 11), then to nibbles: anchor of a negative value
-        // is the one's complement of its magnitude (-V - 1).
-        uint32_t xs[8];
+        float mu[2], sg[2];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) xs[e] = __float_as_uint(x[i][e]);
-        uint32_t n_even = __builtin_amdgcn_perm(xs[2], xs[0], 0x0c0c0b09u) |
-                          __builtin_amdgcn_perm(xs[6], xs[4], 0x0b090c0cu);
-        uint32_t n_odd = __builtin_amdgcn_perm(xs[3], xs[1], 0x0c0c0b09u) |
-                         __builtin_amdgcn_perm(xs[7], xs[5], 0x0b090c0cu);
-        a ^= (n_even & 0x0f0f0f0fu) | (n_odd & 0xf0f0f0f0u);
-        const int row = tok0 + i;
-        __builtin_nontemporal_store(a, anc + row * (kHead / 8) + cg);
-        __builtin_nontemporal_store(r, res + row * (kHead / 8) + cg);
+        for (int e = 0; e < 2; ++e) {
+            // balanced pairwise tree over the 32 tokens of the chunk
+            float t16[16], t8[8], t4[4];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) t16[k] = x[2 * k][e] + x[2 * k + 1][e];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) t8[k] = t16[2 * k] + t16[2 * k + 1];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) t4[k] = t8[2 * k] + t8[2 * k + 1];
+            float s32 = (t4[0] + t4[1]) + (t4[2] + t4[3]);
+            mu[e] = s32 * 0.03125f;
+            float m = 0.0f;
+#pragma unroll
+            for (int i = 0; i < kChunk; ++i) {
+                x[i][e] = x[i][e] - mu[e];
+                m = fmaxf(m, fabsf(x[i][e]));
+            }
+            sg[e] = m;
+        }
+        *(float2 *)(mu_out + cmeta0 + 2 * p) = make_float2(mu[0], mu[1]);
+        *(float2 *)(sigma_out + cmeta0 + 2 * p) = make_float2(sg[0], sg[1]);
+        if (MODE == kModeBlockStats)
+            continue;
+
+        // ---- phase 3: scale, compand, split, pack -------------------------
+        {
+            const float d2[2] = {sg[0] + tab.eps, sg[1] + tab.eps};
+            const bool slow2 = (mu[0] > 0.0f && mu[0] < kMuTiny) || (mu[1] > 0.0f && mu[1] < kMuTiny);
+            if (slow2) {
+                // IEEE quotient; + 0 turns a -0 quotient into +0 so that the
+                // sign bit below is exactly [X_cent < 0].
+#pragma unroll
+                for (int i = 0; i < kChunk; ++i)
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) x[i][e] = __fdiv_rn(x[i][e], d2[e]) + 0.0f;
+            } else {
+                const float r2[2] = {__fdiv_rn(1.0f, d2[0]), __fdiv_rn(1.0f, d2[1])};
+#pragma unroll
+                for (int i = 0; i < kChunk; ++i)
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) x[i][e] = div_fast(x[i][e], d2[e], r2[e]);
+            }
+        }
+        // Magnitudes are clamped into [first value of the lowest bucket, 1]
+        // (every finite |X_final| is <= 1; the lower clamp keeps code 0
+        // since that bucket starts below the first threshold, and
+        // non-finite inputs stay inside the table).  The bucket offset is
+        // folded into the LDS base address.
+        u32x4 av[2], rv[2];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {  // tokens 4q .. 4q+3
+            uint32_t J[4][2];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    float m = __builtin_amdgcn_fmed3f(fabsf(x[4 * q + k][e]), mag_lo, 1.0f);
+                    uint32_t mb = __float_as_uint(m);
+                    uint32_t addr;
+                    asm("v_lshl_add_u32 %0, %1, 3, %2" : "=v"(addr) : "v"(mb >> sh), "s"(tab_base));
+                    u32x2 ent = *(lds_u32x2 *)(uintptr_t)addr;
+                    // J = code + 7: high nibble = anchor magnitude
+                    // (code + 7) >> 4, low nibble ^ 7 = residual (-code) mod 16.
+                    J[k][e] = ent[1] + (mb >= ent[0] ? 1u : 0u);
+                }
+            }
+            // byte k of w0 / w1 = J of channel 2p / 2p+1 at token 4q + k
+            uint32_t w0 = J[0][0] | (J[1][0] << 8) | (J[2][0] << 16) | (J[3][0] << 24);
+            uint32_t w1 = J[0][1] | (J[1][1] << 8) | (J[2][1] << 16) | (J[3][1] << 24);
+            uint32_t a = ((w0 >> 4) & 0x0f0f0f0fu) | (w1 & 0xf0f0f0f0u);
+            uint32_t r = ((w0 & 0x0f0f0f0fu) | ((w1 << 4) & 0xf0f0f0f0u)) ^ 0x77777777u;
+            // Sign bits of the quotients replicated to bytes (v_perm
+            // selectors 9 and 11), then to nibbles: the anchor of a negative
+            // value is the one's complement of its magnitude (-V - 1).
+            const uint32_t *xa = (const uint32_t *)x[4 * q];
+            const uint32_t *xb = (const uint32_t *)x[4 * q + 1];
+            const uint32_t *xc = (const uint32_t *)x[4 * q + 2];
+            const uint32_t *xd = (const uint32_t *)x[4 * q + 3];
+            uint32_t n0 = __builtin_amdgcn_perm(xb[0], xa[0], 0x0c0c0b09u) |
+                          __builtin_amdgcn_perm(xd[0], xc[0], 0x0b090c0cu);
+            uint32_t n1 = __builtin_amdgcn_perm(xb[1], xa[1], 0x0c0c0b09u) |
+                          __builtin_amdgcn_perm(xd[1], xc[1], 0x0b090c0cu);
+            a ^= (n0 & 0x0f0f0f0fu) | (n1 & 0xf0f0f0f0u);
+            av[q >> 2][q & 3] = a;
+            rv[q >> 2][q & 3] = r;
+        }
+        // 32 contiguous bytes per stream: [chunk j][pair][token of chunk]
+        const int64_t coff = b * (kPage * kHead / 2) + j * (kHead / 2 * kChunk) +
+                             (half * kPairs + p) * kChunk;
+        u32x4 *ao = (u32x4 *)(anchor + coff);
+        u32x4 *ro = (u32x4 *)(residual + coff);
+        __builtin_nontemporal_store(av[0], ao);
+        __builtin_nontemporal_store(av[1], ao + 1);
+        __builtin_nontemporal_store(rv[0], ro);
+        __builtin_nontemporal_store(rv[1], ro + 1);
     }
 }
 
 }  // namespace
+
+// Workgroups resident on the device (per kernel variant), cached per device.
+static int resident_workgroups(const void *kernel, int threads) {
+    static int cache[64][3];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 1024;
+    const int slot = kernel == (const void *)quant_kernel<kModeQuantize>     ? 0
+                     : kernel == (const void *)quant_kernel<kModePageStats> ? 1
+                                                                              : 2;
+    if (cache[dev][slot] == 0) {
+        int cus = 0, per_cu = 0;
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0);
+        cache[dev][slot] = (cus > 0 ? cus : 256) * (per_cu > 0 ? per_cu : 1);
+    }
+    return cache[dev][slot];
+}
 
 hipError_t launch_quantize(const uint16_t *kv, const Geometry &g, const QuantTab &tab,
                            uint8_t *anchor, uint8_t *residual, float *gmin, float *gscale,
                            float *mu, float *sigma, int mode, hipStream_t stream) {
     if (g.nblocks == 0)
         return hipSuccess;
-    dim3 grid((unsigned)g.nblocks), block(512);
+    const void *kern = mode == kModeQuantize    ? (const void *)quant_kernel<kModeQuantize>
+                       : mode == kModePageStats ? (const void *)quant_kernel<kModePageStats>
+                                                : (const void *)quant_kernel<kModeBlockStats>;
+    const int64_t units = 2 * g.nblocks;
+    const int64_t res = resident_workgroups(kern, kThreads);
+    Geometry gl = g;
+    gl.grid_wgs = units < res ? units : res;
+    dim3 grid((unsigned)gl.grid_wgs), block(kThreads);
     switch (mode) {
     case kModeQuantize:
-        hipLaunchKernelGGL(quant_kernel<kModeQuantize>, grid, block, 0, stream, kv, g, tab,
+        hipLaunchKernelGGL(quant_kernel<kModeQuantize>, grid, block, 0, stream, kv, gl, tab,
                            anchor, residual, gmin, gscale, mu, sigma);
         break;
     case kModePageStats:
-        hipLaunchKernelGGL(quant_kernel<kModePageStats>, grid, block, 0, stream, kv, g, tab,
+        hipLaunchKernelGGL(quant_kernel<kModePageStats>, grid, block, 0, stream, kv, gl, tab,
                            anchor, residual, gmin, gscale, mu, sigma);
         break;
     default:
-        hipLaunchKernelGGL(quant_kernel<kModeBlockStats>, grid, block, 0, stream, kv, g, tab,
+        hipLaunchKernelGGL(quant_kernel<kModeBlockStats>, grid, block, 0, stream, kv, gl, tab,
                            anchor, residual, gmin, gscale, mu, sigma);
         break;
     }

@@ -142,8 +142,8 @@ def num_blocks(shape: lynx_kv_shape) -> int:
 @dataclass
 class Codes:
     """Device buffers of one quantized KV set (layouts of include/lynx.h)."""
-    anchor: torch.Tensor       # uint8 [nblocks, 256, 64]
-    residual: torch.Tensor     # uint8 [nblocks, 256, 64]
+    anchor: torch.Tensor       # uint8 [nblocks, 8 chunks, 64 channel pairs, 32 tokens]
+    residual: torch.Tensor     # uint8 [nblocks, 8, 64, 32]
     gamma_min: torch.Tensor    # float32 [nblocks, 128]
     gamma_scale: torch.Tensor  # float32 [nblocks, 128]
     mu: torch.Tensor           # float32 [nblocks, 8, 128]
@@ -159,8 +159,8 @@ class Codes:
 def alloc_codes(nblocks: int, device) -> Codes:
     u8 = dict(dtype=torch.uint8, device=device)
     f32 = dict(dtype=torch.float32, device=device)
-    return Codes(torch.empty((nblocks, PAGE_TOKENS, BLOCK_CHANNELS // 2), **u8),
-                 torch.empty((nblocks, PAGE_TOKENS, BLOCK_CHANNELS // 2), **u8),
+    tile = (nblocks, PAGE_TOKENS // CHUNK_TOKENS, BLOCK_CHANNELS // 2, CHUNK_TOKENS)
+    return Codes(torch.empty(tile, **u8), torch.empty(tile, **u8),
                  torch.empty((nblocks, BLOCK_CHANNELS), **f32),
                  torch.empty((nblocks, BLOCK_CHANNELS), **f32),
                  torch.empty((nblocks, PAGE_TOKENS // CHUNK_TOKENS, BLOCK_CHANNELS), **f32),

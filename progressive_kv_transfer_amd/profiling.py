@@ -1,11 +1,12 @@
 """Summaries of rocprofv3 output databases (kernel durations, PMC counters).
 
     python -m progressive_kv_transfer_amd.profiling trace RESULTS_DB [--match lynx]
-    python -m progressive_kv_transfer_amd.profiling pmc RESULTS_DB COUNTER [--match lynx]
+    python -m progressive_kv_transfer_amd.profiling pmc RESULTS_DB [--match lynx]
 
 `trace` prints, per kernel, the number of dispatches and the average,
-minimum and maximum duration (from the kernel-trace table); `pmc` prints the
-per-dispatch value of one counter (rocprofv3 --pmc), averaged per kernel.
+minimum and maximum duration (from the kernel-trace table); `pmc` prints, per
+kernel and counter (rocprofv3 --pmc), the per-dispatch value averaged over
+the dispatches.
 """
 from __future__ import annotations
 
@@ -33,29 +34,27 @@ def trace(db: str, match: str | None = None):
     return out
 
 
-def pmc(db: str, counter: str, match: str | None = None):
+def pmc(db: str, match: str | None = None):
+    """Per kernel and counter: number of dispatches and the per-dispatch
+    average of the counter summed over its hardware instances (and of the
+    per-instance maximum, the right reduction for GRBM_GUI_ACTIVE)."""
     con = sqlite3.connect(db)
-    cols = [r[1] for r in con.execute("pragma table_info(pmc_events)")]
-    name_col = "kernel_name" if "kernel_name" in cols else "name"
-    val_col = "counter_value" if "counter_value" in cols else "value"
-    cnt_col = "counter_name" if "counter_name" in cols else "pmc_name"
-    disp_col = "dispatch_id" if "dispatch_id" in cols else "id"
     rows = con.execute(
-        f"select {name_col}, {disp_col}, sum({val_col}) from pmc_events "
-        f"where {cnt_col} = ? group by {name_col}, {disp_col}", (counter,)).fetchall()
+        "select name, dispatch_id, counter_name, sum(counter_value), max(counter_value) "
+        "from pmc_events group by dispatch_id, counter_name").fetchall()
     by = {}
-    for name, _, v in rows:
+    for name, _, cname, vsum, vmax in rows:
         if match and match not in name:
             continue
-        by.setdefault(_short(name), []).append(v)
-    return [(k, len(v), statistics.mean(v)) for k, v in sorted(by.items())]
+        by.setdefault((_short(name), cname), []).append((vsum, vmax))
+    return [(k, c, len(v), statistics.mean(x[0] for x in v), statistics.mean(x[1] for x in v))
+            for (k, c), v in sorted(by.items())]
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("mode", choices=["trace", "pmc"])
     ap.add_argument("db")
-    ap.add_argument("counter", nargs="?")
     ap.add_argument("--match", default=None)
     a = ap.parse_args()
     if a.mode == "trace":
@@ -64,10 +63,10 @@ def main():
         for k, n, avg, mn, mx in trace(a.db, a.match):
             print(f"| {k} | {n} | {avg:.1f} | {mn:.1f} | {mx:.1f} |")
     else:
-        print(f"| kernel | dispatches | avg {a.counter} per dispatch |")
-        print("|---|---|---|")
-        for k, n, avg in pmc(a.db, a.counter, a.match):
-            print(f"| {k} | {n} | {avg:.1f} |")
+        print("| kernel | counter | dispatches | avg sum over instances | avg max instance |")
+        print("|---|---|---|---|---|")
+        for k, c, n, vsum, vmax in pmc(a.db, a.match):
+            print(f"| {k} | {c} | {n} | {vsum:.1f} | {vmax:.1f} |")
 
 
 if __name__ == "__main__":

@@ -268,8 +268,8 @@ def test_packing_layout_two_valued_page():
     """Two-valued chunks (16 high, 16 low) give X_final = +-sigma/(sigma+eps),
     i.e. code 127 clipped to 120: anchor +7 (0x7) or -8 (0x8), residual -8
     (0x8).  Channel c's pattern is bit (c % 5) of the token index, so the
-    packed bytes expose the nibble order: byte k of a token row holds
-    channel 2k low and channel 2k + 1 high."""
+    packed bytes expose the layout: the byte of token t and channel pair k
+    sits at [t // 32][k][t % 32] and holds channel 2k low, 2k + 1 high."""
     x = bits(kvgen.edge_pages()["two_valued"])
     r = oracle.quantize_block(x)
     P, H = x.shape
@@ -277,7 +277,8 @@ def test_packing_layout_two_valued_page():
     c = np.arange(H)[None, :]
     high = ((t >> (c % 5)) & 1) == 1
     nib = np.where(high, 0x7, 0x8)
-    expect = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    tok_major = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)  # [P][H/2]
+    expect = tok_major.reshape(P // 32, 32, H // 2).transpose(0, 2, 1)
     assert np.array_equal(r.anchor, expect)
     assert np.all(r.residual == 0x88)
 
