@@ -49,7 +49,7 @@ KERNEL_SYMBOL = {
     "dequant_anchor": "dequant_kernel<false>",
     "dequant_full": "dequant_kernel<true>",
 }
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qwen32b_16k.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qwen32b_16k.md")
 
 
 def kernel_source_hash() -> str:
@@ -65,8 +65,9 @@ def load_traffic(kernel: str):
     None if absent or taken on a different kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
+            text = f.read()
+        t = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    except (OSError, ValueError, IndexError):
         return None
     if t.get("kernel_source_hash") != kernel_source_hash():
         return None

@@ -12,12 +12,12 @@
 // four binary32 roundings, then bf16 round-to-nearest-even
 // (v_cvt_pk_bf16_f32).
 //
-// Lane mapping: wave w = chunk w, lane 16 s + g owns channels 8g..8g+7 of
-// tokens 32w + 8s .. +7, so every lane needs the metadata of 8 channels of
-// one chunk only and writes 16-byte row pieces that 16 lanes join into one
-// 256-byte row.  Its codes are four 8-byte runs of the chunk-tiled streams
-// (one per channel pair); the 64 lanes of a wave read each 128-byte line of
-// the chunk's tile completely.
+// Lane mapping: 256 lanes per page block; lane 16 t + g of wave w owns
+// channels 8g..8g+7 of tokens 64w + 16t .. +15 (inside one chunk), so it
+// needs the metadata of 8 channels of one chunk only, reads its codes as
+// four 16-byte runs of the chunk-tiled streams (one per channel pair) and
+// writes 16-byte row pieces that 16 lanes join into one 256-byte row.
+// Workgroups are persistent and build the level table in LDS once.
 #include "lynx_internal.h"
 
 namespace lynx {
@@ -34,118 +34,141 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, h);
 }
 
+constexpr int kThreads = 256;
+// Copies of the full (anchor, residual) level table, interleaved word by
+// word; lane l reads copy l % kCopies, so lanes of a wave looking up
+// different entries spread over the LDS banks.
+constexpr int kCopies = 1;
+
 template <bool FULL>
-__global__ __launch_bounds__(512) void dequant_kernel(
+__global__ __launch_bounds__(kThreads) void dequant_kernel(
     const uint8_t *__restrict__ anchor, const uint8_t *__restrict__ residual,
     const float *__restrict__ gmin, const float *__restrict__ gscale,
     const float *__restrict__ mu, const float *__restrict__ sigma, Geometry g,
     const DequantTab tab, uint16_t *__restrict__ out) {
     constexpr int kLut = FULL ? 256 : 16;
-    __shared__ float s_lut[kLut];
-
-    const int64_t b = g.block0 + __builtin_amdgcn_workgroup_id_x();
-    const int head = (int)(b % g.heads);
-    const int64_t tp = b / g.heads;
-    const int page = (int)(tp % g.pages);
-    const int64_t tensor = tp / g.pages;
-    uint16_t *obase =
-        out + tensor * g.tensor_stride + (int64_t)page * kPage * g.row_stride + head * kHead;
+    constexpr int kCop = FULL ? kCopies : 1;
+    __shared__ float s_lut[kLut * kCop];
 
     const int tid = (int)__builtin_amdgcn_workitem_id_x();
     const int wave = tid >> 6;
     const int lane = tid & 63;
-    const int cg = lane & 15;
-    const int s = lane >> 4;
-    const int tok0 = wave * kChunk + s * 8;
-
-    // Chunk-tiled streams: the 8 bytes of channel pair 4 cg + k for tokens
-    // 32 wave + 8 s .. + 7 sit at [chunk wave][pair][8 s].
-    const int64_t coff = b * (kPage * kHead / 2) + wave * (kHead / 2 * kChunk) +
-                         (4 * cg) * kChunk + 8 * s;
-    u32x2 A[4], R[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        A[k] = __builtin_nontemporal_load((const u32x2 *)(anchor + coff + k * kChunk));
-        if (FULL)
-            R[k] = __builtin_nontemporal_load((const u32x2 *)(residual + coff + k * kChunk));
-    }
-    const float4 *gm4 = (const float4 *)(gmin + b * kHead + cg * 8);
-    const float4 *gs4 = (const float4 *)(gscale + b * kHead + cg * 8);
-    const float4 *mu4 = (const float4 *)(mu + b * (kChunks * kHead) + wave * kHead + cg * 8);
-    const float4 *sg4 = (const float4 *)(sigma + b * (kChunks * kHead) + wave * kHead + cg * 8);
-    float4 m0 = gm4[0], m1 = gm4[1], c0 = gs4[0], c1 = gs4[1];
-    float4 u0 = mu4[0], u1 = mu4[1], q0 = sg4[0], q1 = sg4[1];
-    const float gm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-    const float gs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-    const float um[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-    const float sq[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+    const int cg = lane & 15;      // channels 8 cg .. 8 cg + 7
+    const int tg = lane >> 4;      // tokens 64 wave + 16 tg .. + 15
+    const int j = 2 * wave + (tg >> 1);  // chunk of those tokens
+    const int tok0 = 64 * wave + 16 * tg;
 
     // Signed level of every (anchor nibble, residual nibble) pair.
-    if (tid < kLut) {
-        int a = tid & 15;
+    for (int e = tid; e < kLut * kCop; e += kThreads) {
+        int t = e / kCop;
+        int a = t & 15;
         int av = a >= 8 ? a - 16 : a;
         int v = av < 0 ? -av - 1 : av;
         int code = v << 4;
         if (FULL) {
-            int r = tid >> 4;
+            int r = t >> 4;
             code -= r >= 8 ? r - 16 : r;
             code = code < 0 ? 0 : code;
         }
         float m = tab.level[code];
-        s_lut[tid] = av < 0 ? -m : m;
-    }
-    float d1[8], d2[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        d1[e] = gs[e] + tab.eps;
-        d2[e] = sq[e] + tab.eps;
+        s_lut[e] = av < 0 ? -m : m;
     }
     __syncthreads();
+    const float *lut = s_lut + (lane % kCop);
 
-    // idx[i][e]: table index of token i, channel e of the lane's 8.
-    uint32_t ev[4][2], od[4][2];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            // byte i of ev / od = (anchor nibble) | (residual nibble << 4)
-            // of channel 2k / 2k+1 at token 4h + i.
-            if (FULL) {
-                ev[k][h] = (A[k][h] & 0x0f0f0f0fu) | ((R[k][h] << 4) & 0xf0f0f0f0u);
-                od[k][h] = ((A[k][h] >> 4) & 0x0f0f0f0fu) | (R[k][h] & 0xf0f0f0f0u);
-            } else {
-                ev[k][h] = A[k][h] & 0x0f0f0f0fu;
-                od[k][h] = (A[k][h] >> 4) & 0x0f0f0f0fu;
-            }
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        uint32_t idx[8];
+    for (int64_t u = __builtin_amdgcn_workgroup_id_x(); u < g.nblocks; u += g.grid_wgs) {
+        const int64_t b = g.block0 + u;
+        const int head = (int)(b % g.heads);
+        const int64_t tp = b / g.heads;
+        const int page = (int)(tp % g.pages);
+        const int64_t tensor = tp / g.pages;
+        uint16_t *obase = out + tensor * g.tensor_stride + (int64_t)page * kPage * g.row_stride +
+                          head * kHead + cg * 8;
+
+        // Chunk-tiled streams: the 16 bytes of channel pair 4 cg + k for the
+        // lane's 16 tokens sit at [chunk j][pair][16 (tg & 1)].  Each
+        // 128-byte line of a tile is read in four 16-byte pieces by
+        // successive loads, so these are ordinary (cached) loads.
+        const int64_t coff = b * (kPage * kHead / 2) + j * (kHead / 2 * kChunk) +
+                             (4 * cg) * kChunk + 16 * (tg & 1);
+        u32x4 A[4], R[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            idx[2 * k] = (ev[k][i >> 2] >> (8 * (i & 3))) & 0xffu;
-            idx[2 * k + 1] = (od[k][i >> 2] >> (8 * (i & 3))) & 0xffu;
+            A[k] = *((const u32x4 *)(anchor + coff + k * kChunk));
+            if (FULL)
+                R[k] = *((const u32x4 *)(residual + coff + k * kChunk));
         }
-        float y[8];
+        const float4 *gm4 = (const float4 *)(gmin + b * kHead + cg * 8);
+        const float4 *gs4 = (const float4 *)(gscale + b * kHead + cg * 8);
+        const float4 *mu4 = (const float4 *)(mu + b * (kChunks * kHead) + j * kHead + cg * 8);
+        const float4 *sg4 = (const float4 *)(sigma + b * (kChunks * kHead) + j * kHead + cg * 8);
+        const float4 m0 = gm4[0], m1 = gm4[1], c0 = gs4[0], c1 = gs4[1];
+        const float4 u0 = mu4[0], u1 = mu4[1], q0 = sg4[0], q1 = sg4[1];
+        const float gm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+        const float um[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+        const float d1[8] = {c0.x + tab.eps, c0.y + tab.eps, c0.z + tab.eps, c0.w + tab.eps,
+                             c1.x + tab.eps, c1.y + tab.eps, c1.z + tab.eps, c1.w + tab.eps};
+        const float d2[8] = {q0.x + tab.eps, q0.y + tab.eps, q0.z + tab.eps, q0.w + tab.eps,
+                             q1.x + tab.eps, q1.y + tab.eps, q1.z + tab.eps, q1.w + tab.eps};
+
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float xf = s_lut[idx[e]];
-            float t1 = xf * d2[e];
-            float xn = t1 + um[e];
-            float t2 = xn * d1[e];
-            y[e] = t2 + gm[e];
+        for (int h = 0; h < 4; ++h) {  // tokens 4h .. 4h+3 of the lane's 16
+            // byte i of ev[k] / od[k] = (anchor nibble) | (residual nibble << 4)
+            // of channel 2k / 2k+1 at token 4h + i.
+            uint32_t ev[4], od[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if (FULL) {
+                    ev[k] = (A[k][h] & 0x0f0f0f0fu) | ((R[k][h] << 4) & 0xf0f0f0f0u);
+                    od[k] = ((A[k][h] >> 4) & 0x0f0f0f0fu) | (R[k][h] & 0xf0f0f0f0u);
+                } else {
+                    ev[k] = A[k][h] & 0x0f0f0f0fu;
+                    od[k] = (A[k][h] >> 4) & 0x0f0f0f0fu;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float y[8];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+#pragma unroll
+                    for (int o = 0; o < 2; ++o) {
+                        const int e = 2 * k + o;
+                        uint32_t idx = ((o ? od[k] : ev[k]) >> (8 * i)) & 0xffu;
+                        float xf = lut[idx * kCop];
+                        float t1 = xf * d2[e];
+                        float xn = t1 + um[e];
+                        float t2 = xn * d1[e];
+                        y[e] = t2 + gm[e];
+                    }
+                }
+                u32x4 o4;
+                o4[0] = pack_bf16(y[0], y[1]);
+                o4[1] = pack_bf16(y[2], y[3]);
+                o4[2] = pack_bf16(y[4], y[5]);
+                o4[3] = pack_bf16(y[6], y[7]);
+                __builtin_nontemporal_store(
+                    o4, (u32x4 *)(obase + (int64_t)(tok0 + 4 * h + i) * g.row_stride));
+            }
         }
-        u32x4 o;
-        o[0] = pack_bf16(y[0], y[1]);
-        o[1] = pack_bf16(y[2], y[3]);
-        o[2] = pack_bf16(y[4], y[5]);
-        o[3] = pack_bf16(y[6], y[7]);
-        __builtin_nontemporal_store(o, (u32x4 *)(obase + (int64_t)(tok0 + i) * g.row_stride + cg * 8));
     }
 }
 
 }  // namespace
+
+static int resident_workgroups(const void *kernel, int slot) {
+    static int cache[64][2];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 1024;
+    if (cache[dev][slot] == 0) {
+        int cus = 0, per_cu = 0;
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0);
+        cache[dev][slot] = (cus > 0 ? cus : 256) * (per_cu > 0 ? per_cu : 1);
+    }
+    return cache[dev][slot];
+}
 
 hipError_t launch_dequant(const uint8_t *anchor, const uint8_t *residual, const float *gmin,
                           const float *gscale, const float *mu, const float *sigma,
@@ -153,13 +176,18 @@ hipError_t launch_dequant(const uint8_t *anchor, const uint8_t *residual, const 
                           hipStream_t stream) {
     if (g.nblocks == 0)
         return hipSuccess;
-    dim3 grid((unsigned)g.nblocks), block(512);
+    const void *kern = residual ? (const void *)dequant_kernel<true>
+                                : (const void *)dequant_kernel<false>;
+    const int64_t res = resident_workgroups(kern, residual ? 1 : 0);
+    Geometry gl = g;
+    gl.grid_wgs = g.nblocks;
+    dim3 grid((unsigned)gl.grid_wgs), block(kThreads);
     if (residual)
         hipLaunchKernelGGL(dequant_kernel<true>, grid, block, 0, stream, anchor, residual, gmin,
-                           gscale, mu, sigma, g, tab, out);
+                           gscale, mu, sigma, gl, tab, out);
     else
         hipLaunchKernelGGL(dequant_kernel<false>, grid, block, 0, stream, anchor, residual,
-                           gmin, gscale, mu, sigma, g, tab, out);
+                           gmin, gscale, mu, sigma, gl, tab, out);
     return hipGetLastError();
 }
 

@@ -282,10 +282,11 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
                              (half * kPairs + p) * kChunk;
         u32x4 *ao = (u32x4 *)(anchor + coff);
         u32x4 *ro = (u32x4 *)(residual + coff);
-        __builtin_nontemporal_store(av[0], ao);
-        __builtin_nontemporal_store(av[1], ao + 1);
-        __builtin_nontemporal_store(rv[0], ro);
-        __builtin_nontemporal_store(rv[1], ro + 1);
+        // Ordinary stores: the streams are read again by the dequant kernels.
+        ao[0] = av[0];
+        ao[1] = av[1];
+        ro[0] = rv[0];
+        ro[1] = rv[1];
     }
 }
 
