@@ -13,7 +13,12 @@
  *   - lynx_dequant_full: the residual phase (Section 4.2, Figure 7(c)):
  *     Q_res combined with the stored metadata refines the KV to Q_full;
  *   - lynx_page_stats / lynx_block_stats: Stage 1 and Stage 2 statistics of
- *     Algorithm 1 on their own (the same arithmetic as the fused quantize).
+ *     Algorithm 1 on their own (the same arithmetic as the fused quantize);
+ *   - lynx_decode_attn_dequant: attention O = softmax(Q K^T scale) V
+ *     (Section 2.1) over K, V rebuilt on the fly from their streams: one
+ *     query token (decode on the draft or verification precision) or T
+ *     draft tokens with a causal tail (the single parallel forward pass of
+ *     the verification, Section 4.3).
  *
  * Terms
  *   KV set      num_tensors token-major bf16 tensors [num_tokens][num_channels]
@@ -80,6 +85,10 @@ extern "C" {
 #define LYNX_PAGE_TOKENS 256
 #define LYNX_CHUNK_TOKENS 32
 #define LYNX_BLOCK_CHANNELS 128
+
+/* Output element type of lynx_decode_attn_dequant. */
+#define LYNX_OUT_BF16 0
+#define LYNX_OUT_F32 1
 
 /* Method parameters (Algorithm 1 and Eq. (3)).  alpha > 0 controls the
  * skew of the alpha-law (default 255); eps > 0 is added to both scales
@@ -187,6 +196,43 @@ int lynx_block_stats(const void *kv, const lynx_kv_shape *shape,
                      const lynx_params *params, const float *gamma_min,
                      const float *gamma_scale, float *mu, float *sigma,
                      hipStream_t stream);
+
+/* Workspace bytes lynx_decode_attn_dequant needs for these sizes (0 for
+ * invalid sizes).  Host only. */
+size_t lynx_attn_workspace_bytes(int t_q, int num_q_heads, int num_kv_heads,
+                                 int64_t ctx_len);
+
+/*
+ * Grouped-query attention over Lynx-coded K and V:
+ *   out[r][h] = softmax_p( q[r][h] . K^[p][h / g] * scale ) V^[p][h / g],
+ * g = num_q_heads / num_kv_heads, p over the context positions a query sees.
+ *   q            bf16 [t_q][num_q_heads][128] (device);
+ *   out          [t_q][num_q_heads][128] (device) of LYNX_OUT_BF16 (bf16,
+ *                the binary32 result rounded to nearest even) or
+ *                LYNX_OUT_F32 (binary32) elements, per out_dtype;
+ *   k_*, v_*     the streams and metadata of one quantized tensor each, of
+ *                shape [ctx_len][num_kv_heads * 128] (the outputs of
+ *                lynx_quantize_pages for num_tensors = 1); k_residual /
+ *                v_residual NULL = anchor-only reconstruction.  K^ and V^
+ *                are bit-identical to lynx_dequant_anchor / _full;
+ *   ctx_len      multiple of 256; head_dim must be 128;
+ *   causal_tail  0: every query sees all ctx_len positions; 1: the t_q
+ *                queries are the last t_q positions and row r sees positions
+ *                0 .. ctx_len - t_q + r;
+ *   workspace    >= lynx_attn_workspace_bytes(...) bytes of device memory,
+ *                overwritten (split partials).
+ * Scores, the softmax and the accumulation are binary32 (bf16 x bf16
+ * products are exact).  t_q * g must be <= 64.  Errors as above.
+ */
+int lynx_decode_attn_dequant(const void *q, int t_q, int num_q_heads,
+                             const uint8_t *k_anchor, const uint8_t *k_residual,
+                             lynx_meta k_meta, const uint8_t *v_anchor,
+                             const uint8_t *v_residual, lynx_meta v_meta,
+                             int64_t ctx_len, int num_kv_heads, int head_dim,
+                             float scale, int causal_tail,
+                             const lynx_params *params, void *out,
+                             int out_dtype, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -268,6 +268,35 @@ int dequant_common(const uint8_t *anchor, const uint8_t *residual, lynx_meta met
     return LYNX_OK;
 }
 
+// Split-KV plan of an attention call: padded query rows, splits over the
+// context pages (about 1024 workgroups in total) and pages per split.
+struct AttnPlan {
+    int rows, rows_p, pages, splits, pps;
+    size_t ws_bytes;
+};
+
+int attn_plan(int t_q, int n_qh, int n_kvh, int64_t ctx, AttnPlan *pl) {
+    if (t_q <= 0 || n_qh <= 0 || n_kvh <= 0 || n_qh % n_kvh || ctx <= 0)
+        return LYNX_EINVAL;
+    if (ctx % kPage || ctx / kPage > INT32_MAX)
+        return LYNX_ESHAPE;
+    const int64_t rows = (int64_t)t_q * (n_qh / n_kvh);
+    if (rows > 64)
+        return LYNX_EINVAL;
+    pl->rows = (int)rows;
+    pl->rows_p = attn_padded_rows(pl->rows);
+    pl->pages = (int)(ctx / kPage);
+    int target = 1024 / n_kvh;
+    if (target < 1)
+        target = 1;
+    if (target > pl->pages)
+        target = pl->pages;
+    pl->pps = (pl->pages + target - 1) / target;
+    pl->splits = (pl->pages + pl->pps - 1) / pl->pps;
+    pl->ws_bytes = (size_t)pl->splits * n_kvh * pl->rows_p * (2 + kHead) * sizeof(float);
+    return LYNX_OK;
+}
+
 }  // namespace
 }  // namespace lynx
 
@@ -365,6 +394,81 @@ int lynx_dequant_full(const uint8_t *anchor, const uint8_t *residual, lynx_meta 
     if (!residual)
         return LYNX_EINVAL;
     return dequant_common(anchor, residual, meta, shape, params, out, stream);
+}
+
+size_t lynx_attn_workspace_bytes(int t_q, int num_q_heads, int num_kv_heads, int64_t ctx_len) {
+    AttnPlan pl;
+    return attn_plan(t_q, num_q_heads, num_kv_heads, ctx_len, &pl) ? 0 : pl.ws_bytes;
+}
+
+int lynx_decode_attn_dequant(const void *q, int t_q, int num_q_heads, const uint8_t *k_anchor,
+                             const uint8_t *k_residual, lynx_meta k_meta,
+                             const uint8_t *v_anchor, const uint8_t *v_residual,
+                             lynx_meta v_meta, int64_t ctx_len, int num_kv_heads, int head_dim,
+                             float scale, int causal_tail, const lynx_params *params, void *out,
+                             int out_dtype, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+    const lynx_params p = resolve(params);
+    int rc = check_params(p);
+    if (rc)
+        return rc;
+    if (head_dim != kHead || !(scale > 0.0f) || !(scale < 1e30f) ||
+        (out_dtype != LYNX_OUT_BF16 && out_dtype != LYNX_OUT_F32))
+        return LYNX_EINVAL;
+    AttnPlan pl;
+    if ((rc = attn_plan(t_q, num_q_heads, num_kv_heads, ctx_len, &pl)))
+        return rc;
+    if (causal_tail && ctx_len < t_q)
+        return LYNX_EINVAL;
+    if (!q || !out || !workspace || !k_anchor || !v_anchor || !k_meta.gamma_min ||
+        !k_meta.gamma_scale || !k_meta.mu || !k_meta.sigma || !v_meta.gamma_min ||
+        !v_meta.gamma_scale || !v_meta.mu || !v_meta.sigma)
+        return LYNX_EINVAL;
+    if (workspace_bytes < pl.ws_bytes)
+        return LYNX_EINVAL;
+    for (const void *ptr : {(const void *)q, (const void *)out, (const void *)workspace, (const void *)k_anchor,
+                            (const void *)k_residual, (const void *)v_anchor,
+                            (const void *)v_residual, (const void *)k_meta.gamma_min,
+                            (const void *)k_meta.gamma_scale, (const void *)k_meta.mu,
+                            (const void *)k_meta.sigma, (const void *)v_meta.gamma_min,
+                            (const void *)v_meta.gamma_scale, (const void *)v_meta.mu,
+                            (const void *)v_meta.sigma})
+        if (ptr && !aligned16(ptr))
+            return LYNX_ESHAPE;
+    const Tables *t = tables_for(p);
+    if (!t)
+        return LYNX_EINVAL;
+    DequantTab tab = t->d;
+    tab.eps = p.eps;
+    AttnArgs a;
+    a.q = (const uint16_t *)q;
+    a.k_anc = k_anchor;
+    a.k_res = k_residual;
+    a.v_anc = v_anchor;
+    a.v_res = v_residual;
+    a.k_gmin = k_meta.gamma_min;
+    a.k_gsc = k_meta.gamma_scale;
+    a.k_mu = k_meta.mu;
+    a.k_sg = k_meta.sigma;
+    a.v_gmin = v_meta.gamma_min;
+    a.v_gsc = v_meta.gamma_scale;
+    a.v_mu = v_meta.mu;
+    a.v_sg = v_meta.sigma;
+    a.ws = (float *)workspace;
+    a.out = out;
+    a.out_f32 = out_dtype == LYNX_OUT_F32 ? 1 : 0;
+    a.ctx = ctx_len;
+    a.n_qh = num_q_heads;
+    a.n_kvh = num_kv_heads;
+    a.group = num_q_heads / num_kv_heads;
+    a.t_q = t_q;
+    a.rows = pl.rows;
+    a.pages = pl.pages;
+    a.splits = pl.splits;
+    a.pages_per_split = pl.pps;
+    a.causal = causal_tail ? 1 : 0;
+    a.qk_scale_log2 = (float)((double)scale * 1.4426950408889634);
+    return hip_status(launch_attention(a, tab, stream));
 }
 
 int lynx_page_stats(const void *kv, const lynx_kv_shape *shape, const lynx_params *params,

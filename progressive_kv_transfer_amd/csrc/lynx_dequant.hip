@@ -18,21 +18,13 @@
 // four 16-byte runs of the chunk-tiled streams (one per channel pair) and
 // writes 16-byte row pieces that 16 lanes join into one 256-byte row.
 // Workgroups are persistent and build the level table in LDS once.
-#include "lynx_internal.h"
+#include "lynx_recon.h"
 
 namespace lynx {
 namespace {
 
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-    f32x2 v = {lo, hi};
-    bf16x2 h = __builtin_convertvector(v, bf16x2);
-    return __builtin_bit_cast(uint32_t, h);
-}
 
 constexpr int kThreads = 256;
 // Copies of the full (anchor, residual) level table, interleaved word by
@@ -59,20 +51,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
     const int tok0 = 64 * wave + 16 * tg;
 
     // Signed level of every (anchor nibble, residual nibble) pair.
-    for (int e = tid; e < kLut * kCop; e += kThreads) {
-        int t = e / kCop;
-        int a = t & 15;
-        int av = a >= 8 ? a - 16 : a;
-        int v = av < 0 ? -av - 1 : av;
-        int code = v << 4;
-        if (FULL) {
-            int r = t >> 4;
-            code -= r >= 8 ? r - 16 : r;
-            code = code < 0 ? 0 : code;
-        }
-        float m = tab.level[code];
-        s_lut[e] = av < 0 ? -m : m;
-    }
+    for (int e = tid; e < kLut * kCop; e += kThreads) s_lut[e] = signed_level(tab, e / kCop, FULL);
     __syncthreads();
     const float *lut = s_lut + (lane % kCop);
 
@@ -135,11 +114,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
                     for (int o = 0; o < 2; ++o) {
                         const int e = 2 * k + o;
                         uint32_t idx = ((o ? od[k] : ev[k]) >> (8 * i)) & 0xffu;
-                        float xf = lut[idx * kCop];
-                        float t1 = xf * d2[e];
-                        float xn = t1 + um[e];
-                        float t2 = xn * d1[e];
-                        y[e] = t2 + gm[e];
+                        y[e] = reconstruct(lut[idx * kCop], d2[e], um[e], d1[e], gm[e]);
                     }
                 }
                 u32x4 o4;

@@ -65,4 +65,23 @@ hipError_t launch_dequant(const uint8_t *anchor, const uint8_t *residual, const 
                           const Geometry &g, const DequantTab &tab, uint16_t *out,
                           hipStream_t stream);
 
+// Argument block of the fused dequant + attention kernels.
+struct AttnArgs {
+    const uint16_t *q;  // [t_q][n_qh][128] bf16
+    const uint8_t *k_anc, *k_res, *v_anc, *v_res;
+    const float *k_gmin, *k_gsc, *k_mu, *k_sg;
+    const float *v_gmin, *v_gsc, *v_mu, *v_sg;
+    float *ws;      // partials [split][kv head][padded row][2 + 128]
+    void *out;      // [t_q][n_qh][128], bf16 or binary32
+    int64_t ctx;    // context tokens (multiple of 256)
+    int n_qh, n_kvh, group, t_q;
+    int rows;       // t_q * group
+    int pages, splits, pages_per_split;
+    int causal;
+    int out_f32;
+    float qk_scale_log2;  // scale * log2(e)
+};
+int attn_padded_rows(int rows);
+hipError_t launch_attention(const AttnArgs &a, const DequantTab &tab, hipStream_t stream);
+
 }  // namespace lynx

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_PKG, "liblynx.so")
 PAGE_TOKENS = 256
 CHUNK_TOKENS = 32
 BLOCK_CHANNELS = 128
+OUT_BF16, OUT_F32 = 0, 1  # lynx_decode_attn_dequant output element types
 STATUS = {0: "LYNX_OK", -1: "LYNX_EINVAL", -2: "LYNX_ESHAPE", -3: "LYNX_EHIP"}
 
 
@@ -49,7 +50,8 @@ class lynx_meta(ctypes.Structure):
 EXPORTS = ["lynx_default_params", "lynx_num_blocks", "lynx_stream_bytes",
            "lynx_gamma_floats", "lynx_chunk_floats", "lynx_kv_bytes",
            "lynx_status_string", "lynx_compander_thresholds", "lynx_quantize_pages", "lynx_dequant_anchor",
-           "lynx_dequant_full", "lynx_page_stats", "lynx_block_stats"]
+           "lynx_dequant_full", "lynx_page_stats", "lynx_block_stats",
+           "lynx_attn_workspace_bytes", "lynx_decode_attn_dequant"]
 
 _lib = None
 
@@ -87,8 +89,14 @@ def lib():
         L.lynx_page_stats.argtypes = [vp, P(lynx_kv_shape), P(lynx_params), vp, vp, vp]
         L.lynx_block_stats.argtypes = [vp, P(lynx_kv_shape), P(lynx_params), vp, vp, vp,
                                        vp, vp]
+        L.lynx_attn_workspace_bytes.argtypes = [i32, i32, i32, i64]
+        L.lynx_attn_workspace_bytes.restype = ctypes.c_size_t
+        L.lynx_decode_attn_dequant.argtypes = [vp, i32, i32, vp, vp, lynx_meta, vp, vp,
+                                               lynx_meta, i64, i32, i32, ctypes.c_float, i32,
+                                               P(lynx_params), vp, i32, vp, ctypes.c_size_t,
+                                               vp]
         for f in ("lynx_quantize_pages", "lynx_dequant_anchor", "lynx_dequant_full",
-                  "lynx_page_stats", "lynx_block_stats"):
+                  "lynx_page_stats", "lynx_block_stats", "lynx_decode_attn_dequant"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -236,3 +244,65 @@ def block_stats(kv: torch.Tensor, gamma_min: torch.Tensor, gamma_scale: torch.Te
         kv.data_ptr(), ctypes.byref(sh), ctypes.byref(p) if p else None,
         gamma_min.data_ptr(), gamma_scale.data_ptr(), mu.data_ptr(), sigma.data_ptr(),
         _stream(stream)))
+
+
+@dataclass
+class CodeView:
+    """One quantized tensor inside a Codes set: blocks [b0, b1) and whether the
+    residual stream takes part (False = anchor-only reconstruction)."""
+    codes: Codes
+    b0: int
+    b1: int
+    full: bool = True
+
+    def _ptr(self, t: torch.Tensor, per_block: int) -> int:
+        return t.data_ptr() + self.b0 * per_block * t.element_size()
+
+    def anchor(self) -> int:
+        return self._ptr(self.codes.anchor, self.codes.anchor[0].numel())
+
+    def residual(self):
+        return self._ptr(self.codes.residual, self.codes.residual[0].numel()) if self.full \
+            else None
+
+    def meta(self) -> lynx_meta:
+        c = self.codes
+        m = lynx_meta()
+        m.gamma_min = self._ptr(c.gamma_min, c.gamma_min[0].numel())
+        m.gamma_scale = self._ptr(c.gamma_scale, c.gamma_scale[0].numel())
+        m.mu = self._ptr(c.mu, c.mu[0].numel())
+        m.sigma = self._ptr(c.sigma, c.sigma[0].numel())
+        return m
+
+
+def attn_workspace_bytes(t_q: int, num_q_heads: int, num_kv_heads: int, ctx_len: int) -> int:
+    return int(lib().lynx_attn_workspace_bytes(t_q, num_q_heads, num_kv_heads, ctx_len))
+
+
+def decode_attn_dequant(q: torch.Tensor, k: CodeView, v: CodeView, ctx_len: int,
+                        num_kv_heads: int, scale: float, causal_tail: bool = False,
+                        p: lynx_params | None = None, out: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None, stream=None,
+                        out_dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """lynx_decode_attn_dequant: q bf16 [t_q, num_q_heads, 128] on the device;
+    k / v the code views of one [ctx_len, num_kv_heads * 128] tensor each;
+    the output is bf16 or float32 (out_dtype, or the dtype of `out`)."""
+    _require_cuda(q)
+    if q.dtype != torch.bfloat16 or q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous bf16 [t_q, num_q_heads, head_dim] tensor")
+    t_q, nqh, hd = q.shape
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    if out.dtype not in (torch.bfloat16, torch.float32) or out.shape != q.shape \
+            or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 or float32 tensor shaped like q")
+    code = OUT_F32 if out.dtype == torch.float32 else OUT_BF16
+    need = attn_workspace_bytes(t_q, nqh, num_kv_heads, ctx_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check("lynx_decode_attn_dequant", lib().lynx_decode_attn_dequant(
+        q.data_ptr(), t_q, nqh, k.anchor(), k.residual(), k.meta(), v.anchor(), v.residual(),
+        v.meta(), ctx_len, num_kv_heads, hd, scale, int(causal_tail),
+        ctypes.byref(p) if p else None, out.data_ptr(), code, workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out

@@ -179,3 +179,63 @@ def test_empty_shapes_are_no_ops():
                                      None) == 0
         assert L.lynx_dequant_anchor(None, _meta(None), ctypes.byref(s), None, None,
                                      None) == 0
+
+
+def test_attention_workspace_sizes():
+    """Split-KV workspace: splits x KV heads x padded rows x (2 + 128) floats,
+    about 1024 workgroups over the context pages."""
+    ws = lynx.attn_workspace_bytes
+    # decode, 64 q-heads over 8 KV heads at 32K: 8 rows -> 8, 128 pages, 128 splits
+    assert ws(1, 64, 8, 32768) == 128 * 8 * 8 * 130 * 4
+    # verify, 8 drafts x 32 q-heads over 4 KV heads at 128K: 64 rows, 256 splits of 2 pages
+    assert ws(8, 32, 4, 131072) == 256 * 4 * 64 * 130 * 4
+    # rows are padded to 8 / 16 / 32 / 64
+    assert ws(3, 8, 4, 1024) == 4 * 4 * 8 * 130 * 4
+    assert ws(5, 8, 4, 1024) == 4 * 4 * 16 * 130 * 4
+    # invalid plans report 0
+    assert ws(9, 64, 8, 32768) == 0      # 72 rows per KV head
+    assert ws(1, 6, 4, 1024) == 0        # not grouped-query
+    assert ws(1, 8, 8, 1000) == 0        # context not whole pages
+    assert ws(0, 8, 8, 1024) == 0
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("ok_shape_null_q", -1), ("group", -1), ("rows", -1), ("ctx", -2), ("head_dim", -1),
+    ("scale", -1), ("workspace", -1), ("null_v_meta", -1), ("misaligned_k", -2),
+    ("empty_ctx", -1), ("params", -1), ("out_dtype", -1)])
+def test_attention_argument_errors(case, expect):
+    """Malformed attention calls return their status before any launch."""
+    L = lynx.lib()
+    t_q, nqh, nkvh, ctx, hd, scale, causal = 1, 8, 2, 1024, 128, 0.088, 0
+    q, kanc, kres, vanc, vres, kmeta, vmeta = FAKE, FAKE, FAKE, FAKE, FAKE, _meta(), _meta()
+    wsb = 1 << 30
+    p = lynx.params()
+    odt = lynx.OUT_F32
+    if case == "ok_shape_null_q":
+        q = None
+    elif case == "group":
+        nqh = 7
+    elif case == "rows":
+        t_q = 17
+    elif case == "ctx":
+        ctx = 1000
+    elif case == "head_dim":
+        hd = 64
+    elif case == "scale":
+        scale = float("nan")
+    elif case == "workspace":
+        wsb = 64
+    elif case == "null_v_meta":
+        vmeta = _meta(None)
+    elif case == "misaligned_k":
+        kanc = FAKE + 4
+    elif case == "empty_ctx":
+        ctx, causal = 0, 1
+    elif case == "params":
+        p.alpha = -1.0
+    elif case == "out_dtype":
+        odt = 2
+    rc = L.lynx_decode_attn_dequant(q, t_q, nqh, kanc, kres, kmeta, vanc, vres, vmeta, ctx,
+                                    nkvh, hd, scale, causal, ctypes.byref(p), FAKE, odt, FAKE,
+                                    wsb, None)
+    assert rc == expect

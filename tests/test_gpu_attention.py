@@ -1,0 +1,127 @@
+"""GPU parity of the fused dequant + attention entry point.
+
+Reference: the oracle quantizes the same K and V, rebuilds K^ and V^ (anchor
+only or anchor + residual) and evaluates softmax(q K^T / sqrt(128)) V^ in
+binary64.  Bar (per query row and head) on the binary32 output: relative L2
+error <= 2e-3 and max |error| <= 2e-3 * max |reference|.  The bf16 output
+must be the round-to-nearest-even of the binary32 output, bit for bit (bf16
+rounding alone reaches 2^-8 relative, above the tolerance, so the tolerance
+is checked before it).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from progressive_kv_transfer_amd import kvgen, lynx
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL = 2e-3
+
+
+def announce(msg):
+    print(f"[gpu-attn] {msg}", flush=True)
+
+
+def run_case(kv, q, n_kvh, t_q, full_k, full_v, causal):
+    """kv: bf16 [2, ctx, n_kvh*128] device (K, V); q: bf16 [t_q, n_qh, 128]."""
+    ctx, ch = kv.shape[1], kv.shape[2]
+    n_qh = q.shape[1]
+    codes = lynx.quantize_pages(kv)
+    nb = codes.anchor.shape[0]
+    kview = lynx.CodeView(codes, 0, nb // 2, full_k)
+    vview = lynx.CodeView(codes, nb // 2, nb, full_v)
+    scale = 1.0 / math.sqrt(128.0)
+    out = lynx.decode_attn_dequant(q, kview, vview, ctx, n_kvh, scale, causal_tail=causal,
+                                   out_dtype=torch.float32)
+    out16 = lynx.decode_attn_dequant(q, kview, vview, ctx, n_kvh, scale, causal_tail=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(out16.view(torch.int16), out.to(torch.bfloat16).view(torch.int16))
+    # oracle side
+    xb = kvgen.bf16_bits(kv)
+    ref_codes = oracle.quantize(xb, threads=16)
+    khat = oracle.dequant(ref_codes, xb.shape, full_k, threads=16)[0].reshape(ctx, n_kvh, 128)
+    vhat = oracle.dequant(ref_codes, xb.shape, full_v, threads=16)[1].reshape(ctx, n_kvh, 128)
+    ref = oracle.attention(kvgen.bf16_bits(q), khat, vhat, 1.0 / math.sqrt(128.0), causal,
+                           threads=16)
+    got = out.cpu().double().numpy()
+    err = got - ref
+    worst = max(np.linalg.norm(err[r, h]) / np.linalg.norm(ref[r, h])
+                for r in range(t_q) for h in range(n_qh))
+    announce(f"worst per-head relative L2 error {worst:.3e}")
+    for r in range(t_q):
+        for h in range(n_qh):
+            nref = np.linalg.norm(ref[r, h])
+            assert np.linalg.norm(err[r, h]) <= TOL * nref, (r, h)
+            assert np.abs(err[r, h]).max() <= TOL * np.abs(ref[r, h]).max(), (r, h)
+    return got, ref
+
+
+@pytest.mark.parametrize("full", [False, True])
+def test_decode_small(full):
+    """1 query, 16 q-heads over 2 KV heads, 2048 tokens."""
+    announce(f"decode small full={full}")
+    kv = torch.stack([kvgen.kv_tensor(700 + i, 2048, 256, [3, 130], True, DEV)
+                      for i in range(2)])
+    q = kvgen.queries(701, 1, 16, device=DEV)
+    run_case(kv, q, 2, 1, full, full, False)
+
+
+def test_verify_small_causal():
+    """8 draft queries (rows 64 = 8 x group 8), causal tail, 4096 tokens."""
+    announce("verify small causal")
+    kv = torch.stack([kvgen.kv_tensor(710 + i, 4096, 256, [9], True, DEV) for i in range(2)])
+    q = kvgen.queries(711, 8, 16, device=DEV)
+    got, ref = run_case(kv, q, 2, 8, True, True, True)
+    # rows really differ by their visible prefix
+    assert not np.allclose(ref[0], ref[7])
+
+
+@pytest.mark.parametrize("t_q,n_qh,n_kvh", [(3, 8, 4), (2, 16, 1), (1, 4, 4), (4, 32, 4)])
+def test_other_geometries(t_q, n_qh, n_kvh):
+    """Padded row counts (6, 32, 1, 32 rows), MHA (group 1), one KV head."""
+    announce(f"geometry t_q={t_q} n_qh={n_qh} n_kvh={n_kvh}")
+    kv = torch.stack([kvgen.kv_tensor(720 + i, 1024, 128 * n_kvh, [], True, DEV)
+                      for i in range(2)])
+    q = kvgen.queries(721, t_q, n_qh, device=DEV)
+    run_case(kv, q, n_kvh, t_q, True, False, t_q > 1)
+
+
+def test_attention_argument_errors():
+    kv = torch.stack([kvgen.kv_tensor(730 + i, 256, 128, [], True, DEV) for i in range(2)])
+    codes = lynx.quantize_pages(kv)
+    k = lynx.CodeView(codes, 0, 1)
+    v = lynx.CodeView(codes, 1, 2)
+    q = kvgen.queries(731, 1, 2, device=DEV)
+    with pytest.raises(lynx.LynxError):   # 3 q-heads over 2 KV heads is not GQA
+        lynx.decode_attn_dequant(kvgen.queries(732, 1, 3, device=DEV), k, v, 256, 2, 0.1)
+    with pytest.raises(lynx.LynxError):   # too small a workspace
+        lynx.decode_attn_dequant(q, k, v, 256, 1, 0.1,
+                                 workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
+    with pytest.raises(lynx.LynxError):   # context not a multiple of 256
+        lynx.decode_attn_dequant(q, k, v, 200, 1, 0.1)
+
+
+@pytest.mark.parametrize("name,full", [("decode_attn_32k", False), ("decode_attn_32k", True),
+                                       ("decode_attn_32k_plain", False)])
+def test_decode_attn_32k(name, full):
+    """The decode workload: 1 query token, 64 q-heads over 8 KV heads,
+    32768 tokens, K/V from the single-page generator per head."""
+    announce(f"{name} full={full}")
+    cfg = kvgen.CONFIGS[name]
+    kv = cfg.make(DEV)
+    q = kvgen.queries(3000, 1, 64, device=DEV)
+    run_case(kv, q, 8, 1, full, full, False)
+
+
+def test_verify_attn_128k():
+    """The verification workload: 8 draft tokens x 32 q-heads over 4 KV heads,
+    131072 tokens, anchor + residual codes, causal among the drafts."""
+    announce("verify_attn_128k")
+    cfg = kvgen.CONFIGS["verify_attn_128k"]
+    kv = cfg.make(DEV)
+    q = kvgen.queries(4000, 8, 32, device=DEV)
+    run_case(kv, q, 4, 8, True, True, True)
