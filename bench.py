@@ -15,8 +15,18 @@ over its average launch time against the 8 TB/s HBM peak.  `cpu_baseline`
 times the CPU oracle (test infrastructure, never tuned) on a bounded sample
 of the same workload on this host.
 
+`attention` reports, beside the step, the fused dequant + attention calls
+(lynx_decode_attn_dequant) on their own workloads: decode (1 query token,
+64 q-heads over 8 KV heads, 32768 tokens; anchor-only and full codes) and
+draft verification (8 query tokens, 32 q-heads over 4 KV heads, 131072
+tokens, full codes, causal tail): average time per call over rotating copies
+of the codes (so the codes come from HBM, not the 256 MiB last-level
+cache), algorithmic code + metadata bytes per second against the HBM peak,
+and QK + PV flops per second.
+
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --profile-run      # a few steps only, for rocprofv3
+    python bench.py --attention-only   # the attention calls only
     python bench.py --copy-probe       # plain 1 GiB copy, PMC scale factor
     python bench.py --hbm-probe        # timed copy / read / write bandwidths
 """
@@ -54,7 +64,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qwen32b_16k.md")
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("lynx_quant.hip", "lynx_dequant.hip", "lynx_internal.h"):
+    for f in ("lynx_quant.hip", "lynx_dequant.hip", "lynx_recon.h", "lynx_internal.h"):
         with open(os.path.join(ROOT, "progressive_kv_transfer_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -147,6 +157,76 @@ def copy_probe(timed: bool = False):
     print(json.dumps(out))
 
 
+# (name, KV workload, t_q, q-heads, KV heads, full codes, causal tail, q seed)
+ATTENTION_CASES = [
+    ("decode_32k_anchor", "decode_attn_32k", 1, 64, 8, False, False, 3000),
+    ("decode_32k_full", "decode_attn_32k", 1, 64, 8, True, False, 3000),
+    ("verify_128k_full", "verify_attn_128k", 8, 32, 4, True, True, 4000),
+]
+ROTATE_BYTES = 640 << 20  # > the 256 MiB last-level cache
+
+
+def measure_attention(torch, kvgen, lynx, calls: int, warmup: int):
+    """Average time of lynx_decode_attn_dequant per call on each attention
+    workload, cycling over copies of the codes."""
+    stream = torch.cuda.current_stream()
+    res = {}
+    built = {}
+    for name, wl, t_q, nqh, nkvh, full, causal, qseed in ATTENTION_CASES:
+        cfg = kvgen.CONFIGS[wl]
+        if wl not in built:
+            kv = cfg.make("cuda")
+            built.clear()
+            built[wl] = lynx.quantize_pages(kv)
+            del kv
+        codes = built[wl]
+        ctx = cfg.num_tokens
+        nb = codes.anchor.shape[0]
+        per_copy = sum(t.numel() * t.element_size() for t in (codes.anchor, codes.gamma_min,
+                                                              codes.gamma_scale, codes.mu,
+                                                              codes.sigma))
+        if full:
+            per_copy += codes.residual.numel()
+        copies = [codes] + [lynx.Codes(*(t.clone() for t in (
+            codes.anchor, codes.residual, codes.gamma_min, codes.gamma_scale, codes.mu,
+            codes.sigma))) for _ in range(max(0, -(-ROTATE_BYTES // per_copy) - 1))]
+        views = [(lynx.CodeView(c, 0, nb // 2, full), lynx.CodeView(c, nb // 2, nb, full))
+                 for c in copies]
+        q = kvgen.queries(qseed, t_q, nqh, device="cuda")
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(lynx.attn_workspace_bytes(t_q, nqh, nkvh, ctx), dtype=torch.uint8,
+                         device="cuda")
+        scale = 1.0 / 128 ** 0.5
+        for i in range(warmup):
+            k, v = views[i % len(views)]
+            lynx.decode_attn_dequant(q, k, v, ctx, nkvh, scale, causal, out=out, workspace=ws,
+                                     stream=stream)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for i in range(calls):
+            k, v = views[i % len(views)]
+            lynx.decode_attn_dequant(q, k, v, ctx, nkvh, scale, causal, out=out, workspace=ws,
+                                     stream=stream)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        us = ev[0].elapsed_time(ev[1]) / calls * 1e3
+        algo = per_copy + q.numel() * 2 + out.numel() * 2
+        flops = 4.0 * t_q * nqh * 128 * ctx
+        res[name] = {"workload": wl, "t_q": t_q, "q_heads": nqh, "kv_heads": nkvh,
+                     "context": ctx, "codes": "anchor+residual" if full else "anchor",
+                     "causal_tail": causal, "us_per_call": round(us, 2),
+                     "algorithmic_bytes": int(algo),
+                     "GBps": round(algo / (us * 1e-6) / 1e9, 1),
+                     "hbm_frac": round(algo / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "TFLOPs": round(flops / (us * 1e-6) / 1e12, 2),
+                     "rotating_copies": len(copies)}
+        del views, copies
+    built.clear()
+    torch.cuda.synchronize()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -157,6 +237,9 @@ def main():
     ap.add_argument("--profile-run", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--hbm-probe", action="store_true")
+    ap.add_argument("--no-attention", action="store_true")
+    ap.add_argument("--attention-only", action="store_true")
+    ap.add_argument("--attention-calls", type=int, default=50)
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -176,6 +259,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     lynx.lib()
+    if args.attention_only:
+        print(json.dumps({"attention": measure_attention(torch, kvgen, lynx,
+                                                         args.attention_calls, 5)}), flush=True)
+        return
     cfg = kvgen.CONFIGS[WORKLOAD]
     dev = "cuda"
     kv = cfg.make(dev)
@@ -257,6 +344,9 @@ def main():
                      "algorithmic_bytes_per_launch": int(BYTES_PER_ELEM[dom] * n_elem)},
         "kernels": kern,
     }
+    if not args.no_attention and not args.profile_run:
+        del out_a, out_f
+        out["attention"] = measure_attention(torch, kvgen, lynx, args.attention_calls, 5)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = run_cpu_baseline(cfg, kv, args.cpu_budget)
     print(json.dumps(out), flush=True)

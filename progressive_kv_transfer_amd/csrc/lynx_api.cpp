@@ -268,10 +268,11 @@ int dequant_common(const uint8_t *anchor, const uint8_t *residual, lynx_meta met
     return LYNX_OK;
 }
 
-// Split-KV plan of an attention call: padded query rows, splits over the
-// context pages (about 1024 workgroups in total) and pages per split.
+// Split-KV plan of an attention call: query rows per KV head, splits of the
+// context into runs of 128-token steps (about two resident workgroups per
+// compute unit in total) and the workspace of their partials.
 struct AttnPlan {
-    int rows, rows_p, pages, splits, pps;
+    int rows, pages, splits, sps;
     size_t ws_bytes;
 };
 
@@ -284,16 +285,17 @@ int attn_plan(int t_q, int n_qh, int n_kvh, int64_t ctx, AttnPlan *pl) {
     if (rows > 64)
         return LYNX_EINVAL;
     pl->rows = (int)rows;
-    pl->rows_p = attn_padded_rows(pl->rows);
     pl->pages = (int)(ctx / kPage);
-    int target = 1024 / n_kvh;
-    if (target < 1)
-        target = 1;
-    if (target > pl->pages)
-        target = pl->pages;
-    pl->pps = (pl->pages + target - 1) / target;
-    pl->splits = (pl->pages + pl->pps - 1) / pl->pps;
-    pl->ws_bytes = (size_t)pl->splits * n_kvh * pl->rows_p * (2 + kHead) * sizeof(float);
+    const int64_t steps = ctx / 128;
+    const int64_t target_wgs = 512;
+    int64_t sps = (steps * n_kvh + target_wgs - 1) / target_wgs;
+    if (sps < 1)
+        sps = 1;
+    if (sps > steps)
+        sps = steps;
+    pl->sps = (int)sps;
+    pl->splits = (int)((steps + sps - 1) / sps);
+    pl->ws_bytes = (size_t)pl->splits * n_kvh * pl->rows * (2 + kHead) * sizeof(float);
     return LYNX_OK;
 }
 
@@ -465,7 +467,7 @@ int lynx_decode_attn_dequant(const void *q, int t_q, int num_q_heads, const uint
     a.rows = pl.rows;
     a.pages = pl.pages;
     a.splits = pl.splits;
-    a.pages_per_split = pl.pps;
+    a.steps_per_split = pl.sps;
     a.causal = causal_tail ? 1 : 0;
     a.qk_scale_log2 = (float)((double)scale * 1.4426950408889634);
     return hip_status(launch_attention(a, tab, stream));

@@ -7,235 +7,410 @@
 // decode; T query tokens with a causal tail are the single parallel forward
 // pass that verifies T drafts (Section 4.3).
 //
-// Split-KV: workgroup (kv head h, split s) walks pages [s*pps, (s+1)*pps) of
-// its head for all M = T * group query rows that read that head (GQA), and
-// leaves a partial (running max, running sum, unnormalised output) per row in
-// the workspace; attn_combine_kernel merges the splits.
-//
-// Per 32-token chunk of a page: every lane rebuilds 2 channels x 8 tokens of
-// K^ and of V^ into LDS (bf16 pairs, rows padded to 68 dwords so row reads
-// spread over the banks); scores come from v_dot2_f32_bf16 with the lane's
-// query row kept as 64 packed bf16 pairs in registers (products of bf16 are
-// exact in binary32); an online softmax in base 2 (scores pre-multiplied by
-// scale * log2 e, v_exp_f32); the P V^ update accumulates binary32.
+// Work split.  The M = T * group query rows that read one KV head form RT
+// tiles of 16 rows (M <= 64).  Workgroup (kv head, split) walks a run of
+// 128-token steps (half a page) of its head:
+//   1. every lane rebuilds 32 tokens x 2 channels of K^ and of V^ of the
+//      step from codes prefetched into registers during the previous step,
+//      into LDS (K^ as [token][channel], V^ as [channel][token]), then
+//      issues the loads of the next step;
+//   2. wave w takes row tile w % RT and RT of the step's four 32-token
+//      chunks, and per chunk computes S^T = K^ Q^T with
+//      v_mfma_f32_16x16x32_bf16 (A = K^ rows from LDS, B = Q^T held in
+//      registers; products of bf16 are exact in binary32), an online
+//      softmax in base 2 on the 8 scores each lane holds, and
+//      O^T += V^T P^T with the same MFMA (A = V^ rows from LDS,
+//      B = P^T split into a bf16 high and low part, so P keeps ~16 bits).
+// In this orientation every lane owns one query row in both products, so the
+// running max, sum and output rescale stay lane-local; the four lanes that
+// share a row agree on the max through two lane swaps.  The running max is
+// only moved when a chunk exceeds it by more than 2^8 (weights stay <= 256),
+// which skips most output rescales.  At the end the waves of a row tile are
+// merged in LDS and each live row leaves one partial (max, sum, output) per
+// split in the workspace; attn_combine_kernel merges the splits.
 #include "lynx_recon.h"
 
 namespace lynx {
-
 namespace {
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kAttnThreads = 256;
-constexpr int kRowDw = 68;  // dwords per rebuilt K^ / V^ row in LDS (64 + pad)
-constexpr int kPartial = 2 + kHead;
+constexpr int kStep = 128;               // tokens per step (half a page)
+constexpr int kRowDw = 68;               // dwords per LDS row: 64 + 4 pad
+constexpr int kKDw = kStep * kRowDw;     // K^ [128 tokens][128 channels]
+constexpr int kVDw = kHead * kRowDw;     // V^ [128 channel rows][128 tokens]
+constexpr int kPartial = 2 + kHead;      // max, sum, output
+constexpr int kMergeRow = 132;           // floats per row in the LDS merge area
+constexpr float kLazyLog2 = 8.0f;        // move the max only beyond 2^8
 
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
-                                           __builtin_bit_cast(bf16x2, b), c, false);
+// Codes and metadata of one tensor for one lane's 32 tokens x channel pair.
+struct LaneCodes {
+    u32x4 a0, a1, r0, r1;
+    float2 gm, gs, mu, sg;
+};
+
+__device__ __forceinline__ void load_codes(const uint8_t *anc, const uint8_t *res,
+                                           const float *gmin, const float *gsc, const float *mu,
+                                           const float *sg, int64_t b, int j, int p,
+                                           LaneCodes &L) {
+    const int64_t coff = b * (kPage * kHead / 2) + j * (kHead / 2 * kChunk) + p * kChunk;
+    L.a0 = *(const u32x4 *)(anc + coff);
+    L.a1 = *(const u32x4 *)(anc + coff + 16);
+    if (res) {
+        L.r0 = *(const u32x4 *)(res + coff);
+        L.r1 = *(const u32x4 *)(res + coff + 16);
+    } else {
+        L.r0 = u32x4{0u, 0u, 0u, 0u};
+        L.r1 = u32x4{0u, 0u, 0u, 0u};
+    }
+    L.gm = *(const float2 *)(gmin + b * kHead + 2 * p);
+    L.gs = *(const float2 *)(gsc + b * kHead + 2 * p);
+    L.mu = *(const float2 *)(mu + b * (kChunks * kHead) + j * kHead + 2 * p);
+    L.sg = *(const float2 *)(sg + b * (kChunks * kHead) + j * kHead + 2 * p);
 }
 
-// Rebuild 2 channels (pair p) x 8 tokens (8 qt .. 8 qt + 7) of chunk j of
-// page block b into LDS rows dst[token][p] as packed bf16 pairs.
-__device__ __forceinline__ void rebuild_pair(const uint8_t *anc, const uint8_t *res,
-                                             const float *gmin, const float *gsc,
-                                             const float *mu, const float *sg, float eps,
-                                             const float *lut, int64_t b, int j, int p, int qt,
-                                             uint32_t *dst) {
-    const int64_t coff = b * (kPage * kHead / 2) + j * (kHead / 2 * kChunk) + p * kChunk + 8 * qt;
-    const u32x2 A = *(const u32x2 *)(anc + coff);
-    const u32x2 R = res ? *(const u32x2 *)(res + coff) : u32x2{0u, 0u};
-    const float2 gm = *(const float2 *)(gmin + b * kHead + 2 * p);
-    const float2 gs = *(const float2 *)(gsc + b * kHead + 2 * p);
-    const float2 um = *(const float2 *)(mu + b * (kChunks * kHead) + j * kHead + 2 * p);
-    const float2 sq = *(const float2 *)(sg + b * (kChunks * kHead) + j * kHead + 2 * p);
-    const float d1a = gs.x + eps, d1b = gs.y + eps, d2a = sq.x + eps, d2b = sq.y + eps;
+// Rebuild 4 tokens of channel pair (2p, 2p+1) from one anchor word and one
+// residual word (a byte per token).  lut is indexed by anchor nibble |
+// residual nibble << 4 (residual 0 = anchor-only).
+__device__ __forceinline__ void rebuild_word(uint32_t A, uint32_t R, const LaneCodes &L,
+                                             float eps, const float *lut, float y0[4],
+                                             float y1[4]) {
+    const uint32_t X = (A & 0x0f0f0f0fu) | ((R << 4) & 0xf0f0f0f0u);  // channel 2p
+    const uint32_t Y = ((A >> 4) & 0x0f0f0f0fu) | (R & 0xf0f0f0f0u);  // channel 2p + 1
+    const float d1a = L.gs.x + eps, d1b = L.gs.y + eps;
+    const float d2a = L.sg.x + eps, d2b = L.sg.y + eps;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint32_t ab = (A[i >> 2] >> (8 * (i & 3))) & 0xffu;
-        const uint32_t rb = (R[i >> 2] >> (8 * (i & 3))) & 0xffu;
-        const uint32_t i0 = (ab & 15u) | ((rb & 15u) << 4);  // channel 2p
-        const uint32_t i1 = (ab >> 4) | (rb & 0xf0u);         // channel 2p + 1
-        const float y0 = reconstruct(lut[i0], d2a, um.x, d1a, gm.x);
-        const float y1 = reconstruct(lut[i1], d2b, um.y, d1b, gm.y);
-        dst[(8 * qt + i) * kRowDw + p] = pack_bf16(y0, y1);
+    for (int i = 0; i < 4; ++i) {
+        y0[i] = reconstruct(lut[(X >> (8 * i)) & 0xffu], d2a, L.mu.x, d1a, L.gm.x);
+        y1[i] = reconstruct(lut[(Y >> (8 * i)) & 0xffu], d2b, L.mu.y, d1b, L.gm.y);
     }
 }
 
-template <int ROWS>  // padded rows: 8, 16, 32 or 64
-__global__ __launch_bounds__(kAttnThreads) void attn_partial_kernel(AttnArgs a,
-                                                                    const DequantTab tab) {
-    constexpr int kLpr = kAttnThreads / ROWS;  // lanes per query row
-    constexpr int kTpl = kChunk / kLpr;        // scores per lane per chunk
-    constexpr int kCpl = kHead / kLpr;         // output channels per lane
+// K^ rows: [token][channel] bf16; the lane writes dword p (channels 2p,
+// 2p + 1) of its 32 tokens.
+__device__ __forceinline__ void store_k(const LaneCodes &L, float eps, const float *lut, int p,
+                                        int c, uint32_t *sK) {
+    const u32x4 a[2] = {L.a0, L.a1}, r[2] = {L.r0, L.r1};
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+        float y0[4], y1[4];
+        rebuild_word(a[w >> 2][w & 3], r[w >> 2][w & 3], L, eps, lut, y0, y1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            sK[(32 * c + 4 * w + i) * kRowDw + p] = pack_bf16(y0[i], y1[i]);
+    }
+}
 
-    __shared__ float s_lut_k[256], s_lut_v[256];
-    __shared__ __attribute__((aligned(16))) uint32_t s_k[kChunk * kRowDw];
-    __shared__ __attribute__((aligned(16))) uint32_t s_v[kChunk * kRowDw];
-    __shared__ float s_s[ROWS][kChunk + 1];
+// V^ rows: row p holds channel 2p, row 64 + p channel 2p + 1, each as 128
+// tokens of bf16; the lane writes tokens 32c .. 32c + 31 of both rows.
+__device__ __forceinline__ void store_v(const LaneCodes &L, float eps, const float *lut, int p,
+                                        int c, uint32_t *sV) {
+    const u32x4 a[2] = {L.a0, L.a1}, r[2] = {L.r0, L.r1};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        float y0[8], y1[8];
+        rebuild_word(a[q >> 1][2 * (q & 1)], r[q >> 1][2 * (q & 1)], L, eps, lut, y0, y1);
+        rebuild_word(a[q >> 1][2 * (q & 1) + 1], r[q >> 1][2 * (q & 1) + 1], L, eps, lut,
+                     y0 + 4, y1 + 4);
+        const u32x4 e = {pack_bf16(y0[0], y0[1]), pack_bf16(y0[2], y0[3]),
+                         pack_bf16(y0[4], y0[5]), pack_bf16(y0[6], y0[7])};
+        const u32x4 o = {pack_bf16(y1[0], y1[1]), pack_bf16(y1[2], y1[3]),
+                         pack_bf16(y1[4], y1[5]), pack_bf16(y1[6], y1[7])};
+        *(u32x4 *)(sV + p * kRowDw + 16 * c + 4 * q) = e;
+        *(u32x4 *)(sV + (64 + p) * kRowDw + 16 * c + 4 * q) = o;
+    }
+}
+
+// Max / sum over the lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lanes of a row).
+__device__ __forceinline__ float row_max4(float x) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                              false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                              false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float row_sum4(float x) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                              false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                              false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Channel held by LDS V^ row rho.
+__device__ __forceinline__ int v_row_channel(int rho) {
+    return rho < 64 ? 2 * rho : 2 * (rho - 64) + 1;
+}
+
+template <int RT>  // row tiles of 16: 1, 2 or 4
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(AttnArgs a,
+                                                                       const DequantTab tab) {
+    constexpr int kWavesPerTile = 4 / RT;
+
+    __shared__ __attribute__((aligned(16))) uint32_t sK[kKDw];
+    __shared__ __attribute__((aligned(16))) uint32_t sV[kVDw];
+    __shared__ float s_lut[256];
 
     const int tid = (int)__builtin_amdgcn_workitem_id_x();
     const int wg = (int)__builtin_amdgcn_workgroup_id_x();
     const int kvh = wg % a.n_kvh;
     const int split = wg / a.n_kvh;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
 
-    for (int e = tid; e < 256; e += kAttnThreads) {
-        s_lut_k[e] = signed_level(tab, a.k_res ? e : (e & 15), a.k_res != nullptr);
-        s_lut_v[e] = signed_level(tab, a.v_res ? e : (e & 15), a.v_res != nullptr);
-    }
+    s_lut[tid] = signed_level(tab, tid, true);
 
-    // This lane's query row (scores and output), rows >= a.rows are padding.
-    const int h = tid / kLpr;
-    const int sub = tid % kLpr;
+    // Steps [st0, st1) of this split.
+    const int steps = a.pages * 2;
+    const int st0 = split * a.steps_per_split;
+    const int st1 = min(steps, st0 + a.steps_per_split);
+
+    // Rebuild role: channel pair p, chunk (= wave) c_fill of the step.
+    const int p = lane;
+    const int c_fill = wave;
+
+    // MFMA role: row tile rt, query row h = 16 rt + lane % 16, k-group g.
+    const int rt = wave % RT;
+    const int r16 = lane & 15;
+    const int g = lane >> 4;
+    const int h = 16 * rt + r16;
     const bool live = h < a.rows;
-    const int r = live ? h / a.group : 0;
-    const int qh = live ? kvh * a.group + h % a.group : 0;
-    const int64_t limit = a.causal ? a.ctx - a.t_q + r : a.ctx - 1;
-    uint32_t q2[64];
+    bf16x8 qreg[4];
     {
-        const u32x4 *qp = (const u32x4 *)(a.q + ((int64_t)r * a.n_qh + qh) * kHead);
+        const int r = live ? h / a.group : 0;
+        const int qh = live ? kvh * a.group + h % a.group : 0;
+        const uint16_t *qp = a.q + ((int64_t)r * a.n_qh + qh) * kHead + 8 * g;
 #pragma unroll
-        for (int w = 0; w < 16; ++w) {
-            u32x4 v = live ? qp[w] : u32x4{0u, 0u, 0u, 0u};
-            q2[4 * w] = v[0];
-            q2[4 * w + 1] = v[1];
-            q2[4 * w + 2] = v[2];
-            q2[4 * w + 3] = v[3];
+        for (int kb = 0; kb < 4; ++kb) {
+            const u32x4 v = live ? *(const u32x4 *)(qp + 32 * kb) : u32x4{0u, 0u, 0u, 0u};
+            qreg[kb] = as_bf16x8(v);
         }
     }
-    float m_run = -INFINITY, l_run = 0.0f;
-    float o[kCpl];
-#pragma unroll
-    for (int c = 0; c < kCpl; ++c) o[c] = 0.0f;
+    // Last visible position of this lane's row.
+    const int64_t limit =
+        a.causal ? a.ctx - a.t_q + (live ? h / a.group : a.t_q - 1) : a.ctx - 1;
+    const float cs = a.qk_scale_log2;
+    const float lazy = kLazyLog2 / cs;
 
-    const int p = tid & 63;   // rebuild: channel pair
-    const int qt = tid >> 6;  // rebuild: tokens 8 qt .. 8 qt + 7
-    const int pg0 = split * a.pages_per_split;
-    const int pg1 = min(a.pages, pg0 + a.pages_per_split);
-    __syncthreads();
-    for (int pg = pg0; pg < pg1; ++pg) {
-        const int64_t b = (int64_t)pg * a.n_kvh + kvh;
-        for (int j = 0; j < kChunks; ++j) {
-            const int64_t pos0 = (int64_t)pg * kPage + j * kChunk;
-            rebuild_pair(a.k_anc, a.k_res, a.k_gmin, a.k_gsc, a.k_mu, a.k_sg, tab.eps, s_lut_k,
-                         b, j, p, qt, s_k);
-            rebuild_pair(a.v_anc, a.v_res, a.v_gmin, a.v_gsc, a.v_mu, a.v_sg, tab.eps, s_lut_v,
-                         b, j, p, qt, s_v);
-            __syncthreads();
-            // scores of row h for tokens sub + k * kLpr
+    float m_run = -INFINITY;  // running max of raw scores q.k
+    float l_run = 0.0f;       // this lane's share of the row sum
+    f32x4 o[8];
 #pragma unroll
-            for (int k = 0; k < kTpl; ++k) {
-                const int t = sub + k * kLpr;
-                const u32x4 *kr = (const u32x4 *)(s_k + t * kRowDw);
-                float acc0 = 0.0f, acc1 = 0.0f;
-#pragma unroll
-                for (int w = 0; w < 16; ++w) {
-                    const u32x4 kv = kr[w];
-                    acc0 = dot2(q2[4 * w], kv[0], acc0);
-                    acc1 = dot2(q2[4 * w + 1], kv[1], acc1);
-                    acc0 = dot2(q2[4 * w + 2], kv[2], acc0);
-                    acc1 = dot2(q2[4 * w + 3], kv[3], acc1);
-                }
-                const float s = (acc0 + acc1) * a.qk_scale_log2;
-                s_s[h][t] = (live && pos0 + t <= limit) ? s : -INFINITY;
-            }
-            __syncthreads();
-            // online softmax over the chunk, then O += P V^
-            float mc = -INFINITY;
-#pragma unroll
-            for (int t = 0; t < kChunk; ++t) mc = fmaxf(mc, s_s[h][t]);
-            const float m_new = fmaxf(m_run, mc);
-            const bool none = m_new == -INFINITY;
-            const float corr = none ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-            l_run *= corr;
-#pragma unroll
-            for (int c = 0; c < kCpl; ++c) o[c] *= corr;
-            const int c0 = sub * kCpl;
-#pragma unroll 8
-            for (int t = 0; t < kChunk; ++t) {
-                const float pt = none ? 0.0f : __builtin_amdgcn_exp2f(s_s[h][t] - m_new);
-                l_run += pt;
-                const uint32_t *vr = s_v + t * kRowDw + c0 / 2;
-#pragma unroll
-                for (int c = 0; c < kCpl; c += 2) {
-                    const uint32_t w = vr[c / 2];
-                    o[c] = __builtin_fmaf(pt, __uint_as_float(w << 16), o[c]);
-                    o[c + 1] = __builtin_fmaf(pt, __uint_as_float(w & 0xffff0000u), o[c + 1]);
-                }
-            }
-            m_run = m_new;
-            __syncthreads();  // s_k, s_v and s_s are rewritten by the next chunk
+    for (int mt = 0; mt < 8; ++mt) o[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    LaneCodes ck, cv;
+    if (st0 < st1) {
+        const int64_t b = (int64_t)(st0 >> 1) * a.n_kvh + kvh;
+        const int j = (st0 & 1) * 4 + c_fill;
+        load_codes(a.k_anc, a.k_res, a.k_gmin, a.k_gsc, a.k_mu, a.k_sg, b, j, p, ck);
+        load_codes(a.v_anc, a.v_res, a.v_gmin, a.v_gsc, a.v_mu, a.v_sg, b, j, p, cv);
+    }
+    __syncthreads();  // s_lut
+
+    for (int st = st0; st < st1; ++st) {
+        store_k(ck, tab.eps, s_lut, p, c_fill, sK);
+        store_v(cv, tab.eps, s_lut, p, c_fill, sV);
+        if (st + 1 < st1) {
+            const int64_t b = (int64_t)((st + 1) >> 1) * a.n_kvh + kvh;
+            const int j = ((st + 1) & 1) * 4 + c_fill;
+            load_codes(a.k_anc, a.k_res, a.k_gmin, a.k_gsc, a.k_mu, a.k_sg, b, j, p, ck);
+            load_codes(a.v_anc, a.v_res, a.v_gmin, a.v_gsc, a.v_mu, a.v_sg, b, j, p, cv);
         }
-    }
-    float *part = a.ws + (((int64_t)split * a.n_kvh + kvh) * ROWS + h) * kPartial;
-    if (sub == 0) {
-        part[0] = m_run;
-        part[1] = l_run;
-    }
+        __syncthreads();
+
+        const int64_t tok0 = (int64_t)st * kStep;
+        const bool need_mask = tok0 + kStep - 1 > a.ctx - a.t_q;  // uniform
 #pragma unroll
-    for (int c = 0; c < kCpl; ++c) part[2 + sub * kCpl + c] = o[c];
+        for (int ci = 0; ci < RT; ++ci) {
+            const int c = wave / RT + kWavesPerTile * ci;
+            // S^T tiles: s[tt][e] is the score of token 32c + 16 tt + 4g + e.
+            f32x4 s[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+            const uint32_t *kr = sK + (32 * c + r16) * kRowDw + 4 * g;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const bf16x8 a0 = as_bf16x8(*(const u32x4 *)(kr + 16 * kb));
+                const bf16x8 a1 = as_bf16x8(*(const u32x4 *)(kr + 16 * kRowDw + 16 * kb));
+                s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qreg[kb], s[0], 0, 0, 0);
+                s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qreg[kb], s[1], 0, 0, 0);
+            }
+            if (need_mask) {
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (tok0 + 32 * c + 16 * tt + 4 * g + e > limit) s[tt][e] = -INFINITY;
+            }
+            float mc = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                             fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+            mc = row_max4(mc);
+            const bool grow = mc > m_run + lazy;
+            if (__builtin_amdgcn_ballot_w64(grow)) {
+                const float corr = grow ? __builtin_amdgcn_exp2f((m_run - mc) * cs) : 1.0f;
+                l_run *= corr;
+#pragma unroll
+                for (int mt = 0; mt < 8; ++mt) o[mt] *= corr;
+                m_run = grow ? mc : m_run;
+            }
+            const float base = m_run == -INFINITY ? 0.0f : m_run * cs;
+            float pr[8];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    pr[4 * tt + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tt][e], cs, -base));
+                    l_run += pr[4 * tt + e];
+                }
+            // P^T operands: k-slot 8g + e' <-> token 16 (e' / 4) + 4g + e' % 4.
+            u32x4 hi, lo;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t hw = pack_bf16(pr[2 * i], pr[2 * i + 1]);
+                hi[i] = hw;
+                lo[i] = pack_bf16(pr[2 * i] - __uint_as_float(hw << 16),
+                                  pr[2 * i + 1] - __uint_as_float(hw & 0xffff0000u));
+            }
+            const bf16x8 phi = as_bf16x8(hi), plo = as_bf16x8(lo);
+            const uint32_t *vr = sV + r16 * kRowDw + 16 * c + 2 * g;
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) {
+                const u32x2 t0 = *(const u32x2 *)(vr + 16 * mt * kRowDw);
+                const u32x2 t1 = *(const u32x2 *)(vr + 16 * mt * kRowDw + 8);
+                const bf16x8 av = as_bf16x8(u32x4{t0[0], t0[1], t1[0], t1[1]});
+                o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, phi, o[mt], 0, 0, 0);
+                o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, plo, o[mt], 0, 0, 0);
+            }
+        }
+        __syncthreads();  // sK / sV are refilled by the next step
+    }
+
+    // Merge the waves of each row tile in LDS (reusing the K^ area), then
+    // write one partial per live row.
+    const float l_row = row_sum4(l_run);
+    float *sm = (float *)sK;  // [wave][16 rows][kMergeRow]: max, sum, -, -, 128 outputs
+    {
+        float *row = sm + (wave * 16 + r16) * kMergeRow;
+        if (g == 0) {
+            row[0] = m_run == -INFINITY ? -INFINITY : m_run * cs;
+            row[1] = l_row;
+        }
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) row[4 + v_row_channel(16 * mt + 4 * g + e)] = o[mt][e];
+    }
+    __syncthreads();
+    float *part = a.ws + ((int64_t)split * a.n_kvh + kvh) * a.rows * kPartial;
+    for (int idx = tid; idx < a.rows * kHead; idx += kAttnThreads) {
+        const int hr = idx >> 7, ch = idx & (kHead - 1);
+        const int t = hr >> 4, rr = hr & 15;
+        float M = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < kWavesPerTile; ++k)
+            M = fmaxf(M, sm[((t + RT * k) * 16 + rr) * kMergeRow]);
+        float l = 0.0f, acc = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kWavesPerTile; ++k) {
+            const float *row = sm + ((t + RT * k) * 16 + rr) * kMergeRow;
+            const float w = row[0] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(row[0] - M);
+            l = __builtin_fmaf(row[1], w, l);
+            acc = __builtin_fmaf(row[4 + ch], w, acc);
+        }
+        float *dst = part + hr * kPartial;
+        if (ch == 0) {
+            dst[0] = M;
+            dst[1] = l;
+        }
+        dst[2 + ch] = acc;
+    }
 }
 
-// One workgroup of 128 lanes per (kv head, live row): lane c merges channel
-// c over the splits and writes the bf16 output.
-template <int ROWS>
-__global__ __launch_bounds__(kHead) void attn_combine_kernel(AttnArgs a) {
+// One workgroup of 256 lanes per (kv head, live row): the maximum over the
+// splits, then lanes (half, channel) accumulate alternate splits.
+__global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(AttnArgs a) {
+    __shared__ float s_red[kAttnThreads];
+    __shared__ float s_acc[kHead + 1];
     const int wg = (int)__builtin_amdgcn_workgroup_id_x();
     const int kvh = wg % a.n_kvh;
     const int h = wg / a.n_kvh;
-    const int c = (int)__builtin_amdgcn_workitem_id_x();
+    const int tid = (int)__builtin_amdgcn_workitem_id_x();
+    const int64_t split_stride = (int64_t)a.n_kvh * a.rows * kPartial;
+    const float *base = a.ws + ((int64_t)kvh * a.rows + h) * kPartial;
+
     float m = -INFINITY;
-    for (int s = 0; s < a.splits; ++s)
-        m = fmaxf(m, a.ws[(((int64_t)s * a.n_kvh + kvh) * ROWS + h) * kPartial]);
+    for (int s = tid; s < a.splits; s += kAttnThreads) m = fmaxf(m, base[s * split_stride]);
+    s_red[tid] = m;
+    __syncthreads();
+    for (int w = kAttnThreads / 2; w > 0; w >>= 1) {
+        if (tid < w) s_red[tid] = fmaxf(s_red[tid], s_red[tid + w]);
+        __syncthreads();
+    }
+    const float M = s_red[0];
+    const int half = tid >> 7, c = tid & (kHead - 1);
     float l = 0.0f, acc = 0.0f;
-    if (m != -INFINITY) {
-        for (int s = 0; s < a.splits; ++s) {
-            const float *part = a.ws + (((int64_t)s * a.n_kvh + kvh) * ROWS + h) * kPartial;
-            const float w = __builtin_amdgcn_exp2f(part[0] - m);
-            l = __builtin_fmaf(part[1], w, l);
-            acc = __builtin_fmaf(part[2 + c], w, acc);
+    if (M != -INFINITY) {
+#pragma unroll 4
+        for (int s = half; s < a.splits; s += 2) {
+            const float *pt = base + s * split_stride;
+            const float ms = pt[0];
+            const float w = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
+            l = __builtin_fmaf(pt[1], w, l);
+            acc = __builtin_fmaf(pt[2 + c], w, acc);
         }
     }
-    const float y = l > 0.0f ? acc / l : 0.0f;
-    const int r = h / a.group;
-    const int qh = kvh * a.group + h % a.group;
-    const int64_t at = ((int64_t)r * a.n_qh + qh) * kHead + c;
-    if (a.out_f32)
-        ((float *)a.out)[at] = y;
-    else
-        ((uint16_t *)a.out)[at] = (uint16_t)(pack_bf16(y, 0.0f) & 0xffffu);
+    if (half == 1) {
+        s_acc[c] = acc;
+        if (c == 0) s_acc[kHead] = l;
+    }
+    __syncthreads();
+    if (half == 0) {
+        acc += s_acc[c];
+        l += s_acc[kHead];
+        const float y = l > 0.0f ? acc / l : 0.0f;
+        const int r = h / a.group;
+        const int qh = kvh * a.group + h % a.group;
+        const int64_t at = ((int64_t)r * a.n_qh + qh) * kHead + c;
+        if (a.out_f32)
+            ((float *)a.out)[at] = y;
+        else
+            ((uint16_t *)a.out)[at] = (uint16_t)(pack_bf16(y, 0.0f) & 0xffffu);
+    }
 }
 
-template <int ROWS>
-hipError_t launch_rows(const AttnArgs &a, const DequantTab &tab, hipStream_t stream) {
-    hipLaunchKernelGGL(attn_partial_kernel<ROWS>, dim3((unsigned)(a.n_kvh * a.splits)),
+template <int RT>
+hipError_t launch_tiles(const AttnArgs &a, const DequantTab &tab, hipStream_t stream) {
+    hipLaunchKernelGGL(attn_partial_kernel<RT>, dim3((unsigned)(a.n_kvh * a.splits)),
                        dim3(kAttnThreads), 0, stream, a, tab);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(attn_combine_kernel<ROWS>, dim3((unsigned)(a.n_kvh * a.rows)), dim3(kHead),
-                       0, stream, a);
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(a.n_kvh * a.rows)),
+                       dim3(kAttnThreads), 0, stream, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-int attn_padded_rows(int rows) {
-    return rows <= 8 ? 8 : rows <= 16 ? 16 : rows <= 32 ? 32 : rows <= 64 ? 64 : -1;
+int attn_row_tiles(int rows) {
+    return rows < 1 ? -1 : rows <= 16 ? 1 : rows <= 32 ? 2 : rows <= 64 ? 4 : -1;
 }
 
 hipError_t launch_attention(const AttnArgs &a, const DequantTab &tab, hipStream_t stream) {
-    switch (attn_padded_rows(a.rows)) {
-    case 8:
-        return launch_rows<8>(a, tab, stream);
-    case 16:
-        return launch_rows<16>(a, tab, stream);
-    case 32:
-        return launch_rows<32>(a, tab, stream);
-    case 64:
-        return launch_rows<64>(a, tab, stream);
+    switch (attn_row_tiles(a.rows)) {
+    case 1:
+        return launch_tiles<1>(a, tab, stream);
+    case 2:
+        return launch_tiles<2>(a, tab, stream);
+    case 4:
+        return launch_tiles<4>(a, tab, stream);
     default:
         return hipErrorInvalidValue;
     }

@@ -71,17 +71,17 @@ struct AttnArgs {
     const uint8_t *k_anc, *k_res, *v_anc, *v_res;
     const float *k_gmin, *k_gsc, *k_mu, *k_sg;
     const float *v_gmin, *v_gsc, *v_mu, *v_sg;
-    float *ws;      // partials [split][kv head][padded row][2 + 128]
+    float *ws;      // partials [split][kv head][row][2 + 128]
     void *out;      // [t_q][n_qh][128], bf16 or binary32
     int64_t ctx;    // context tokens (multiple of 256)
     int n_qh, n_kvh, group, t_q;
     int rows;       // t_q * group
-    int pages, splits, pages_per_split;
+    int pages, splits, steps_per_split;  // steps of 128 tokens
     int causal;
     int out_f32;
     float qk_scale_log2;  // scale * log2(e)
 };
-int attn_padded_rows(int rows);
+int attn_row_tiles(int rows);  // tiles of 16 query rows, -1 if rows > 64
 hipError_t launch_attention(const AttnArgs &a, const DequantTab &tab, hipStream_t stream);
 
 }  // namespace lynx

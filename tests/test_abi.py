@@ -182,16 +182,17 @@ def test_empty_shapes_are_no_ops():
 
 
 def test_attention_workspace_sizes():
-    """Split-KV workspace: splits x KV heads x padded rows x (2 + 128) floats,
-    about 1024 workgroups over the context pages."""
+    """Split-KV workspace: splits x KV heads x query rows x (2 + 128) floats,
+    splits cutting the context into runs of 128-token steps so that about 512
+    workgroups run."""
     ws = lynx.attn_workspace_bytes
-    # decode, 64 q-heads over 8 KV heads at 32K: 8 rows -> 8, 128 pages, 128 splits
-    assert ws(1, 64, 8, 32768) == 128 * 8 * 8 * 130 * 4
-    # verify, 8 drafts x 32 q-heads over 4 KV heads at 128K: 64 rows, 256 splits of 2 pages
-    assert ws(8, 32, 4, 131072) == 256 * 4 * 64 * 130 * 4
-    # rows are padded to 8 / 16 / 32 / 64
-    assert ws(3, 8, 4, 1024) == 4 * 4 * 8 * 130 * 4
-    assert ws(5, 8, 4, 1024) == 4 * 4 * 16 * 130 * 4
+    # decode, 64 q-heads over 8 KV heads at 32K: 8 rows, 256 steps, 4 per split
+    assert ws(1, 64, 8, 32768) == 64 * 8 * 8 * 130 * 4
+    # verify, 8 drafts x 32 q-heads over 4 KV heads at 128K: 64 rows, 8 steps per split
+    assert ws(8, 32, 4, 131072) == 128 * 4 * 64 * 130 * 4
+    # small contexts: one step per split
+    assert ws(3, 8, 4, 1024) == 8 * 4 * 6 * 130 * 4
+    assert ws(5, 8, 4, 1024) == 8 * 4 * 10 * 130 * 4
     # invalid plans report 0
     assert ws(9, 64, 8, 32768) == 0      # 72 rows per KV head
     assert ws(1, 6, 4, 1024) == 0        # not grouped-query
