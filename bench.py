@@ -26,14 +26,13 @@ and QK + PV flops per second.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --profile-run      # a few steps only, for rocprofv3
-    python bench.py --attention-only   # the attention calls only
+    python bench.py --attention-only [--attention-case NAME]   # attention calls only
     python bench.py --copy-probe       # plain 1 GiB copy, PMC scale factor
     python bench.py --hbm-probe        # timed copy / read / write bandwidths
 """
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -62,14 +61,6 @@ KERNEL_SYMBOL = {
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qwen32b_16k.md")
 
 
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for f in ("lynx_quant.hip", "lynx_dequant.hip", "lynx_recon.h", "lynx_internal.h"):
-        with open(os.path.join(ROOT, "progressive_kv_transfer_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
 def load_traffic(kernel: str):
     """Measured HBM bytes per launch from the committed PMC summary, or
     None if absent or taken on a different kernel source."""
@@ -79,6 +70,7 @@ def load_traffic(kernel: str):
         t = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
     except (OSError, ValueError, IndexError):
         return None
+    from progressive_kv_transfer_amd.profiling import kernel_source_hash
     if t.get("kernel_source_hash") != kernel_source_hash():
         return None
     k = t.get("kernels", {}).get(kernel)
@@ -166,13 +158,15 @@ ATTENTION_CASES = [
 ROTATE_BYTES = 640 << 20  # > the 256 MiB last-level cache
 
 
-def measure_attention(torch, kvgen, lynx, calls: int, warmup: int):
+def measure_attention(torch, kvgen, lynx, calls: int, warmup: int, only=None):
     """Average time of lynx_decode_attn_dequant per call on each attention
-    workload, cycling over copies of the codes."""
+    workload (or only the named one), cycling over copies of the codes."""
     stream = torch.cuda.current_stream()
     res = {}
     built = {}
     for name, wl, t_q, nqh, nkvh, full, causal, qseed in ATTENTION_CASES:
+        if only and name != only:
+            continue
         cfg = kvgen.CONFIGS[wl]
         if wl not in built:
             kv = cfg.make("cuda")
@@ -240,6 +234,8 @@ def main():
     ap.add_argument("--no-attention", action="store_true")
     ap.add_argument("--attention-only", action="store_true")
     ap.add_argument("--attention-calls", type=int, default=50)
+    ap.add_argument("--attention-case", default=None,
+                    choices=[c[0] for c in ATTENTION_CASES])
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -260,8 +256,8 @@ def main():
         sys.exit(2)
     lynx.lib()
     if args.attention_only:
-        print(json.dumps({"attention": measure_attention(torch, kvgen, lynx,
-                                                         args.attention_calls, 5)}), flush=True)
+        print(json.dumps({"attention": measure_attention(
+            torch, kvgen, lynx, args.attention_calls, 5, args.attention_case)}), flush=True)
         return
     cfg = kvgen.CONFIGS[WORKLOAD]
     dev = "cuda"

@@ -333,55 +333,86 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(AttnArgs 
     }
 }
 
-// One workgroup of 256 lanes per (kv head, live row): the maximum over the
-// splits, then lanes (half, channel) accumulate alternate splits.
+// Sum / max over the 64 lanes of a wave.
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) x = fmaxf(x, __shfl_xor(x, d, 64));
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) x += __shfl_xor(x, d, 64);
+    return x;
+}
+
+// One workgroup of 256 lanes per (kv head, live row) merges the split
+// partials: the maximum M over the splits, then lane t takes the items
+// (split s, channel quarter t % 4) for s = t / 4, t / 4 + 64, ... (all loads of
+// a lane issued together), weights them by 2^(m_s - M), and the 64 lanes of
+// each quarter are summed through LDS.
 __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(AttnArgs a) {
-    __shared__ float s_red[kAttnThreads];
-    __shared__ float s_acc[kHead + 1];
+    __shared__ float s_red[2][kAttnThreads / 64];
+    __shared__ float s_acc[64][4 * 33];
     const int wg = (int)__builtin_amdgcn_workgroup_id_x();
     const int kvh = wg % a.n_kvh;
     const int h = wg / a.n_kvh;
     const int tid = (int)__builtin_amdgcn_workitem_id_x();
+    const int wave = tid >> 6;
     const int64_t split_stride = (int64_t)a.n_kvh * a.rows * kPartial;
     const float *base = a.ws + ((int64_t)kvh * a.rows + h) * kPartial;
 
     float m = -INFINITY;
     for (int s = tid; s < a.splits; s += kAttnThreads) m = fmaxf(m, base[s * split_stride]);
-    s_red[tid] = m;
+    m = wave_max(m);
+    if ((tid & 63) == 0) s_red[0][wave] = m;
     __syncthreads();
-    for (int w = kAttnThreads / 2; w > 0; w >>= 1) {
-        if (tid < w) s_red[tid] = fmaxf(s_red[tid], s_red[tid + w]);
-        __syncthreads();
+    const float M = fmaxf(fmaxf(s_red[0][0], s_red[0][1]), fmaxf(s_red[0][2], s_red[0][3]));
+
+    float l = 0.0f;
+    for (int s = tid; s < a.splits; s += kAttnThreads) {
+        const float ms = base[s * split_stride];
+        if (ms != -INFINITY) l = __builtin_fmaf(base[s * split_stride + 1],
+                                                __builtin_amdgcn_exp2f(ms - M), l);
     }
-    const float M = s_red[0];
-    const int half = tid >> 7, c = tid & (kHead - 1);
-    float l = 0.0f, acc = 0.0f;
-    if (M != -INFINITY) {
-#pragma unroll 4
-        for (int s = half; s < a.splits; s += 2) {
-            const float *pt = base + s * split_stride;
-            const float ms = pt[0];
-            const float w = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
-            l = __builtin_fmaf(pt[1], w, l);
-            acc = __builtin_fmaf(pt[2 + c], w, acc);
+    l = wave_sum(l);
+    if ((tid & 63) == 0) s_red[1][wave] = l;
+
+    const int cq = tid & 3;
+    float acc[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) acc[i] = 0.0f;
+    for (int s = tid >> 2; s < a.splits; s += kAttnThreads / 4) {
+        const float *pt = base + s * split_stride;
+        const float ms = pt[0];
+        const float w = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
+#pragma unroll
+        for (int i = 0; i < 32; i += 2) {
+            const float2 v = *(const float2 *)(pt + 2 + 32 * cq + i);
+            acc[i] = __builtin_fmaf(v.x, w, acc[i]);
+            acc[i + 1] = __builtin_fmaf(v.y, w, acc[i + 1]);
         }
     }
-    if (half == 1) {
-        s_acc[c] = acc;
-        if (c == 0) s_acc[kHead] = l;
-    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) s_acc[tid >> 2][cq * 33 + i] = acc[i];
+    __syncthreads();
+    const int c = tid & (kHead - 1), half = tid >> 7;
+    float y = 0.0f;
+    for (int k = half; k < 64; k += 2) y += s_acc[k][(c >> 5) * 33 + (c & 31)];
+    __syncthreads();
+    if (half == 1) s_acc[0][c] = y;
     __syncthreads();
     if (half == 0) {
-        acc += s_acc[c];
-        l += s_acc[kHead];
-        const float y = l > 0.0f ? acc / l : 0.0f;
+        y += s_acc[0][c];
+        const float lt = s_red[1][0] + s_red[1][1] + s_red[1][2] + s_red[1][3];
+        const float o = lt > 0.0f ? y / lt : 0.0f;
         const int r = h / a.group;
         const int qh = kvh * a.group + h % a.group;
         const int64_t at = ((int64_t)r * a.n_qh + qh) * kHead + c;
         if (a.out_f32)
-            ((float *)a.out)[at] = y;
+            ((float *)a.out)[at] = o;
         else
-            ((uint16_t *)a.out)[at] = (uint16_t)(pack_bf16(y, 0.0f) & 0xffffu);
+            ((uint16_t *)a.out)[at] = (uint16_t)(pack_bf16(o, 0.0f) & 0xffffu);
     }
 }
 

@@ -2,17 +2,46 @@
 
     python -m progressive_kv_transfer_amd.profiling trace RESULTS_DB [--match lynx]
     python -m progressive_kv_transfer_amd.profiling pmc RESULTS_DB [--match lynx]
+    python -m progressive_kv_transfer_amd.profiling traffic FETCH_DB WRITE_DB \
+        COPY_FETCH_DB COPY_WRITE_DB --elements N [--title T]
 
 `trace` prints, per kernel, the number of dispatches and the average,
 minimum and maximum duration (from the kernel-trace table); `pmc` prints, per
 kernel and counter (rocprofv3 --pmc), the per-dispatch value averaged over
-the dispatches.
+the dispatches; `traffic` turns FETCH_SIZE / WRITE_SIZE passes over the codec
+kernels (and over a plain 1 GiB copy, which fixes the counters' scale) into
+HBM bytes per launch against the algorithmic bytes of N bf16 elements, as a
+markdown table plus the JSON block that bench.py reads.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
+import json
+import os
 import sqlite3
 import statistics
+
+_CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+# Sources of the codec kernels whose traffic the committed summary describes.
+CODEC_SOURCES = ("lynx_quant.hip", "lynx_dequant.hip", "lynx_recon.h", "lynx_internal.h")
+# kernel symbol -> (name, algorithmic HBM bytes per bf16 element)
+CODEC_KERNELS = {
+    "lynx::quant_kernel<0>": ("quantize", 2.0 + 0.5 + 0.5 + 0.28125),
+    "lynx::dequant_kernel<false>": ("dequant_anchor", 0.5 + 0.28125 + 2.0),
+    "lynx::dequant_kernel<true>": ("dequant_full", 0.5 + 0.5 + 0.28125 + 2.0),
+}
+COPY_BYTES = 1 << 30
+
+
+def kernel_source_hash(files=CODEC_SOURCES) -> str:
+    """SHA-256 prefix of the kernel sources (a summary taken on other
+    sources no longer describes the kernels)."""
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(_CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def _short(name: str) -> str:
@@ -51,12 +80,79 @@ def pmc(db: str, match: str | None = None):
             for (k, c), v in sorted(by.items())]
 
 
+def _counter(db: str, match: str, counter: str) -> dict:
+    return {k: vsum for k, c, _, vsum, _ in pmc(db, match) if c == counter}
+
+
+def traffic(fetch_db, write_db, copy_fetch_db, copy_write_db, elements: int,
+            title: str, command: str) -> str:
+    cf = list(_counter(copy_fetch_db, "copy", "FETCH_SIZE").values())[0]
+    cw = list(_counter(copy_write_db, "copy", "WRITE_SIZE").values())[0]
+    fscale = COPY_BYTES / 1024.0 / cf
+    wscale = COPY_BYTES / 1024.0 / cw
+    fetch = _counter(fetch_db, "lynx", "FETCH_SIZE")
+    write = _counter(write_db, "lynx", "WRITE_SIZE")
+    gib = float(1 << 30)
+    rows, kern = [], {}
+    for sym, (name, bpe) in CODEC_KERNELS.items():
+        if sym not in fetch or sym not in write:
+            continue
+        rd = fetch[sym] * 1024.0 * fscale
+        wr = write[sym] * 1024.0 * wscale
+        algo = bpe * elements
+        rows.append(f"| {sym} | {fetch[sym]:.0f} | {write[sym]:.0f} | {rd / gib:.4f} GiB | "
+                    f"{wr / gib:.4f} GiB | {(rd + wr) / gib:.4f} GiB | {algo / gib:.4f} GiB | "
+                    f"{(rd + wr) / algo:.4f} |")
+        kern[name] = {"kernel": sym, "fetch_size_kib": round(fetch[sym], 1),
+                      "write_size_kib": round(write[sym], 1), "hbm_read_bytes": int(rd),
+                      "hbm_write_bytes": int(wr), "hbm_bytes_per_launch": int(rd + wr),
+                      "algorithmic_bytes_per_launch": int(algo)}
+    blob = {"kernel_source_hash": kernel_source_hash(), "fetch_scale": fscale,
+            "write_scale": wscale,
+            "copy_probe": {"bytes": COPY_BYTES, "fetch_size_kib": cf, "write_size_kib": cw},
+            "kernels": kern}
+    out = [f"# HBM traffic per launch: {title}", "",
+           "Commands (on the MI355X box, repository root `$R`, one counter per pass):", "",
+           *("    " + line for line in command.strip().splitlines()), "",
+           f"Scale factors from a plain 1 GiB device copy (`bench.py --copy-probe`): "
+           f"FETCH_SIZE reads {cf:.0f} KiB for 1 GiB fetched (x{fscale:.3f}); WRITE_SIZE "
+           f"reads {cw:.0f} KiB for 1 GiB written (x{wscale:.3f}).", "",
+           "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read (scaled) | HBM write | total "
+           "| algorithmic | ratio |", "|---|---|---|---|---|---|---|---|", *rows, "",
+           "Machine-readable (read by bench.py; `kernel_source_hash` is the SHA-256 prefix of "
+           "the kernel sources the counters were taken on):", "", "```json",
+           json.dumps(blob, indent=1), "```"]
+    return "\n".join(out) + "\n"
+
+
+TRAFFIC_COMMAND = """
+cd /tmp && export TMPDIR=/tmp
+rocprofv3 --pmc FETCH_SIZE -d /tmp/pr/FETCH_SIZE -o run -- python3 $R/bench.py --profile-run
+rocprofv3 --pmc WRITE_SIZE -d /tmp/pr/WRITE_SIZE -o run -- python3 $R/bench.py --profile-run
+rocprofv3 --pmc FETCH_SIZE -d /tmp/pr/copy_FETCH_SIZE -o run -- python3 $R/bench.py --copy-probe
+rocprofv3 --pmc WRITE_SIZE -d /tmp/pr/copy_WRITE_SIZE -o run -- python3 $R/bench.py --copy-probe
+cd $R && python3 -m progressive_kv_transfer_amd.profiling traffic \\
+    /tmp/pr/FETCH_SIZE/run_results.db /tmp/pr/WRITE_SIZE/run_results.db \\
+    /tmp/pr/copy_FETCH_SIZE/run_results.db /tmp/pr/copy_WRITE_SIZE/run_results.db \\
+    --elements 2147483648
+"""
+
+
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("mode", choices=["trace", "pmc"])
-    ap.add_argument("db")
+    ap.add_argument("mode", choices=["trace", "pmc", "traffic"])
+    ap.add_argument("db", nargs="+")
     ap.add_argument("--match", default=None)
+    ap.add_argument("--elements", type=int, default=1 << 31)
+    ap.add_argument("--title", default="Qwen-32B-shaped KV at 16K (64 layers x K,V x 16384 x "
+                                        "1024 bf16)")
     a = ap.parse_args()
+    if a.mode == "traffic":
+        if len(a.db) != 4:
+            ap.error("traffic needs FETCH_DB WRITE_DB COPY_FETCH_DB COPY_WRITE_DB")
+        print(traffic(*a.db, a.elements, a.title, TRAFFIC_COMMAND), end="")
+        return
+    a.db = a.db[0]
     if a.mode == "trace":
         print("| kernel | dispatches | avg us | min us | max us |")
         print("|---|---|---|---|---|")
