@@ -14,6 +14,10 @@
 // covers half a page block (64 channels x 256 tokens); its lanes meet once
 // in LDS for the page minimum / maximum.  Rows are read with buffer loads
 // (scalar row offsets): 32 lanes x 4 bytes = one 128-byte line per row.
+// The loads go straight to LDS (buffer_load_dword ... lds), one unit ahead:
+// each wave stages the 32 rows of its next unit in its own 8 KiB region
+// while it computes the current one, so HBM latency overlaps a whole unit
+// of arithmetic without holding registers.
 // The anchor and residual bytes of a lane are 32 contiguous bytes of the
 // chunk-tiled stream layout, so a workgroup writes whole cache lines that no
 // other workgroup touches.  Workgroups are persistent (grid = resident
@@ -74,10 +78,14 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
     __shared__ float2 s_max[kChunks][kPairs];
     __shared__ float4 s_ch[kHalf];  // gamma_min, d1, r1, slow flag
     __shared__ u32x2 s_tab[MODE == kModeQuantize ? kMaxBuckets : 1];
+    // Staged rows of the next unit: [wave][row of chunk][lane].
+    __shared__ uint32_t s_stage[kThreads / 64][kChunk][64];
 
     const int tid = (int)__builtin_amdgcn_workitem_id_x();
     const int p = tid & (kPairs - 1);  // channel pair: channels 2p, 2p+1 of the unit
     const int j = tid / kPairs;        // chunk: tokens 32 j .. 32 j + 31
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
 
     // Compander table into LDS, once per workgroup.
     if (MODE == kModeQuantize) {
@@ -93,34 +101,66 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
                               (uint32_t)tab.bucket_lo * (uint32_t)sizeof(u32x2);
     const uint32_t row_bytes = (uint32_t)g.row_stride * 2u;
     const int64_t nunits = 2 * g.nblocks;
+    const uint32_t voff = (uint32_t)(j * kChunk) * row_bytes + (uint32_t)p * 4u;
+
+    // First element of unit v in the KV set.
+    auto unit_base = [&](int64_t v) {
+        const int64_t bv = g.block0 + (v >> 1);
+        const int64_t tpv = bv / g.heads;
+        return kv + (tpv / g.pages) * g.tensor_stride +
+               (int64_t)(tpv % g.pages) * kPage * g.row_stride + (bv % g.heads) * kHead +
+               (v & 1) * kHalf;
+    };
+    // Issue the 32 row loads (4 B per lane: channels 2p, 2p+1 of the unit,
+    // tokens 32 j + i) of the unit at bp into this wave's staging rows.
+    typedef __attribute__((address_space(3))) void lds_void;
+    // LDS address of this wave's staging rows, as a wave-uniform scalar.
+    const uint32_t stage_lds = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(lds_void *)&s_stage[wave][0][0]);
+    // The row offsets are stepped with opaque scalar adds so that the 64
+    // per-row constants are not hoisted out of the unit loop into SGPRs.
+    auto stage = [&](const uint16_t *bp) {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(bp);
+        uint32_t soff = 0, lds = stage_lds;
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(uintptr_t)lds, 4, voff,
+                                                     soff, 0, 0);
+            asm volatile("s_add_u32 %0, %0, %1" : "+s"(soff) : "s"(row_bytes));
+            asm volatile("s_add_u32 %0, %0, 0x100" : "+s"(lds));
+        }
+    };
+    if ((int64_t)__builtin_amdgcn_workgroup_id_x() < nunits)
+        stage(unit_base(__builtin_amdgcn_workgroup_id_x()));
 
     for (int64_t u = __builtin_amdgcn_workgroup_id_x(); u < nunits;
          u += g.grid_wgs) {
         const int64_t b = g.block0 + (u >> 1);
         const int half = (int)(u & 1);
-        const int head = (int)(b % g.heads);
-        const int64_t tp = b / g.heads;
-        const int page = (int)(tp % g.pages);
-        const int64_t tensor = tp / g.pages;
-        const uint16_t *base = kv + tensor * g.tensor_stride +
-                               (int64_t)page * kPage * g.row_stride + head * kHead +
-                               half * kHalf;
-        const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(base);
         const int64_t meta0 = b * kHead + half * kHalf;
         const int64_t cmeta0 = b * (kChunks * kHead) + j * kHead + half * kHalf;
+        // Address of the next unit, computed here where few registers are
+        // live (the empty asm keeps it from being sunk to its use).
+        const bool has_next = u + g.grid_wgs < nunits;
+        const uint16_t *next_base = has_next ? unit_base(u + g.grid_wgs) : kv;
+        asm volatile("" ::"s"(next_base));
 
-        // ---- load 32 token rows x 2 channels (4 B per row) ---------------
-        const uint32_t voff = (uint32_t)(j * kChunk) * row_bytes + (uint32_t)p * 4u;
+        // ---- 32 token rows x 2 channels (4 B per row) from the stage -----
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         uint32_t raw[kChunk];
 #pragma unroll
-        for (int i = 0; i < kChunk; ++i)
-            raw[i] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, voff, i * row_bytes, 0);
+        for (int i = 0; i < kChunk; ++i) raw[i] = s_stage[wave][i][lane];
         float x[kChunk][2];
 #pragma unroll
         for (int i = 0; i < kChunk; ++i) {
             x[i][0] = bf16_lo(raw[i]);
             x[i][1] = bf16_hi(raw[i]);
         }
+        // The staging rows are refilled now: all reads of them have
+        // returned (their values are used above).
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (has_next)
+            stage(next_base);
 
         // ---- phase 1: page statistics ------------------------------------
         if (MODE != kModeBlockStats) {
@@ -183,10 +223,15 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
 #pragma unroll
                     for (int e = 0; e < 2; ++e) x[i][e] = div_fast(x[i][e] - gm[e], d1[e], r1[e]);
             } else {
+                // Rare path; the scheduling barriers keep its register
+                // footprint below the fast path's.
 #pragma unroll
                 for (int i = 0; i < kChunk; ++i)
 #pragma unroll
-                    for (int e = 0; e < 2; ++e) x[i][e] = __fdiv_rn(x[i][e] - gm[e], d1[e]);
+                    for (int e = 0; e < 2; ++e) {
+                        x[i][e] = __fdiv_rn(x[i][e] - gm[e], d1[e]);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
             }
         }
         float mu[2], sg[2];
@@ -225,7 +270,10 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
 #pragma unroll
                 for (int i = 0; i < kChunk; ++i)
 #pragma unroll
-                    for (int e = 0; e < 2; ++e) x[i][e] = __fdiv_rn(x[i][e], d2[e]) + 0.0f;
+                    for (int e = 0; e < 2; ++e) {
+                        x[i][e] = __fdiv_rn(x[i][e], d2[e]) + 0.0f;
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
             } else {
                 const float r2[2] = {__fdiv_rn(1.0f, d2[0]), __fdiv_rn(1.0f, d2[1])};
 #pragma unroll
