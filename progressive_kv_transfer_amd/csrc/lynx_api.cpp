@@ -75,7 +75,11 @@ bool build_quant_tab(float alpha, float code_scale, QuantTab *t) {
         return c;
     };
     const uint32_t one = f2u(1.0f);
-    for (int mbits = 3; mbits <= 8; ++mbits) {
+    // 7 mantissa bits first: the bucket is then the upper 16 bits of the
+    // magnitude, which the kernel turns into a table address with one
+    // instruction; otherwise the coarsest resolution that works.
+    static const int kOrder[] = {7, 3, 4, 5, 6, 8};
+    for (int mbits : kOrder) {
         const int shift = 23 - mbits;
         const uint32_t lo = (f2u(t->thr[1]) - 1u) >> shift;
         const uint32_t hi = one >> shift;

@@ -13,7 +13,7 @@ constexpr int kChunk = 32;      // C: tokens per chunk
 constexpr int kHead = 128;      // H: channels per page block
 constexpr int kChunks = kPage / kChunk;
 constexpr int kCodeMax = 120;   // largest code whose anchor fits 4 bits
-constexpr int kMaxBuckets = 1536;
+constexpr int kMaxBuckets = 1792;  // 14 KiB: with the 32 KiB stage, 3 workgroups per CU
 
 // Compander tables, built once per (alpha, code_scale) on the host and
 // passed by value as a kernel argument.

@@ -69,7 +69,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base) {
                                              0x00020000);
 }
 
-template <int MODE>
+// SH16: the compander buckets are the upper 16 bits of the magnitude, so the
+// table address is one v_mad_u32_u16 (high half x 8 + base).
+template <int MODE, bool SH16>
 __global__ __launch_bounds__(kThreads) void quant_kernel(
     const uint16_t *__restrict__ kv, Geometry g, const QuantTab tab,
     uint8_t *__restrict__ anchor, uint8_t *__restrict__ residual, float *__restrict__ gmin_io,
@@ -298,7 +300,11 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
                     float m = __builtin_amdgcn_fmed3f(fabsf(x[4 * q + k][e]), mag_lo, 1.0f);
                     uint32_t mb = __float_as_uint(m);
                     uint32_t addr;
-                    asm("v_lshl_add_u32 %0, %1, 3, %2" : "=v"(addr) : "v"(mb >> sh), "s"(tab_base));
+                    if (SH16)
+                        asm("v_mad_u32_u16 %0, %1, 8, %2 op_sel:[1,0,0,0]"
+                            : "=v"(addr) : "v"(mb), "s"(tab_base));
+                    else
+                        asm("v_lshl_add_u32 %0, %1, 3, %2" : "=v"(addr) : "v"(mb >> sh), "s"(tab_base));
                     u32x2 ent = *(lds_u32x2 *)(uintptr_t)addr;
                     // J = code + 7: high nibble = anchor magnitude
                     // (code + 7) >> 4, low nibble ^ 7 = residual (-code) mod 16.
@@ -341,14 +347,11 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
 }  // namespace
 
 // Workgroups resident on the device (per kernel variant), cached per device.
-static int resident_workgroups(const void *kernel, int threads) {
-    static int cache[64][3];
+static int resident_workgroups(const void *kernel, int slot, int threads) {
+    static int cache[64][4];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
         return 1024;
-    const int slot = kernel == (const void *)quant_kernel<kModeQuantize>     ? 0
-                     : kernel == (const void *)quant_kernel<kModePageStats> ? 1
-                                                                              : 2;
     if (cache[dev][slot] == 0) {
         int cus = 0, per_cu = 0;
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -358,34 +361,40 @@ static int resident_workgroups(const void *kernel, int threads) {
     return cache[dev][slot];
 }
 
+template <int MODE, bool SH16>
+static hipError_t launch_variant(int slot, const uint16_t *kv, const Geometry &g,
+                                 const QuantTab &tab, uint8_t *anchor, uint8_t *residual,
+                                 float *gmin, float *gscale, float *mu, float *sigma,
+                                 hipStream_t stream) {
+    const int64_t units = 2 * g.nblocks;
+    const int64_t res =
+        resident_workgroups((const void *)quant_kernel<MODE, SH16>, slot, kThreads);
+    Geometry gl = g;
+    gl.grid_wgs = units < res ? units : res;
+    hipLaunchKernelGGL((quant_kernel<MODE, SH16>), dim3((unsigned)gl.grid_wgs), dim3(kThreads),
+                       0, stream, kv, gl, tab, anchor, residual, gmin, gscale, mu, sigma);
+    return hipGetLastError();
+}
+
 hipError_t launch_quantize(const uint16_t *kv, const Geometry &g, const QuantTab &tab,
                            uint8_t *anchor, uint8_t *residual, float *gmin, float *gscale,
                            float *mu, float *sigma, int mode, hipStream_t stream) {
     if (g.nblocks == 0)
         return hipSuccess;
-    const void *kern = mode == kModeQuantize    ? (const void *)quant_kernel<kModeQuantize>
-                       : mode == kModePageStats ? (const void *)quant_kernel<kModePageStats>
-                                                : (const void *)quant_kernel<kModeBlockStats>;
-    const int64_t units = 2 * g.nblocks;
-    const int64_t res = resident_workgroups(kern, kThreads);
-    Geometry gl = g;
-    gl.grid_wgs = units < res ? units : res;
-    dim3 grid((unsigned)gl.grid_wgs), block(kThreads);
     switch (mode) {
     case kModeQuantize:
-        hipLaunchKernelGGL(quant_kernel<kModeQuantize>, grid, block, 0, stream, kv, gl, tab,
-                           anchor, residual, gmin, gscale, mu, sigma);
-        break;
+        if (tab.shift == 16)
+            return launch_variant<kModeQuantize, true>(0, kv, g, tab, anchor, residual, gmin,
+                                                       gscale, mu, sigma, stream);
+        return launch_variant<kModeQuantize, false>(1, kv, g, tab, anchor, residual, gmin,
+                                                    gscale, mu, sigma, stream);
     case kModePageStats:
-        hipLaunchKernelGGL(quant_kernel<kModePageStats>, grid, block, 0, stream, kv, gl, tab,
-                           anchor, residual, gmin, gscale, mu, sigma);
-        break;
+        return launch_variant<kModePageStats, false>(2, kv, g, tab, anchor, residual, gmin,
+                                                     gscale, mu, sigma, stream);
     default:
-        hipLaunchKernelGGL(quant_kernel<kModeBlockStats>, grid, block, 0, stream, kv, gl, tab,
-                           anchor, residual, gmin, gscale, mu, sigma);
-        break;
+        return launch_variant<kModeBlockStats, false>(3, kv, g, tab, anchor, residual, gmin,
+                                                      gscale, mu, sigma, stream);
     }
-    return hipGetLastError();
 }
 
 }  // namespace lynx

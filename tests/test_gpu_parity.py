@@ -114,7 +114,11 @@ def test_strided_multi_block_set():
 @pytest.mark.parametrize("alpha,eps,code_scale", [(100.0, 1e-6, 127.0),
                                                   (255.0, 1e-6, 120.0),
                                                   (255.0, 2.0 ** -20, 127.0),
-                                                  (8.0, 1e-3, 127.0)])
+                                                  (8.0, 1e-3, 127.0),
+                                                  # thresholds over > 16 octaves: the
+                                                  # compander falls back to coarser buckets
+                                                  (1e6, 1e-6, 127.0),
+                                                  (1e12, 1e-6, 127.0)])
 def test_parameter_variants(alpha, eps, code_scale):
     announce(f"params alpha={alpha} eps={eps} code_scale={code_scale}")
     kv = torch.stack([kvgen.kv_tensor(400 + i, 512, 256, [7, 200], True, DEV)
