@@ -14,6 +14,8 @@
  *     Q_res combined with the stored metadata refines the KV to Q_full;
  *   - lynx_page_stats / lynx_block_stats: Stage 1 and Stage 2 statistics of
  *     Algorithm 1 on their own (the same arithmetic as the fused quantize);
+ *   - lynx_split_stream_transfer: the prioritized transmission of Section
+ *     4.2 (Figure 7) emulated on one GPU through a wire buffer;
  *   - lynx_decode_attn_dequant: attention O = softmax(Q K^T scale) V
  *     (Section 2.1) over K, V rebuilt on the fly from their streams: one
  *     query token (decode on the draft or verification precision) or T
@@ -233,6 +235,66 @@ int lynx_decode_attn_dequant(const void *q, int t_q, int num_q_heads,
                              const lynx_params *params, void *out,
                              int out_dtype, void *workspace,
                              size_t workspace_bytes, hipStream_t stream);
+
+/* Streams and metadata of a KV set in one memory space (device memory or
+ * pinned host memory), layouts as above. */
+typedef struct lynx_codes {
+    uint8_t *anchor;
+    uint8_t *residual;
+    lynx_meta meta;
+} lynx_codes;
+
+/* Milestones of lynx_split_stream_transfer, in milliseconds after its start
+ * (HIP events on the streams that reach them). */
+typedef struct lynx_transfer_times {
+    float quantized;          /* sender: last object quantized             */
+    float anchor_arrived;     /* last anchor + metadata object in rx        */
+    float residual_arrived;   /* last residual object in rx                 */
+    float first_anchor_ready; /* receiver: first object rebuilt from anchor */
+    float anchor_ready;       /* receiver: every object rebuilt from anchor */
+    float full_ready;         /* receiver: every object refined             */
+} lynx_transfer_times;
+
+#define LYNX_TRANSFER_COPIES_ONLY 1 /* move the codes only: no quantize, no
+                                       rebuild (the link's own time)       */
+
+/*
+ * Progressive split-stream transfer of a KV set through a wire buffer, on
+ * one GPU (the paper's Section 4.2, Figure 7: the serializer quantizes KV
+ * objects into Q_anc, Q_res and metadata, pushes the Anchor and the Residual
+ * through two queues with the Anchor drained first, and overlaps the
+ * transmission of object i with the quantization of object i + 1; the
+ * deserializer rebuilds the cache from the Anchor first and refines it when
+ * the Residual arrives).
+ *
+ * The set's page blocks (block order of the layouts above) are cut into
+ * objects of object_blocks blocks.  Per object i:
+ *   sender stream:   quantize the object into tx;
+ *   anchor_link:     after it, copy its anchor and metadata tx -> wire -> rx;
+ *   residual_link:   after the anchor copy of the same object, copy its
+ *                    residual tx -> wire -> rx;
+ *   receiver stream: after the anchor copy, rebuild the object from the
+ *                    anchor into kv_anchor;
+ * then, once every object is rebuilt from its anchor, per object: after its
+ * residual copy, rebuild it from anchor + residual into kv_full.
+ *   kv, shape, params  as lynx_quantize_pages;
+ *   tx, wire, rx       code buffers of the whole set: tx and rx device
+ *                      memory, wire pinned host memory (or device memory);
+ *   kv_anchor, kv_full device bf16 outputs laid out by shape;
+ *   flags              0, or LYNX_TRANSFER_COPIES_ONLY (kv, kv_anchor and
+ *                      kv_full unused and may be NULL; tx must hold codes);
+ *   times              if not NULL, the milestones.
+ * Blocking: returns when all four streams have finished the transfer.  No
+ * memory is allocated (HIP events only).  Errors as above; a HIP failure
+ * mid-way still waits for the streams before returning LYNX_EHIP.
+ */
+int lynx_split_stream_transfer(const void *kv, const lynx_kv_shape *shape,
+                               const lynx_params *params, int64_t object_blocks,
+                               lynx_codes tx, lynx_codes wire, lynx_codes rx,
+                               void *kv_anchor, void *kv_full, int flags,
+                               hipStream_t sender, hipStream_t anchor_link,
+                               hipStream_t residual_link, hipStream_t receiver,
+                               lynx_transfer_times *times);
 
 #ifdef __cplusplus
 }

@@ -10,6 +10,7 @@
 #include <mutex>
 #include <string>
 #include <utility>
+#include <vector>
 
 #include "lynx_internal.h"
 
@@ -308,6 +309,66 @@ int attn_plan(int t_q, int n_qh, int n_kvh, int64_t ctx, AttnPlan *pl) {
 
 using namespace lynx;
 
+// ------------------------------------------------- split-stream transfer --
+
+// HIP events owned by one transfer call, destroyed when it returns (after
+// every stream has been synchronised).
+struct EventSet {
+    std::vector<hipEvent_t> ev;
+    hipError_t err = hipSuccess;
+    hipEvent_t make(bool timing) {
+        hipEvent_t e = nullptr;
+        const hipError_t r =
+            hipEventCreateWithFlags(&e, timing ? hipEventDefault : hipEventDisableTiming);
+        if (r != hipSuccess) {
+            if (err == hipSuccess)
+                err = r;
+            return nullptr;
+        }
+        ev.push_back(e);
+        return e;
+    }
+    ~EventSet() {
+        for (hipEvent_t e : ev)
+            hipEventDestroy(e);
+    }
+};
+
+// Anchor stream + metadata (or the residual stream) of blocks [b0, b0 + n)
+// from one code set to another.
+hipError_t copy_anchor_meta(const lynx_codes &src, const lynx_codes &dst, int64_t b0, int64_t n,
+                            hipStream_t s) {
+    const size_t stream_b = (size_t)kPage * kHead / 2, gam = kHead, chk = (size_t)kChunks * kHead;
+    hipError_t e = hipMemcpyAsync(dst.anchor + b0 * stream_b, src.anchor + b0 * stream_b,
+                                  n * stream_b, hipMemcpyDefault, s);
+    const float *sm[4] = {src.meta.gamma_min, src.meta.gamma_scale, src.meta.mu, src.meta.sigma};
+    float *dm[4] = {dst.meta.gamma_min, dst.meta.gamma_scale, dst.meta.mu, dst.meta.sigma};
+    for (int k = 0; k < 4 && e == hipSuccess; ++k) {
+        const size_t per = k < 2 ? gam : chk;
+        e = hipMemcpyAsync(dm[k] + b0 * per, sm[k] + b0 * per, n * per * sizeof(float),
+                           hipMemcpyDefault, s);
+    }
+    return e;
+}
+
+hipError_t copy_residual(const lynx_codes &src, const lynx_codes &dst, int64_t b0, int64_t n,
+                         hipStream_t s) {
+    const size_t stream_b = (size_t)kPage * kHead / 2;
+    return hipMemcpyAsync(dst.residual + b0 * stream_b, src.residual + b0 * stream_b,
+                          n * stream_b, hipMemcpyDefault, s);
+}
+
+bool codes_ok(const lynx_codes &c) {
+    const void *ptrs[6] = {c.anchor, c.residual, c.meta.gamma_min, c.meta.gamma_scale,
+                           c.meta.mu, c.meta.sigma};
+    for (const void *q : ptrs)
+        if (!q || !aligned16(q))
+            return false;
+    return true;
+}
+
+constexpr int64_t kMaxTransferObjects = 4096;
+
 extern "C" {
 
 void lynx_default_params(lynx_params *p) {
@@ -488,6 +549,136 @@ int lynx_block_stats(const void *kv, const lynx_kv_shape *shape, const lynx_para
                      hipStream_t stream) {
     return quantize_common(kv, shape, params, nullptr, nullptr, (float *)gamma_min,
                            (float *)gamma_scale, mu, sigma, kModeBlockStats, stream);
+}
+
+int lynx_split_stream_transfer(const void *kv, const lynx_kv_shape *shape,
+                               const lynx_params *params, int64_t object_blocks, lynx_codes tx,
+                               lynx_codes wire, lynx_codes rx, void *kv_anchor, void *kv_full,
+                               int flags, hipStream_t sender, hipStream_t anchor_link,
+                               hipStream_t residual_link, hipStream_t receiver,
+                               lynx_transfer_times *times) {
+    const lynx_params p = resolve(params);
+    int rc = check_params(p);
+    if (rc)
+        return rc;
+    int64_t nb = 0;
+    if ((rc = check_shape(shape, &nb)))
+        return rc;
+    if (object_blocks <= 0 || (flags & ~LYNX_TRANSFER_COPIES_ONLY))
+        return LYNX_EINVAL;
+    const bool copies_only = (flags & LYNX_TRANSFER_COPIES_ONLY) != 0;
+    if (times)
+        memset(times, 0, sizeof *times);
+    if (nb == 0)
+        return LYNX_OK;
+    const int64_t nobj = (nb + object_blocks - 1) / object_blocks;
+    if (nobj > kMaxTransferObjects)
+        return LYNX_EINVAL;
+    if (!codes_ok(tx) || !codes_ok(wire) || !codes_ok(rx))
+        return LYNX_EINVAL;
+    if (!copies_only) {
+        if (!kv || !kv_anchor || !kv_full)
+            return LYNX_EINVAL;
+        if (!aligned16(kv) || !aligned16(kv_anchor) || !aligned16(kv_full))
+            return LYNX_ESHAPE;
+    }
+    const Tables *t = tables_for(p);
+    if (!t)
+        return LYNX_EINVAL;
+    QuantTab qt = t->q;
+    qt.eps = p.eps;
+    DequantTab dt = t->d;
+    dt.eps = p.eps;
+    const Geometry g0 = geometry(shape, nb);
+
+    EventSet es;
+    hipEvent_t start = es.make(true), t_q = es.make(true), t_a = es.make(true),
+               t_r = es.make(true), t_da0 = es.make(true), t_da = es.make(true),
+               t_df = es.make(true);
+    std::vector<hipEvent_t> q(nobj), a(nobj), r(nobj);
+    for (int64_t i = 0; i < nobj; ++i) {
+        q[i] = es.make(false);
+        a[i] = es.make(false);
+        r[i] = es.make(false);
+    }
+    if (es.err != hipSuccess)
+        return hip_status(es.err);
+
+    hipError_t err = hipSuccess;
+    auto ok = [&](hipError_t e) {
+        if (err == hipSuccess && e != hipSuccess)
+            err = e;
+        return err == hipSuccess;
+    };
+    ok(hipEventRecord(start, sender));
+    for (hipStream_t s : {anchor_link, residual_link, receiver})
+        ok(hipStreamWaitEvent(s, start, 0));
+    for (int64_t i = 0; i < nobj && err == hipSuccess; ++i) {
+        const int64_t b0 = i * object_blocks;
+        const int64_t n = (nb - b0) < object_blocks ? (nb - b0) : object_blocks;
+        Geometry g = g0;
+        g.block0 = b0;
+        g.nblocks = n;
+        // serializer: quantize object i (object i + 1 then overlaps its sending)
+        if (!copies_only)
+            ok(launch_quantize((const uint16_t *)kv, g, qt, tx.anchor, tx.residual,
+                               tx.meta.gamma_min, tx.meta.gamma_scale, tx.meta.mu, tx.meta.sigma,
+                               kModeQuantize, sender));
+        ok(hipEventRecord(q[i], sender));
+        // anchor queue: anchor + metadata over the wire
+        ok(hipStreamWaitEvent(anchor_link, q[i], 0));
+        ok(copy_anchor_meta(tx, wire, b0, n, anchor_link));
+        ok(copy_anchor_meta(wire, rx, b0, n, anchor_link));
+        ok(hipEventRecord(a[i], anchor_link));
+        // residual queue: only behind the anchor of the same object
+        ok(hipStreamWaitEvent(residual_link, a[i], 0));
+        ok(copy_residual(tx, wire, b0, n, residual_link));
+        ok(copy_residual(wire, rx, b0, n, residual_link));
+        ok(hipEventRecord(r[i], residual_link));
+        // deserializer, anchor phase
+        ok(hipStreamWaitEvent(receiver, a[i], 0));
+        if (!copies_only)
+            ok(launch_dequant(rx.anchor, nullptr, rx.meta.gamma_min, rx.meta.gamma_scale,
+                              rx.meta.mu, rx.meta.sigma, g, dt, (uint16_t *)kv_anchor,
+                              receiver));
+        if (i == 0)
+            ok(hipEventRecord(t_da0, receiver));
+    }
+    ok(hipEventRecord(t_q, sender));
+    ok(hipEventRecord(t_a, anchor_link));
+    ok(hipEventRecord(t_r, residual_link));
+    ok(hipEventRecord(t_da, receiver));
+    // deserializer, residual phase (after the whole anchor phase)
+    for (int64_t i = 0; i < nobj && err == hipSuccess; ++i) {
+        const int64_t b0 = i * object_blocks;
+        const int64_t n = (nb - b0) < object_blocks ? (nb - b0) : object_blocks;
+        Geometry g = g0;
+        g.block0 = b0;
+        g.nblocks = n;
+        ok(hipStreamWaitEvent(receiver, r[i], 0));
+        if (!copies_only)
+            ok(launch_dequant(rx.anchor, rx.residual, rx.meta.gamma_min, rx.meta.gamma_scale,
+                              rx.meta.mu, rx.meta.sigma, g, dt, (uint16_t *)kv_full, receiver));
+    }
+    ok(hipEventRecord(t_df, receiver));
+    // Blocking: every stream drains before the events go away.
+    for (hipStream_t s : {sender, anchor_link, residual_link, receiver}) {
+        const hipError_t e = hipStreamSynchronize(s);
+        if (err == hipSuccess)
+            err = e;
+    }
+    if (err != hipSuccess)
+        return hip_status(err);
+    if (times) {
+        float *out[6] = {&times->quantized,          &times->anchor_arrived,
+                         &times->residual_arrived,   &times->first_anchor_ready,
+                         &times->anchor_ready,       &times->full_ready};
+        hipEvent_t ev[6] = {t_q, t_a, t_r, t_da0, t_da, t_df};
+        for (int k = 0; k < 6; ++k)
+            if (!ok(hipEventElapsedTime(out[k], start, ev[k])))
+                return hip_status(err);
+    }
+    return LYNX_OK;
 }
 
 }  // extern "C"

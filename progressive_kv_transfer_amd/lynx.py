@@ -46,12 +46,26 @@ class lynx_meta(ctypes.Structure):
                 ("mu", ctypes.c_void_p), ("sigma", ctypes.c_void_p)]
 
 
+class lynx_codes(ctypes.Structure):
+    _fields_ = [("anchor", ctypes.c_void_p), ("residual", ctypes.c_void_p),
+                ("meta", lynx_meta)]
+
+
+class lynx_transfer_times(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_float) for n in ("quantized", "anchor_arrived", "residual_arrived",
+                                              "first_anchor_ready", "anchor_ready",
+                                              "full_ready")]
+
+
+TRANSFER_COPIES_ONLY = 1
+
 # Every symbol include/lynx.h declares.
 EXPORTS = ["lynx_default_params", "lynx_num_blocks", "lynx_stream_bytes",
            "lynx_gamma_floats", "lynx_chunk_floats", "lynx_kv_bytes",
            "lynx_status_string", "lynx_compander_thresholds", "lynx_quantize_pages", "lynx_dequant_anchor",
            "lynx_dequant_full", "lynx_page_stats", "lynx_block_stats",
-           "lynx_attn_workspace_bytes", "lynx_decode_attn_dequant"]
+           "lynx_attn_workspace_bytes", "lynx_decode_attn_dequant",
+           "lynx_split_stream_transfer"]
 
 _lib = None
 
@@ -95,8 +109,12 @@ def lib():
                                                lynx_meta, i64, i32, i32, ctypes.c_float, i32,
                                                P(lynx_params), vp, i32, vp, ctypes.c_size_t,
                                                vp]
+        L.lynx_split_stream_transfer.argtypes = [vp, P(lynx_kv_shape), P(lynx_params), i64,
+                                                 lynx_codes, lynx_codes, lynx_codes, vp, vp,
+                                                 i32, vp, vp, vp, vp, P(lynx_transfer_times)]
         for f in ("lynx_quantize_pages", "lynx_dequant_anchor", "lynx_dequant_full",
-                  "lynx_page_stats", "lynx_block_stats", "lynx_decode_attn_dequant"):
+                  "lynx_page_stats", "lynx_block_stats", "lynx_decode_attn_dequant",
+                  "lynx_split_stream_transfer"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -163,10 +181,22 @@ class Codes:
         m.mu, m.sigma = self.mu.data_ptr(), self.sigma.data_ptr()
         return m
 
+    def c_struct(self) -> lynx_codes:
+        c = lynx_codes()
+        c.anchor, c.residual = self.anchor.data_ptr(), self.residual.data_ptr()
+        c.meta = self.meta()
+        return c
 
-def alloc_codes(nblocks: int, device) -> Codes:
-    u8 = dict(dtype=torch.uint8, device=device)
-    f32 = dict(dtype=torch.float32, device=device)
+    def tensors(self):
+        return (self.anchor, self.residual, self.gamma_min, self.gamma_scale, self.mu,
+                self.sigma)
+
+
+def alloc_codes(nblocks: int, device, pin_memory: bool = False) -> Codes:
+    """Code buffers for nblocks page blocks on `device`; on the CPU with
+    pin_memory=True they are pinned host memory (a transfer's wire)."""
+    u8 = dict(dtype=torch.uint8, device=device, pin_memory=pin_memory)
+    f32 = dict(dtype=torch.float32, device=device, pin_memory=pin_memory)
     tile = (nblocks, PAGE_TOKENS // CHUNK_TOKENS, BLOCK_CHANNELS // 2, CHUNK_TOKENS)
     return Codes(torch.empty(tile, **u8), torch.empty(tile, **u8),
                  torch.empty((nblocks, BLOCK_CHANNELS), **f32),
@@ -306,3 +336,25 @@ def decode_attn_dequant(q: torch.Tensor, k: CodeView, v: CodeView, ctx_len: int,
         ctypes.byref(p) if p else None, out.data_ptr(), code, workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
+
+
+def split_stream_transfer(kv: torch.Tensor | None, shape: lynx_kv_shape, object_blocks: int,
+                          tx: Codes, wire: Codes, rx: Codes,
+                          kv_anchor: torch.Tensor | None = None,
+                          kv_full: torch.Tensor | None = None, copies_only: bool = False,
+                          p: lynx_params | None = None, streams=None) -> dict:
+    """lynx_split_stream_transfer (blocking); returns the milestones in ms.
+    streams: (sender, anchor_link, residual_link, receiver), default four new
+    streams of default priority."""
+    for c in (tx, rx):
+        _require_cuda(*c.tensors())
+    if streams is None:
+        streams = tuple(torch.cuda.Stream() for _ in range(4))
+    t = lynx_transfer_times()
+    ptr = lambda x: None if x is None else x.data_ptr()
+    _check("lynx_split_stream_transfer", lib().lynx_split_stream_transfer(
+        ptr(kv), ctypes.byref(shape), ctypes.byref(p) if p else None, object_blocks,
+        tx.c_struct(), wire.c_struct(), rx.c_struct(), ptr(kv_anchor), ptr(kv_full),
+        TRANSFER_COPIES_ONLY if copies_only else 0,
+        *(ctypes.c_void_p(s.cuda_stream) for s in streams), ctypes.byref(t)))
+    return {n: float(getattr(t, n)) for n, _ in lynx_transfer_times._fields_}

@@ -240,3 +240,56 @@ def test_attention_argument_errors(case, expect):
                                     nkvh, hd, scale, causal, ctypes.byref(p), FAKE, odt, FAKE,
                                     wsb, None)
     assert rc == expect
+
+
+def _codes(ptr=FAKE):
+    c = lynx.lynx_codes()
+    c.anchor = c.residual = ptr
+    c.meta = _meta(ptr)
+    return c
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("object_blocks", -1), ("flags", -1), ("null_wire", -1), ("misaligned_rx", -1),
+    ("misaligned_kv", -2), ("null_out", -1), ("too_many_objects", -1), ("tokens", -2),
+    ("params", -1)])
+def test_transfer_argument_errors(case, expect):
+    """Malformed transfers are rejected before any stream or event is used."""
+    L = lynx.lib()
+    s, p = _shape(), lynx.params()
+    ob, flags = 1, 0
+    kv, ka, kf = FAKE, FAKE, FAKE
+    tx, wire, rx = _codes(), _codes(), _codes()
+    if case == "object_blocks":
+        ob = 0
+    elif case == "flags":
+        flags = 2
+    elif case == "null_wire":
+        wire = _codes(None)
+    elif case == "misaligned_rx":
+        rx.meta.mu = FAKE + 4
+    elif case == "misaligned_kv":
+        kv = FAKE + 2
+    elif case == "null_out":
+        kf = None
+    elif case == "too_many_objects":
+        s = _shape(nt=4097, T=256, ts=256 * 128)  # 4097 blocks, one object each
+    elif case == "tokens":
+        s = _shape(T=300)
+    elif case == "params":
+        p.eps = 1.0
+    t = lynx.lynx_transfer_times()
+    rc = L.lynx_split_stream_transfer(kv, ctypes.byref(s), ctypes.byref(p), ob, tx, wire, rx,
+                                      ka, kf, flags, None, None, None, None, ctypes.byref(t))
+    assert rc == expect
+
+
+def test_transfer_empty_set_and_copies_only_needs_no_kv():
+    L = lynx.lib()
+    t = lynx.lynx_transfer_times()
+    t.full_ready = 5.0
+    for s in (_shape(nt=0), _shape(T=0)):
+        assert L.lynx_split_stream_transfer(None, ctypes.byref(s), None, 4, _codes(), _codes(),
+                                            _codes(), None, None, 1, None, None, None, None,
+                                            ctypes.byref(t)) == 0
+        assert t.full_ready == 0.0
