@@ -47,7 +47,9 @@
  * Numerics: binary32 with one IEEE round-to-nearest-even rounding per step
  * of Algorithm 1 (no contraction); the compander code is the exact
  * real-arithmetic rounding (half-up) of Eq. (3) applied to the binary32
- * X_final, clipped at 120 so the anchor fits 4 bits; reconstruction is
+ * X_final with the compander scaled to code_scale (default 120, so every
+ * code fits the 4 + 4 split; with 127 codes above 120 are clipped so the
+ * anchor fits 4 bits); reconstruction is
  * ((S * L[code]) * (sigma + eps) + mu) * (gamma_scale + eps) + gamma_min with
  * L[k] = ((1 + alpha)^(k / code_scale) - 1) / alpha rounded to binary32, then
  * bf16 round-to-nearest-even.  Anchor-only uses code = anchor magnitude << 4.
@@ -94,8 +96,11 @@ extern "C" {
 
 /* Method parameters (Algorithm 1 and Eq. (3)).  alpha > 0 controls the
  * skew of the alpha-law (default 255); eps > 0 is added to both scales
- * (default 1e-6); code_scale is the 2^7 - 1 = 127 of Eq. (3) (120 is also
- * accepted: then no code needs the clip).  page_tokens, chunk_tokens and
+ * (default 1e-6); code_scale is the top of the compander's code range: the
+ * default 120 is the largest code a 4-bit anchor plus a 4-bit residual can
+ * carry (anchor magnitude (code + 7) >> 4 <= 7), so every |X_final| in
+ * [0, 1] keeps its code; 127 (the 2^7 - 1 printed in Eq. (3)) is accepted and
+ * then codes above 120 are clipped to 120.  page_tokens, chunk_tokens and
  * block_channels must be 256, 32 and 128. */
 typedef struct lynx_params {
     float alpha;
@@ -123,7 +128,7 @@ typedef struct lynx_meta {
     float *sigma;
 } lynx_meta;
 
-/* Fills *p with alpha = 255, eps = 1e-6, code_scale = 127, P = 256,
+/* Fills *p with alpha = 255, eps = 1e-6, code_scale = 120, P = 256,
  * C = 32, H = 128. */
 void lynx_default_params(lynx_params *p);
 
@@ -146,7 +151,7 @@ uint64_t lynx_kv_bytes(int64_t k_factor, int64_t seq_len, int64_t hidden,
 /* The 128 compander thresholds the kernels use for `params` (NULL =
  * defaults): thr[k], k = 1..120, is the smallest binary32 magnitude whose
  * Eq. (3) value reaches k - 1/2 (so code(|x|) = #{k : |x| >= thr[k]});
- * thr[0] = 0 and thr[k] = +inf for codes the clip at 120 removes.  Host
+ * thr[0] = 0 and thr[k] = +inf for codes above 120 or out of reach.  Host
  * only, no GPU needed.  Returns LYNX_EINVAL for bad parameters. */
 int lynx_compander_thresholds(const lynx_params *params, float *thr128);
 

@@ -36,6 +36,12 @@ _lock = threading.Lock()
 _lib = None
 
 P_DEFAULT, C_DEFAULT, H_DEFAULT = 256, 32, 128
+# Top of the compander's code range: Eq. (3) prints 2^7 - 1 = 127, but a
+# 4-bit anchor (Algorithm 1 Stage 4: magnitude (I + 7) >> 4 <= 7) carries
+# codes up to 120 only; the compander is scaled to 120 so that every
+# |X_final| in [0, 1] keeps its code (127 with the clip at 120 remains a
+# parameter value).
+CODE_SCALE = 120.0
 
 
 def build(force: bool = True) -> str:
@@ -103,17 +109,17 @@ def _ptr(a: np.ndarray | None):
 
 # ---------------------------------------------------------------- scalars --
 
-def code(x_abs: float, alpha: float = 255.0, code_scale: float = 127.0) -> int:
+def code(x_abs: float, alpha: float = 255.0, code_scale: float = CODE_SCALE) -> int:
     """Round(Eq. (3)) of one binary32 magnitude, before the 120 clip."""
     return lib().oracle_code(x_abs, alpha, code_scale)
 
 
-def code_real(x_abs: float, alpha: float = 255.0, code_scale: float = 127.0) -> float:
+def code_real(x_abs: float, alpha: float = 255.0, code_scale: float = CODE_SCALE) -> float:
     """Y of Eq. (3) in binary64 (used to measure rounding margins)."""
     return lib().oracle_code_real(x_abs, alpha, code_scale)
 
 
-def level(k: int, alpha: float = 255.0, code_scale: float = 127.0) -> float:
+def level(k: int, alpha: float = 255.0, code_scale: float = CODE_SCALE) -> float:
     """Reconstruction magnitude of code k (inverse of Eq. (3))."""
     return lib().oracle_level(k, alpha, code_scale)
 
@@ -155,7 +161,7 @@ class BlockResult:
         self.sign = np.zeros((H, P), np.int8)
 
 
-def quantize_block(x_bf16: np.ndarray, alpha=255.0, eps=1e-6, code_scale=127.0,
+def quantize_block(x_bf16: np.ndarray, alpha=255.0, eps=1e-6, code_scale=CODE_SCALE,
                    C=C_DEFAULT) -> BlockResult:
     """Quantize one page block given token-major as uint16 bf16 bits [P][H]."""
     x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
@@ -172,7 +178,7 @@ def quantize_block(x_bf16: np.ndarray, alpha=255.0, eps=1e-6, code_scale=127.0,
 
 
 def dequant_block(r: BlockResult, full: bool, alpha=255.0, eps=1e-6,
-                  code_scale=127.0, C=C_DEFAULT) -> np.ndarray:
+                  code_scale=CODE_SCALE, C=C_DEFAULT) -> np.ndarray:
     """Reconstruct a block from its codes: anchor-only or anchor + residual."""
     nch, Hh, C = r.anchor.shape
     P, H = nch * C, Hh * 2
@@ -207,7 +213,7 @@ def _ranges(n, parts):
     return [(b, min(n, b + step)) for b in range(0, n, step)]
 
 
-def quantize(kv: np.ndarray, alpha=255.0, eps=1e-6, code_scale=127.0,
+def quantize(kv: np.ndarray, alpha=255.0, eps=1e-6, code_scale=CODE_SCALE,
              H=H_DEFAULT, P=P_DEFAULT, C=C_DEFAULT, threads=1,
              blocks: tuple[int, int] | None = None) -> Codes:
     """Quantize kv (uint16 bf16 bits, shape [num_tensors, T, Ch]).
@@ -243,7 +249,7 @@ def quantize(kv: np.ndarray, alpha=255.0, eps=1e-6, code_scale=127.0,
 
 
 def dequant(codes: Codes, shape, full: bool, alpha=255.0, eps=1e-6,
-            code_scale=127.0, H=H_DEFAULT, P=P_DEFAULT, C=C_DEFAULT, threads=1,
+            code_scale=CODE_SCALE, H=H_DEFAULT, P=P_DEFAULT, C=C_DEFAULT, threads=1,
             blocks: tuple[int, int] | None = None) -> np.ndarray:
     """Reconstruct bf16 bits [num_tensors, T, Ch] from codes.
 

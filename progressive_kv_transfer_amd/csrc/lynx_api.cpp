@@ -376,7 +376,7 @@ void lynx_default_params(lynx_params *p) {
         return;
     p->alpha = 255.0f;
     p->eps = 1e-6f;
-    p->code_scale = 127.0f;
+    p->code_scale = 120.0f;
     p->page_tokens = kPage;
     p->chunk_tokens = kChunk;
     p->block_channels = kHead;

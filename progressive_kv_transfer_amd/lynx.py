@@ -125,7 +125,7 @@ def _check(fn, rc):
         raise LynxError(fn, rc, lib().lynx_status_string(rc).decode())
 
 
-def params(alpha=255.0, eps=1e-6, code_scale=127.0) -> lynx_params:
+def params(alpha=255.0, eps=1e-6, code_scale=120.0) -> lynx_params:
     p = lynx_params()
     lib().lynx_default_params(ctypes.byref(p))
     p.alpha, p.eps, p.code_scale = alpha, eps, code_scale

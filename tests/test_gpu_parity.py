@@ -51,7 +51,7 @@ def assert_codes_equal(gpu: lynx.Codes, ref: oracle.Codes, sel=slice(None)):
         assert np.array_equal(g, r), name  # IEEE ==
 
 
-def full_check(kv, alpha=255.0, eps=1e-6, code_scale=127.0):
+def full_check(kv, alpha=255.0, eps=1e-6, code_scale=120.0):
     p = lynx.params(alpha=alpha, eps=eps, code_scale=code_scale)
     codes, out_a, out_f = run_gpu(kv, p)
     xb = bits(kv.contiguous())
@@ -112,7 +112,8 @@ def test_strided_multi_block_set():
 
 
 @pytest.mark.parametrize("alpha,eps,code_scale", [(100.0, 1e-6, 127.0),
-                                                  (255.0, 1e-6, 120.0),
+                                                  # Eq. (3)'s printed 127, clip at 120
+                                                  (255.0, 1e-6, 127.0),
                                                   (255.0, 2.0 ** -20, 127.0),
                                                   (8.0, 1e-3, 127.0),
                                                   # thresholds over > 16 octaves: the

@@ -97,18 +97,21 @@ def test_unsplit_clamps_unreachable_codes():
 
 # ------------------------------------------------- Eq. (3) compander --
 
+@pytest.mark.parametrize("code_scale", [127.0, 120.0])
 @pytest.mark.parametrize("alpha", [255.0, 100.0, 1.0, 0.5])
-def test_compander_endpoints_and_levels(alpha):
-    """Eq. (3): Y(0) = 0, Y(1) = 2^7 - 1.  Eq. (4) inverse levels are 0 at
-    code 0, 1 at code 127, strictly increasing, and each level maps back to
-    its own code."""
-    assert oracle.code(0.0, alpha) == 0
-    assert oracle.code(1.0, alpha) == 127
-    levels = [oracle.level(k, alpha) for k in range(128)]
-    assert levels[0] == 0.0 and levels[127] == 1.0
+def test_compander_endpoints_and_levels(alpha, code_scale):
+    """Eq. (3): Y(0) = 0, Y(1) = the code scale (2^7 - 1 as printed, or 120,
+    the largest code a 4 + 4 split carries).  Eq. (4) inverse levels are 0 at
+    code 0, 1 at the top code, strictly increasing, and each level maps back
+    to its own code."""
+    top = int(code_scale)
+    assert oracle.code(0.0, alpha, code_scale) == 0
+    assert oracle.code(1.0, alpha, code_scale) == top
+    levels = [oracle.level(k, alpha, code_scale) for k in range(top + 1)]
+    assert levels[0] == 0.0 and levels[top] == 1.0
     assert all(b > a for a, b in zip(levels, levels[1:]))
     for k, lv in enumerate(levels):
-        assert oracle.code(lv, alpha) == k
+        assert oracle.code(lv, alpha, code_scale) == k
 
 
 def test_compander_alpha_to_zero_is_uniform():
@@ -120,20 +123,25 @@ def test_compander_alpha_to_zero_is_uniform():
         y_lin = 127.0 * float(x)
         if abs(y_lin - math.floor(y_lin) - 0.5) < 1e-3:
             continue
-        assert oracle.code(float(x), 1e-7) == int(math.floor(y_lin + 0.5))
+        assert oracle.code(float(x), 1e-7, 127.0) == int(math.floor(y_lin + 0.5))
 
 
 def test_compander_closed_form_alpha_one():
     """alpha = 1: Y = 127 log2(1 + x).  x = 1/3 -> 127 log2(4/3) = 52.71;
     x = 1/2 -> 127 log2(3/2) = 74.29; x = 0.9 -> 127 log2(1.9) = 117.6."""
-    assert oracle.code(float(F32(1.0) / F32(3.0)), 1.0) == 53
-    assert oracle.code(0.5, 1.0) == 74
-    assert oracle.code(0.9, 1.0) == 118
+    assert oracle.code(float(F32(1.0) / F32(3.0)), 1.0, 127.0) == 53
+    assert oracle.code(0.5, 1.0, 127.0) == 74
+    assert oracle.code(0.9, 1.0, 127.0) == 118
+    # the same closed form at the default scale 120: 120 log2(1 + x)
+    assert oracle.code(0.5, 1.0) == 70        # 70.20
+    assert oracle.code(0.9, 1.0) == 111       # 111.12
 
 
 def test_compander_mu_law_value():
-    """alpha = 255 at |x| = 0.5: Y = 127 ln(128.5) / ln(256) = 111.21."""
-    assert oracle.code(0.5, 255.0) == 111
+    """alpha = 255 at |x| = 0.5: Y = 127 ln(128.5) / ln(256) = 111.21, and
+    120 ln(128.5) / ln(256) = 105.08 at the default scale."""
+    assert oracle.code(0.5, 255.0, 127.0) == 111
+    assert oracle.code(0.5, 255.0) == 105
 
 
 @pytest.mark.parametrize("alpha", [255.0, 100.0])
@@ -308,13 +316,13 @@ def _max_dev(code, anchor_only, thr, lev):
     return max(rec - lo, hi - rec)
 
 
-def check_error_bound(x, full, alpha=255.0, eps=1e-6):
+def check_error_bound(x, full, alpha=255.0, eps=1e-6, code_scale=oracle.CODE_SCALE):
     """Every element of the page is reconstructed within the width of its
     code's cell, scaled back by (sigma + eps)(gamma_scale + eps), plus
     binary32 and bf16 rounding."""
-    r = oracle.quantize_block(x, alpha=alpha, eps=eps)
-    out = oracle.dequant_block(r, full, alpha=alpha, eps=eps)
-    thr, lev = _level_bounds(alpha, 127.0)
+    r = oracle.quantize_block(x, alpha=alpha, eps=eps, code_scale=code_scale)
+    out = oracle.dequant_block(r, full, alpha=alpha, eps=eps, code_scale=code_scale)
+    thr, lev = _level_bounds(alpha, code_scale)
     xf = bf16_to_f32(x).astype(np.float64)
     xr = bf16_to_f32(out).astype(np.float64)
     P, H = x.shape
@@ -348,6 +356,33 @@ def test_reconstruction_error_bound_alpha(alpha):
     """The same brute-force bound at another skew."""
     check_error_bound(bits(PAGES["K"]), True, alpha=alpha)
     check_error_bound(bits(PAGES["V"]), False, alpha=alpha)
+
+
+@pytest.mark.parametrize("full", [True, False])
+def test_reconstruction_error_bound_printed_scale(full):
+    """With Eq. (3)'s printed 127, codes above 120 are clipped to 120: the
+    top cell then spans [T_120, 1] and the bound still holds (it is only
+    wider)."""
+    check_error_bound(bits(PAGES["K"]), full, code_scale=127.0)
+    check_error_bound(bits(PAGES["V"]), full, code_scale=127.0)
+
+
+def test_full_code_keeps_the_chunk_maximum():
+    """With the default scale every |X_final| in [0, 1] keeps its code, so the
+    largest element of every chunk (|X_final| = sigma / (sigma + eps)) is
+    rebuilt within one code cell; with 127 and the clip it loses the top of
+    the range (L[120] ~ 0.73 at alpha = 255)."""
+    x = bits(PAGES["K"])
+    for cs, tol in ((oracle.CODE_SCALE, 0.03), (127.0, 0.2)):
+        r = oracle.quantize_block(x, code_scale=cs)
+        xf = np.abs(r.xfinal)
+        top = xf == xf.reshape(xf.shape[0], -1, 32).max(axis=2).repeat(32, axis=1)
+        lev = np.array([oracle.level(int(min(c, 120)), 255.0, cs) for c in r.code_raw[top]])
+        rel = np.abs(lev - xf[top]) / xf[top]
+        if cs == 127.0:
+            assert rel.max() > tol
+        else:
+            assert rel.max() < tol
 
 
 def test_reconstruction_exact_cases():
