@@ -15,6 +15,11 @@ over its average launch time against the 8 TB/s HBM peak.  `cpu_baseline`
 times the CPU oracle (test infrastructure, never tuned) on a bounded sample
 of the same workload on this host.
 
+`transfer` reports the split-stream transfer of the same set through
+pinned host memory (lynx_split_stream_transfer, objects of 4096 page
+blocks): the link alone and the pipelined quantize -> anchor link ->
+residual link -> rebuild, and how much of the codec time the pipeline hides.
+
 `attention` reports, beside the step, the fused dequant + attention calls
 (lynx_decode_attn_dequant) on their own workloads: decode (1 query token,
 64 q-heads over 8 KV heads, 32768 tokens; anchor-only and full codes) and
@@ -52,11 +57,6 @@ BYTES_PER_ELEM = {
     "quantize": 2.0 + 0.5 + 0.5 + 0.28125,
     "dequant_anchor": 0.5 + 0.28125 + 2.0,
     "dequant_full": 0.5 + 0.5 + 0.28125 + 2.0,
-}
-KERNEL_SYMBOL = {
-    "quantize": "quant_kernel<0>",
-    "dequant_anchor": "dequant_kernel<false>",
-    "dequant_full": "dequant_kernel<true>",
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qwen32b_16k.md")
 
@@ -221,6 +221,60 @@ def measure_attention(torch, kvgen, lynx, calls: int, warmup: int, only=None):
     return res
 
 
+TRANSFER_OBJECT_BLOCKS = 4096  # 256 MiB of bf16 KV per transfer object (16 objects)
+
+
+def measure_transfer(torch, lynx, kv, codes, out_a, out_f, kern_ms):
+    """Split-stream transfer of the whole set through pinned host memory:
+    the link alone (codes already made) and the full pipeline (quantize,
+    two link streams, rebuild from anchor, refine)."""
+    shape = lynx.shape_of(kv)
+    nb = lynx.num_blocks(shape)
+    rx = lynx.alloc_codes(nb, "cuda")
+    wire = lynx.alloc_codes(nb, "cpu", pin_memory=True)
+    streams = tuple(torch.cuda.Stream() for _ in range(4))
+    # Raw PCIe rates of one 1 GiB pinned copy each way (the link's floor).
+    pcie = {}
+    for name, src, dst in (("d2h", codes.anchor, wire.anchor), ("h2d", wire.anchor, rx.anchor)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(streams[1]):
+            for rep in range(2):
+                e0.record()
+                dst.copy_(src, non_blocking=True)
+                e1.record()
+        streams[1].synchronize()
+        pcie[name] = src.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    ob = TRANSFER_OBJECT_BLOCKS
+    lynx.split_stream_transfer(None, shape, ob, codes, wire, rx, copies_only=True,
+                               streams=streams)  # warm-up
+    link = lynx.split_stream_transfer(None, shape, ob, codes, wire, rx, copies_only=True,
+                                      streams=streams)
+    pipe = lynx.split_stream_transfer(kv, shape, ob, codes, wire, rx, out_a, out_f,
+                                      streams=streams)
+    anchor_bytes = nb * (16384 + 9216)
+    residual_bytes = nb * 16384
+    serial_anchor = kern_ms["quantize"] + link["anchor_arrived"] + kern_ms["dequant_anchor"]
+    exposed = pipe["anchor_ready"] - link["anchor_arrived"]
+    del rx, wire
+    return {
+        "workload": WORKLOAD, "object_blocks": ob, "objects": -(-nb // ob),
+        "wire": "pinned host memory (device -> host -> device per object)",
+        "pcie_GBps": {k: round(v, 1) for k, v in pcie.items()},
+        "link_floor_ms": round((anchor_bytes + residual_bytes) / 1e9 / min(pcie.values()) * 1e3,
+                               2),
+        "anchor_metadata_bytes": anchor_bytes, "residual_bytes": residual_bytes,
+        "link_only_ms": {k: round(v, 3) for k, v in link.items()},
+        "pipeline_ms": {k: round(v, 3) for k, v in pipe.items()},
+        "link_anchor_GBps": round(anchor_bytes / (link["anchor_arrived"] * 1e-3) / 1e9, 2),
+        "serial_anchor_ready_ms": round(serial_anchor, 3),
+        "exposed_anchor_overhead_ms": round(exposed, 3),
+        # share of quantize + anchor rebuild time that does not show up
+        # after the link (1 when the pipeline is no slower than the link)
+        "hidden_fraction_of_codec_time": round(min(1.0, max(0.0, 1.0 - max(exposed, 0.0) / (
+            kern_ms["quantize"] + kern_ms["dequant_anchor"]))), 4),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -232,6 +286,7 @@ def main():
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--hbm-probe", action="store_true")
     ap.add_argument("--no-attention", action="store_true")
+    ap.add_argument("--no-transfer", action="store_true")
     ap.add_argument("--attention-only", action="store_true")
     ap.add_argument("--attention-calls", type=int, default=50)
     ap.add_argument("--attention-case", default=None,
@@ -331,7 +386,7 @@ def main():
         "config": {"workload": WORKLOAD, "layers": cfg.layers, "tensors": cfg.num_tensors,
                    "tokens": cfg.num_tokens, "channels": cfg.num_channels,
                    "page_tokens": 256, "chunk_tokens": 32, "head_channels": 128,
-                   "alpha": 255.0, "eps": 1e-6, "code_scale": 127.0,
+                   "alpha": p.alpha, "eps": p.eps, "code_scale": p.code_scale,
                    "kv_bf16_bytes": 2 * n_elem, "step": "quantize+anchor_dequant+full_dequant"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -340,6 +395,9 @@ def main():
                      "algorithmic_bytes_per_launch": int(BYTES_PER_ELEM[dom] * n_elem)},
         "kernels": kern,
     }
+    if not args.no_transfer and not args.profile_run:
+        out["transfer"] = measure_transfer(torch, lynx, kv, codes, out_a, out_f,
+                                           {n: kern[n]["ms"] for n in names})
     if not args.no_attention and not args.profile_run:
         del out_a, out_f
         out["attention"] = measure_attention(torch, kvgen, lynx, args.attention_calls, 5)
