@@ -93,6 +93,9 @@ def lib():
             L.oracle_dequant.argtypes = [
                 vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, i32,
                 f32, f32, f32, i64, i64, i64, vp]
+            L.oracle_spec_verify.restype = i32
+            L.oracle_spec_verify.argtypes = [vp, vp, vp, vp, f64, i32, i32,
+                                             ctypes.POINTER(i32), ctypes.POINTER(i32)]
             L.oracle_attention.restype = i32
             L.oracle_attention.argtypes = [
                 vp, vp, vp, i32, i32, i32, i32, i64, f64, i32, i32, i32, vp]
@@ -311,3 +314,21 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
         with ThreadPoolExecutor(len(ranges)) as ex:
             list(ex.map(run, ranges))
     return out
+
+
+def spec_verify(draft_logits: np.ndarray, target_logits: np.ndarray, tokens: np.ndarray,
+                u_accept: np.ndarray, u_sample: float):
+    """Speculative verification (accept prefix, correct at the first
+    rejection): returns (n_accepted, next_token)."""
+    d = np.ascontiguousarray(draft_logits, np.float32)
+    t = np.ascontiguousarray(target_logits, np.float32)
+    s = np.ascontiguousarray(tokens, np.int32)
+    u = np.ascontiguousarray(u_accept, np.float64)
+    T, V = d.shape
+    assert t.shape == (T + 1, V) and s.shape == (T,) and u.shape == (T,)
+    n, tok = ctypes.c_int(0), ctypes.c_int(0)
+    rc = lib().oracle_spec_verify(_ptr(d), _ptr(t), _ptr(s), _ptr(u), float(u_sample), T, V,
+                                  ctypes.byref(n), ctypes.byref(tok))
+    if rc:
+        raise ValueError("oracle_spec_verify rejected the arguments")
+    return n.value, tok.value

@@ -27,10 +27,13 @@
  *   - the 32-token mean is a balanced pairwise tree sum, then / C;
  *   - S = Sign(X_cent), with +0 and -0 counted as non-negative;
  *   - Round is round-half-up of the real value Y;
- *   - the integer code is clipped at 120 so that the anchor magnitude
- *     (I + 7) >> 4 fits a 4-bit two's-complement nibble;
+ *   - the compander's top code is a parameter (code_scale): 120 by default,
+ *     the largest code whose anchor magnitude (I + 7) >> 4 fits a 4-bit
+ *     two's-complement nibble; with Eq. (3)'s printed 127 the integer code
+ *     is clipped at 120;
  *   - anchor-only reconstruction uses code V << 4;
- *   - the exact inverse of Eq. (3) is ((1 + alpha)^(I / 127) - 1) / alpha;
+ *   - the exact inverse of Eq. (3) is ((1 + alpha)^(I / code_scale) - 1) /
+ *     alpha;
  *   - denormalisation is the literal inverse of lines "X_final" then
  *     "X <- (X - gamma_min) / (gamma_scale + eps)", four roundings, then
  *     bf16 round-to-nearest-even;
@@ -468,5 +471,95 @@ int oracle_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     }
     free(s);
     free(qv);
+    return ORACLE_OK;
+}
+
+/* ----------------------------------------------- speculative verification -- */
+
+/*
+ * Verification of T draft tokens (Lynx paper, Section 4.3: the drafts made
+ * on the Anchor-only cache are checked in one forward pass on the full
+ * cache; the notes' "推测验证与无损纠错", Eq. (10) and Eq. (11)).
+ *   draft_logits  : [T][V] binary32, the logits the drafts were drawn from
+ *                   (q_t = softmax of row t);
+ *   target_logits : [T + 1][V] binary32, the full-precision logits (p_t);
+ *   tokens        : [T] the draft tokens s_t;
+ *   u_accept      : [T] uniforms in [0, 1); u_sample: one uniform in [0, 1).
+ * Token t is accepted when u_t < p_t(s_t) / q_t(s_t) (probability
+ * min(1, p/q), Eq. 10); the first rejection at position k stops the scan and
+ * the next token is drawn from max(0, p_k - q_k) (Eq. 11) by inverse CDF:
+ * the smallest x with sum_{y <= x} r(y) > u_sample * sum_y r(y).  If every
+ * draft is accepted, the next token is drawn from p_T the same way (the
+ * standard speculative sampling step the paper adopts).  Softmaxes, ratios
+ * and sums in binary64, sums in increasing token order.
+ * Writes *n_accepted (0..T) and *token.
+ */
+static void softmax_row(const float *l, int V, double *out)
+{
+    double mx = -INFINITY, den = 0.0;
+    for (int i = 0; i < V; ++i)
+        if ((double)l[i] > mx) mx = (double)l[i];
+    for (int i = 0; i < V; ++i) {
+        out[i] = exp((double)l[i] - mx);
+        den += out[i];
+    }
+    for (int i = 0; i < V; ++i)
+        out[i] /= den;
+}
+
+static int sample_inverse_cdf(const double *w, int V, double u)
+{
+    double total = 0.0;
+    for (int i = 0; i < V; ++i)
+        total += w[i];
+    const double target = u * total;
+    double run = 0.0;
+    int last = -1;
+    for (int i = 0; i < V; ++i) {
+        if (w[i] > 0.0)
+            last = i;
+        run += w[i];
+        if (run > target)
+            return i;
+    }
+    return last;  /* rounding left target at the very top: last positive entry */
+}
+
+int oracle_spec_verify(const float *draft_logits, const float *target_logits,
+                       const int32_t *tokens, const double *u_accept, double u_sample,
+                       int T, int V, int32_t *n_accepted, int32_t *token)
+{
+    if (T < 0 || V <= 0)
+        return ORACLE_EINVAL;
+    double *p = (double *)malloc(sizeof(double) * (size_t)V);
+    double *q = (double *)malloc(sizeof(double) * (size_t)V);
+    if (!p || !q) {
+        free(p); free(q);
+        return ORACLE_EINVAL;
+    }
+    int k = 0;
+    for (; k < T; ++k) {
+        const int32_t s = tokens[k];
+        if (s < 0 || s >= V) {
+            free(p); free(q);
+            return ORACLE_EINVAL;
+        }
+        softmax_row(target_logits + (size_t)k * V, V, p);
+        softmax_row(draft_logits + (size_t)k * V, V, q);
+        if (!(u_accept[k] < p[s] / q[s]))
+            break;
+    }
+    *n_accepted = k;
+    if (k < T) {
+        /* p, q hold row k: residual distribution max(0, p - q) */
+        for (int i = 0; i < V; ++i)
+            p[i] = p[i] > q[i] ? p[i] - q[i] : 0.0;
+        *token = sample_inverse_cdf(p, V, u_sample);
+    } else {
+        softmax_row(target_logits + (size_t)T * V, V, p);
+        *token = sample_inverse_cdf(p, V, u_sample);
+    }
+    free(p);
+    free(q);
     return ORACLE_OK;
 }
