@@ -16,6 +16,8 @@
  *     Algorithm 1 on their own (the same arithmetic as the fused quantize);
  *   - lynx_split_stream_transfer: the prioritized transmission of Section
  *     4.2 (Figure 7) emulated on one GPU through a wire buffer;
+ *   - lynx_spec_verify: the verification that closes a speculative round
+ *     (Section 4.3): accepted prefix and corrected next token;
  *   - lynx_decode_attn_dequant: attention O = softmax(Q K^T scale) V
  *     (Section 2.1) over K, V rebuilt on the fly from their streams: one
  *     query token (decode on the draft or verification precision) or T
@@ -300,6 +302,34 @@ int lynx_split_stream_transfer(const void *kv, const lynx_kv_shape *shape,
                                hipStream_t sender, hipStream_t anchor_link,
                                hipStream_t residual_link, hipStream_t receiver,
                                lynx_transfer_times *times);
+
+/* Workspace bytes of lynx_spec_verify (0 for invalid sizes).  Host only. */
+size_t lynx_spec_verify_workspace_bytes(int t_draft, int vocab);
+
+/*
+ * Speculative verification of t_draft draft tokens (the paper's Section 4.3:
+ * the drafts decoded on the Anchor-only cache are checked in one forward
+ * pass on the full cache, the longest valid prefix is accepted and the first
+ * divergence corrected; the notes' Eq. (10) and Eq. (11)).
+ *   draft_logits   float32 [t_draft][vocab] (device): the logits the drafts
+ *                  were drawn from, q_t = softmax(row t);
+ *   target_logits  float32 [t_draft + 1][vocab] (device): p_t on Q_full;
+ *   draft_tokens   int32 [t_draft] (device); u_accept float64 [t_draft]
+ *                  (device), uniforms in [0, 1); u_sample in [0, 1);
+ *   out            int32 [2] (device): accepted drafts k (0..t_draft) and the
+ *                  next token.
+ * Draft t is accepted when u_accept[t] < p_t(s_t) / q_t(s_t); at the first
+ * rejection k the next token is the smallest x whose running sum of
+ * max(0, p_k - q_k) exceeds u_sample times its total; if all drafts pass it
+ * is drawn the same way from p_{t_draft}.  Softmaxes in binary64.  A draft
+ * token outside [0, vocab) counts as rejected.  t_draft <= 64.  Errors as
+ * above.
+ */
+int lynx_spec_verify(const float *draft_logits, const float *target_logits,
+                     const int32_t *draft_tokens, const double *u_accept,
+                     double u_sample, int t_draft, int vocab, int32_t *out,
+                     void *workspace, size_t workspace_bytes,
+                     hipStream_t stream);
 
 #ifdef __cplusplus
 }

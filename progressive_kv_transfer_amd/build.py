@@ -31,7 +31,7 @@ DEVICE = [f"--offload-arch={ARCH}", "-ffp-contract=off", "-fno-honor-nans",
           "-Xclang", "-packed-fp32-ops"]
 HOST = ["-ffp-contract=off", "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include"]
 
-DEVICE_SOURCES = ["lynx_quant.hip", "lynx_dequant.hip", "lynx_attn.hip"]
+DEVICE_SOURCES = ["lynx_quant.hip", "lynx_dequant.hip", "lynx_attn.hip", "lynx_verify.hip"]
 HOST_SOURCES = ["lynx_api.cpp"]
 
 

@@ -681,4 +681,41 @@ int lynx_split_stream_transfer(const void *kv, const lynx_kv_shape *shape,
     return LYNX_OK;
 }
 
+size_t lynx_spec_verify_workspace_bytes(int t_draft, int vocab) {
+    if (t_draft < 0 || t_draft > kVerifyMaxDraft || vocab <= 0)
+        return 0;
+    const int64_t chunks = (vocab + kVerifyChunk - 1) / kVerifyChunk;
+    return (size_t)(2 * t_draft + 1) * chunks * 2 * sizeof(double);
+}
+
+int lynx_spec_verify(const float *draft_logits, const float *target_logits,
+                     const int32_t *draft_tokens, const double *u_accept, double u_sample,
+                     int t_draft, int vocab, int32_t *out, void *workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+    if (t_draft < 0 || t_draft > kVerifyMaxDraft || vocab <= 0 || vocab > (1 << 26))
+        return LYNX_EINVAL;
+    if (!(u_sample >= 0.0) || !(u_sample < 1.0))
+        return LYNX_EINVAL;
+    if (!target_logits || !out || !workspace)
+        return LYNX_EINVAL;
+    if (t_draft > 0 && (!draft_logits || !draft_tokens || !u_accept))
+        return LYNX_EINVAL;
+    if (workspace_bytes < lynx_spec_verify_workspace_bytes(t_draft, vocab))
+        return LYNX_EINVAL;
+    if (((uintptr_t)workspace & 7u) || ((uintptr_t)u_accept & 7u) || ((uintptr_t)out & 3u))
+        return LYNX_ESHAPE;
+    VerifyArgs a;
+    a.draft = draft_logits;
+    a.target = target_logits;
+    a.tokens = draft_tokens;
+    a.u_accept = u_accept;
+    a.u_sample = u_sample;
+    a.t = t_draft;
+    a.vocab = vocab;
+    a.chunks = (vocab + kVerifyChunk - 1) / kVerifyChunk;
+    a.ws = (double *)workspace;
+    a.out = out;
+    return hip_status(launch_verify(a, stream));
+}
+
 }  // extern "C"

@@ -84,4 +84,19 @@ struct AttnArgs {
 int attn_row_tiles(int rows);  // tiles of 16 query rows, -1 if rows > 64
 hipError_t launch_attention(const AttnArgs &a, const DequantTab &tab, hipStream_t stream);
 
+// Speculative verification (lynx_verify.hip).
+constexpr int kVerifyChunk = 8192;    // tokens per statistics workgroup
+constexpr int kVerifyMaxDraft = 64;   // draft tokens per call at most
+struct VerifyArgs {
+    const float *draft;      // [t][vocab] logits the drafts were drawn from
+    const float *target;     // [t + 1][vocab] full-precision logits
+    const int32_t *tokens;   // [t] draft tokens
+    const double *u_accept;  // [t] uniforms
+    double u_sample;         // uniform of the correction / bonus draw
+    int t, vocab, chunks;    // chunks = ceil(vocab / kVerifyChunk)
+    double *ws;              // [2t + 1][chunks][2]: chunk max, chunk sum
+    int32_t *out;            // [2]: accepted drafts, next token
+};
+hipError_t launch_verify(const VerifyArgs &a, hipStream_t stream);
+
 }  // namespace lynx

@@ -238,3 +238,27 @@ def edge_pages(seed: int = 7) -> dict[str, torch.Tensor]:
     out["all_negative"] = _bf16_from_f32(-(lap.abs() + 0.01))
     out["zeros"] = _bf16_from_f32(torch.zeros((P, H)))
     return out
+
+
+def verify_inputs(seed: int, t_draft: int, vocab: int, noise: float = 0.3,
+                  logit_scale: float = 2.5):
+    """Synthetic inputs of one speculative verification (host tensors):
+    target logits [t_draft + 1][vocab] ~ N(0, logit_scale^2), draft logits =
+    the first t_draft target rows + N(0, noise^2) (the draft model's
+    approximation), draft tokens drawn from softmax(draft rows), uniforms
+    u_accept [t_draft] and u_sample (float64)."""
+    g = torch.Generator().manual_seed(seed)
+    target = torch.randn((t_draft + 1, vocab), generator=g) * logit_scale
+    draft = target[:t_draft] + torch.randn((t_draft, vocab), generator=g) * noise
+    if t_draft:
+        tokens = torch.multinomial(torch.softmax(draft.double(), dim=1), 1,
+                                   generator=g)[:, 0].to(torch.int32)
+    else:
+        tokens = torch.zeros(0, dtype=torch.int32)
+    u_accept = torch.rand(t_draft, dtype=torch.float64, generator=g)
+    u_sample = float(torch.rand(1, dtype=torch.float64, generator=g))
+    return draft.contiguous(), target.contiguous(), tokens, u_accept, u_sample
+
+
+# Speculative verification workload: 8 drafts over a Qwen3-sized vocabulary.
+VERIFY_T, VERIFY_VOCAB = 8, 151936

@@ -65,7 +65,8 @@ EXPORTS = ["lynx_default_params", "lynx_num_blocks", "lynx_stream_bytes",
            "lynx_status_string", "lynx_compander_thresholds", "lynx_quantize_pages", "lynx_dequant_anchor",
            "lynx_dequant_full", "lynx_page_stats", "lynx_block_stats",
            "lynx_attn_workspace_bytes", "lynx_decode_attn_dequant",
-           "lynx_split_stream_transfer"]
+           "lynx_split_stream_transfer", "lynx_spec_verify_workspace_bytes",
+           "lynx_spec_verify"]
 
 _lib = None
 
@@ -112,9 +113,13 @@ def lib():
         L.lynx_split_stream_transfer.argtypes = [vp, P(lynx_kv_shape), P(lynx_params), i64,
                                                  lynx_codes, lynx_codes, lynx_codes, vp, vp,
                                                  i32, vp, vp, vp, vp, P(lynx_transfer_times)]
+        L.lynx_spec_verify_workspace_bytes.argtypes = [i32, i32]
+        L.lynx_spec_verify_workspace_bytes.restype = ctypes.c_size_t
+        L.lynx_spec_verify.argtypes = [vp, vp, vp, vp, ctypes.c_double, i32, i32, vp, vp,
+                                       ctypes.c_size_t, vp]
         for f in ("lynx_quantize_pages", "lynx_dequant_anchor", "lynx_dequant_full",
                   "lynx_page_stats", "lynx_block_stats", "lynx_decode_attn_dequant",
-                  "lynx_split_stream_transfer"):
+                  "lynx_split_stream_transfer", "lynx_spec_verify"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -358,3 +363,32 @@ def split_stream_transfer(kv: torch.Tensor | None, shape: lynx_kv_shape, object_
         TRANSFER_COPIES_ONLY if copies_only else 0,
         *(ctypes.c_void_p(s.cuda_stream) for s in streams), ctypes.byref(t)))
     return {n: float(getattr(t, n)) for n, _ in lynx_transfer_times._fields_}
+
+
+def spec_verify_workspace_bytes(t_draft: int, vocab: int) -> int:
+    return int(lib().lynx_spec_verify_workspace_bytes(t_draft, vocab))
+
+
+def spec_verify(draft_logits: torch.Tensor, target_logits: torch.Tensor, tokens: torch.Tensor,
+                u_accept: torch.Tensor, u_sample: float, out: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """lynx_spec_verify: float32 logits [T, V] / [T + 1, V], int32 tokens [T],
+    float64 uniforms [T] on the device; returns int32 [2] (accepted drafts,
+    next token) on the device."""
+    _require_cuda(target_logits)
+    t_draft, vocab = target_logits.shape[0] - 1, target_logits.shape[1]
+    for x, dt in ((draft_logits, torch.float32), (target_logits, torch.float32),
+                  (tokens, torch.int32), (u_accept, torch.float64)):
+        if x.dtype != dt or not x.is_contiguous():
+            raise ValueError("spec_verify: contiguous float32 logits, int32 tokens and "
+                             "float64 uniforms expected")
+    if out is None:
+        out = torch.empty(2, dtype=torch.int32, device=target_logits.device)
+    if workspace is None:
+        workspace = torch.empty(max(spec_verify_workspace_bytes(t_draft, vocab), 16),
+                                dtype=torch.uint8, device=target_logits.device)
+    _check("lynx_spec_verify", lib().lynx_spec_verify(
+        draft_logits.data_ptr(), target_logits.data_ptr(), tokens.data_ptr(),
+        u_accept.data_ptr(), float(u_sample), t_draft, vocab, out.data_ptr(),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out

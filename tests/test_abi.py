@@ -293,3 +293,20 @@ def test_transfer_empty_set_and_copies_only_needs_no_kv():
                                             _codes(), None, None, 1, None, None, None, None,
                                             ctypes.byref(t)) == 0
         assert t.full_ready == 0.0
+
+
+def test_spec_verify_workspace_and_errors():
+    L = lynx.lib()
+    ws = lynx.spec_verify_workspace_bytes
+    assert ws(8, 151936) == 17 * 19 * 16     # 2T + 1 rows x ceil(V / 8192) chunks
+    assert ws(0, 1) == 16
+    assert ws(65, 100) == 0 and ws(-1, 100) == 0 and ws(3, 0) == 0
+    ok = dict(d=FAKE, t=FAKE, s=FAKE, u=FAKE, us=0.5, T=8, V=1000, out=FAKE, w=FAKE, wb=1 << 20)
+    cases = [dict(T=65), dict(V=0), dict(us=1.0), dict(us=float("nan")), dict(t=None),
+             dict(d=None), dict(out=None), dict(w=None), dict(wb=16), dict(u=FAKE + 4)]
+    expect = [-1, -1, -1, -1, -1, -1, -1, -1, -1, -2]
+    for c, e in zip(cases, expect):
+        a = {**ok, **c}
+        rc = L.lynx_spec_verify(a["d"], a["t"], a["s"], a["u"], a["us"], a["T"], a["V"],
+                                a["out"], a["w"], a["wb"], None)
+        assert rc == e, (c, rc)
