@@ -20,6 +20,10 @@ pinned host memory (lynx_split_stream_transfer, objects of 4096 page
 blocks): the link alone and the pipelined quantize -> anchor link ->
 residual link -> rebuild, and how much of the codec time the pipeline hides.
 
+`verify` reports the speculative verification (lynx_spec_verify) of 8
+drafts over a 151936-token vocabulary: time per call and logit bytes per
+second.
+
 `attention` reports, beside the step, the fused dequant + attention calls
 (lynx_decode_attn_dequant) on their own workloads: decode (1 query token,
 64 q-heads over 8 KV heads, 32768 tokens; anchor-only and full codes) and
@@ -221,6 +225,36 @@ def measure_attention(torch, kvgen, lynx, calls: int, warmup: int, only=None):
     return res
 
 
+def measure_verify(torch, kvgen, lynx, calls: int = 200, sets: int = 32):
+    """Speculative verification of 8 drafts over a Qwen-sized vocabulary:
+    average time per call over `sets` different input sets (more bytes than
+    the last-level cache), algorithmic bytes = the 2T + 1 logit rows once
+    plus the two rows of the correction pass."""
+    T, V = kvgen.VERIFY_T, kvgen.VERIFY_VOCAB
+    inputs = []
+    for i in range(sets):
+        d, t, s, u, us = kvgen.verify_inputs(7000 + i, T, V, 0.3)
+        inputs.append((d.cuda(), t.cuda(), s.cuda(), u.cuda(), us))
+    ws = torch.empty(lynx.spec_verify_workspace_bytes(T, V), dtype=torch.uint8, device="cuda")
+    out = torch.empty(2, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for i in range(10):
+        lynx.spec_verify(*inputs[i % sets], out=out, workspace=ws, stream=stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(calls):
+        lynx.spec_verify(*inputs[i % sets], out=out, workspace=ws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us_call = e0.elapsed_time(e1) / calls * 1e3
+    algo = (2 * T + 1 + 2) * V * 4
+    return {"drafts": T, "vocab": V, "us_per_call": round(us_call, 2),
+            "algorithmic_bytes": algo, "GBps": round(algo / (us_call * 1e-6) / 1e9, 1),
+            "hbm_frac": round(algo / (us_call * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "input_sets": sets}
+
+
 TRANSFER_OBJECT_BLOCKS = 4096  # 256 MiB of bf16 KV per transfer object (16 objects)
 
 
@@ -401,6 +435,8 @@ def main():
     if not args.no_attention and not args.profile_run:
         del out_a, out_f
         out["attention"] = measure_attention(torch, kvgen, lynx, args.attention_calls, 5)
+    if not args.profile_run:
+        out["verify"] = measure_verify(torch, kvgen, lynx)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = run_cpu_baseline(cfg, kv, args.cpu_budget)
     print(json.dumps(out), flush=True)
