@@ -81,6 +81,21 @@ def load_traffic(kernel: str):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
+def load_counters():
+    """VALU figures of the quantize kernel from the committed SQ-counter
+    summary, or None if absent or taken on different kernel sources."""
+    try:
+        with open(os.path.join(ROOT, "profiles", "counters_qwen32b_16k.md")) as f:
+            text = f.read()
+        t = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    except (OSError, ValueError, IndexError):
+        return None
+    from progressive_kv_transfer_amd.profiling import kernel_source_hash
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("quantize")
+
+
 def cpu_threads() -> int:
     try:
         n = len(os.sched_getaffinity(0))
@@ -426,7 +441,12 @@ def main():
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": None if traffic is None else int(traffic),
-                     "algorithmic_bytes_per_launch": int(BYTES_PER_ELEM[dom] * n_elem)},
+                     "algorithmic_bytes_per_launch": int(BYTES_PER_ELEM[dom] * n_elem),
+                     # share of the kernel's cycles the SIMDs spend issuing
+                     # VALU work, from the committed rocprofv3 SQ counters
+                     # (null when the kernel sources changed since)
+                     "valu_busy": (load_counters() or {}).get("valu_busy")
+                     if dom == "quantize" else None},
         "kernels": kern,
     }
     if not args.no_transfer and not args.profile_run:

@@ -2,8 +2,11 @@
 // O = softmax(Q K^T * scale) V (the paper's Section 2.1) where K^ and V^ are
 // rebuilt on the fly from the Anchor stream alone (the speculative draft,
 // Section 4.2 Figure 7(b)) or from Anchor + Residual (the verification
-// precision, Figure 7(c)), bit-identical to lynx_dequant_anchor /
-// lynx_dequant_full (shared arithmetic in lynx_recon.h).  One query token is
+// precision, Figure 7(c)).  Eq. (4) is evaluated as one fused multiply-add
+// per element, S L * a + b, with a and b folded per chunk and channel, so
+// K^ and V^ equal those of lynx_dequant_anchor / lynx_dequant_full up to
+// rounding order (the two can differ by one bf16 unit in the last place
+// where a value lies next to a rounding boundary).  One query token is
 // decode; T query tokens with a causal tail are the single parallel forward
 // pass that verifies T drafts (Section 4.3).
 //
@@ -53,6 +56,21 @@ struct LaneCodes {
     float2 gm, gs, mu, sg;
 };
 
+// Eq. (4) folded per (chunk, channel): x^ = S L * a + b with
+// a = (sigma + eps)(gamma_scale + eps), b = mu (gamma_scale + eps) + gamma_min,
+// one fused multiply-add per element (channels 2p in .x, 2p + 1 in .y).
+struct Affine {
+    float2 a, b;
+};
+
+__device__ __forceinline__ Affine fold(const LaneCodes &L, float eps) {
+    const float d1x = L.gs.x + eps, d1y = L.gs.y + eps;
+    Affine f;
+    f.a = make_float2((L.sg.x + eps) * d1x, (L.sg.y + eps) * d1y);
+    f.b = make_float2(__builtin_fmaf(L.mu.x, d1x, L.gm.x), __builtin_fmaf(L.mu.y, d1y, L.gm.y));
+    return f;
+}
+
 __device__ __forceinline__ void load_codes(const uint8_t *anc, const uint8_t *res,
                                            const float *gmin, const float *gsc, const float *mu,
                                            const float *sg, int64_t b, int j, int p,
@@ -73,32 +91,76 @@ __device__ __forceinline__ void load_codes(const uint8_t *anc, const uint8_t *re
     L.sg = *(const float2 *)(sg + b * (kChunks * kHead) + j * kHead + 2 * p);
 }
 
+// Byte i of w shifted left by S (an SDWA byte select: one instruction).
+template <int S>
+__device__ __forceinline__ uint32_t byte_shl(uint32_t w, int i) {
+    uint32_t r;
+    switch (i) {
+    case 0:
+        asm("v_lshlrev_b32_sdwa %0, %2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD "
+            "src0_sel:DWORD src1_sel:BYTE_0" : "=v"(r) : "v"(w), "i"(S));
+        break;
+    case 1:
+        asm("v_lshlrev_b32_sdwa %0, %2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD "
+            "src0_sel:DWORD src1_sel:BYTE_1" : "=v"(r) : "v"(w), "i"(S));
+        break;
+    case 2:
+        asm("v_lshlrev_b32_sdwa %0, %2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD "
+            "src0_sel:DWORD src1_sel:BYTE_2" : "=v"(r) : "v"(w), "i"(S));
+        break;
+    default:
+        asm("v_lshlrev_b32_sdwa %0, %2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD "
+            "src0_sel:DWORD src1_sel:BYTE_3" : "=v"(r) : "v"(w), "i"(S));
+        break;
+    }
+    return r;
+}
+
+// Signed-level tables at the start of the kernel's LDS (so a table address
+// is the shifted code byte itself): lut[anchor nibble | residual nibble << 4]
+// for full codes, lut2[anchor byte] = the levels of both channels of the
+// byte for anchor-only codes (one 8-byte read per token).
+struct Luts {
+    const float *lut;
+    const float2 *lut2;
+};
+
 // Rebuild 4 tokens of channel pair (2p, 2p+1) from one anchor word and one
-// residual word (a byte per token).  lut is indexed by anchor nibble |
-// residual nibble << 4 (residual 0 = anchor-only).
-__device__ __forceinline__ void rebuild_word(uint32_t A, uint32_t R, const LaneCodes &L,
-                                             float eps, const float *lut, float y0[4],
-                                             float y1[4]) {
-    const uint32_t X = (A & 0x0f0f0f0fu) | ((R << 4) & 0xf0f0f0f0u);  // channel 2p
-    const uint32_t Y = ((A >> 4) & 0x0f0f0f0fu) | (R & 0xf0f0f0f0u);  // channel 2p + 1
-    const float d1a = L.gs.x + eps, d1b = L.gs.y + eps;
-    const float d2a = L.sg.x + eps, d2b = L.sg.y + eps;
+// residual word (a byte per token).
+template <bool FULL>
+__device__ __forceinline__ void rebuild_word(uint32_t A, uint32_t R, const Affine &f,
+                                             const Luts &t, float y0[4], float y1[4]) {
+    if (FULL) {
+        const uint32_t X = (A & 0x0f0f0f0fu) | ((R << 4) & 0xf0f0f0f0u);  // channel 2p
+        const uint32_t Y = ((A >> 4) & 0x0f0f0f0fu) | (R & 0xf0f0f0f0u);  // channel 2p + 1
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        y0[i] = reconstruct(lut[(X >> (8 * i)) & 0xffu], d2a, L.mu.x, d1a, L.gm.x);
-        y1[i] = reconstruct(lut[(Y >> (8 * i)) & 0xffu], d2b, L.mu.y, d1b, L.gm.y);
+        for (int i = 0; i < 4; ++i) {
+            const float s0 = *(const float *)((const char *)t.lut + byte_shl<2>(X, i));
+            const float s1 = *(const float *)((const char *)t.lut + byte_shl<2>(Y, i));
+            y0[i] = __builtin_fmaf(s0, f.a.x, f.b.x);
+            y1[i] = __builtin_fmaf(s1, f.a.y, f.b.y);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float2 sl = *(const float2 *)((const char *)t.lut2 + byte_shl<3>(A, i));
+            y0[i] = __builtin_fmaf(sl.x, f.a.x, f.b.x);
+            y1[i] = __builtin_fmaf(sl.y, f.a.y, f.b.y);
+        }
     }
 }
 
 // K^ rows: [token][channel] bf16; the lane writes dword p (channels 2p,
 // 2p + 1) of its 32 tokens.
-__device__ __forceinline__ void store_k(const LaneCodes &L, float eps, const float *lut, int p,
+template <bool FULL>
+__device__ __forceinline__ void store_k(const LaneCodes &L, float eps, const Luts &t, int p,
                                         int c, uint32_t *sK) {
     const u32x4 a[2] = {L.a0, L.a1}, r[2] = {L.r0, L.r1};
+    const Affine f = fold(L, eps);
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
         float y0[4], y1[4];
-        rebuild_word(a[w >> 2][w & 3], r[w >> 2][w & 3], L, eps, lut, y0, y1);
+        rebuild_word<FULL>(a[w >> 2][w & 3], r[w >> 2][w & 3], f, t, y0, y1);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             sK[(32 * c + 4 * w + i) * kRowDw + p] = pack_bf16(y0[i], y1[i]);
@@ -107,15 +169,17 @@ __device__ __forceinline__ void store_k(const LaneCodes &L, float eps, const flo
 
 // V^ rows: row p holds channel 2p, row 64 + p channel 2p + 1, each as 128
 // tokens of bf16; the lane writes tokens 32c .. 32c + 31 of both rows.
-__device__ __forceinline__ void store_v(const LaneCodes &L, float eps, const float *lut, int p,
+template <bool FULL>
+__device__ __forceinline__ void store_v(const LaneCodes &L, float eps, const Luts &t, int p,
                                         int c, uint32_t *sV) {
     const u32x4 a[2] = {L.a0, L.a1}, r[2] = {L.r0, L.r1};
+    const Affine f = fold(L, eps);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         float y0[8], y1[8];
-        rebuild_word(a[q >> 1][2 * (q & 1)], r[q >> 1][2 * (q & 1)], L, eps, lut, y0, y1);
-        rebuild_word(a[q >> 1][2 * (q & 1) + 1], r[q >> 1][2 * (q & 1) + 1], L, eps, lut,
-                     y0 + 4, y1 + 4);
+        rebuild_word<FULL>(a[q >> 1][2 * (q & 1)], r[q >> 1][2 * (q & 1)], f, t, y0, y1);
+        rebuild_word<FULL>(a[q >> 1][2 * (q & 1) + 1], r[q >> 1][2 * (q & 1) + 1], f, t,
+                           y0 + 4, y1 + 4);
         const u32x4 e = {pack_bf16(y0[0], y0[1]), pack_bf16(y0[2], y0[3]),
                          pack_bf16(y0[4], y0[5]), pack_bf16(y0[6], y0[7])};
         const u32x4 o = {pack_bf16(y1[0], y1[1]), pack_bf16(y1[2], y1[3]),
@@ -146,6 +210,18 @@ __device__ __forceinline__ float row_sum4(float x) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Step boundary between the rebuild and the products.  With one row tile
+// every wave reads back only the chunk it wrote itself, and a wave's LDS
+// instructions execute in program order, so the compiler only has to keep
+// its LDS accesses on their side of this point; otherwise the waves meet.
+template <int RT>
+__device__ __forceinline__ void step_sync() {
+    if (RT == 1)
+        asm volatile("" ::: "memory");
+    else
+        __syncthreads();
+}
+
 // Channel held by LDS V^ row rho.
 __device__ __forceinline__ int v_row_channel(int rho) {
     return rho < 64 ? 2 * rho : 2 * (rho - 64) + 1;
@@ -156,9 +232,19 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(AttnArgs 
                                                                        const DequantTab tab) {
     constexpr int kWavesPerTile = 4 / RT;
 
-    __shared__ __attribute__((aligned(16))) uint32_t sK[kKDw];
-    __shared__ __attribute__((aligned(16))) uint32_t sV[kVDw];
-    __shared__ float s_lut[256];
+    // One LDS block with the level tables first (address 0 of the
+    // workgroup's LDS), then K^ and V^.
+    struct Lds {
+        float lut[256];
+        float2 lut2[256];
+        __attribute__((aligned(16))) uint32_t k[kKDw];
+        __attribute__((aligned(16))) uint32_t v[kVDw];
+    };
+    __shared__ Lds lds;
+    uint32_t *const sK = lds.k;
+    uint32_t *const sV = lds.v;
+    float *const s_lut = lds.lut;
+    float2 *const s_lut2 = lds.lut2;
 
     const int tid = (int)__builtin_amdgcn_workitem_id_x();
     const int wg = (int)__builtin_amdgcn_workgroup_id_x();
@@ -168,6 +254,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(AttnArgs 
     const int wave = tid >> 6;
 
     s_lut[tid] = signed_level(tab, tid, true);
+    s_lut2[tid] = make_float2(signed_level(tab, tid & 15, false),
+                              signed_level(tab, tid >> 4, false));
+    const Luts luts = {s_lut, s_lut2};
 
     // Steps [st0, st1) of this split.
     const int steps = a.pages * 2;
@@ -217,15 +306,21 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(AttnArgs 
     __syncthreads();  // s_lut
 
     for (int st = st0; st < st1; ++st) {
-        store_k(ck, tab.eps, s_lut, p, c_fill, sK);
-        store_v(cv, tab.eps, s_lut, p, c_fill, sV);
+        if (a.k_res)
+            store_k<true>(ck, tab.eps, luts, p, c_fill, sK);
+        else
+            store_k<false>(ck, tab.eps, luts, p, c_fill, sK);
+        if (a.v_res)
+            store_v<true>(cv, tab.eps, luts, p, c_fill, sV);
+        else
+            store_v<false>(cv, tab.eps, luts, p, c_fill, sV);
         if (st + 1 < st1) {
             const int64_t b = (int64_t)((st + 1) >> 1) * a.n_kvh + kvh;
             const int j = ((st + 1) & 1) * 4 + c_fill;
             load_codes(a.k_anc, a.k_res, a.k_gmin, a.k_gsc, a.k_mu, a.k_sg, b, j, p, ck);
             load_codes(a.v_anc, a.v_res, a.v_gmin, a.v_gsc, a.v_mu, a.v_sg, b, j, p, cv);
         }
-        __syncthreads();
+        step_sync<RT>();
 
         const int64_t tok0 = (int64_t)st * kStep;
         const bool need_mask = tok0 + kStep - 1 > a.ctx - a.t_q;  // uniform
@@ -289,8 +384,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(AttnArgs 
                 o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, plo, o[mt], 0, 0, 0);
             }
         }
-        __syncthreads();  // sK / sV are refilled by the next step
+        step_sync<RT>();  // sK / sV are refilled by the next step
     }
+    __syncthreads();  // the merge area overlaps every wave's K^ rows
 
     // Merge the waves of each row tile in LDS (reusing the K^ area), then
     // write one partial per live row.
@@ -348,9 +444,9 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 // One workgroup of 256 lanes per (kv head, live row) merges the split
 // partials: the maximum M over the splits, then lane t takes the items
-// (split s, channel quarter t % 4) for s = t / 4, t / 4 + 64, ... (all loads of
-// a lane issued together), weights them by 2^(m_s - M), and the 64 lanes of
-// each quarter are summed through LDS.
+// (split s, channel quarter t % 4) for s = t / 4, t / 4 + 64, ... (up to 64
+// splits this is a single round of loads), weights them by 2^(m_s - M), and
+// the 64 lanes of each quarter are summed through LDS.
 __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(AttnArgs a) {
     __shared__ float s_red[2][kAttnThreads / 64];
     __shared__ float s_acc[64][4 * 33];
@@ -362,30 +458,42 @@ __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(AttnArgs a) 
     const int64_t split_stride = (int64_t)a.n_kvh * a.rows * kPartial;
     const float *base = a.ws + ((int64_t)kvh * a.rows + h) * kPartial;
 
-    float m = -INFINITY;
-    for (int s = tid; s < a.splits; s += kAttnThreads) m = fmaxf(m, base[s * split_stride]);
+    // Lane t holds split t / 4, channel quarter t % 4 (its max, sum and 32
+    // outputs loaded together); splits beyond 64 are read in later passes.
+    const int cq = tid & 3;
+    const int s_first = tid >> 2;
+    float m0 = -INFINITY, l0 = 0.0f;
+    float acc[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) acc[i] = 0.0f;
+    if (s_first < a.splits) {
+        const float *pt = base + s_first * split_stride;
+        m0 = pt[0];
+        l0 = pt[1];
+#pragma unroll
+        for (int i = 0; i < 32; i += 2) {
+            const float2 v = *(const float2 *)(pt + 2 + 32 * cq + i);
+            acc[i] = v.x;
+            acc[i + 1] = v.y;
+        }
+    }
+    float m = m0;
+    for (int s = s_first + kAttnThreads / 4; s < a.splits; s += kAttnThreads / 4)
+        m = fmaxf(m, base[s * split_stride]);
     m = wave_max(m);
     if ((tid & 63) == 0) s_red[0][wave] = m;
     __syncthreads();
     const float M = fmaxf(fmaxf(s_red[0][0], s_red[0][1]), fmaxf(s_red[0][2], s_red[0][3]));
 
-    float l = 0.0f;
-    for (int s = tid; s < a.splits; s += kAttnThreads) {
-        const float ms = base[s * split_stride];
-        if (ms != -INFINITY) l = __builtin_fmaf(base[s * split_stride + 1],
-                                                __builtin_amdgcn_exp2f(ms - M), l);
-    }
-    l = wave_sum(l);
-    if ((tid & 63) == 0) s_red[1][wave] = l;
-
-    const int cq = tid & 3;
-    float acc[32];
+    const float w0 = m0 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m0 - M);
+    float l = cq == 0 ? l0 * w0 : 0.0f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) acc[i] = 0.0f;
-    for (int s = tid >> 2; s < a.splits; s += kAttnThreads / 4) {
+    for (int i = 0; i < 32; ++i) acc[i] *= w0;
+    for (int s = s_first + kAttnThreads / 4; s < a.splits; s += kAttnThreads / 4) {
         const float *pt = base + s * split_stride;
         const float ms = pt[0];
         const float w = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
+        if (cq == 0) l = __builtin_fmaf(pt[1], w, l);
 #pragma unroll
         for (int i = 0; i < 32; i += 2) {
             const float2 v = *(const float2 *)(pt + 2 + 32 * cq + i);
@@ -393,6 +501,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(AttnArgs a) 
             acc[i + 1] = __builtin_fmaf(v.y, w, acc[i + 1]);
         }
     }
+    l = wave_sum(l);
+    if ((tid & 63) == 0) s_red[1][wave] = l;
+
 #pragma unroll
     for (int i = 0; i < 32; ++i) s_acc[tid >> 2][cq * 33 + i] = acc[i];
     __syncthreads();
