@@ -223,7 +223,10 @@ size_t lynx_attn_workspace_bytes(int t_q, int num_q_heads, int num_kv_heads,
  *                shape [ctx_len][num_kv_heads * 128] (the outputs of
  *                lynx_quantize_pages for num_tensors = 1); k_residual /
  *                v_residual NULL = anchor-only reconstruction.  K^ and V^
- *                are bit-identical to lynx_dequant_anchor / _full;
+ *                follow Eq. (4) as one fused multiply-add per element with
+ *                the coefficients folded per chunk and channel, so they
+ *                equal lynx_dequant_anchor / _full up to rounding order (at
+ *                most one bf16 unit apart, on rare elements);
  *   ctx_len      multiple of 256; head_dim must be 128;
  *   causal_tail  0: every query sees all ctx_len positions; 1: the t_q
  *                queries are the last t_q positions and row r sees positions
