@@ -117,9 +117,11 @@ __device__ __forceinline__ uint32_t byte_shl(uint32_t w, int i) {
 }
 
 // Signed-level tables at the start of the kernel's LDS (so a table address
-// is the shifted code byte itself): lut[anchor nibble | residual nibble << 4]
-// for full codes, lut2[anchor byte] = the levels of both channels of the
-// byte for anchor-only codes (one 8-byte read per token).
+// is the shifted code byte itself): lut[residual nibble | anchor nibble << 4]
+// for full codes (the residual, the more evenly spread of the two, sits in
+// the low bits that pick the LDS bank: fewer conflicts between lanes), and
+// lut2[anchor byte] = the levels of both channels of the byte for
+// anchor-only codes (one 8-byte read per token).
 struct Luts {
     const float *lut;
     const float2 *lut2;
@@ -131,8 +133,8 @@ template <bool FULL>
 __device__ __forceinline__ void rebuild_word(uint32_t A, uint32_t R, const Affine &f,
                                              const Luts &t, float y0[4], float y1[4]) {
     if (FULL) {
-        const uint32_t X = (A & 0x0f0f0f0fu) | ((R << 4) & 0xf0f0f0f0u);  // channel 2p
-        const uint32_t Y = ((A >> 4) & 0x0f0f0f0fu) | (R & 0xf0f0f0f0u);  // channel 2p + 1
+        const uint32_t X = ((A << 4) & 0xf0f0f0f0u) | (R & 0x0f0f0f0fu);  // channel 2p
+        const uint32_t Y = (A & 0xf0f0f0f0u) | ((R >> 4) & 0x0f0f0f0fu);  // channel 2p + 1
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float s0 = *(const float *)((const char *)t.lut + byte_shl<2>(X, i));
@@ -253,7 +255,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(AttnArgs 
     const int lane = tid & 63;
     const int wave = tid >> 6;
 
-    s_lut[tid] = signed_level(tab, tid, true);
+    s_lut[tid] = signed_level(tab, ((tid & 15) << 4) | (tid >> 4), true);
     s_lut2[tid] = make_float2(signed_level(tab, tid & 15, false),
                               signed_level(tab, tid >> 4, false));
     const Luts luts = {s_lut, s_lut2};
