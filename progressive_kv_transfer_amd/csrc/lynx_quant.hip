@@ -10,16 +10,17 @@
 //
 // Each lane owns one whole 32-token chunk of a channel pair (64 values), so
 // the chunk mean and max |X - mu| need no cross-lane traffic and every
-// per-channel cost is spread over 32 tokens.  A workgroup of 256 lanes
-// covers half a page block (64 channels x 256 tokens); its lanes meet once
-// in LDS for the page minimum / maximum.  Rows are read with buffer loads
-// (scalar row offsets): 32 lanes x 4 bytes = one 128-byte line per row.
-// The loads go straight to LDS (buffer_load_dword ... lds), one unit ahead:
-// each wave stages the 32 rows of its next unit in its own 8 KiB region
-// while it computes the current one, so HBM latency overlaps a whole unit
-// of arithmetic without holding registers.
+// per-channel cost is spread over 32 tokens.  A workgroup of 512 lanes
+// covers a whole page block: wave w takes chunk w, lane l channel pair l;
+// the waves meet once in LDS for the page minimum / maximum.  Rows are read
+// with buffer loads (scalar row offsets) of 16 bytes per lane, four whole
+// 256-byte block rows per instruction, straight into LDS (buffer_load_dwordx4
+// ... lds), kDepth blocks ahead: each wave stages the 32 rows of its chunk of
+// the coming blocks in its own 8 KiB regions while it computes the current
+// one, so HBM latency overlaps whole blocks of arithmetic without holding
+// registers.
 // The anchor and residual bytes of a lane are 32 contiguous bytes of the
-// chunk-tiled stream layout, so a workgroup writes whole cache lines that no
+// chunk-tiled stream layout, so a wave writes 2 KiB of each stream that no
 // other workgroup touches.  Workgroups are persistent (grid = resident
 // workgroups) and build the compander table in LDS once.
 //
@@ -55,14 +56,26 @@ constexpr float kHuge125 = 0x1p125f;
 constexpr float kMuTiny = 0x1p-74f;
 
 // Lane tile: 2 channels x 32 tokens, i.e. one whole chunk of a channel
-// pair.  A work unit is half a page block (64 channels x 256 tokens;
-// statistics are per channel, so the halves are independent); unit u is
-// half (u & 1) of block block0 + (u >> 1).  A workgroup (4 wave64s) walks
-// units u = workgroup, workgroup + grid, ... so the compander table is
-// built once per workgroup.
-constexpr int kHalf = kHead / 2;        // channels per unit
-constexpr int kPairs = kHalf / 2;       // channel pairs per unit (lanes per chunk)
-constexpr int kThreads = kPairs * kChunks;  // 256
+// pair.  A workgroup (8 wave64s) walks blocks u = workgroup,
+// workgroup + grid, ... so the compander table is built once per workgroup.
+constexpr int kPairs = kHead / 2;            // channel pairs per block (lanes per chunk)
+constexpr int kThreads = kPairs * kChunks;   // 512
+constexpr int kWaves = kThreads / 64;        // 8, one per chunk
+constexpr int kDepth = 1;                    // blocks staged ahead (2 measured no faster)
+constexpr int kStageLoads = kChunk / 4;      // 16-byte loads per wave and block
+
+// Workgroup barrier over LDS traffic only: each wave waits for its own LDS
+// operations, not for its global loads and stores, so the staged loads of
+// the next unit and the stores of the current one stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Wait until at most N vector memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, 0x7fffffff,
@@ -78,16 +91,21 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
     float *__restrict__ gscale_io, float *__restrict__ mu_out, float *__restrict__ sigma_out) {
     __shared__ float2 s_min[kChunks][kPairs];
     __shared__ float2 s_max[kChunks][kPairs];
-    __shared__ float4 s_ch[kHalf];  // gamma_min, d1, r1, slow flag
+    __shared__ float4 s_ch[kHead];  // gamma_min, d1, r1, slow flag
     __shared__ u32x2 s_tab[MODE == kModeQuantize ? kMaxBuckets : 1];
-    // Staged rows of the next unit: [wave][row of chunk][lane].
-    __shared__ uint32_t s_stage[kThreads / 64][kChunk][64];
+    // Staged rows of the coming blocks, per buffer and wave: the 32 token
+    // rows of its chunk x 128 channels, token-major.
+    __shared__ uint32_t s_stage[kDepth][kWaves][kChunk * kPairs];
 
+    // Global stores every wave issues per block after its staging loads:
+    // mu and sigma (2), then the anchor and residual words (4).  Page
+    // statistics alone store from waves 0 and 1 only.
+    constexpr int kStoresAfterStage =
+        MODE == kModeQuantize ? 6 : MODE == kModeBlockStats ? 2 : 0;
     const int tid = (int)__builtin_amdgcn_workitem_id_x();
-    const int p = tid & (kPairs - 1);  // channel pair: channels 2p, 2p+1 of the unit
+    const int p = tid & (kPairs - 1);  // channel pair: channels 2p, 2p+1 of the block
     const int j = tid / kPairs;        // chunk: tokens 32 j .. 32 j + 31
-    const int wave = tid >> 6;
-    const int lane = tid & 63;
+    const int wave = tid >> 6;         // = j
 
     // Compander table into LDS, once per workgroup.
     if (MODE == kModeQuantize) {
@@ -102,56 +120,88 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
     const uint32_t tab_base = (uint32_t)(uintptr_t)(lds_u32x2 *)s_tab -
                               (uint32_t)tab.bucket_lo * (uint32_t)sizeof(u32x2);
     const uint32_t row_bytes = (uint32_t)g.row_stride * 2u;
-    const int64_t nunits = 2 * g.nblocks;
-    const uint32_t voff = (uint32_t)(j * kChunk) * row_bytes + (uint32_t)p * 4u;
+    const int64_t nunits = g.nblocks;
+    // Staging load of lane l: 16 bytes (channels 8 (l % 16) .. + 7) of
+    // token row l / 16 of a 4-row group of the wave's chunk.
+    const uint32_t voff = (uint32_t)(wave * kChunk + (p >> 4)) * row_bytes +
+                          (uint32_t)(p & 15) * 16u;
 
-    // First element of unit v in the KV set.
+    // First element of block block0 + v in the KV set.
     auto unit_base = [&](int64_t v) {
-        const int64_t bv = g.block0 + (v >> 1);
+        const int64_t bv = g.block0 + v;
         const int64_t tpv = bv / g.heads;
         return kv + (tpv / g.pages) * g.tensor_stride +
-               (int64_t)(tpv % g.pages) * kPage * g.row_stride + (bv % g.heads) * kHead +
-               (v & 1) * kHalf;
+               (int64_t)(tpv % g.pages) * kPage * g.row_stride + (bv % g.heads) * kHead;
     };
-    // Issue the 32 row loads (4 B per lane: channels 2p, 2p+1 of the unit,
-    // tokens 32 j + i) of the unit at bp into this wave's staging rows.
+    // Issue the kStageLoads loads of the wave's 32 token rows of the block at
+    // bp (4 whole rows of 256 bytes each, 16 bytes per lane) into staging
+    // buffer buf.
     typedef __attribute__((address_space(3))) void lds_void;
+    constexpr uint32_t kStageBytes = kWaves * kChunk * kPairs * 4;
     // LDS address of this wave's staging rows, as a wave-uniform scalar.
     const uint32_t stage_lds = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(lds_void *)&s_stage[wave][0][0]);
-    // The row offsets are stepped with opaque scalar adds so that the 64
-    // per-row constants are not hoisted out of the unit loop into SGPRs.
-    auto stage = [&](const uint16_t *bp) {
+        (uint32_t)(uintptr_t)(lds_void *)&s_stage[0][wave][0]);
+    // The row offsets are stepped with opaque scalar adds so that the
+    // per-row constants are not hoisted out of the block loop into SGPRs.
+    const uint32_t group_bytes = 4u * row_bytes;
+    auto stage = [&](const uint16_t *bp, int buf) {
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(bp);
-        uint32_t soff = 0, lds = stage_lds;
+        uint32_t soff = 0, lds = stage_lds + (uint32_t)buf * kStageBytes;
 #pragma unroll
-        for (int i = 0; i < kChunk; ++i) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(uintptr_t)lds, 4, voff,
+        for (int k = 0; k < kStageLoads; ++k) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(uintptr_t)lds, 16, voff,
                                                      soff, 0, 0);
-            asm volatile("s_add_u32 %0, %0, %1" : "+s"(soff) : "s"(row_bytes));
-            asm volatile("s_add_u32 %0, %0, 0x100" : "+s"(lds));
+            asm volatile("s_add_u32 %0, %0, %1" : "+s"(soff) : "s"(group_bytes));
+            asm volatile("s_add_u32 %0, %0, 0x400" : "+s"(lds));
         }
     };
-    if ((int64_t)__builtin_amdgcn_workgroup_id_x() < nunits)
-        stage(unit_base(__builtin_amdgcn_workgroup_id_x()));
+    const int64_t wg0 = (int64_t)__builtin_amdgcn_workgroup_id_x();
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d)
+        if (wg0 + d * g.grid_wgs < nunits)
+            stage(unit_base(wg0 + d * g.grid_wgs), d);
 
-    for (int64_t u = __builtin_amdgcn_workgroup_id_x(); u < nunits;
-         u += g.grid_wgs) {
-        const int64_t b = g.block0 + (u >> 1);
-        const int half = (int)(u & 1);
-        const int64_t meta0 = b * kHead + half * kHalf;
-        const int64_t cmeta0 = b * (kChunks * kHead) + j * kHead + half * kHalf;
-        // Address of the next unit, computed here where few registers are
-        // live (the empty asm keeps it from being sunk to its use).
+    int n = 0;  // blocks done by this workgroup
+    for (int64_t u = wg0; u < nunits; u += g.grid_wgs, ++n) {
+        const int64_t b = g.block0 + u;
+        const int buf = n % kDepth;
+        const int64_t meta0 = b * kHead;
+        const int64_t cmeta0 = b * (kChunks * kHead) + j * kHead;
+        // Address of the block staged during this one, computed here where
+        // few registers are live (the empty asm keeps it from being sunk to
+        // its use).
         const bool has_next = u + g.grid_wgs < nunits;
-        const uint16_t *next_base = has_next ? unit_base(u + g.grid_wgs) : kv;
-        asm volatile("" ::"s"(next_base));
+        const bool has_ahead = u + kDepth * g.grid_wgs < nunits;
+        const uint16_t *ahead_base = has_ahead ? unit_base(u + kDepth * g.grid_wgs) : kv;
+        asm volatile("" ::"s"(ahead_base));
 
         // ---- 32 token rows x 2 channels (4 B per row) from the stage -----
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // Vector memory operations complete in issue order.  Issued after
+        // this block's staging loads are the stores of the previous
+        // min(n, kDepth) blocks (kStoresAfterStage or more each) and, with
+        // two blocks staged ahead and a next block, that block's staging
+        // loads (issued in the prologue or while the previous block was
+        // computed); all of those may stay in flight.
+        static_assert(kDepth == 1 || kDepth == 2, "wait counts cover one or two staged blocks");
+        constexpr int S = kStoresAfterStage, L = kStageLoads;
+        if (kDepth == 2 && has_next) {
+            if (n == 0)
+                vm_wait<L>();
+            else if (n == 1)
+                vm_wait<S + L>();
+            else
+                vm_wait<kDepth * S + L>();
+        } else {
+            if (n == 0)
+                vm_wait<0>();
+            else if (n == 1 || kDepth == 1)
+                vm_wait<S>();
+            else
+                vm_wait<kDepth * S>();
+        }
         uint32_t raw[kChunk];
 #pragma unroll
-        for (int i = 0; i < kChunk; ++i) raw[i] = s_stage[wave][i][lane];
+        for (int i = 0; i < kChunk; ++i) raw[i] = s_stage[buf][wave][i * kPairs + p];
         float x[kChunk][2];
 #pragma unroll
         for (int i = 0; i < kChunk; ++i) {
@@ -161,8 +211,8 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
         // The staging rows are refilled now: all reads of them have
         // returned (their values are used above).
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        if (has_next)
-            stage(next_base);
+        if (has_ahead)
+            stage(ahead_base, buf);
 
         // ---- phase 1: page statistics ------------------------------------
         if (MODE != kModeBlockStats) {
@@ -180,8 +230,8 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
             s_min[j][p] = make_float2(mn[0], mn[1]);
             s_max[j][p] = make_float2(mx[0], mx[1]);
         }
-        __syncthreads();
-        if (tid < kHalf) {
+        lds_barrier();
+        if (tid < kHead) {
             float gmin, gsc;
             if (MODE == kModeBlockStats) {
                 gmin = gmin_io[meta0 + tid];
@@ -192,8 +242,8 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
                 float a = mn[0], m = mx[0];
 #pragma unroll
                 for (int w = 1; w < kChunks; ++w) {
-                    a = fminf(a, mn[w * kHalf]);
-                    m = fmaxf(m, mx[w * kHalf]);
+                    a = fminf(a, mn[w * kHead]);
+                    m = fmaxf(m, mx[w * kHead]);
                 }
                 gmin = a + 0.0f;  // canonical +0 for a zero minimum
                 gsc = m - gmin;
@@ -210,10 +260,10 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
             s_ch[tid] = make_float4(gmin, d1, r1, fast ? 0.0f : 1.0f);
         }
         if (MODE == kModePageStats) {
-            __syncthreads();  // s_min is rewritten by the next unit
+            lds_barrier();  // s_min is rewritten by the next unit
             continue;
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- phase 2: normalise, chunk mean and max |X - mu| -------------
         {
@@ -333,7 +383,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
         }
         // 32 contiguous bytes per stream: [chunk j][pair][token of chunk]
         const int64_t coff = b * (kPage * kHead / 2) + j * (kHead / 2 * kChunk) +
-                             (half * kPairs + p) * kChunk;
+                             p * kChunk;
         u32x4 *ao = (u32x4 *)(anchor + coff);
         u32x4 *ro = (u32x4 *)(residual + coff);
         // Ordinary stores: the streams are read again by the dequant kernels.
@@ -366,7 +416,7 @@ static hipError_t launch_variant(int slot, const uint16_t *kv, const Geometry &g
                                  const QuantTab &tab, uint8_t *anchor, uint8_t *residual,
                                  float *gmin, float *gscale, float *mu, float *sigma,
                                  hipStream_t stream) {
-    const int64_t units = 2 * g.nblocks;
+    const int64_t units = g.nblocks;
     const int64_t res =
         resident_workgroups((const void *)quant_kernel<MODE, SH16>, slot, kThreads);
     Geometry gl = g;
