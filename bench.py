@@ -179,7 +179,9 @@ ROTATE_BYTES = 640 << 20  # > the 256 MiB last-level cache
 
 def measure_attention(torch, kvgen, lynx, calls: int, warmup: int, only=None):
     """Average time of lynx_decode_attn_dequant per call on each attention
-    workload (or only the named one), cycling over copies of the codes."""
+    workload (or only the named one), cycling over copies of the codes:
+    us_per_call from replaying the calls captured in one HIP graph (device
+    time), us_per_call_eager from issuing them one by one from Python."""
     stream = torch.cuda.current_stream()
     res = {}
     built = {}
@@ -223,12 +225,40 @@ def measure_attention(torch, kvgen, lynx, calls: int, warmup: int, only=None):
                                      stream=stream)
         ev[1].record(stream)
         torch.cuda.synchronize()
-        us = ev[0].elapsed_time(ev[1]) / calls * 1e3
+        us_eager = ev[0].elapsed_time(ev[1]) / calls * 1e3
+        ref = out.clone()
+        # The same calls captured once in a HIP graph and replayed: the device
+        # time per call without the Python / launch cost of each call (how a
+        # decode loop runs them).  Each replay's output must equal the eager
+        # result of the last call bit for bit.
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.graph(graph, stream=cap):
+            for i in range(calls):
+                k, v = views[i % len(views)]
+                lynx.decode_attn_dequant(q, k, v, ctx, nkvh, scale, causal, out=out,
+                                         workspace=ws, stream=cap)
+        stream.wait_stream(cap)
+        times = []
+        for r in range(3):
+            out.zero_()
+            torch.cuda.synchronize()
+            ev[0].record(stream)
+            graph.replay()
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            times.append(ev[0].elapsed_time(ev[1]) / calls * 1e3)
+            if not torch.equal(out, ref):
+                raise RuntimeError(f"{name}: graph replay {r} differs from the eager result")
+        us = min(times)
+        del graph
         algo = per_copy + q.numel() * 2 + out.numel() * 2
         flops = 4.0 * t_q * nqh * 128 * ctx
         res[name] = {"workload": wl, "t_q": t_q, "q_heads": nqh, "kv_heads": nkvh,
                      "context": ctx, "codes": "anchor+residual" if full else "anchor",
                      "causal_tail": causal, "us_per_call": round(us, 2),
+                     "us_per_call_eager": round(us_eager, 2),
                      "algorithmic_bytes": int(algo),
                      "GBps": round(algo / (us * 1e-6) / 1e9, 1),
                      "hbm_frac": round(algo / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
