@@ -273,8 +273,9 @@ def measure_attention(torch, kvgen, lynx, calls: int, warmup: int, only=None):
 def measure_verify(torch, kvgen, lynx, calls: int = 200, sets: int = 32):
     """Speculative verification of 8 drafts over a Qwen-sized vocabulary:
     average time per call over `sets` different input sets (more bytes than
-    the last-level cache), algorithmic bytes = the 2T + 1 logit rows once
-    plus the two rows of the correction pass."""
+    the last-level cache), from a replayed HIP graph of the calls (device
+    time) and issued one by one (eager); algorithmic bytes = the 2T + 1
+    logit rows once plus the two rows of the correction pass."""
     T, V = kvgen.VERIFY_T, kvgen.VERIFY_VOCAB
     inputs = []
     for i in range(sets):
@@ -292,9 +293,33 @@ def measure_verify(torch, kvgen, lynx, calls: int = 200, sets: int = 32):
         lynx.spec_verify(*inputs[i % sets], out=out, workspace=ws, stream=stream)
     e1.record(stream)
     torch.cuda.synchronize()
-    us_call = e0.elapsed_time(e1) / calls * 1e3
+    us_eager = e0.elapsed_time(e1) / calls * 1e3
+    ref = out.clone()
+    # Device time: the same calls captured once in a HIP graph and replayed;
+    # each replay must end with the eager result of the last call.
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.graph(graph, stream=cap):
+        for i in range(calls):
+            lynx.spec_verify(*inputs[i % sets], out=out, workspace=ws, stream=cap)
+    stream.wait_stream(cap)
+    times = []
+    for r in range(3):
+        out.fill_(-7)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / calls * 1e3)
+        if not torch.equal(out, ref):
+            raise RuntimeError(f"verify: graph replay {r} differs from the eager result")
+    del graph
+    us_call = min(times)
     algo = (2 * T + 1 + 2) * V * 4
     return {"drafts": T, "vocab": V, "us_per_call": round(us_call, 2),
+            "us_per_call_eager": round(us_eager, 2),
             "algorithmic_bytes": algo, "GBps": round(algo / (us_call * 1e-6) / 1e9, 1),
             "hbm_frac": round(algo / (us_call * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
             "input_sets": sets}

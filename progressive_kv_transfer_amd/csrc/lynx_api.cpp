@@ -685,8 +685,7 @@ size_t lynx_spec_verify_workspace_bytes(int t_draft, int vocab) {
     if (t_draft < 0 || t_draft > kVerifyMaxDraft || vocab <= 0)
         return 0;
     const int64_t chunks = (vocab + kVerifyChunk - 1) / kVerifyChunk;
-    // chunk statistics of the 2T + 1 rows, then the chosen row's chunk sums
-    return ((size_t)(2 * t_draft + 1) * chunks * 2 + chunks) * sizeof(double);
+    return verify_workspace_doubles(t_draft, chunks) * sizeof(double);
 }
 
 int lynx_spec_verify(const float *draft_logits, const float *target_logits,

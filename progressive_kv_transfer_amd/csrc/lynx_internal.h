@@ -85,7 +85,7 @@ int attn_row_tiles(int rows);  // tiles of 16 query rows, -1 if rows > 64
 hipError_t launch_attention(const AttnArgs &a, const DequantTab &tab, hipStream_t stream);
 
 // Speculative verification (lynx_verify.hip).
-constexpr int kVerifyChunk = 8192;    // tokens per statistics workgroup
+constexpr int kVerifyChunk = 2048;    // tokens per statistics workgroup
 constexpr int kVerifyMaxDraft = 64;   // draft tokens per call at most
 struct VerifyArgs {
     const float *draft;      // [t][vocab] logits the drafts were drawn from
@@ -94,9 +94,11 @@ struct VerifyArgs {
     const double *u_accept;  // [t] uniforms
     double u_sample;         // uniform of the correction / bonus draw
     int t, vocab, chunks;    // chunks = ceil(vocab / kVerifyChunk)
-    double *ws;              // [2t + 1][chunks][2]: chunk max, chunk sum
+    double *ws;              // [2t + 1][chunks][2] chunk max and sum, [chunks]
+                             // weight sums, [8] the decision
     int32_t *out;            // [2]: accepted drafts, next token
 };
+size_t verify_workspace_doubles(int t, int64_t chunks);
 hipError_t launch_verify(const VerifyArgs &a, hipStream_t stream);
 
 }  // namespace lynx

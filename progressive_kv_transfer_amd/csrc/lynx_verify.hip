@@ -6,15 +6,20 @@
 // correction from max(0, p_k - q_k)); after a fully accepted draft the next
 // token is drawn from the target distribution.
 //
-//   verify_stats_kernel   one workgroup per (row, 8192-token chunk) of the
+//   verify_stats_kernel   one workgroup per (row, 2048-token chunk) of the
 //                         2T + 1 logit rows (T draft rows q, T + 1 target
-//                         rows p): chunk max and sum of exp(l - max) in
-//                         binary64;
+//                         rows p): chunk max and sum of exp_d(l - max) in
+//                         binary64, 8 independent exponentials per lane;
 //   verify_chunk_kernel   one workgroup per chunk of the chosen row: each
-//                         merges the statistics and walks the drafts (a few
-//                         exponentials), then sums its chunk's weights;
-//   verify_select_kernel  one workgroup: the chunk that holds u * total, the
-//                         32-token range inside it (wave scan), the token.
+//                         takes the decision (16 lanes per row merge the
+//                         chunk statistics, 16 rows at a time; one lane per
+//                         draft tests Eq. (10)), workgroup 0 stores it (the
+//                         first rejection k and the statistics of the row to
+//                         sample from), and each sums its chunk's weights;
+//   verify_select_kernel  one workgroup: the chunk that holds u * total
+//                         (lanes over runs of chunks, block scan), then the
+//                         8-token run inside it (block scan of the lane
+//                         sums), then the token inside the run.
 // Ratios and sums are binary64, so a decision can only differ from a
 // sequential evaluation within ~1e-15 of its threshold.
 #include "lynx_internal.h"
@@ -22,9 +27,43 @@
 namespace lynx {
 namespace {
 
-constexpr int kStatThreads = 256;
-constexpr int kDecideThreads = 256;
-static_assert(kVerifyChunk % kDecideThreads == 0, "lanes split a chunk evenly");
+constexpr int kThreads = 256;
+constexpr int kPer = kVerifyChunk / kThreads;  // 8 tokens per lane and chunk
+static_assert(kVerifyChunk % kThreads == 0, "lanes split a chunk evenly");
+
+// e^x in binary64, inlined (the library exponential is an out-of-line call,
+// which serializes a lane's exponentials): Cody and Waite's reduction
+// x = k ln 2 + r with ln 2 held as RN(ln 2) + RN(ln 2 - RN(ln 2)) and both
+// products by k formed inside an FMA, |r| <= ln 2 / 2, then the Taylor
+// polynomial of e^r to degree 13 (truncation below 1e-17 relative, the
+// coefficients RN(1/n!)) by Horner's rule, scaled by 2^k.  NaN passes
+// through, arguments below -746 (and -inf) give 0.  Within 1 ulp of the C
+// library's exp on 2e8 arguments in [-746, 0] (CPU check of the same steps).
+__device__ __forceinline__ double exp_d(double x) {
+    constexpr double kLog2e = 0x1.71547652b82fep+0;   // RN(1 / ln 2)
+    constexpr double kLn2Hi = 0x1.62e42fefa39efp-1;   // RN(ln 2)
+    constexpr double kLn2Lo = 0x1.abc9e3b39803fp-56;  // RN(ln 2 - kLn2Hi)
+    if (!(x > -746.0))
+        return x != x ? x : 0.0;
+    const double k = __builtin_rint(x * kLog2e);
+    double r = __builtin_fma(-k, kLn2Hi, x);
+    r = __builtin_fma(-k, kLn2Lo, r);
+    double p = 1.6059043836821613e-10;        // 1/13!
+    p = __builtin_fma(p, r, 2.08767569878681e-09);    // 1/12!
+    p = __builtin_fma(p, r, 2.505210838544172e-08);   // 1/11!
+    p = __builtin_fma(p, r, 2.755731922398589e-07);   // 1/10!
+    p = __builtin_fma(p, r, 2.7557319223985893e-06);  // 1/9!
+    p = __builtin_fma(p, r, 2.48015873015873e-05);    // 1/8!
+    p = __builtin_fma(p, r, 0.0001984126984126984);   // 1/7!
+    p = __builtin_fma(p, r, 0.001388888888888889);    // 1/6!
+    p = __builtin_fma(p, r, 0.008333333333333333);    // 1/5!
+    p = __builtin_fma(p, r, 0.041666666666666664);    // 1/4!
+    p = __builtin_fma(p, r, 0.16666666666666666);     // 1/3!
+    p = __builtin_fma(p, r, 0.5);
+    p = __builtin_fma(p, r, 1.0);
+    p = __builtin_fma(p, r, 1.0);
+    return __builtin_ldexp(p, (int)k);
+}
 
 __device__ __forceinline__ double wave_max_d(double x) {
 #pragma unroll
@@ -38,7 +77,7 @@ __device__ __forceinline__ double wave_sum_d(double x) {
     return x;
 }
 
-// Block-wide max / sum of one double per lane (256 lanes = 4 waves).
+// Block-wide (256 lanes = 4 waves) reductions; every lane gets the result.
 __device__ double block_max_d(double x, double *s_red) {
     x = wave_max_d(x);
     const int tid = (int)__builtin_amdgcn_workitem_id_x();
@@ -57,43 +96,6 @@ __device__ double block_sum_d(double x, double *s_red) {
     return (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
 }
 
-// Row r < T is draft row r; row T + i is target row i.
-__device__ __forceinline__ const float *row_ptr(const VerifyArgs &a, int r) {
-    return r < a.t ? a.draft + (int64_t)r * a.vocab : a.target + (int64_t)(r - a.t) * a.vocab;
-}
-
-__global__ __launch_bounds__(kStatThreads) void verify_stats_kernel(VerifyArgs a) {
-    __shared__ double s_red[4];
-    const int tid = (int)__builtin_amdgcn_workitem_id_x();
-    const int wg = (int)__builtin_amdgcn_workgroup_id_x();
-    const int r = wg / a.chunks, c = wg % a.chunks;
-    const float *l = row_ptr(a, r);
-    const int x0 = c * kVerifyChunk;
-    const int x1 = min(a.vocab, x0 + kVerifyChunk);
-    double m = -INFINITY;
-    for (int x = x0 + tid; x < x1; x += kStatThreads) m = fmax(m, (double)l[x]);
-    m = block_max_d(m, s_red);
-    double s = 0.0;
-    for (int x = x0 + tid; x < x1; x += kStatThreads) s += exp((double)l[x] - m);
-    s = block_sum_d(s, s_red);
-    if (tid == 0) {
-        a.ws[(int64_t)wg * 2] = m;
-        a.ws[(int64_t)wg * 2 + 1] = s;
-    }
-}
-
-// Row statistics (max, sum of exp(l - max)) merged from the chunk partials.
-__device__ __forceinline__ void merge_row(const VerifyArgs &a, int r, double &m, double &s) {
-    m = -INFINITY;
-    for (int c = 0; c < a.chunks; ++c) m = fmax(m, a.ws[((int64_t)r * a.chunks + c) * 2]);
-    s = 0.0;
-    for (int c = 0; c < a.chunks; ++c) {
-        const double mc = a.ws[((int64_t)r * a.chunks + c) * 2];
-        s += a.ws[((int64_t)r * a.chunks + c) * 2 + 1] * exp(mc - m);
-    }
-}
-
-// Smallest / largest value over the block (256 lanes).
 __device__ int block_min_i(int x, int *s_int) {
 #pragma unroll
     for (int d = 32; d > 0; d >>= 1) x = min(x, __shfl_xor(x, d, 64));
@@ -114,6 +116,79 @@ __device__ int block_max_i(int x, int *s_int) {
     return max(max(s_int[0], s_int[1]), max(s_int[2], s_int[3]));
 }
 
+// Lane intervals of one double per lane in lane order: lane l gets
+// [lo_l, hi_l) with lo_l the sum of lanes 0 .. l - 1 and hi_l = lo_{l+1}
+// (the total for the last lane), so the intervals tile [0, total) without
+// gaps.
+__device__ void block_intervals(double x, double *s_pre, double *s_wsum, double *lo,
+                                double *hi, double *total) {
+    const int tid = (int)__builtin_amdgcn_workitem_id_x();
+    const int lane = tid & 63, wave = tid >> 6;
+    double incl = x;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const double y = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += y;
+    }
+    __syncthreads();
+    if (lane == 63) s_wsum[wave] = incl;
+    __syncthreads();
+    double off = 0.0;
+    for (int w = 0; w < wave; ++w) off += s_wsum[w];
+    const double t = (s_wsum[0] + s_wsum[1]) + (s_wsum[2] + s_wsum[3]);
+    *lo = off + incl - x;
+    s_pre[tid] = *lo;
+    __syncthreads();
+    *hi = tid + 1 < kThreads ? s_pre[tid + 1] : t;
+    *total = t;
+}
+
+// Row r < T is draft row r; row T + i is target row i.
+__device__ __forceinline__ const float *row_ptr(const VerifyArgs &a, int r) {
+    return r < a.t ? a.draft + (int64_t)r * a.vocab : a.target + (int64_t)(r - a.t) * a.vocab;
+}
+
+__device__ __forceinline__ double *chunk_sums(const VerifyArgs &a) {
+    return a.ws + (int64_t)(2 * a.t + 1) * a.chunks * 2;
+}
+
+// The decision: k, then mp, rp, mq, rq.
+__device__ __forceinline__ double *choice_slots(const VerifyArgs &a) {
+    return chunk_sums(a) + a.chunks;
+}
+
+__global__ __launch_bounds__(kThreads) void verify_stats_kernel(VerifyArgs a) {
+    __shared__ double s_red[4];
+    const int tid = (int)__builtin_amdgcn_workitem_id_x();
+    const int wg = (int)__builtin_amdgcn_workgroup_id_x();
+    const int r = wg / a.chunks, c = wg % a.chunks;
+    const float *l = row_ptr(a, r);
+    const int x0 = c * kVerifyChunk;
+    double v[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int x = x0 + tid + kThreads * i;
+        v[i] = x < a.vocab ? (double)l[x] : -INFINITY;
+    }
+    double m = v[0];
+#pragma unroll
+    for (int i = 1; i < kPer; ++i) m = fmax(m, v[i]);
+    m = block_max_d(m, s_red);
+    double s = 0.0;
+    if (m != -INFINITY) {  // a chunk of -inf logits holds no mass
+        double e[kPer];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) e[i] = exp_d(v[i] - m);
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) s += e[i];
+    }
+    s = block_sum_d(s, s_red);
+    if (tid == 0) {
+        a.ws[(int64_t)wg * 2] = m;
+        a.ws[(int64_t)wg * 2 + 1] = s;
+    }
+}
+
 // Accepted prefix k (Eq. 10) and the statistics of the row the next token is
 // drawn from: target row k, minus draft row k when k < T (Eq. 11); rp, rq
 // are the reciprocals of the row sums.
@@ -122,28 +197,90 @@ struct Choice {
     double mp, rp, mq, rq;
 };
 
-// Block-wide: lane r merges row r, lane t tests draft t, the first rejection
-// is a block minimum.  Every lane returns the same choice.
-__device__ Choice choose(const VerifyArgs &a, double *s_m, double *s_s, int *s_int) {
+// Max / sum over the 16 lanes of a lane group (lanes 16 g .. 16 g + 15).
+__device__ __forceinline__ double group_max16(double x) {
+#pragma unroll
+    for (int d = 8; d > 0; d >>= 1) x = fmax(x, __shfl_xor(x, d, 16));
+    return x;
+}
+
+__device__ __forceinline__ double group_sum16(double x) {
+#pragma unroll
+    for (int d = 8; d > 0; d >>= 1) x += __shfl_xor(x, d, 16);
+    return x;
+}
+
+// The decision, computed by every lane of the block: row statistics merged
+// from the chunk statistics, then Eq. (10) per draft.
+__device__ Choice decide(const VerifyArgs &a, double *s_m, double *s_s, int *s_int) {
     const int tid = (int)__builtin_amdgcn_workitem_id_x();
-    for (int r = tid; r < 2 * a.t + 1; r += kDecideThreads) {
-        double m, sum;
-        merge_row(a, r, m, sum);
-        s_m[r] = m;
-        s_s[r] = sum;
+    // The draft lanes' loads go out first, so that they overlap the merge.
+    double lp = 0.0, lq = 0.0, ua = 0.0;
+    bool in_vocab = false;
+    if (tid < a.t) {
+        const int s = a.tokens[tid];
+        in_vocab = s >= 0 && s < a.vocab;  // not a token: rejected, nothing read
+        if (in_vocab) {
+            lp = (double)a.target[(int64_t)tid * a.vocab + s];
+            lq = (double)a.draft[(int64_t)tid * a.vocab + s];
+        }
+        ua = a.u_accept[tid];
+    }
+    // Row statistics (max, sum of exp_d(l - max)) merged from the chunks: a
+    // group of 16 lanes per row, 16 rows at a time.  Up to 8 x 16 chunks a
+    // lane holds its chunks' statistics in registers (all loads in flight at
+    // once, independent exponentials); beyond that it streams them twice.
+    constexpr int kHeld = 8;
+    const int grp = tid >> 4, sub = tid & 15;
+    for (int r0 = 0; r0 < 2 * a.t + 1; r0 += kThreads / 16) {
+        const int r = r0 + grp;
+        const bool live = r < 2 * a.t + 1;
+        const double *st = a.ws + (int64_t)(live ? r : 0) * a.chunks * 2;
+        double m = -INFINITY, s = 0.0;
+        if (a.chunks <= 16 * kHeld) {  // uniform
+            double mm[kHeld], ss[kHeld];
+#pragma unroll
+            for (int i = 0; i < kHeld; ++i) {
+                const int c = sub + 16 * i;
+                const bool ok = live && c < a.chunks;
+                mm[i] = ok ? st[2 * c] : -INFINITY;
+                ss[i] = ok ? st[2 * c + 1] : 0.0;
+            }
+#pragma unroll
+            for (int i = 0; i < kHeld; ++i) m = fmax(m, mm[i]);
+            m = group_max16(m);
+            double e[kHeld];
+#pragma unroll
+            for (int i = 0; i < kHeld; ++i)
+                e[i] = mm[i] != -INFINITY ? ss[i] * exp_d(mm[i] - m) : 0.0;
+#pragma unroll
+            for (int i = 0; i < kHeld; ++i) s += e[i];
+        } else {
+            if (live)
+                for (int c = sub; c < a.chunks; c += 16) m = fmax(m, st[2 * c]);
+            m = group_max16(m);
+            if (live)
+                for (int c = sub; c < a.chunks; c += 16) {
+                    const double mc = st[2 * c];
+                    if (mc != -INFINITY) s += st[2 * c + 1] * exp_d(mc - m);
+                }
+        }
+        s = group_sum16(s);
+        if (live && sub == 0) {
+            s_m[r] = m;
+            s_s[r] = s;
+        }
     }
     __syncthreads();
     int rej = a.t;
-    for (int t = tid; t < a.t; t += kDecideThreads) {
-        const int s = a.tokens[t];
-        bool ok = s >= 0 && s < a.vocab;  // not a token: rejected, nothing read
+    if (tid < a.t) {
+        bool ok = in_vocab;
         if (ok) {
-            const double p = exp((double)a.target[(int64_t)t * a.vocab + s] - s_m[a.t + t]) /
-                             s_s[a.t + t];
-            const double q = exp((double)a.draft[(int64_t)t * a.vocab + s] - s_m[t]) / s_s[t];
-            ok = a.u_accept[t] < p / q;
+            const double p = exp_d(lp - s_m[a.t + tid]) / s_s[a.t + tid];
+            const double q = exp_d(lq - s_m[tid]) / s_s[tid];
+            ok = ua < p / q;
         }
-        if (!ok) rej = min(rej, t);
+        if (!ok) rej = tid;
     }
     Choice c;
     c.k = block_min_i(rej, s_int);
@@ -154,116 +291,168 @@ __device__ Choice choose(const VerifyArgs &a, double *s_m, double *s_s, int *s_i
     return c;
 }
 
-__device__ __forceinline__ double weight(const VerifyArgs &a, const Choice &c, int x) {
-    const double p = exp((double)a.target[(int64_t)c.k * a.vocab + x] - c.mp) * c.rp;
-    if (c.k >= a.t)
-        return p;
-    const double q = exp((double)a.draft[(int64_t)c.k * a.vocab + x] - c.mq) * c.rq;
-    return p > q ? p - q : 0.0;
+__device__ __forceinline__ Choice load_choice(const VerifyArgs &a) {
+    const double *ch = choice_slots(a);
+    Choice c;
+    c.k = (int)ch[0];
+    c.mp = ch[1];
+    c.rp = ch[2];
+    c.mq = ch[3];
+    c.rq = ch[4];
+    return c;
 }
 
-// One workgroup per 8192-token chunk of the chosen row: the chunk's weight
-// sum into the workspace tail.
-__global__ __launch_bounds__(kDecideThreads) void verify_chunk_kernel(VerifyArgs a) {
+// Weights max(0, p_k - q_k) (p_T after a full accept) of the kPer
+// consecutive tokens x0 .. x0 + kPer - 1 (0 beyond the vocabulary).
+__device__ __forceinline__ void lane_weights(const VerifyArgs &a, const Choice &c, int x0,
+                                             double w[kPer]) {
+    const float *pr = a.target + (int64_t)c.k * a.vocab;
+    const bool two = c.k < a.t;
+    const float *qr = two ? a.draft + (int64_t)c.k * a.vocab : pr;
+    double lp[kPer], lq[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const bool in = x0 + i < a.vocab;
+        lp[i] = in ? (double)pr[x0 + i] : -INFINITY;
+        lq[i] = in && two ? (double)qr[x0 + i] : -INFINITY;
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const double p = exp_d(lp[i] - c.mp) * c.rp;
+        if (!two) {
+            w[i] = p;
+        } else {
+            const double q = exp_d(lq[i] - c.mq) * c.rq;
+            w[i] = p > q ? p - q : 0.0;
+        }
+    }
+}
+
+// One workgroup per chunk of the chosen row: each takes the decision (a few
+// hundred loads of chunk statistics, cheaper than a launch of its own),
+// workgroup 0 stores it for the select kernel, and each sums its chunk's
+// weights.
+__global__ __launch_bounds__(kThreads) void verify_chunk_kernel(VerifyArgs a) {
     __shared__ double s_m[2 * kVerifyMaxDraft + 1], s_s[2 * kVerifyMaxDraft + 1];
     __shared__ double s_red[4];
     __shared__ int s_int[4];
     const int tid = (int)__builtin_amdgcn_workitem_id_x();
     const int c = (int)__builtin_amdgcn_workgroup_id_x();
-    const Choice ch = choose(a, s_m, s_s, s_int);
-    const int x0 = c * kVerifyChunk, x1 = min(a.vocab, x0 + kVerifyChunk);
+    const Choice ch = decide(a, s_m, s_s, s_int);
+    if (c == 0 && tid == 0) {
+        double *slot = choice_slots(a);
+        slot[0] = (double)ch.k;
+        slot[1] = ch.mp;
+        slot[2] = ch.rp;
+        slot[3] = ch.mq;
+        slot[4] = ch.rq;
+    }
+    double w[kPer];
+    lane_weights(a, ch, c * kVerifyChunk + tid * kPer, w);
     double part = 0.0;
-    for (int x = x0 + tid; x < x1; x += kDecideThreads) part += weight(a, ch, x);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) part += w[i];
     part = block_sum_d(part, s_red);
-    if (tid == 0)
-        a.ws[(int64_t)(2 * a.t + 1) * a.chunks * 2 + c] = part;
+    if (tid == 0) chunk_sums(a)[c] = part;
 }
 
-// One workgroup: the chunk holding u * total (chunk sums in order), then the
-// 32-token lane range inside it (interval j = [prefix_j, prefix_j+1) of one
-// computed prefix sequence; the smallest matching lane wins), then the token
-// by a sequential rescan.  Where rounding leaves the target at the top, the
-// last token with positive weight (of the chunk, or of the row) is taken.
-__global__ __launch_bounds__(kDecideThreads) void verify_select_kernel(VerifyArgs a) {
-    __shared__ double s_m[2 * kVerifyMaxDraft + 1], s_s[2 * kVerifyMaxDraft + 1];
-    __shared__ double s_pre[kDecideThreads];
+// One workgroup.  Chunk level: lane l sums the chunk sums of its run of
+// chunks in order and gets its interval of the running total; the first
+// lane whose interval holds u * total walks its run to the chunk (the last
+// chunk of the row ends at the total; if rounding leaves the target past
+// the walked sums, the run's last chunk is taken).  Token level, inside
+// that chunk: the same with 8-token runs and their weights.  Where
+// rounding leaves the target at the top, the last token with positive
+// weight (of the chunk, or of the row) is taken; -1 when there is no mass
+// at all.
+__global__ __launch_bounds__(kThreads) void verify_select_kernel(VerifyArgs a) {
+    __shared__ double s_pre[kThreads];
     __shared__ double s_wsum[4];
     __shared__ double s_target;
-    __shared__ int s_found, s_search, s_int[4], s_tok;
-    constexpr int kPer = kVerifyChunk / kDecideThreads;  // 32 tokens per lane
+    __shared__ int s_int[4], s_cs, s_tok;
     const int tid = (int)__builtin_amdgcn_workitem_id_x();
-    const int lane = tid & 63, wave = tid >> 6;
-    const double *sums = a.ws + (int64_t)(2 * a.t + 1) * a.chunks * 2;
-    const Choice ch = choose(a, s_m, s_s, s_int);
+    const Choice ch = load_choice(a);
+    const double *sums = chunk_sums(a);
+
+    // ---- chunk level ----
+    const int per = (a.chunks + kThreads - 1) / kThreads;
+    const int c0 = min(a.chunks, tid * per), c1 = min(a.chunks, c0 + per);
+    double run_sum = 0.0;
+    int last_pos_chunk = -1;
+    for (int c = c0; c < c1; ++c) {
+        run_sum += sums[c];
+        if (sums[c] > 0.0) last_pos_chunk = c;
+    }
+    double lo, hi, total;
+    block_intervals(run_sum, s_pre, s_wsum, &lo, &hi, &total);
+    const double target = a.u_sample * total;
+    const bool match = c0 < c1 && lo <= target && target < hi;
+    const int first = block_min_i(match ? tid : kThreads, s_int);
     if (tid == 0) {
-        double total = 0.0;
-        for (int c = 0; c < a.chunks; ++c) total += sums[c];
-        const double target = a.u_sample * total;
-        double lo = 0.0;
-        int cs = -1, last_pos_chunk = -1;
+        s_cs = -1;
         s_target = 0.0;
-        for (int c = 0; c < a.chunks; ++c) {
-            if (sums[c] > 0.0) last_pos_chunk = c;
-            const double hi = c + 1 < a.chunks ? lo + sums[c] : total;
-            if (cs < 0 && lo <= target && target < hi) {
-                cs = c;
-                s_target = target - lo;
-            }
-            lo = hi;
-        }
-        // No chunk holds the target (rounding at the top, or no mass at
-        // all): search the last chunk with mass for its last positive token.
-        s_found = cs >= 0 ? 1 : 0;
-        s_search = cs >= 0 ? cs : last_pos_chunk;  // -1: no mass anywhere
     }
     __syncthreads();
-    const bool found = s_found != 0;
-    const int cs = s_search;
-    const int x0 = cs >= 0 ? min(a.vocab, cs * kVerifyChunk + tid * kPer) : 0;
-    const int x1 = cs >= 0 ? min(a.vocab, min(x0 + kPer, cs * kVerifyChunk + kVerifyChunk)) : 0;
+    if (tid == first) {
+        double clo = lo;
+        int pick = c1 - 1;
+        double pick_lo = clo;
+        for (int c = c0; c < c1; ++c) {
+            const double chi = c + 1 < a.chunks ? clo + sums[c] : total;
+            pick_lo = clo;
+            if (clo <= target && target < chi) {
+                pick = c;
+                break;
+            }
+            clo = chi;
+        }
+        s_cs = pick;
+        s_target = target - pick_lo;
+    }
+    __syncthreads();
+    int cs = s_cs;
+    const bool found = cs >= 0;
+    if (!found)  // uniform: the last chunk with mass, for its last positive token
+        cs = block_max_i(last_pos_chunk, s_int);
+
+    // ---- token level inside chunk cs ----
+    double w[kPer];
+    const int x0 = (cs >= 0 ? cs : 0) * kVerifyChunk + tid * kPer;
+    if (cs >= 0) {
+        lane_weights(a, ch, x0, w);
+    } else {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) w[i] = 0.0;
+    }
     double part = 0.0;
     int last_pos = -1;
-    for (int x = x0; x < x1; ++x) {
-        const double w = weight(a, ch, x);
-        part += w;
-        if (w > 0.0) last_pos = x;
-    }
-    // exclusive prefix of the lane sums: wave scan, then wave offsets
-    double incl = part;
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const double y = __shfl_up(incl, d, 64);
-        if (lane >= d) incl += y;
+    for (int i = 0; i < kPer; ++i) {
+        part += w[i];
+        if (w[i] > 0.0) last_pos = x0 + i;
     }
-    if (lane == 63) s_wsum[wave] = incl;
-    __syncthreads();
-    double off = 0.0;
-    for (int w = 0; w < wave; ++w) off += s_wsum[w];
-    const double lo = off + incl - part;
-    s_pre[tid] = lo;
-    __syncthreads();
-    const double hi = tid + 1 < kDecideThreads
-                          ? s_pre[tid + 1]
-                          : (s_wsum[0] + s_wsum[1]) + (s_wsum[2] + s_wsum[3]);
-    const double target = s_target;
-    const bool match = found && x0 < x1 && lo <= target && target < hi;
-    const int first = block_min_i(match ? tid : kDecideThreads, s_int);
+    double tlo, thi, ctotal;
+    block_intervals(part, s_pre, s_wsum, &tlo, &thi, &ctotal);
+    const double ctarget = s_target;
+    const bool tmatch = found && cs >= 0 && x0 < a.vocab && tlo <= ctarget && ctarget < thi;
+    const int tfirst = block_min_i(tmatch ? tid : kThreads, s_int);
     if (tid == 0) s_tok = -1;
     __syncthreads();
-    if (first < kDecideThreads && tid == first) {
-        double run = lo;
+    if (tid == tfirst) {
+        double run = tlo;
         int tok = last_pos;
-        for (int x = x0; x < x1; ++x) {
-            run += weight(a, ch, x);
-            if (run > target) {
-                tok = x;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            run += w[i];
+            if (run > ctarget) {
+                tok = x0 + i;
                 break;
             }
         }
         s_tok = tok;
     }
     __syncthreads();
-    if (first == kDecideThreads) {  // uniform: no lane holds the target
+    if (tfirst == kThreads) {  // uniform: no run holds the target
         const int lp = block_max_i(last_pos, s_int);
         if (tid == 0) s_tok = lp;
     }
@@ -276,17 +465,23 @@ __global__ __launch_bounds__(kDecideThreads) void verify_select_kernel(VerifyArg
 
 }  // namespace
 
+size_t verify_workspace_doubles(int t, int64_t chunks) {
+    // chunk statistics of the 2t + 1 rows, the chosen row's chunk sums, the
+    // decision (k, mp, rp, mq, rq)
+    return (size_t)(2 * t + 1) * (size_t)chunks * 2 + (size_t)chunks + 8;
+}
+
 hipError_t launch_verify(const VerifyArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL(verify_stats_kernel, dim3((unsigned)((2 * a.t + 1) * a.chunks)),
-                       dim3(kStatThreads), 0, stream, a);
+                       dim3(kThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(verify_chunk_kernel, dim3((unsigned)a.chunks), dim3(kDecideThreads), 0,
+    hipLaunchKernelGGL(verify_chunk_kernel, dim3((unsigned)a.chunks), dim3(kThreads), 0,
                        stream, a);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
-    hipLaunchKernelGGL(verify_select_kernel, dim3(1), dim3(kDecideThreads), 0, stream, a);
+    hipLaunchKernelGGL(verify_select_kernel, dim3(1), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

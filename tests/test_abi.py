@@ -298,8 +298,10 @@ def test_transfer_empty_set_and_copies_only_needs_no_kv():
 def test_spec_verify_workspace_and_errors():
     L = lynx.lib()
     ws = lynx.spec_verify_workspace_bytes
-    assert ws(8, 151936) == (17 * 19 * 2 + 19) * 8   # 2T+1 rows x 19 chunks, + chunk sums
-    assert ws(0, 1) == 3 * 8
+    # 2T+1 rows x 75 chunks of 2048 tokens (max, sum), the chunk weight sums,
+    # 8 slots for the decision
+    assert ws(8, 151936) == (17 * 75 * 2 + 75 + 8) * 8
+    assert ws(0, 1) == (2 + 1 + 8) * 8
     assert ws(65, 100) == 0 and ws(-1, 100) == 0 and ws(3, 0) == 0
     ok = dict(d=FAKE, t=FAKE, s=FAKE, u=FAKE, us=0.5, T=8, V=1000, out=FAKE, w=FAKE, wb=1 << 20)
     cases = [dict(T=65), dict(V=0), dict(us=1.0), dict(us=float("nan")), dict(t=None),
