@@ -38,7 +38,8 @@ static_assert(kVerifyChunk % kThreads == 0, "lanes split a chunk evenly");
 // polynomial of e^r to degree 13 (truncation below 1e-17 relative, the
 // coefficients RN(1/n!)) by Horner's rule, scaled by 2^k.  NaN passes
 // through, arguments below -746 (and -inf) give 0.  Within 1 ulp of the C
-// library's exp on 2e8 arguments in [-746, 0] (CPU check of the same steps).
+// library's exp on 2e8 arguments in [-746, 0] (the same steps in C on the
+// CPU; a 1e6-argument run of that check is part of the CPU test suite).
 __device__ __forceinline__ double exp_d(double x) {
     constexpr double kLog2e = 0x1.71547652b82fep+0;   // RN(1 / ln 2)
     constexpr double kLn2Hi = 0x1.62e42fefa39efp-1;   // RN(ln 2)
