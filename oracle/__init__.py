@@ -72,27 +72,29 @@ def lib():
             L.oracle_code_real.argtypes = [f32, f32, f32]
             L.oracle_level.restype = f32
             L.oracle_level.argtypes = [i32, f32, f32]
-            L.oracle_split.restype = None
-            L.oracle_split.argtypes = [i32, i32, ctypes.POINTER(i32),
-                                       ctypes.POINTER(i32), ctypes.POINTER(i32)]
-            L.oracle_unsplit.restype = i32
-            L.oracle_unsplit.argtypes = [ctypes.c_uint, i32, ctypes.c_uint,
-                                         ctypes.POINTER(i32)]
-            L.oracle_quantize_block_ex.restype = i32
-            L.oracle_quantize_block_ex.argtypes = [
-                vp, i64, i32, i32, i32, f32, f32, f32, vp, vp, vp, vp, vp, vp,
+            L.oracle_code_max.restype = i32
+            L.oracle_code_max.argtypes = [i32]
+            L.oracle_split_bits.restype = None
+            L.oracle_split_bits.argtypes = [i32, i32, i32, ctypes.POINTER(i32),
+                                            ctypes.POINTER(i32), ctypes.POINTER(i32)]
+            L.oracle_unsplit_bits.restype = i32
+            L.oracle_unsplit_bits.argtypes = [ctypes.c_uint, i32, ctypes.c_uint, i32,
+                                              ctypes.POINTER(i32)]
+            L.oracle_quantize_block_bits.restype = i32
+            L.oracle_quantize_block_bits.argtypes = [
+                vp, i64, i32, i32, i32, f32, f32, f32, i32, vp, vp, vp, vp, vp, vp,
                 vp, vp, vp, vp, vp]
-            L.oracle_dequant_block.restype = i32
-            L.oracle_dequant_block.argtypes = [
-                vp, vp, vp, vp, vp, vp, i32, i32, i32, f32, f32, f32, vp, i64]
-            L.oracle_quantize.restype = i32
-            L.oracle_quantize.argtypes = [
-                vp, i64, i64, i64, i64, i64, i32, i32, i32, f32, f32, f32,
+            L.oracle_dequant_block_bits.restype = i32
+            L.oracle_dequant_block_bits.argtypes = [
+                vp, vp, vp, vp, vp, vp, i32, i32, i32, f32, f32, f32, i32, vp, i64]
+            L.oracle_quantize_bits.restype = i32
+            L.oracle_quantize_bits.argtypes = [
+                vp, i64, i64, i64, i64, i64, i32, i32, i32, f32, f32, f32, i32,
                 i64, i64, i64, vp, vp, vp, vp, vp, vp]
-            L.oracle_dequant.restype = i32
-            L.oracle_dequant.argtypes = [
+            L.oracle_dequant_bits.restype = i32
+            L.oracle_dequant_bits.argtypes = [
                 vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, i32,
-                f32, f32, f32, i64, i64, i64, vp]
+                f32, f32, f32, i32, i64, i64, i64, vp]
             L.oracle_spec_verify.restype = i32
             L.oracle_spec_verify.argtypes = [vp, vp, vp, vp, f64, i32, i32,
                                              ctypes.POINTER(i32), ctypes.POINTER(i32)]
@@ -127,19 +129,27 @@ def level(k: int, alpha: float = 255.0, code_scale: float = CODE_SCALE) -> float
     return lib().oracle_level(k, alpha, code_scale)
 
 
-def split(code_c: int, sign: int):
-    """Algorithm 1 Stage 4 on one clipped code: returns (V_mag, Q_res, Q_anc)."""
+def code_max(anchor_bits: int = 4) -> int:
+    """Largest code whose anchor magnitude fits an anchor_bits-bit anchor
+    (a + b = 8): 2^7 - 2^(b-1), 120 for the paper's 4 + 4 split."""
+    return lib().oracle_code_max(anchor_bits)
+
+
+def split(code_c: int, sign: int, anchor_bits: int = 4):
+    """Algorithm 1 Stage 4 on one clipped code: returns (V_mag, Q_res, Q_anc)
+    (the paper's 4 + 4 split by default)."""
     v, r, a = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
-    lib().oracle_split(code_c, sign, ctypes.byref(v), ctypes.byref(r),
-                       ctypes.byref(a))
+    lib().oracle_split_bits(code_c, sign, anchor_bits, ctypes.byref(v), ctypes.byref(r),
+                            ctypes.byref(a))
     return v.value, r.value, a.value
 
 
-def unsplit(anchor_nibble: int, residual_nibble: int | None):
-    """Decoder side of Stage 4: (code, sign) from the nibbles."""
+def unsplit(anchor_field: int, residual_field: int | None, anchor_bits: int = 4):
+    """Decoder side of Stage 4: (code, sign) from the anchor field (and the
+    residual field for the full code)."""
     s = ctypes.c_int()
-    c = lib().oracle_unsplit(anchor_nibble, residual_nibble is not None,
-                             residual_nibble or 0, ctypes.byref(s))
+    c = lib().oracle_unsplit_bits(anchor_field, residual_field is not None,
+                                  residual_field or 0, anchor_bits, ctypes.byref(s))
     return c, s.value
 
 
@@ -148,11 +158,13 @@ def unsplit(anchor_nibble: int, residual_nibble: int | None):
 class BlockResult:
     """Outputs of one oracle page block (plus optional intermediates)."""
 
-    def __init__(self, H, P, C):
+    def __init__(self, H, P, C, anchor_bits=4):
         nch = P // C
-        # chunk-tiled streams: [chunk][channel pair][token of the chunk]
-        self.anchor = np.zeros((nch, H // 2, C), np.uint8)
-        self.residual = np.zeros((nch, H // 2, C), np.uint8)
+        self.C, self.anchor_bits = C, anchor_bits
+        # chunk-tiled streams: [chunk][channel pair][run of 2C w-bit fields]
+        # (for w = 4: [chunk][channel pair][token of the chunk])
+        self.anchor = np.zeros((nch, H // 2, C * anchor_bits // 4), np.uint8)
+        self.residual = np.zeros((nch, H // 2, C * (8 - anchor_bits) // 4), np.uint8)
         self.gamma_min = np.zeros(H, np.float32)
         self.gamma_scale = np.zeros(H, np.float32)
         self.mu = np.zeros((nch, H), np.float32)
@@ -165,33 +177,34 @@ class BlockResult:
 
 
 def quantize_block(x_bf16: np.ndarray, alpha=255.0, eps=1e-6, code_scale=CODE_SCALE,
-                   C=C_DEFAULT) -> BlockResult:
+                   C=C_DEFAULT, anchor_bits=4) -> BlockResult:
     """Quantize one page block given token-major as uint16 bf16 bits [P][H]."""
     x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
     P, H = x.shape
-    r = BlockResult(H, P, C)
-    rc = lib().oracle_quantize_block_ex(
-        _ptr(x), H, H, P, C, alpha, eps, code_scale, _ptr(r.anchor),
+    r = BlockResult(H, P, C, anchor_bits)
+    rc = lib().oracle_quantize_block_bits(
+        _ptr(x), H, H, P, C, alpha, eps, code_scale, anchor_bits, _ptr(r.anchor),
         _ptr(r.residual), _ptr(r.gamma_min), _ptr(r.gamma_scale), _ptr(r.mu),
         _ptr(r.sigma), _ptr(r.xn), _ptr(r.xcent), _ptr(r.xfinal),
         _ptr(r.code_raw), _ptr(r.sign))
     if rc:
-        raise ValueError("oracle_quantize_block_ex rejected the block")
+        raise ValueError("oracle_quantize_block_bits rejected the block")
     return r
 
 
 def dequant_block(r: BlockResult, full: bool, alpha=255.0, eps=1e-6,
-                  code_scale=CODE_SCALE, C=C_DEFAULT) -> np.ndarray:
+                  code_scale=CODE_SCALE) -> np.ndarray:
     """Reconstruct a block from its codes: anchor-only or anchor + residual."""
-    nch, Hh, C = r.anchor.shape
+    nch, Hh = r.anchor.shape[:2]
+    C = r.C
     P, H = nch * C, Hh * 2
     out = np.zeros((P, H), np.uint16)
-    rc = lib().oracle_dequant_block(
+    rc = lib().oracle_dequant_block_bits(
         _ptr(r.anchor), _ptr(r.residual) if full else None, _ptr(r.gamma_min),
         _ptr(r.gamma_scale), _ptr(r.mu), _ptr(r.sigma), H, P, C, alpha, eps,
-        code_scale, _ptr(out), H)
+        code_scale, r.anchor_bits, _ptr(out), H)
     if rc:
-        raise ValueError("oracle_dequant_block rejected the block")
+        raise ValueError("oracle_dequant_block_bits rejected the block")
     return out
 
 
@@ -200,10 +213,12 @@ def dequant_block(r: BlockResult, full: bool, alpha=255.0, eps=1e-6,
 class Codes:
     """Oracle outputs for a KV set of num_tensors [T][Ch] tensors."""
 
-    def __init__(self, nblocks, H=H_DEFAULT, P=P_DEFAULT, C=C_DEFAULT):
+    def __init__(self, nblocks, H=H_DEFAULT, P=P_DEFAULT, C=C_DEFAULT, anchor_bits=4):
         self.nblocks = nblocks
-        self.anchor = np.zeros((nblocks, P // C, H // 2, C), np.uint8)
-        self.residual = np.zeros((nblocks, P // C, H // 2, C), np.uint8)
+        self.anchor_bits = anchor_bits
+        self.anchor = np.zeros((nblocks, P // C, H // 2, C * anchor_bits // 4), np.uint8)
+        self.residual = np.zeros((nblocks, P // C, H // 2, C * (8 - anchor_bits) // 4),
+                                 np.uint8)
         self.gamma_min = np.zeros((nblocks, H), np.float32)
         self.gamma_scale = np.zeros((nblocks, H), np.float32)
         self.mu = np.zeros((nblocks, P // C, H), np.float32)
@@ -218,7 +233,7 @@ def _ranges(n, parts):
 
 def quantize(kv: np.ndarray, alpha=255.0, eps=1e-6, code_scale=CODE_SCALE,
              H=H_DEFAULT, P=P_DEFAULT, C=C_DEFAULT, threads=1,
-             blocks: tuple[int, int] | None = None) -> Codes:
+             blocks: tuple[int, int] | None = None, anchor_bits=4) -> Codes:
     """Quantize kv (uint16 bf16 bits, shape [num_tensors, T, Ch]).
 
     ``blocks=(b0, b1)`` restricts the work (and the returned arrays) to page
@@ -229,14 +244,14 @@ def quantize(kv: np.ndarray, alpha=255.0, eps=1e-6, code_scale=CODE_SCALE,
     nt, T, Ch = kv.shape
     nblocks = nt * (T // P) * (Ch // H)
     b0, b1 = blocks if blocks is not None else (0, nblocks)
-    out = Codes(b1 - b0, H, P, C)
+    out = Codes(b1 - b0, H, P, C, anchor_bits)
     L = lib()
 
     def run(r):
         lo, hi = r
-        rc = L.oracle_quantize(
+        rc = L.oracle_quantize_bits(
             _ptr(kv), nt, T * Ch, T, Ch, Ch, H, P, C, alpha, eps, code_scale,
-            lo, hi, b0, _ptr(out.anchor), _ptr(out.residual),
+            anchor_bits, lo, hi, b0, _ptr(out.anchor), _ptr(out.residual),
             _ptr(out.gamma_min), _ptr(out.gamma_scale), _ptr(out.mu),
             _ptr(out.sigma))
         if rc:
@@ -268,11 +283,11 @@ def dequant(codes: Codes, shape, full: bool, alpha=255.0, eps=1e-6,
 
     def run(r):
         lo, hi = r
-        rc = L.oracle_dequant(
+        rc = L.oracle_dequant_bits(
             _ptr(codes.anchor), _ptr(codes.residual) if full else None,
             _ptr(codes.gamma_min), _ptr(codes.gamma_scale), _ptr(codes.mu),
             _ptr(codes.sigma), nt, T * Ch, T, Ch, Ch, H, P, C, alpha, eps,
-            code_scale, lo, hi, b0, _ptr(out))
+            code_scale, getattr(codes, "anchor_bits", 4), lo, hi, b0, _ptr(out))
         if rc:
             raise ValueError("oracle_dequant rejected the arguments")
 

@@ -40,7 +40,14 @@
  *   - nibble packing: two channels per byte (channel 2k in the low nibble,
  *     2k+1 in the high nibble), one byte per token; bytes are chunk-tiled,
  *     [chunk j][channel pair k][token i of the chunk], so every chunk of a
- *     page block is one contiguous (H/2) x C byte tile.
+ *     page block is one contiguous (H/2) x C byte tile;
+ *   - other splits of the 8-bit code (a anchor bits, b = 8 - a residual
+ *     bits; the paper's split is 4 + 4): the bias of Stage 4 becomes
+ *     2^(b-1) - 1 (the paper's +7 for b = 4), codes are clipped to the
+ *     largest one whose anchor magnitude fits a bits, and the fields are
+ *     packed as an LSB-first bit stream per (chunk, channel pair): value
+ *     2 i + e (token i of the chunk, channel 2k + e) at bit w (2 i + e) of
+ *     the pair's C w / 4 bytes.  For a = 4 this is the nibble layout above.
  */
 #include <math.h>
 #include <stdint.h>
@@ -96,9 +103,17 @@ double oracle_code_real(float x_abs, float alpha, float code_scale)
            log1p((double)alpha);
 }
 
-/* Largest code whose anchor magnitude (I + 7) >> 4 still fits the 4-bit
- * two's-complement anchor nibble (0..7 for either sign). */
-#define ORACLE_CODE_MAX 120
+/* Largest code whose anchor magnitude (I + 2^(b-1) - 1) >> b still fits an
+ * a-bit two's-complement anchor (magnitude <= 2^(a-1) - 1 for either sign),
+ * a + b = 8: 2^7 - 2^(b-1), i.e. 120 for the paper's 4 + 4 split. */
+static int valid_anchor_bits(int a) { return a >= 2 && a <= 7; }
+
+int oracle_code_max(int anchor_bits)
+{
+    if (!valid_anchor_bits(anchor_bits))
+        return -1;
+    return 128 - (1 << (8 - anchor_bits - 1));
+}
 
 /* Reconstruction level of code k, the inverse of Eq. (3)
  * (|x^| grows as (1 + alpha)^(y / 127), Eq. (4)):
@@ -112,43 +127,78 @@ float oracle_level(int k, float alpha, float code_scale)
 
 /* ------------------------------------------------------------ Stage 4 -- */
 
-/* Split-stream construction of one clipped code I (0..120) with sign S
- * (Algorithm 1, Stage 4):
- *   I_bias = I + 7;  V_mag = I_bias >> 4;  V_recon = V_mag << 4;
- *   Q_res = V_recon - I;  Q_anc = V_mag * S + min(S, 0). */
-void oracle_split(int code, int sign, int *v_mag, int *q_res, int *q_anc)
+/* Split-stream construction of one clipped code I with sign S (Algorithm
+ * 1, Stage 4), for a anchor bits and b = 8 - a residual bits:
+ *   I_bias = I + 2^(b-1) - 1;  V_mag = I_bias >> b;  V_recon = V_mag << b;
+ *   Q_res = V_recon - I;  Q_anc = V_mag * S + min(S, 0).
+ * The paper's split (a = b = 4) has the bias +7. */
+void oracle_split_bits(int code, int sign, int anchor_bits, int *v_mag, int *q_res,
+                       int *q_anc)
 {
-    int i_bias = code + 7;
-    int v = i_bias >> 4;
-    int v_recon = v << 4;
+    int b = 8 - anchor_bits;
+    int i_bias = code + (1 << (b - 1)) - 1;
+    int v = i_bias >> b;
+    int v_recon = v << b;
     *v_mag = v;
     *q_res = v_recon - code;
     *q_anc = v * sign + (sign < 0 ? sign : 0);
+}
+
+void oracle_split(int code, int sign, int *v_mag, int *q_res, int *q_anc)
+{
+    oracle_split_bits(code, sign, 4, v_mag, q_res, q_anc);
 }
 
 /* Inverse of the split: the code that the decoder rebuilds from an anchor
  * nibble alone (V << 4) or from anchor and residual ((V << 4) - Q_res),
  * plus the sign carried by the anchor.  Codes below 0 (only reachable with
  * a residual the quantizer never writes) are clamped to 0. */
-static int sext4(unsigned nib)
+static int sext(unsigned field, int w)
 {
-    nib &= 0xfu;
-    return (nib & 0x8u) ? (int)nib - 16 : (int)nib;
+    field &= (1u << w) - 1u;
+    return (field >> (w - 1)) & 1u ? (int)field - (1 << w) : (int)field;
 }
 
-int oracle_unsplit(unsigned anc_nib, int have_res, unsigned res_nib, int *sign)
+int oracle_unsplit_bits(unsigned anc_field, int have_res, unsigned res_field,
+                        int anchor_bits, int *sign)
 {
-    int a = sext4(anc_nib);
+    int b = 8 - anchor_bits;
+    int a = sext(anc_field, anchor_bits);
     int s = a < 0 ? -1 : 1;
     int v = a < 0 ? -a - 1 : a;
-    int code = v << 4;
+    int code = v << b;
     if (have_res)
-        code -= sext4(res_nib);
+        code -= sext(res_field, b);
     if (code < 0)
         code = 0;
     *sign = s;
     return code;
 }
+
+int oracle_unsplit(unsigned anc_nib, int have_res, unsigned res_nib, int *sign)
+{
+    return oracle_unsplit_bits(anc_nib, have_res, res_nib, 4, sign);
+}
+
+/* Bit stream of one (chunk, channel pair) run: field f of width w at bit
+ * pos, LSB first, byte by byte (the run starts zeroed). */
+static void put_bits(uint8_t *run, int pos, int w, unsigned f)
+{
+    for (int k = 0; k < w; ++k)
+        if ((f >> k) & 1u)
+            run[(pos + k) >> 3] |= (uint8_t)(1u << ((pos + k) & 7));
+}
+
+static unsigned get_bits(const uint8_t *run, int pos, int w)
+{
+    unsigned f = 0;
+    for (int k = 0; k < w; ++k)
+        f |= (unsigned)((run[(pos + k) >> 3] >> ((pos + k) & 7)) & 1u) << k;
+    return f;
+}
+
+/* Bytes of one (chunk, channel pair) run of w-bit fields: 2 C values. */
+static int run_bytes(int C, int w) { return C * w / 4; }
 
 /* ------------------------------------------------------------- Stage 2 -- */
 
@@ -170,8 +220,9 @@ static int is_pow2(int n) { return n > 0 && (n & (n - 1)) == 0; }
  * (channel c, token t) is x[t * row_stride + c] (bfloat16 bits).
  *
  * Outputs (all caller-owned):
- *   anchor, residual : P * H / 2 bytes each (packed nibbles, chunk-tiled,
- *                      see header);
+ *   anchor, residual : P * H * a / 8 and P * H * (8 - a) / 8 bytes
+ *                      (chunk-tiled bit streams, see header; P * H / 2 each
+ *                      for the paper's a = 4);
  *   gamma_min, gamma_scale : H floats;
  *   mu, sigma : (P/C) x H floats, chunk-major ([chunk][channel]).
  * Optional intermediates (NULL to skip), each H x P, channel-major
@@ -179,17 +230,19 @@ static int is_pow2(int n) { return n > 0 && (n & (n - 1)) == 0; }
  *   xn (Stage 1 output), xcent, xfinal (Stage 2), code_raw (Round(Y) before
  *   the clip), sign (+1 / -1).
  */
-int oracle_quantize_block_ex(const uint16_t *x, int64_t row_stride, int H,
-                             int P, int C, float alpha, float eps,
-                             float code_scale, uint8_t *anchor,
-                             uint8_t *residual, float *gamma_min,
-                             float *gamma_scale, float *mu, float *sigma,
-                             float *xn_out, float *xcent_out,
-                             float *xfinal_out, int32_t *code_raw_out,
-                             int8_t *sign_out)
+int oracle_quantize_block_bits(const uint16_t *x, int64_t row_stride, int H,
+                               int P, int C, float alpha, float eps,
+                               float code_scale, int anchor_bits,
+                               uint8_t *anchor, uint8_t *residual,
+                               float *gamma_min, float *gamma_scale, float *mu,
+                               float *sigma, float *xn_out, float *xcent_out,
+                               float *xfinal_out, int32_t *code_raw_out,
+                               int8_t *sign_out)
 {
-    if (H <= 0 || (H & 1) || P <= 0 || !is_pow2(C) || P % C)
+    if (H <= 0 || (H & 1) || P <= 0 || !is_pow2(C) || P % C || C % 4 ||
+        !valid_anchor_bits(anchor_bits))
         return ORACLE_EINVAL;
+    const int code_max = oracle_code_max(anchor_bits);
     const int nchunk = P / C;
     float *xn = (float *)malloc(sizeof(float) * (size_t)P);
     float *xc = (float *)malloc(sizeof(float) * (size_t)P);
@@ -240,9 +293,9 @@ int oracle_quantize_block_ex(const uint16_t *x, int64_t row_stride, int H,
                 float xf = xc[t] / d2;
                 int code = oracle_code(fabsf(xf), alpha, code_scale);
                 int s = xc[t] < 0.0f ? -1 : 1;
-                int code_c = code < ORACLE_CODE_MAX ? code : ORACLE_CODE_MAX;
+                int code_c = code < code_max ? code : code_max;
                 int v, q_res, q_anc;
-                oracle_split(code_c, s, &v, &q_res, &q_anc);
+                oracle_split_bits(code_c, s, anchor_bits, &v, &q_res, &q_anc);
                 qa[(size_t)t * H + c] = (int8_t)q_anc;
                 qr[(size_t)t * H + c] = (int8_t)q_res;
                 if (xfinal_out) xfinal_out[(size_t)c * P + t] = xf;
@@ -256,23 +309,42 @@ int oracle_quantize_block_ex(const uint16_t *x, int64_t row_stride, int H,
             memcpy(xcent_out + (size_t)c * P, xc, sizeof(float) * (size_t)P);
     }
 
-    /* Packing: two's-complement nibbles, even channel in the low nibble,
-     * chunk-tiled: for chunk j, channel pair k, token i of the chunk, the
-     * byte sits at j * (H / 2) * C + k * C + i. */
+    /* Packing: two's-complement fields, chunk-tiled bit streams: for chunk
+     * j and channel pair k the run of w-bit fields starts at byte
+     * (j * (H / 2) + k) * C * w / 4; token i of the chunk and channel
+     * 2k + e is field 2 i + e.  (For w = 4: byte i of the run, channel 2k
+     * in the low nibble.) */
+    const int wa = anchor_bits, wr = 8 - anchor_bits;
+    memset(anchor, 0, (size_t)P * H * wa / 8);
+    memset(residual, 0, (size_t)P * H * wr / 8);
     for (int t = 0; t < P; ++t) {
         const int j = t / C, i = t % C;
         for (int k = 0; k < H / 2; ++k) {
-            unsigned a0 = (unsigned)qa[(size_t)t * H + 2 * k] & 0xfu;
-            unsigned a1 = (unsigned)qa[(size_t)t * H + 2 * k + 1] & 0xfu;
-            unsigned r0 = (unsigned)qr[(size_t)t * H + 2 * k] & 0xfu;
-            unsigned r1 = (unsigned)qr[(size_t)t * H + 2 * k + 1] & 0xfu;
-            size_t off = ((size_t)j * (H / 2) + k) * C + i;
-            anchor[off] = (uint8_t)(a0 | (a1 << 4));
-            residual[off] = (uint8_t)(r0 | (r1 << 4));
+            uint8_t *ra = anchor + ((size_t)j * (H / 2) + k) * run_bytes(C, wa);
+            uint8_t *rr = residual + ((size_t)j * (H / 2) + k) * run_bytes(C, wr);
+            for (int e = 0; e < 2; ++e) {
+                const int v = 2 * i + e;
+                put_bits(ra, wa * v, wa, (unsigned)qa[(size_t)t * H + 2 * k + e]);
+                put_bits(rr, wr * v, wr, (unsigned)qr[(size_t)t * H + 2 * k + e]);
+            }
         }
     }
     free(xn); free(xc); free(qa); free(qr);
     return ORACLE_OK;
+}
+
+int oracle_quantize_block_ex(const uint16_t *x, int64_t row_stride, int H,
+                             int P, int C, float alpha, float eps,
+                             float code_scale, uint8_t *anchor,
+                             uint8_t *residual, float *gamma_min,
+                             float *gamma_scale, float *mu, float *sigma,
+                             float *xn_out, float *xcent_out,
+                             float *xfinal_out, int32_t *code_raw_out,
+                             int8_t *sign_out)
+{
+    return oracle_quantize_block_bits(x, row_stride, H, P, C, alpha, eps, code_scale, 4,
+                                      anchor, residual, gamma_min, gamma_scale, mu, sigma,
+                                      xn_out, xcent_out, xfinal_out, code_raw_out, sign_out);
 }
 
 /*
@@ -282,30 +354,31 @@ int oracle_quantize_block_ex(const uint16_t *x, int64_t row_stride, int H,
  *   x^_f = S * L[code];  x^_n = x^_f * (sigma + eps) + mu;
  *   x^ = x^_n * (gamma_scale + eps) + gamma_min;  out = bf16_rne(x^).
  */
-int oracle_dequant_block(const uint8_t *anchor, const uint8_t *residual,
-                         const float *gamma_min, const float *gamma_scale,
-                         const float *mu, const float *sigma, int H, int P,
-                         int C, float alpha, float eps, float code_scale,
-                         uint16_t *out, int64_t out_row_stride)
+int oracle_dequant_block_bits(const uint8_t *anchor, const uint8_t *residual,
+                              const float *gamma_min, const float *gamma_scale,
+                              const float *mu, const float *sigma, int H, int P,
+                              int C, float alpha, float eps, float code_scale,
+                              int anchor_bits, uint16_t *out,
+                              int64_t out_row_stride)
 {
-    if (H <= 0 || (H & 1) || P <= 0 || C <= 0 || P % C)
+    if (H <= 0 || (H & 1) || P <= 0 || C <= 0 || P % C || C % 4 ||
+        !valid_anchor_bits(anchor_bits))
         return ORACLE_EINVAL;
+    const int wa = anchor_bits, wr = 8 - anchor_bits;
     float lut[128];
     for (int k = 0; k < 128; ++k)
         lut[k] = oracle_level(k, alpha, code_scale);
     for (int t = 0; t < P; ++t) {
         int j = t / C;
         for (int c = 0; c < H; ++c) {
-            size_t off = ((size_t)j * (H / 2) + c / 2) * C + (t % C);
-            unsigned ab = anchor[off];
-            unsigned an = (c & 1) ? (ab >> 4) : (ab & 0xfu);
+            const size_t run = (size_t)j * (H / 2) + c / 2;
+            const int v = 2 * (t % C) + (c & 1);
+            unsigned an = get_bits(anchor + run * run_bytes(C, wa), wa * v, wa);
             unsigned rn = 0;
-            if (residual) {
-                unsigned rb = residual[off];
-                rn = (c & 1) ? (rb >> 4) : (rb & 0xfu);
-            }
+            if (residual)
+                rn = get_bits(residual + run * run_bytes(C, wr), wr * v, wr);
             int s;
-            int code = oracle_unsplit(an, residual != NULL, rn, &s);
+            int code = oracle_unsplit_bits(an, residual != NULL, rn, anchor_bits, &s);
             float m = lut[code];
             float xf = s < 0 ? -m : m;
             float d2 = sigma[j * H + c] + eps;
@@ -318,6 +391,16 @@ int oracle_dequant_block(const uint8_t *anchor, const uint8_t *residual,
         }
     }
     return ORACLE_OK;
+}
+
+int oracle_dequant_block(const uint8_t *anchor, const uint8_t *residual,
+                         const float *gamma_min, const float *gamma_scale,
+                         const float *mu, const float *sigma, int H, int P,
+                         int C, float alpha, float eps, float code_scale,
+                         uint16_t *out, int64_t out_row_stride)
+{
+    return oracle_dequant_block_bits(anchor, residual, gamma_min, gamma_scale, mu, sigma, H,
+                                     P, C, alpha, eps, code_scale, 4, out, out_row_stride);
 }
 
 /* ------------------------------------------------------- whole tensors -- */
@@ -344,6 +427,43 @@ static int block_geometry(int64_t b, int64_t T, int64_t Ch, int H, int P,
     return 0;
 }
 
+int oracle_quantize_bits(const uint16_t *kv, int64_t num_tensors,
+                         int64_t tensor_stride, int64_t T, int64_t Ch,
+                         int64_t row_stride, int H, int P, int C, float alpha,
+                         float eps, float code_scale, int anchor_bits,
+                         int64_t block_begin, int64_t block_end,
+                         int64_t out_first_block, uint8_t *anchor,
+                         uint8_t *residual, float *gamma_min,
+                         float *gamma_scale, float *mu, float *sigma)
+{
+    if (!valid_anchor_bits(anchor_bits))
+        return ORACLE_EINVAL;
+    if (T % P || Ch % H || num_tensors < 0)
+        return ORACLE_EINVAL;
+    const int64_t nblocks = num_tensors * (T / P) * (Ch / H);
+    if (block_begin < 0 || block_end > nblocks || block_begin > block_end ||
+        out_first_block > block_begin)
+        return ORACLE_EINVAL;
+    const int64_t anchor_bytes = (int64_t)P * H * anchor_bits / 8;
+    const int64_t residual_bytes = (int64_t)P * H * (8 - anchor_bits) / 8;
+    const int64_t chunk_meta = (int64_t)(P / C) * H;
+    for (int64_t b = block_begin; b < block_end; ++b) {
+        int64_t tensor, page, group;
+        block_geometry(b, T, Ch, H, P, &tensor, &page, &group);
+        const uint16_t *x = kv + tensor * tensor_stride +
+                            page * P * row_stride + group * H;
+        const int64_t o = b - out_first_block;
+        int rc = oracle_quantize_block_bits(
+            x, row_stride, H, P, C, alpha, eps, code_scale, anchor_bits,
+            anchor + o * anchor_bytes, residual + o * residual_bytes,
+            gamma_min + o * H, gamma_scale + o * H, mu + o * chunk_meta,
+            sigma + o * chunk_meta, NULL, NULL, NULL, NULL, NULL);
+        if (rc)
+            return rc;
+    }
+    return ORACLE_OK;
+}
+
 int oracle_quantize(const uint16_t *kv, int64_t num_tensors,
                     int64_t tensor_stride, int64_t T, int64_t Ch,
                     int64_t row_stride, int H, int P, int C, float alpha,
@@ -353,25 +473,43 @@ int oracle_quantize(const uint16_t *kv, int64_t num_tensors,
                     float *gamma_min, float *gamma_scale, float *mu,
                     float *sigma)
 {
+    return oracle_quantize_bits(kv, num_tensors, tensor_stride, T, Ch, row_stride, H, P, C,
+                                alpha, eps, code_scale, 4, block_begin, block_end,
+                                out_first_block, anchor, residual, gamma_min, gamma_scale,
+                                mu, sigma);
+}
+
+int oracle_dequant_bits(const uint8_t *anchor, const uint8_t *residual,
+                        const float *gamma_min, const float *gamma_scale,
+                        const float *mu, const float *sigma, int64_t num_tensors,
+                        int64_t tensor_stride, int64_t T, int64_t Ch,
+                        int64_t row_stride, int H, int P, int C, float alpha,
+                        float eps, float code_scale, int anchor_bits,
+                        int64_t block_begin, int64_t block_end,
+                        int64_t in_first_block, uint16_t *out)
+{
+    if (!valid_anchor_bits(anchor_bits))
+        return ORACLE_EINVAL;
     if (T % P || Ch % H || num_tensors < 0)
         return ORACLE_EINVAL;
     const int64_t nblocks = num_tensors * (T / P) * (Ch / H);
     if (block_begin < 0 || block_end > nblocks || block_begin > block_end ||
-        out_first_block > block_begin)
+        in_first_block > block_begin)
         return ORACLE_EINVAL;
-    const int64_t code_bytes = (int64_t)P * H / 2;
+    const int64_t anchor_bytes = (int64_t)P * H * anchor_bits / 8;
+    const int64_t residual_bytes = (int64_t)P * H * (8 - anchor_bits) / 8;
     const int64_t chunk_meta = (int64_t)(P / C) * H;
     for (int64_t b = block_begin; b < block_end; ++b) {
         int64_t tensor, page, group;
         block_geometry(b, T, Ch, H, P, &tensor, &page, &group);
-        const uint16_t *x = kv + tensor * tensor_stride +
-                            page * P * row_stride + group * H;
-        const int64_t o = b - out_first_block;
-        int rc = oracle_quantize_block_ex(
-            x, row_stride, H, P, C, alpha, eps, code_scale,
-            anchor + o * code_bytes, residual + o * code_bytes,
-            gamma_min + o * H, gamma_scale + o * H, mu + o * chunk_meta,
-            sigma + o * chunk_meta, NULL, NULL, NULL, NULL, NULL);
+        uint16_t *o = out + tensor * tensor_stride + page * P * row_stride +
+                      group * H;
+        const int64_t i = b - in_first_block;
+        int rc = oracle_dequant_block_bits(
+            anchor + i * anchor_bytes, residual ? residual + i * residual_bytes : NULL,
+            gamma_min + i * H, gamma_scale + i * H, mu + i * chunk_meta,
+            sigma + i * chunk_meta, H, P, C, alpha, eps, code_scale, anchor_bits, o,
+            row_stride);
         if (rc)
             return rc;
     }
@@ -386,29 +524,10 @@ int oracle_dequant(const uint8_t *anchor, const uint8_t *residual,
                    float eps, float code_scale, int64_t block_begin,
                    int64_t block_end, int64_t in_first_block, uint16_t *out)
 {
-    if (T % P || Ch % H || num_tensors < 0)
-        return ORACLE_EINVAL;
-    const int64_t nblocks = num_tensors * (T / P) * (Ch / H);
-    if (block_begin < 0 || block_end > nblocks || block_begin > block_end ||
-        in_first_block > block_begin)
-        return ORACLE_EINVAL;
-    const int64_t code_bytes = (int64_t)P * H / 2;
-    const int64_t chunk_meta = (int64_t)(P / C) * H;
-    for (int64_t b = block_begin; b < block_end; ++b) {
-        int64_t tensor, page, group;
-        block_geometry(b, T, Ch, H, P, &tensor, &page, &group);
-        uint16_t *o = out + tensor * tensor_stride + page * P * row_stride +
-                      group * H;
-        const int64_t i = b - in_first_block;
-        int rc = oracle_dequant_block(
-            anchor + i * code_bytes, residual ? residual + i * code_bytes : NULL,
-            gamma_min + i * H, gamma_scale + i * H, mu + i * chunk_meta,
-            sigma + i * chunk_meta, H, P, C, alpha, eps, code_scale, o,
-            row_stride);
-        if (rc)
-            return rc;
-    }
-    return ORACLE_OK;
+    return oracle_dequant_bits(anchor, residual, gamma_min, gamma_scale, mu, sigma,
+                               num_tensors, tensor_stride, T, Ch, row_stride, H, P, C, alpha,
+                               eps, code_scale, 4, block_begin, block_end, in_first_block,
+                               out);
 }
 
 /* ----------------------------------------------------------- attention -- */
