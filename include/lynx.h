@@ -43,6 +43,13 @@
  *               back: one contiguous stream.
  *   residual    uint8 [nblocks][P/C][H/2][C], same layout, 4-bit signed
  *               residual (code = (anchor magnitude << 4) - residual).
+ *   With anchor_bits = a other than 4 (the other splits of the 8-bit code,
+ *   b = 8 - a residual bits): each (chunk j, pair k) holds a run of 8 w
+ *   bytes (w = a for the anchor, b for the residual) at byte
+ *   [b][j][k] x 8 w of the block's 4096 w bytes: an LSB-first bit stream
+ *   of 64 two's-complement w-bit fields, field 2 i + e (token 32 j + i,
+ *   channel 2k + e) at bit w (2 i + e).  For w = 4 this is the nibble
+ *   layout above.
  *   gamma_min, gamma_scale   float32 [nblocks][H]
  *   mu, sigma               float32 [nblocks][P/C][H]
  *
@@ -51,10 +58,13 @@
  * real-arithmetic rounding (half-up) of Eq. (3) applied to the binary32
  * X_final with the compander scaled to code_scale (default 120, so every
  * code fits the 4 + 4 split; with 127 codes above 120 are clipped so the
- * anchor fits 4 bits); reconstruction is
+ * anchor fits 4 bits; with a anchor bits the clip is at 128 - 2^(7 - a),
+ * the largest code whose anchor magnitude (code + 2^(7-a) - 1) >> (8 - a)
+ * fits a bits); reconstruction is
  * ((S * L[code]) * (sigma + eps) + mu) * (gamma_scale + eps) + gamma_min with
  * L[k] = ((1 + alpha)^(k / code_scale) - 1) / alpha rounded to binary32, then
- * bf16 round-to-nearest-even.  Anchor-only uses code = anchor magnitude << 4.
+ * bf16 round-to-nearest-even.  Anchor-only uses code = anchor magnitude << 4
+ * (<< (8 - a) in general).
  * Results are deterministic and independent of launch geometry.
  * Non-finite inputs, and channels whose max - min overflows binary32, give
  * unspecified (but in-bounds) outputs.
@@ -103,7 +113,11 @@ extern "C" {
  * carry (anchor magnitude (code + 7) >> 4 <= 7), so every |X_final| in
  * [0, 1] keeps its code; 127 (the 2^7 - 1 printed in Eq. (3)) is accepted and
  * then codes above 120 are clipped to 120.  page_tokens, chunk_tokens and
- * block_channels must be 256, 32 and 128. */
+ * block_channels must be 256, 32 and 128.  anchor_bits (3..6, default 4 =
+ * the paper's split) is the width a of the anchor field, 8 - a that of the
+ * residual (the bias of Stage 4 is 2^(7 - a) - 1, +7 for a = 4); the
+ * anchor and residual streams then take 4096 a and 4096 (8 - a) bytes per
+ * block.  Only quantize and the two dequant calls accept a != 4. */
 typedef struct lynx_params {
     float alpha;
     float eps;
@@ -111,6 +125,7 @@ typedef struct lynx_params {
     int32_t page_tokens;
     int32_t chunk_tokens;
     int32_t block_channels;
+    int32_t anchor_bits;
 } lynx_params;
 
 /* Shape of a KV set (element strides, bf16 elements). */
@@ -131,7 +146,7 @@ typedef struct lynx_meta {
 } lynx_meta;
 
 /* Fills *p with alpha = 255, eps = 1e-6, code_scale = 120, P = 256,
- * C = 32, H = 128. */
+ * C = 32, H = 128, anchor_bits = 4. */
 void lynx_default_params(lynx_params *p);
 
 /* Number of page blocks of a shape, or a negative status if the shape is
@@ -139,8 +154,12 @@ void lynx_default_params(lynx_params *p);
 int64_t lynx_num_blocks(const lynx_kv_shape *shape);
 
 /* Bytes of one stream (anchor or residual) and number of floats of each
- * metadata array, for a shape; 0 if the shape is invalid. */
+ * metadata array, for a shape; 0 if the shape is invalid.
+ * lynx_stream_bytes is the 4-bit stream of the paper's split;
+ * lynx_field_stream_bytes the stream of field_bits-bit fields (1..7),
+ * nblocks x 4096 x field_bits. */
 size_t lynx_stream_bytes(const lynx_kv_shape *shape);
+size_t lynx_field_stream_bytes(const lynx_kv_shape *shape, int field_bits);
 size_t lynx_gamma_floats(const lynx_kv_shape *shape);
 size_t lynx_chunk_floats(const lynx_kv_shape *shape);
 
@@ -153,7 +172,8 @@ uint64_t lynx_kv_bytes(int64_t k_factor, int64_t seq_len, int64_t hidden,
 /* The 128 compander thresholds the kernels use for `params` (NULL =
  * defaults): thr[k], k = 1..120, is the smallest binary32 magnitude whose
  * Eq. (3) value reaches k - 1/2 (so code(|x|) = #{k : |x| >= thr[k]});
- * thr[0] = 0 and thr[k] = +inf for codes above 120 or out of reach.  Host
+ * thr[0] = 0 and thr[k] = +inf for codes above 120 (above the split's
+ * largest code 128 - 2^(7 - anchor_bits) in general) or out of reach.  Host
  * only, no GPU needed.  Returns LYNX_EINVAL for bad parameters. */
 int lynx_compander_thresholds(const lynx_params *params, float *thr128);
 
@@ -163,8 +183,9 @@ const char *lynx_status_string(int status);
 
 /*
  * Algorithm 1 on every page block of the KV set `kv` (bf16, layout given
- * by `shape`): writes anchor, residual (nblocks * 16384 bytes each) and the
- * four metadata arrays.  `params` NULL means the defaults.
+ * by `shape`): writes anchor, residual (nblocks * 16384 bytes each; nblocks
+ * * 4096 * anchor_bits and nblocks * 4096 * (8 - anchor_bits) for the other
+ * splits) and the four metadata arrays.  `params` NULL means the defaults.
  */
 int lynx_quantize_pages(const void *kv, const lynx_kv_shape *shape,
                         const lynx_params *params, uint8_t *anchor,
@@ -234,7 +255,8 @@ size_t lynx_attn_workspace_bytes(int t_q, int num_q_heads, int num_kv_heads,
  *   workspace    >= lynx_attn_workspace_bytes(...) bytes of device memory,
  *                overwritten (split partials).
  * Scores, the softmax and the accumulation are binary32 (bf16 x bf16
- * products are exact).  t_q * g must be <= 64.  Errors as above.
+ * products are exact).  t_q * g must be <= 64; params->anchor_bits must be
+ * 4.  Errors as above.
  */
 int lynx_decode_attn_dequant(const void *q, int t_q, int num_q_heads,
                              const uint8_t *k_anchor, const uint8_t *k_residual,
@@ -287,7 +309,7 @@ typedef struct lynx_transfer_times {
  *                    anchor into kv_anchor;
  * then, once every object is rebuilt from its anchor, per object: after its
  * residual copy, rebuild it from anchor + residual into kv_full.
- *   kv, shape, params  as lynx_quantize_pages;
+ *   kv, shape, params  as lynx_quantize_pages (anchor_bits must be 4);
  *   tx, wire, rx       code buffers of the whole set: tx and rx device
  *                      memory, wire pinned host memory (or device memory);
  *   kv_anchor, kv_full device bf16 outputs laid out by shape;

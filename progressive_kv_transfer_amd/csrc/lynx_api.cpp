@@ -9,6 +9,7 @@
 #include <map>
 #include <mutex>
 #include <string>
+#include <tuple>
 #include <utility>
 #include <vector>
 
@@ -45,12 +46,12 @@ long double eq3(float x, long double alpha, long double cs, long double l1pa) {
 // magnitudes that reach them, then the bucket table (at most one threshold
 // per bucket of 2^shift consecutive bit patterns).  Returns false if no
 // bucket width up to 8 mantissa bits fits kMaxBuckets.
-bool build_quant_tab(float alpha, float code_scale, QuantTab *t) {
+bool build_quant_tab(float alpha, float code_scale, int code_max, QuantTab *t) {
     memset(t, 0, sizeof *t);
     const long double a = alpha, cs = code_scale, l1pa = log1pl(a);
     t->thr[0] = 0.0f;
     for (int k = 1; k < 128; ++k) {
-        if (k > kCodeMax) {
+        if (k > code_max) {
             t->thr[k] = INFINITY;
             continue;
         }
@@ -120,16 +121,16 @@ struct Tables {
 };
 
 std::mutex g_mu;
-std::map<std::pair<uint32_t, uint32_t>, Tables> g_cache;
+std::map<std::tuple<uint32_t, uint32_t, int>, Tables> g_cache;
 
 const Tables *tables_for(const lynx_params &p) {
     std::lock_guard<std::mutex> lock(g_mu);
-    auto key = std::make_pair(f2u(p.alpha), f2u(p.code_scale));
+    auto key = std::make_tuple(f2u(p.alpha), f2u(p.code_scale), (int)p.anchor_bits);
     auto it = g_cache.find(key);
     if (it != g_cache.end())
         return &it->second;
     Tables t;
-    if (!build_quant_tab(p.alpha, p.code_scale, &t.q))
+    if (!build_quant_tab(p.alpha, p.code_scale, code_max_of(p.anchor_bits), &t.q))
         return nullptr;
     build_dequant_tab(p.alpha, p.code_scale, &t.d);
     return &g_cache.emplace(key, t).first->second;
@@ -151,6 +152,8 @@ int check_params(const lynx_params &p) {
     if (!(p.eps >= 0x1p-40f) || !(p.eps <= 0x1p-8f))
         return LYNX_EINVAL;
     if (!(p.code_scale >= 1.0f) || !(p.code_scale <= 127.0f))
+        return LYNX_EINVAL;
+    if (p.anchor_bits < kMinAnchorBits || p.anchor_bits > kMaxAnchorBits)
         return LYNX_EINVAL;
     return LYNX_OK;
 }
@@ -230,7 +233,7 @@ int quantize_common(const void *kv, const lynx_kv_shape *shape, const lynx_param
         g.block0 = b0;
         g.nblocks = (nb - b0) < kMaxLaunchBlocks ? (nb - b0) : kMaxLaunchBlocks;
         rc = hip_status(launch_quantize((const uint16_t *)kv, g, tab, anchor, residual, gmin,
-                                        gscale, mu, sigma, mode, stream));
+                                        gscale, mu, sigma, mode, p.anchor_bits, stream));
         if (rc)
             return rc;
     }
@@ -266,7 +269,8 @@ int dequant_common(const uint8_t *anchor, const uint8_t *residual, lynx_meta met
         g.block0 = b0;
         g.nblocks = (nb - b0) < kMaxLaunchBlocks ? (nb - b0) : kMaxLaunchBlocks;
         rc = hip_status(launch_dequant(anchor, residual, meta.gamma_min, meta.gamma_scale,
-                                       meta.mu, meta.sigma, g, tab, (uint16_t *)out, stream));
+                                       meta.mu, meta.sigma, g, tab, (uint16_t *)out,
+                                       p.anchor_bits, stream));
         if (rc)
             return rc;
     }
@@ -380,6 +384,7 @@ void lynx_default_params(lynx_params *p) {
     p->page_tokens = kPage;
     p->chunk_tokens = kChunk;
     p->block_channels = kHead;
+    p->anchor_bits = 4;
 }
 
 int64_t lynx_num_blocks(const lynx_kv_shape *shape) {
@@ -391,6 +396,13 @@ int64_t lynx_num_blocks(const lynx_kv_shape *shape) {
 size_t lynx_stream_bytes(const lynx_kv_shape *shape) {
     int64_t nb = lynx_num_blocks(shape);
     return nb < 0 ? 0 : (size_t)nb * (kPage * kHead / 2);
+}
+
+size_t lynx_field_stream_bytes(const lynx_kv_shape *shape, int field_bits) {
+    int64_t nb = lynx_num_blocks(shape);
+    if (nb < 0 || field_bits < 1 || field_bits > 7)
+        return 0;
+    return (size_t)nb * (kPage * kHead / 8) * (size_t)field_bits;
 }
 
 size_t lynx_gamma_floats(const lynx_kv_shape *shape) {
@@ -479,6 +491,8 @@ int lynx_decode_attn_dequant(const void *q, int t_q, int num_q_heads, const uint
     int rc = check_params(p);
     if (rc)
         return rc;
+    if (p.anchor_bits != 4)
+        return LYNX_EINVAL;
     if (head_dim != kHead || !(scale > 0.0f) || !(scale < 1e30f) ||
         (out_dtype != LYNX_OUT_BF16 && out_dtype != LYNX_OUT_F32))
         return LYNX_EINVAL;
@@ -561,6 +575,8 @@ int lynx_split_stream_transfer(const void *kv, const lynx_kv_shape *shape,
     int rc = check_params(p);
     if (rc)
         return rc;
+    if (p.anchor_bits != 4)
+        return LYNX_EINVAL;
     int64_t nb = 0;
     if ((rc = check_shape(shape, &nb)))
         return rc;
@@ -623,7 +639,7 @@ int lynx_split_stream_transfer(const void *kv, const lynx_kv_shape *shape,
         if (!copies_only)
             ok(launch_quantize((const uint16_t *)kv, g, qt, tx.anchor, tx.residual,
                                tx.meta.gamma_min, tx.meta.gamma_scale, tx.meta.mu, tx.meta.sigma,
-                               kModeQuantize, sender));
+                               kModeQuantize, 4, sender));
         ok(hipEventRecord(q[i], sender));
         // anchor queue: anchor + metadata over the wire
         ok(hipStreamWaitEvent(anchor_link, q[i], 0));
@@ -639,7 +655,7 @@ int lynx_split_stream_transfer(const void *kv, const lynx_kv_shape *shape,
         ok(hipStreamWaitEvent(receiver, a[i], 0));
         if (!copies_only)
             ok(launch_dequant(rx.anchor, nullptr, rx.meta.gamma_min, rx.meta.gamma_scale,
-                              rx.meta.mu, rx.meta.sigma, g, dt, (uint16_t *)kv_anchor,
+                              rx.meta.mu, rx.meta.sigma, g, dt, (uint16_t *)kv_anchor, 4,
                               receiver));
         if (i == 0)
             ok(hipEventRecord(t_da0, receiver));
@@ -658,7 +674,8 @@ int lynx_split_stream_transfer(const void *kv, const lynx_kv_shape *shape,
         ok(hipStreamWaitEvent(receiver, r[i], 0));
         if (!copies_only)
             ok(launch_dequant(rx.anchor, rx.residual, rx.meta.gamma_min, rx.meta.gamma_scale,
-                              rx.meta.mu, rx.meta.sigma, g, dt, (uint16_t *)kv_full, receiver));
+                              rx.meta.mu, rx.meta.sigma, g, dt, (uint16_t *)kv_full, 4,
+                              receiver));
     }
     ok(hipEventRecord(t_df, receiver));
     // Blocking: every stream drains before the events go away.

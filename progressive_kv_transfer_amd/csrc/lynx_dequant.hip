@@ -18,6 +18,9 @@
 // four 16-byte runs of the chunk-tiled streams (one per channel pair) and
 // writes 16-byte row pieces that 16 lanes join into one 256-byte row.
 // Workgroups are persistent and build the level table in LDS once.
+// The other splits of the 8-bit code (ABITS anchor bits, 8 - ABITS residual
+// bits) read the lane's fields from the per-(chunk, pair) bit-stream runs:
+// the lane's 16 tokens of a pair are ABITS (8 - ABITS) consecutive dwords.
 #include "lynx_recon.h"
 
 namespace lynx {
@@ -32,13 +35,44 @@ constexpr int kThreads = 256;
 // different entries spread over the LDS banks.
 constexpr int kCopies = 1;
 
-template <bool FULL>
+// Signed level S * L[code] of table entry t for a anchor bits: t's low a
+// bits are the anchor field, the next 8 - a the residual field (full), as
+// signed_level does for a = 4.
+__device__ __forceinline__ float signed_level_bits(const DequantTab &tab, int t, bool full,
+                                                   int abits) {
+    const int bbits = 8 - abits;
+    const int af = t & ((1 << abits) - 1);
+    const int av = af >= (1 << (abits - 1)) ? af - (1 << abits) : af;
+    const int v = av < 0 ? -av - 1 : av;
+    int code = v << bbits;
+    if (full) {
+        const int rf = (t >> abits) & ((1 << bbits) - 1);
+        code -= rf >= (1 << (bbits - 1)) ? rf - (1 << bbits) : rf;
+        code = code < 0 ? 0 : code;
+    }
+    const float m = tab.level[code];
+    return av < 0 ? -m : m;
+}
+
+// W-bit field v of an LSB-first bit stream held in dwords (v a compile-time
+// constant after unrolling).
+template <int W>
+__device__ __forceinline__ uint32_t get_field(const uint32_t *w, int v) {
+    const int pos = W * v, d = pos >> 5, s = pos & 31;
+    uint32_t f = w[d] >> s;
+    if (s + W > 32)
+        f |= w[d + 1] << (32 - s);
+    return f & ((1u << W) - 1u);
+}
+
+template <bool FULL, int ABITS>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(
     const uint8_t *__restrict__ anchor, const uint8_t *__restrict__ residual,
     const float *__restrict__ gmin, const float *__restrict__ gscale,
     const float *__restrict__ mu, const float *__restrict__ sigma, Geometry g,
     const DequantTab tab, uint16_t *__restrict__ out) {
-    constexpr int kLut = FULL ? 256 : 16;
+    constexpr int kBits = 8 - ABITS;
+    constexpr int kLut = FULL ? 256 : (1 << ABITS);
     constexpr int kCop = FULL ? kCopies : 1;
     __shared__ float s_lut[kLut * kCop];
 
@@ -51,7 +85,9 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
     const int tok0 = 64 * wave + 16 * tg;
 
     // Signed level of every (anchor nibble, residual nibble) pair.
-    for (int e = tid; e < kLut * kCop; e += kThreads) s_lut[e] = signed_level(tab, e / kCop, FULL);
+    for (int e = tid; e < kLut * kCop; e += kThreads)
+        s_lut[e] = ABITS == 4 ? signed_level(tab, e / kCop, FULL)
+                              : signed_level_bits(tab, e / kCop, FULL, ABITS);
     __syncthreads();
     const float *lut = s_lut + (lane % kCop);
 
@@ -67,15 +103,36 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
         // Chunk-tiled streams: the 16 bytes of channel pair 4 cg + k for the
         // lane's 16 tokens sit at [chunk j][pair][16 (tg & 1)].  Each
         // 128-byte line of a tile is read in four 16-byte pieces by
-        // successive loads, so these are ordinary (cached) loads.
-        const int64_t coff = b * (kPage * kHead / 2) + j * (kHead / 2 * kChunk) +
-                             (4 * cg) * kChunk + 16 * (tg & 1);
+        // successive loads, so these are ordinary (cached) loads.  Other
+        // splits: the pair's run of 8 w bytes, dwords w (tg & 1) .. + w - 1.
         u32x4 A[4], R[4];
+        uint32_t Aw[4][ABITS == 4 ? 1 : ABITS], Rw[4][ABITS == 4 ? 1 : kBits];
+        if constexpr (ABITS == 4) {
+            const int64_t coff = b * (kPage * kHead / 2) + j * (kHead / 2 * kChunk) +
+                                 (4 * cg) * kChunk + 16 * (tg & 1);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            A[k] = *((const u32x4 *)(anchor + coff + k * kChunk));
-            if (FULL)
-                R[k] = *((const u32x4 *)(residual + coff + k * kChunk));
+            for (int k = 0; k < 4; ++k) {
+                A[k] = *((const u32x4 *)(anchor + coff + k * kChunk));
+                if (FULL)
+                    R[k] = *((const u32x4 *)(residual + coff + k * kChunk));
+            }
+        } else {
+            const uint32_t *ar = (const uint32_t *)(anchor + b * (kPage * kHead / 8 * ABITS) +
+                                                    (int64_t)(j * (kHead / 2) + 4 * cg) *
+                                                        (8 * ABITS)) +
+                                 ABITS * (tg & 1);
+            const uint32_t *rr = (const uint32_t *)(residual + b * (kPage * kHead / 8 * kBits) +
+                                                    (int64_t)(j * (kHead / 2) + 4 * cg) *
+                                                        (8 * kBits)) +
+                                 kBits * (tg & 1);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+#pragma unroll
+                for (int d = 0; d < ABITS; ++d) Aw[k][d] = ar[k * 2 * ABITS + d];
+                if (FULL)
+#pragma unroll
+                    for (int d = 0; d < kBits; ++d) Rw[k][d] = rr[k * 2 * kBits + d];
+            }
         }
         const float4 *gm4 = (const float4 *)(gmin + b * kHead + cg * 8);
         const float4 *gs4 = (const float4 *)(gscale + b * kHead + cg * 8);
@@ -97,7 +154,9 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
             uint32_t ev[4], od[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                if (FULL) {
+                if (ABITS != 4) {
+                    ev[k] = od[k] = 0u;
+                } else if (FULL) {
                     ev[k] = (A[k][h] & 0x0f0f0f0fu) | ((R[k][h] << 4) & 0xf0f0f0f0u);
                     od[k] = ((A[k][h] >> 4) & 0x0f0f0f0fu) | (R[k][h] & 0xf0f0f0f0u);
                 } else {
@@ -113,7 +172,16 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
 #pragma unroll
                     for (int o = 0; o < 2; ++o) {
                         const int e = 2 * k + o;
-                        uint32_t idx = ((o ? od[k] : ev[k]) >> (8 * i)) & 0xffu;
+                        uint32_t idx;
+                        if constexpr (ABITS == 4) {
+                            idx = ((o ? od[k] : ev[k]) >> (8 * i)) & 0xffu;
+                        } else {
+                            // field of token 4h + i, channel 2k + o of the run
+                            const int v = 2 * (4 * h + i) + o;
+                            idx = get_field<ABITS>(Aw[k], v);
+                            if (FULL)
+                                idx |= get_field<kBits>(Rw[k], v) << ABITS;
+                        }
                         y[e] = reconstruct(lut[idx * kCop], d2[e], um[e], d1[e], gm[e]);
                     }
                 }
@@ -131,39 +199,49 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
 
 }  // namespace
 
-static int resident_workgroups(const void *kernel, int slot) {
-    static int cache[64][2];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
-        return 1024;
-    if (cache[dev][slot] == 0) {
-        int cus = 0, per_cu = 0;
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0);
-        cache[dev][slot] = (cus > 0 ? cus : 256) * (per_cu > 0 ? per_cu : 1);
-    }
-    return cache[dev][slot];
+template <bool FULL, int ABITS>
+static hipError_t launch_one(const uint8_t *anchor, const uint8_t *residual,
+                             const float *gmin, const float *gscale, const float *mu,
+                             const float *sigma, const Geometry &g, const DequantTab &tab,
+                             uint16_t *out, hipStream_t stream) {
+    Geometry gl = g;
+    gl.grid_wgs = g.nblocks;
+    hipLaunchKernelGGL((dequant_kernel<FULL, ABITS>), dim3((unsigned)gl.grid_wgs),
+                       dim3(kThreads), 0, stream, anchor, residual, gmin, gscale, mu, sigma, gl,
+                       tab, out);
+    return hipGetLastError();
+}
+
+template <int ABITS>
+static hipError_t launch_split(const uint8_t *anchor, const uint8_t *residual,
+                               const float *gmin, const float *gscale, const float *mu,
+                               const float *sigma, const Geometry &g, const DequantTab &tab,
+                               uint16_t *out, hipStream_t stream) {
+    if (residual)
+        return launch_one<true, ABITS>(anchor, residual, gmin, gscale, mu, sigma, g, tab, out,
+                                       stream);
+    return launch_one<false, ABITS>(anchor, residual, gmin, gscale, mu, sigma, g, tab, out,
+                                    stream);
 }
 
 hipError_t launch_dequant(const uint8_t *anchor, const uint8_t *residual, const float *gmin,
                           const float *gscale, const float *mu, const float *sigma,
                           const Geometry &g, const DequantTab &tab, uint16_t *out,
-                          hipStream_t stream) {
+                          int anchor_bits, hipStream_t stream) {
     if (g.nblocks == 0)
         return hipSuccess;
-    const void *kern = residual ? (const void *)dequant_kernel<true>
-                                : (const void *)dequant_kernel<false>;
-    const int64_t res = resident_workgroups(kern, residual ? 1 : 0);
-    Geometry gl = g;
-    gl.grid_wgs = g.nblocks;
-    dim3 grid((unsigned)gl.grid_wgs), block(kThreads);
-    if (residual)
-        hipLaunchKernelGGL(dequant_kernel<true>, grid, block, 0, stream, anchor, residual, gmin,
-                           gscale, mu, sigma, gl, tab, out);
-    else
-        hipLaunchKernelGGL(dequant_kernel<false>, grid, block, 0, stream, anchor, residual,
-                           gmin, gscale, mu, sigma, gl, tab, out);
-    return hipGetLastError();
+    switch (anchor_bits) {
+    case 3:
+        return launch_split<3>(anchor, residual, gmin, gscale, mu, sigma, g, tab, out, stream);
+    case 4:
+        return launch_split<4>(anchor, residual, gmin, gscale, mu, sigma, g, tab, out, stream);
+    case 5:
+        return launch_split<5>(anchor, residual, gmin, gscale, mu, sigma, g, tab, out, stream);
+    case 6:
+        return launch_split<6>(anchor, residual, gmin, gscale, mu, sigma, g, tab, out, stream);
+    default:
+        return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace lynx

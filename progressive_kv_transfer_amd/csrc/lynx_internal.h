@@ -12,7 +12,12 @@ constexpr int kPage = 256;      // P: tokens per page block
 constexpr int kChunk = 32;      // C: tokens per chunk
 constexpr int kHead = 128;      // H: channels per page block
 constexpr int kChunks = kPage / kChunk;
-constexpr int kCodeMax = 120;   // largest code whose anchor fits 4 bits
+// Splits of the 8-bit code: a anchor bits and 8 - a residual bits (the
+// paper's split is a = 4).  The largest code whose anchor magnitude
+// (code + 2^(7-a) - 1) >> (8 - a) fits a two's-complement bits is
+// 128 - 2^(7-a) (120 for a = 4).
+constexpr int kMinAnchorBits = 3, kMaxAnchorBits = 6;
+constexpr int code_max_of(int anchor_bits) { return 128 - (1 << (7 - anchor_bits)); }
 constexpr int kMaxBuckets = 1792;  // 14 KiB: with the 32 KiB stage, 3 workgroups per CU
 
 // Compander tables, built once per (alpha, code_scale) on the host and
@@ -58,12 +63,13 @@ enum StatsMode : int { kModeQuantize = 0, kModePageStats = 1, kModeBlockStats = 
 
 hipError_t launch_quantize(const uint16_t *kv, const Geometry &g, const QuantTab &tab,
                            uint8_t *anchor, uint8_t *residual, float *gmin, float *gscale,
-                           float *mu, float *sigma, int mode, hipStream_t stream);
+                           float *mu, float *sigma, int mode, int anchor_bits,
+                           hipStream_t stream);
 
 hipError_t launch_dequant(const uint8_t *anchor, const uint8_t *residual, const float *gmin,
                           const float *gscale, const float *mu, const float *sigma,
                           const Geometry &g, const DequantTab &tab, uint16_t *out,
-                          hipStream_t stream);
+                          int anchor_bits, hipStream_t stream);
 
 // Argument block of the fused dequant + attention kernels.
 struct AttnArgs {

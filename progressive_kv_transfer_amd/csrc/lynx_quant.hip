@@ -82,9 +82,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base) {
                                              0x00020000);
 }
 
+// OR a W-bit field into an LSB-first bit stream held in dwords, at field
+// index v (bit W v); v is a compile-time constant after unrolling.
+template <int W>
+__device__ __forceinline__ void put_field(uint32_t *w, int v, uint32_t f) {
+    const int pos = W * v, d = pos >> 5, s = pos & 31;
+    w[d] |= f << s;
+    if (s + W > 32)
+        w[d + 1] |= f >> (32 - s);
+}
+
 // SH16: the compander buckets are the upper 16 bits of the magnitude, so the
-// table address is one v_mad_u32_u16 (high half x 8 + base).
-template <int MODE, bool SH16>
+// table address is one v_mad_u32_u16 (high half x 8 + base).  ABITS: width
+// of the anchor field (4 = the paper's split; the residual has 8 - ABITS).
+template <int MODE, bool SH16, int ABITS>
 __global__ __launch_bounds__(kThreads) void quant_kernel(
     const uint16_t *__restrict__ kv, Geometry g, const QuantTab tab,
     uint8_t *__restrict__ anchor, uint8_t *__restrict__ residual, float *__restrict__ gmin_io,
@@ -98,8 +109,11 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
     __shared__ uint32_t s_stage[kDepth][kWaves][kChunk * kPairs];
 
     // Global stores every wave issues per block after its staging loads:
-    // mu and sigma (2), then the anchor and residual words (4).  Page
-    // statistics alone store from waves 0 and 1 only.
+    // mu and sigma (2), then at least 4 for the anchor and residual words
+    // (4 with the paper's split, 8 with the others).  Page statistics alone
+    // store from waves 0 and 1 only.
+    constexpr int kBits = 8 - ABITS;              // residual field width
+    constexpr uint32_t kBias = (1u << (kBits - 1)) - 1u;  // Stage 4 bias (+7 at 4 + 4)
     constexpr int kStoresAfterStage =
         MODE == kModeQuantize ? 6 : MODE == kModeBlockStats ? 2 : 0;
     const int tid = (int)__builtin_amdgcn_workitem_id_x();
@@ -111,7 +125,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
     if (MODE == kModeQuantize) {
         for (int i = tid; i < tab.nbuckets; i += kThreads) {
             uint32_t c = tab.bucket_code[i];
-            s_tab[i] = u32x2{__float_as_uint(tab.thr[c + 1]), c + 7u};
+            s_tab[i] = u32x2{__float_as_uint(tab.thr[c + 1]), c + kBias};
         }
     }
     typedef __attribute__((address_space(3))) const u32x2 lds_u32x2;
@@ -339,58 +353,94 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
         // since that bucket starts below the first threshold, and
         // non-finite inputs stay inside the table).  The bucket offset is
         // folded into the LDS base address.
-        u32x4 av[2], rv[2];
+        // J = code + bias of Stage 4 for one quotient.
+        auto code_j = [&](float xq) {
+            float m = __builtin_amdgcn_fmed3f(fabsf(xq), mag_lo, 1.0f);
+            uint32_t mb = __float_as_uint(m);
+            uint32_t addr;
+            if (SH16)
+                asm("v_mad_u32_u16 %0, %1, 8, %2 op_sel:[1,0,0,0]"
+                    : "=v"(addr) : "v"(mb), "s"(tab_base));
+            else
+                asm("v_lshl_add_u32 %0, %1, 3, %2" : "=v"(addr) : "v"(mb >> sh), "s"(tab_base));
+            u32x2 ent = *(lds_u32x2 *)(uintptr_t)addr;
+            return ent[1] + (mb >= ent[0] ? 1u : 0u);
+        };
+        if constexpr (ABITS == 4) {
+            u32x4 av[2], rv[2];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {  // tokens 4q .. 4q+3
-            uint32_t J[4][2];
+            for (int q = 0; q < 8; ++q) {  // tokens 4q .. 4q+3
+                uint32_t J[4][2];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
+                for (int k = 0; k < 4; ++k)
+#pragma unroll
+                    for (int e = 0; e < 2; ++e)
+                        // J = code + 7: high nibble = anchor magnitude
+                        // (code + 7) >> 4, low nibble ^ 7 = residual (-code) mod 16.
+                        J[k][e] = code_j(x[4 * q + k][e]);
+                // byte k of w0 / w1 = J of channel 2p / 2p+1 at token 4q + k
+                uint32_t w0 = J[0][0] | (J[1][0] << 8) | (J[2][0] << 16) | (J[3][0] << 24);
+                uint32_t w1 = J[0][1] | (J[1][1] << 8) | (J[2][1] << 16) | (J[3][1] << 24);
+                uint32_t a = ((w0 >> 4) & 0x0f0f0f0fu) | (w1 & 0xf0f0f0f0u);
+                uint32_t r = ((w0 & 0x0f0f0f0fu) | ((w1 << 4) & 0xf0f0f0f0u)) ^ 0x77777777u;
+                // Sign bits of the quotients replicated to bytes (v_perm
+                // selectors 9 and 11), then to nibbles: the anchor of a
+                // negative value is the one's complement of its magnitude
+                // (-V - 1).
+                const uint32_t *xa = (const uint32_t *)x[4 * q];
+                const uint32_t *xb = (const uint32_t *)x[4 * q + 1];
+                const uint32_t *xc = (const uint32_t *)x[4 * q + 2];
+                const uint32_t *xd = (const uint32_t *)x[4 * q + 3];
+                uint32_t n0 = __builtin_amdgcn_perm(xb[0], xa[0], 0x0c0c0b09u) |
+                              __builtin_amdgcn_perm(xd[0], xc[0], 0x0b090c0cu);
+                uint32_t n1 = __builtin_amdgcn_perm(xb[1], xa[1], 0x0c0c0b09u) |
+                              __builtin_amdgcn_perm(xd[1], xc[1], 0x0b090c0cu);
+                a ^= (n0 & 0x0f0f0f0fu) | (n1 & 0xf0f0f0f0u);
+                av[q >> 2][q & 3] = a;
+                rv[q >> 2][q & 3] = r;
+            }
+            // 32 contiguous bytes per stream: [chunk j][pair][token of chunk]
+            const int64_t coff = b * (kPage * kHead / 2) + j * (kHead / 2 * kChunk) +
+                                 p * kChunk;
+            u32x4 *ao = (u32x4 *)(anchor + coff);
+            u32x4 *ro = (u32x4 *)(residual + coff);
+            // Ordinary stores: the streams are read again by the dequant kernels.
+            ao[0] = av[0];
+            ao[1] = av[1];
+            ro[0] = rv[0];
+            ro[1] = rv[1];
+        } else {
+            // Other splits: field 2 i + e (token i, channel 2p + e) of the
+            // lane's run at bit w (2 i + e); the anchor field is the
+            // magnitude J >> b, one's-complemented for a negative quotient,
+            // the residual (J ^ bias) mod 2^b = (-code) mod 2^b.
+            constexpr uint32_t kMaskA = (1u << ABITS) - 1u, kMaskR = (1u << kBits) - 1u;
+            uint32_t aw[2 * ABITS], rw[2 * kBits];
+#pragma unroll
+            for (int d = 0; d < 2 * ABITS; ++d) aw[d] = 0u;
+#pragma unroll
+            for (int d = 0; d < 2 * kBits; ++d) rw[d] = 0u;
+#pragma unroll
+            for (int i = 0; i < kChunk; ++i)
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
-                    float m = __builtin_amdgcn_fmed3f(fabsf(x[4 * q + k][e]), mag_lo, 1.0f);
-                    uint32_t mb = __float_as_uint(m);
-                    uint32_t addr;
-                    if (SH16)
-                        asm("v_mad_u32_u16 %0, %1, 8, %2 op_sel:[1,0,0,0]"
-                            : "=v"(addr) : "v"(mb), "s"(tab_base));
-                    else
-                        asm("v_lshl_add_u32 %0, %1, 3, %2" : "=v"(addr) : "v"(mb >> sh), "s"(tab_base));
-                    u32x2 ent = *(lds_u32x2 *)(uintptr_t)addr;
-                    // J = code + 7: high nibble = anchor magnitude
-                    // (code + 7) >> 4, low nibble ^ 7 = residual (-code) mod 16.
-                    J[k][e] = ent[1] + (mb >= ent[0] ? 1u : 0u);
+                    const uint32_t J = code_j(x[i][e]);
+                    const uint32_t neg = (uint32_t)((int32_t)__float_as_uint(x[i][e]) >> 31);
+                    put_field<ABITS>(aw, 2 * i + e, ((J >> kBits) ^ neg) & kMaskA);
+                    put_field<kBits>(rw, 2 * i + e, (J ^ kBias) & kMaskR);
                 }
-            }
-            // byte k of w0 / w1 = J of channel 2p / 2p+1 at token 4q + k
-            uint32_t w0 = J[0][0] | (J[1][0] << 8) | (J[2][0] << 16) | (J[3][0] << 24);
-            uint32_t w1 = J[0][1] | (J[1][1] << 8) | (J[2][1] << 16) | (J[3][1] << 24);
-            uint32_t a = ((w0 >> 4) & 0x0f0f0f0fu) | (w1 & 0xf0f0f0f0u);
-            uint32_t r = ((w0 & 0x0f0f0f0fu) | ((w1 << 4) & 0xf0f0f0f0u)) ^ 0x77777777u;
-            // Sign bits of the quotients replicated to bytes (v_perm
-            // selectors 9 and 11), then to nibbles: the anchor of a negative
-            // value is the one's complement of its magnitude (-V - 1).
-            const uint32_t *xa = (const uint32_t *)x[4 * q];
-            const uint32_t *xb = (const uint32_t *)x[4 * q + 1];
-            const uint32_t *xc = (const uint32_t *)x[4 * q + 2];
-            const uint32_t *xd = (const uint32_t *)x[4 * q + 3];
-            uint32_t n0 = __builtin_amdgcn_perm(xb[0], xa[0], 0x0c0c0b09u) |
-                          __builtin_amdgcn_perm(xd[0], xc[0], 0x0b090c0cu);
-            uint32_t n1 = __builtin_amdgcn_perm(xb[1], xa[1], 0x0c0c0b09u) |
-                          __builtin_amdgcn_perm(xd[1], xc[1], 0x0b090c0cu);
-            a ^= (n0 & 0x0f0f0f0fu) | (n1 & 0xf0f0f0f0u);
-            av[q >> 2][q & 3] = a;
-            rv[q >> 2][q & 3] = r;
+            // Run of 8 w bytes per (chunk, pair), 4096 w bytes per block.
+            const int64_t aoff = b * (kPage * kHead / 8 * ABITS) +
+                                 (int64_t)(j * (kHead / 2) + p) * (8 * ABITS);
+            const int64_t roff = b * (kPage * kHead / 8 * kBits) +
+                                 (int64_t)(j * (kHead / 2) + p) * (8 * kBits);
+            u32x2 *ao = (u32x2 *)(anchor + aoff);
+            u32x2 *ro = (u32x2 *)(residual + roff);
+#pragma unroll
+            for (int d = 0; d < ABITS; ++d) ao[d] = u32x2{aw[2 * d], aw[2 * d + 1]};
+#pragma unroll
+            for (int d = 0; d < kBits; ++d) ro[d] = u32x2{rw[2 * d], rw[2 * d + 1]};
         }
-        // 32 contiguous bytes per stream: [chunk j][pair][token of chunk]
-        const int64_t coff = b * (kPage * kHead / 2) + j * (kHead / 2 * kChunk) +
-                             p * kChunk;
-        u32x4 *ao = (u32x4 *)(anchor + coff);
-        u32x4 *ro = (u32x4 *)(residual + coff);
-        // Ordinary stores: the streams are read again by the dequant kernels.
-        ao[0] = av[0];
-        ao[1] = av[1];
-        ro[0] = rv[0];
-        ro[1] = rv[1];
     }
 }
 
@@ -398,7 +448,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
 
 // Workgroups resident on the device (per kernel variant), cached per device.
 static int resident_workgroups(const void *kernel, int slot, int threads) {
-    static int cache[64][4];
+    static int cache[64][10];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
         return 1024;
@@ -411,39 +461,64 @@ static int resident_workgroups(const void *kernel, int slot, int threads) {
     return cache[dev][slot];
 }
 
-template <int MODE, bool SH16>
+template <int MODE, bool SH16, int ABITS>
 static hipError_t launch_variant(int slot, const uint16_t *kv, const Geometry &g,
                                  const QuantTab &tab, uint8_t *anchor, uint8_t *residual,
                                  float *gmin, float *gscale, float *mu, float *sigma,
                                  hipStream_t stream) {
     const int64_t units = g.nblocks;
     const int64_t res =
-        resident_workgroups((const void *)quant_kernel<MODE, SH16>, slot, kThreads);
+        resident_workgroups((const void *)quant_kernel<MODE, SH16, ABITS>, slot, kThreads);
     Geometry gl = g;
     gl.grid_wgs = units < res ? units : res;
-    hipLaunchKernelGGL((quant_kernel<MODE, SH16>), dim3((unsigned)gl.grid_wgs), dim3(kThreads),
-                       0, stream, kv, gl, tab, anchor, residual, gmin, gscale, mu, sigma);
+    hipLaunchKernelGGL((quant_kernel<MODE, SH16, ABITS>), dim3((unsigned)gl.grid_wgs),
+                       dim3(kThreads), 0, stream, kv, gl, tab, anchor, residual, gmin, gscale,
+                       mu, sigma);
     return hipGetLastError();
+}
+
+template <int ABITS>
+static hipError_t launch_split(int slot, const uint16_t *kv, const Geometry &g,
+                               const QuantTab &tab, uint8_t *anchor, uint8_t *residual,
+                               float *gmin, float *gscale, float *mu, float *sigma,
+                               hipStream_t stream) {
+    if (tab.shift == 16)
+        return launch_variant<kModeQuantize, true, ABITS>(slot, kv, g, tab, anchor, residual,
+                                                          gmin, gscale, mu, sigma, stream);
+    return launch_variant<kModeQuantize, false, ABITS>(slot + 1, kv, g, tab, anchor, residual,
+                                                       gmin, gscale, mu, sigma, stream);
 }
 
 hipError_t launch_quantize(const uint16_t *kv, const Geometry &g, const QuantTab &tab,
                            uint8_t *anchor, uint8_t *residual, float *gmin, float *gscale,
-                           float *mu, float *sigma, int mode, hipStream_t stream) {
+                           float *mu, float *sigma, int mode, int anchor_bits,
+                           hipStream_t stream) {
     if (g.nblocks == 0)
         return hipSuccess;
     switch (mode) {
     case kModeQuantize:
-        if (tab.shift == 16)
-            return launch_variant<kModeQuantize, true>(0, kv, g, tab, anchor, residual, gmin,
-                                                       gscale, mu, sigma, stream);
-        return launch_variant<kModeQuantize, false>(1, kv, g, tab, anchor, residual, gmin,
-                                                    gscale, mu, sigma, stream);
+        switch (anchor_bits) {
+        case 3:
+            return launch_split<3>(4, kv, g, tab, anchor, residual, gmin, gscale, mu, sigma,
+                                   stream);
+        case 4:
+            return launch_split<4>(0, kv, g, tab, anchor, residual, gmin, gscale, mu, sigma,
+                                   stream);
+        case 5:
+            return launch_split<5>(6, kv, g, tab, anchor, residual, gmin, gscale, mu, sigma,
+                                   stream);
+        case 6:
+            return launch_split<6>(8, kv, g, tab, anchor, residual, gmin, gscale, mu, sigma,
+                                   stream);
+        default:
+            return hipErrorInvalidValue;
+        }
     case kModePageStats:
-        return launch_variant<kModePageStats, false>(2, kv, g, tab, anchor, residual, gmin,
-                                                     gscale, mu, sigma, stream);
+        return launch_variant<kModePageStats, false, 4>(2, kv, g, tab, anchor, residual, gmin,
+                                                        gscale, mu, sigma, stream);
     default:
-        return launch_variant<kModeBlockStats, false>(3, kv, g, tab, anchor, residual, gmin,
-                                                      gscale, mu, sigma, stream);
+        return launch_variant<kModeBlockStats, false, 4>(3, kv, g, tab, anchor, residual, gmin,
+                                                         gscale, mu, sigma, stream);
     }
 }
 

@@ -32,7 +32,8 @@ class LynxError(RuntimeError):
 class lynx_params(ctypes.Structure):
     _fields_ = [("alpha", ctypes.c_float), ("eps", ctypes.c_float),
                 ("code_scale", ctypes.c_float), ("page_tokens", ctypes.c_int32),
-                ("chunk_tokens", ctypes.c_int32), ("block_channels", ctypes.c_int32)]
+                ("chunk_tokens", ctypes.c_int32), ("block_channels", ctypes.c_int32),
+                ("anchor_bits", ctypes.c_int32)]
 
 
 class lynx_kv_shape(ctypes.Structure):
@@ -61,6 +62,7 @@ TRANSFER_COPIES_ONLY = 1
 
 # Every symbol include/lynx.h declares.
 EXPORTS = ["lynx_default_params", "lynx_num_blocks", "lynx_stream_bytes",
+           "lynx_field_stream_bytes",
            "lynx_gamma_floats", "lynx_chunk_floats", "lynx_kv_bytes",
            "lynx_status_string", "lynx_compander_thresholds", "lynx_quantize_pages", "lynx_dequant_anchor",
            "lynx_dequant_full", "lynx_page_stats", "lynx_block_stats",
@@ -89,6 +91,8 @@ def lib():
         for f in ("lynx_stream_bytes", "lynx_gamma_floats", "lynx_chunk_floats"):
             getattr(L, f).argtypes = [P(lynx_kv_shape)]
             getattr(L, f).restype = ctypes.c_size_t
+        L.lynx_field_stream_bytes.argtypes = [P(lynx_kv_shape), i32]
+        L.lynx_field_stream_bytes.restype = ctypes.c_size_t
         L.lynx_kv_bytes.argtypes = [i64] * 5
         L.lynx_kv_bytes.restype = ctypes.c_uint64
         L.lynx_compander_thresholds.argtypes = [P(lynx_params), vp]
@@ -130,11 +134,18 @@ def _check(fn, rc):
         raise LynxError(fn, rc, lib().lynx_status_string(rc).decode())
 
 
-def params(alpha=255.0, eps=1e-6, code_scale=120.0) -> lynx_params:
+def params(alpha=255.0, eps=1e-6, code_scale=120.0, anchor_bits=4) -> lynx_params:
+    """Method parameters; anchor_bits = width of the anchor field (4 = the
+    paper's split, 3..6 for the other splits of the 8-bit code)."""
     p = lynx_params()
     lib().lynx_default_params(ctypes.byref(p))
-    p.alpha, p.eps, p.code_scale = alpha, eps, code_scale
+    p.alpha, p.eps, p.code_scale, p.anchor_bits = alpha, eps, code_scale, anchor_bits
     return p
+
+
+def code_max(anchor_bits: int = 4) -> int:
+    """Largest code of the split: 128 - 2^(7 - anchor_bits) (120 for 4 + 4)."""
+    return 128 - (1 << (7 - anchor_bits))
 
 
 def shape_of(kv: torch.Tensor) -> lynx_kv_shape:
@@ -197,13 +208,17 @@ class Codes:
                 self.sigma)
 
 
-def alloc_codes(nblocks: int, device, pin_memory: bool = False) -> Codes:
+def alloc_codes(nblocks: int, device, pin_memory: bool = False, anchor_bits: int = 4) -> Codes:
     """Code buffers for nblocks page blocks on `device`; on the CPU with
-    pin_memory=True they are pinned host memory (a transfer's wire)."""
+    pin_memory=True they are pinned host memory (a transfer's wire).  The
+    streams hold [block][chunk][channel pair][run of 8 w bytes] with
+    w = anchor_bits for the anchor, 8 - anchor_bits for the residual (for
+    w = 4 the run is the pair's 32 tokens, one byte each)."""
     u8 = dict(dtype=torch.uint8, device=device, pin_memory=pin_memory)
     f32 = dict(dtype=torch.float32, device=device, pin_memory=pin_memory)
-    tile = (nblocks, PAGE_TOKENS // CHUNK_TOKENS, BLOCK_CHANNELS // 2, CHUNK_TOKENS)
-    return Codes(torch.empty(tile, **u8), torch.empty(tile, **u8),
+    tile = (nblocks, PAGE_TOKENS // CHUNK_TOKENS, BLOCK_CHANNELS // 2)
+    return Codes(torch.empty(tile + (8 * anchor_bits,), **u8),
+                 torch.empty(tile + (8 * (8 - anchor_bits),), **u8),
                  torch.empty((nblocks, BLOCK_CHANNELS), **f32),
                  torch.empty((nblocks, BLOCK_CHANNELS), **f32),
                  torch.empty((nblocks, PAGE_TOKENS // CHUNK_TOKENS, BLOCK_CHANNELS), **f32),
@@ -230,7 +245,8 @@ def quantize_pages(kv: torch.Tensor, p: lynx_params | None = None,
         raise ValueError("KV must be bfloat16")
     sh = shape_of(kv)
     nb = num_blocks(sh)
-    codes = out if out is not None else alloc_codes(nb, kv.device)
+    codes = out if out is not None else alloc_codes(nb, kv.device,
+                                                    anchor_bits=p.anchor_bits if p else 4)
     _check("lynx_quantize_pages", lib().lynx_quantize_pages(
         kv.data_ptr(), ctypes.byref(sh), ctypes.byref(p) if p else None,
         codes.anchor.data_ptr(), codes.residual.data_ptr(), codes.meta(), _stream(stream)))

@@ -312,3 +312,39 @@ def test_spec_verify_workspace_and_errors():
         rc = L.lynx_spec_verify(a["d"], a["t"], a["s"], a["u"], a["us"], a["T"], a["V"],
                                 a["out"], a["w"], a["wb"], None)
         assert rc == e, (c, rc)
+
+
+def test_split_parameters_and_stream_sizes():
+    """anchor_bits: default 4, 3..6 accepted by the codec calls, rejected by
+    attention and the transfer; the compander clips at 128 - 2^(7 - a);
+    field streams take 4096 x bits bytes per block."""
+    L = lynx.lib()
+    p = lynx.params()
+    assert p.anchor_bits == 4
+    sh = lynx.lynx_kv_shape(1, 256 * 128, 256, 128, 128)
+    assert L.lynx_stream_bytes(ctypes.byref(sh)) == 16384
+    for bits_ in range(1, 8):
+        assert L.lynx_field_stream_bytes(ctypes.byref(sh), bits_) == 4096 * bits_
+    assert L.lynx_field_stream_bytes(ctypes.byref(sh), 0) == 0
+    assert L.lynx_field_stream_bytes(ctypes.byref(sh), 8) == 0
+    thr = np.zeros(128, np.float32)
+    for a, top in ((3, 112), (4, 120), (5, 124), (6, 126)):
+        q = lynx.params(code_scale=127.0, anchor_bits=a)
+        assert L.lynx_compander_thresholds(ctypes.byref(q), thr.ctypes.data) == 0
+        assert np.isfinite(thr[top]) and np.all(np.isinf(thr[top + 1:])), a
+        assert lynx.code_max(a) == top
+    for a in (2, 7, 0):
+        q = lynx.params(anchor_bits=a)
+        assert L.lynx_compander_thresholds(ctypes.byref(q), thr.ctypes.data) == -1
+        assert L.lynx_quantize_pages(FAKE, ctypes.byref(sh), ctypes.byref(q), FAKE, FAKE,
+                                     lynx.lynx_meta(FAKE, FAKE, FAKE, FAKE), None) == -1
+    q5 = lynx.params(anchor_bits=5)
+    m = lynx.lynx_meta(FAKE, FAKE, FAKE, FAKE)
+    assert L.lynx_decode_attn_dequant(FAKE, 1, 8, FAKE, FAKE, m, FAKE, FAKE, m, 256, 1, 128,
+                                      0.1, 0, ctypes.byref(q5), FAKE, 0, FAKE, 1 << 20,
+                                      None) == -1
+    c = lynx.lynx_codes(FAKE, FAKE, m)
+    t = lynx.lynx_transfer_times()
+    assert L.lynx_split_stream_transfer(FAKE, ctypes.byref(sh), ctypes.byref(q5), 1, c, c, c,
+                                        FAKE, FAKE, 0, None, None, None, None,
+                                        ctypes.byref(t)) == -1

@@ -87,3 +87,41 @@ def test_vnmse_without_outliers():
     r = measure("decode_attn_32k_plain")
     assert r["lynx"] < r["int8"]
     assert r["lynx"] < 5e-3 and r["lynx_int4"] < 1.0
+
+
+def test_vnmse_of_the_splits():
+    """The other splits of the 8-bit code (anchor bits a = 3, 5, 6 beside the
+    paper's 4), each at its own code range: the attention error of the
+    draft (anchor alone) shrinks as anchor bits are added; the full 8-bit
+    code keeps its small error for every split.  K^, V^ from
+    the GPU dequant, attention by the oracle in binary64; values printed for
+    the record."""
+    cfg = kvgen.CONFIGS["decode_attn_32k"]
+    kv = cfg.make(DEV)
+    ctx, ch = kv.shape[1], kv.shape[2]
+    n_kvh, n_qh = ch // 128, 64
+    scale = 1.0 / math.sqrt(128.0)
+    xb = kvgen.bf16_bits(kv)
+    k_exact, v_exact = xb[0].reshape(ctx, n_kvh, 128), xb[1].reshape(ctx, n_kvh, 128)
+    qs = [kvgen.bf16_bits(kvgen.queries(5100 + s, 1, n_qh, device=DEV)) for s in range(2)]
+    refs = [oracle.attention(q, k_exact, v_exact, scale, False, threads=16) for q in qs]
+    res = {}
+    for a in (3, 4, 5, 6):
+        p = lynx.params(code_scale=float(lynx.code_max(a)), anchor_bits=a)
+        codes = lynx.quantize_pages(kv, p)
+        out = torch.empty_like(kv)
+        for full in (False, True):
+            (lynx.dequant_full if full else lynx.dequant_anchor)(codes, out, p)
+            torch.cuda.synchronize()
+            ob = kvgen.bf16_bits(out)
+            kh, vh = ob[0].reshape(ctx, n_kvh, 128), ob[1].reshape(ctx, n_kvh, 128)
+            res[(a, full)] = float(np.mean([
+                vnmse(oracle.attention(q, kh, vh, scale, False, threads=16), r)
+                for q, r in zip(qs, refs)]))
+    print("[gpu-vnmse] splits (anchor-only, full): " + ", ".join(
+        f"{a}+{8 - a} {res[(a, False)]:.3g} {res[(a, True)]:.3g}" for a in (3, 4, 5, 6)),
+        flush=True)
+    drafts = [res[(a, False)] for a in (3, 4, 5, 6)]
+    assert drafts[0] > drafts[1] > drafts[2] > drafts[3]
+    for a in (3, 4, 5, 6):
+        assert res[(a, True)] < 5e-3
