@@ -66,7 +66,7 @@ constexpr int kStageLoads = kChunk / 4;      // 16-byte loads per wave and block
 
 // Workgroup barrier over LDS traffic only: each wave waits for its own LDS
 // operations, not for its global loads and stores, so the staged loads of
-// the next unit and the stores of the current one stay in flight across it.
+// the next block and the stores of the current one stay in flight across it.
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
     const uint32_t tab_base = (uint32_t)(uintptr_t)(lds_u32x2 *)s_tab -
                               (uint32_t)tab.bucket_lo * (uint32_t)sizeof(u32x2);
     const uint32_t row_bytes = (uint32_t)g.row_stride * 2u;
-    const int64_t nunits = g.nblocks;
+    const int64_t nblocks = g.nblocks;
     // Staging load of lane l: 16 bytes (channels 8 (l % 16) .. + 7) of
     // token row l / 16 of a 4-row group of the wave's chunk.
     const uint32_t voff = (uint32_t)(wave * kChunk + (p >> 4)) * row_bytes +
@@ -172,11 +172,11 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
     const int64_t wg0 = (int64_t)__builtin_amdgcn_workgroup_id_x();
 #pragma unroll
     for (int d = 0; d < kDepth; ++d)
-        if (wg0 + d * g.grid_wgs < nunits)
+        if (wg0 + d * g.grid_wgs < nblocks)
             stage(unit_base(wg0 + d * g.grid_wgs), d);
 
     int n = 0;  // blocks done by this workgroup
-    for (int64_t u = wg0; u < nunits; u += g.grid_wgs, ++n) {
+    for (int64_t u = wg0; u < nblocks; u += g.grid_wgs, ++n) {
         const int64_t b = g.block0 + u;
         const int buf = n % kDepth;
         const int64_t meta0 = b * kHead;
@@ -184,8 +184,8 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
         // Address of the block staged during this one, computed here where
         // few registers are live (the empty asm keeps it from being sunk to
         // its use).
-        const bool has_next = u + g.grid_wgs < nunits;
-        const bool has_ahead = u + kDepth * g.grid_wgs < nunits;
+        const bool has_next = u + g.grid_wgs < nblocks;
+        const bool has_ahead = u + kDepth * g.grid_wgs < nblocks;
         const uint16_t *ahead_base = has_ahead ? unit_base(u + kDepth * g.grid_wgs) : kv;
         asm volatile("" ::"s"(ahead_base));
 
@@ -274,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
             s_ch[tid] = make_float4(gmin, d1, r1, fast ? 0.0f : 1.0f);
         }
         if (MODE == kModePageStats) {
-            lds_barrier();  // s_min is rewritten by the next unit
+            lds_barrier();  // s_min is rewritten by the next block
             continue;
         }
         lds_barrier();
@@ -466,11 +466,10 @@ static hipError_t launch_variant(int slot, const uint16_t *kv, const Geometry &g
                                  const QuantTab &tab, uint8_t *anchor, uint8_t *residual,
                                  float *gmin, float *gscale, float *mu, float *sigma,
                                  hipStream_t stream) {
-    const int64_t units = g.nblocks;
     const int64_t res =
         resident_workgroups((const void *)quant_kernel<MODE, SH16, ABITS>, slot, kThreads);
     Geometry gl = g;
-    gl.grid_wgs = units < res ? units : res;
+    gl.grid_wgs = g.nblocks < res ? g.nblocks : res;
     hipLaunchKernelGGL((quant_kernel<MODE, SH16, ABITS>), dim3((unsigned)gl.grid_wgs),
                        dim3(kThreads), 0, stream, kv, gl, tab, anchor, residual, gmin, gscale,
                        mu, sigma);
