@@ -39,7 +39,7 @@ cache), algorithmic code + metadata bytes per second against the HBM peak,
 and QK + PV flops per second.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-    python bench.py --profile-run      # a few steps only, for rocprofv3
+    python bench.py --profile-run      # the codec steps only, for rocprofv3
     python bench.py --attention-only [--attention-case NAME]   # attention calls only
     python bench.py --copy-probe       # plain 1 GiB copy, PMC scale factor
     python bench.py --hbm-probe        # timed copy / read / write bandwidths
@@ -460,8 +460,8 @@ def main():
     if args.copy_probe or args.hbm_probe:
         copy_probe(timed=args.hbm_probe)
         return
-    if args.profile_run:
-        args.steps, args.warmup, args.no_cpu_baseline = 3, 1, True
+    if args.profile_run:  # the timed steps only (same steps and warm-up)
+        args.no_cpu_baseline = True
 
     import torch
     from progressive_kv_transfer_amd import kvgen, lynx
