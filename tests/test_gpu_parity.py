@@ -5,8 +5,9 @@ Bar: anchor and residual bytes identical; metadata equal as binary32 values
 identical for the anchor-only and the full dequant.  Cases: the single-page
 workload, adversarial pages, strided multi-block sets, other parameters,
 the separately launched statistics kernels, determinism, and the two
-full-size KV workloads (Qwen-32B-shaped at 16K, Qwen3-235B-A22B-shaped at
-128K) on sampled page blocks.
+full-size KV workloads: every page block of the Qwen-32B-shaped set at 16K;
+every block of four layers plus a seeded 1% sample of all blocks of the
+Qwen3-235B-A22B-shaped set at 128K.
 """
 import numpy as np
 import pytest
@@ -167,49 +168,64 @@ def _block_region(b, pages, heads):
     return tensor, slice(page * 256, page * 256 + 256), slice(head * 128, head * 128 + 128)
 
 
-def sampled_check(cfg, nsample, seed):
-    """Full-size workload on the device, sampled blocks against the oracle
-    block routine (first and last blocks always included)."""
+def test_qwen32b_16k_every_block():
+    """The whole Qwen-32B-shaped set (64 layers x K,V x 16384 x 1024, 65536
+    page blocks, 4 GiB bf16): every block's codes, metadata and both
+    reconstructions equal to the oracle's (16 host threads)."""
+    cfg = kvgen.CONFIGS["qwen32b_16k"]
     announce(f"{cfg.name}: generating {cfg.num_tensors} x {cfg.num_tokens} x "
              f"{cfg.num_channels} on the device")
     kv = cfg.make(DEV)
-    announce(f"{cfg.name}: quantize + dequant")
+    announce(f"{cfg.name}: quantize + dequant on the device")
+    codes, out_a, out_f = run_gpu(kv)
+    xb = bits(kv)
+    del kv
+    announce(f"{cfg.name}: oracle on every one of the {xb.size // 32768} blocks")
+    ref = oracle.quantize(xb, threads=16)
+    assert_codes_equal(codes, ref)
+    del codes
+    for out, full in ((out_a, False), (out_f, True)):
+        np.testing.assert_array_equal(bits(out), oracle.dequant(ref, xb.shape, full, threads=16))
+    del out_a, out_f
+    torch.cuda.empty_cache()
+
+
+def test_qwen3_235b_128k_four_layers_and_sample():
+    """The Qwen3-235B-A22B-shaped set (94 layers x K,V x 131072 x 512, 23.5
+    GiB bf16, 385024 blocks) on the device: every block of layers 0, 31, 62
+    and 93 against the oracle, and a seeded 1% sample of all blocks against
+    the oracle's block routine."""
+    cfg = kvgen.CONFIGS["qwen3_235b_128k"]
+    announce(f"{cfg.name}: generating {cfg.num_tensors} x {cfg.num_tokens} x "
+             f"{cfg.num_channels} on the device")
+    kv = cfg.make(DEV)
+    announce(f"{cfg.name}: quantize + dequant on the device")
     codes, out_a, out_f = run_gpu(kv)
     pages, heads = cfg.num_tokens // 256, cfg.num_channels // 128
-    nb = cfg.num_tensors * pages * heads
-    rng = np.random.default_rng(seed)
-    sample = sorted(set([0, 1, nb - 1] + list(rng.choice(nb, nsample, replace=False))))
-    announce(f"{cfg.name}: checking {len(sample)} of {nb} blocks")
+    per_tensor = pages * heads
+    layers = [0, 31, 62, 93]
+    tensors = [2 * l + kv_ for l in layers for kv_ in (0, 1)]
+    announce(f"{cfg.name}: every block of layers {layers}")
+    for t in tensors:
+        xb = bits(kv[t:t + 1])
+        ref = oracle.quantize(xb, threads=16)
+        assert_codes_equal(codes, ref, slice(t * per_tensor, (t + 1) * per_tensor))
+        for out, full in ((out_a, False), (out_f, True)):
+            np.testing.assert_array_equal(bits(out[t:t + 1]),
+                                          oracle.dequant(ref, xb.shape, full, threads=16))
+    nb = cfg.num_tensors * per_tensor
+    rng = np.random.default_rng(12)
+    sample = sorted(set([0, 1, nb - 1] + list(rng.choice(nb, nb // 100, replace=False))))
+    announce(f"{cfg.name}: sampled {len(sample)} of {nb} blocks")
     for b in sample:
         t, rows, cols = _block_region(b, pages, heads)
         xb = bits(kv[t, rows, cols])
         r = oracle.quantize_block(xb)
         np.testing.assert_array_equal(host(codes.anchor[b]), r.anchor)
         np.testing.assert_array_equal(host(codes.residual[b]), r.residual)
-        assert np.array_equal(host(codes.gamma_min[b]), r.gamma_min)
-        assert np.array_equal(host(codes.gamma_scale[b]), r.gamma_scale)
-        assert np.array_equal(host(codes.mu[b]), r.mu)
-        assert np.array_equal(host(codes.sigma[b]), r.sigma)
+        for name in ("gamma_min", "gamma_scale", "mu", "sigma"):
+            assert np.array_equal(host(getattr(codes, name)[b]), getattr(r, name)), (b, name)
         np.testing.assert_array_equal(bits(out_a[t, rows, cols]), oracle.dequant_block(r, False))
         np.testing.assert_array_equal(bits(out_f[t, rows, cols]), oracle.dequant_block(r, True))
     del kv, codes, out_a, out_f
     torch.cuda.empty_cache()
-
-
-def test_qwen32b_16k_full_size_sampled():
-    """64 layers x K,V x 16384 tokens x 1024 channels (4 GiB bf16)."""
-    sampled_check(kvgen.CONFIGS["qwen32b_16k"], 300, 11)
-
-
-def test_qwen3_235b_128k_full_size_sampled():
-    """94 layers x K,V x 131072 tokens x 512 channels (23.5 GiB bf16)."""
-    sampled_check(kvgen.CONFIGS["qwen3_235b_128k"], 300, 12)
-
-
-def test_qwen32b_16k_two_layers_every_block():
-    """Every block of the first and last layer of the 16K workload."""
-    cfg = kvgen.CONFIGS["qwen32b_16k"]
-    announce("qwen32b_16k layers 0 and 63, every block")
-    idx = [0, 1, cfg.num_tensors - 2, cfg.num_tensors - 1]
-    kv = cfg.make(DEV, tensors=idx)
-    full_check(kv)
