@@ -73,28 +73,28 @@ def lib():
             L.oracle_level.restype = f32
             L.oracle_level.argtypes = [i32, f32, f32]
             L.oracle_code_max.restype = i32
-            L.oracle_code_max.argtypes = [i32]
+            L.oracle_code_max.argtypes = [i32, i32]
             L.oracle_split_bits.restype = None
-            L.oracle_split_bits.argtypes = [i32, i32, i32, ctypes.POINTER(i32),
+            L.oracle_split_bits.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32),
                                             ctypes.POINTER(i32), ctypes.POINTER(i32)]
             L.oracle_unsplit_bits.restype = i32
-            L.oracle_unsplit_bits.argtypes = [ctypes.c_uint, i32, ctypes.c_uint, i32,
+            L.oracle_unsplit_bits.argtypes = [ctypes.c_uint, i32, ctypes.c_uint, i32, i32,
                                               ctypes.POINTER(i32)]
             L.oracle_quantize_block_bits.restype = i32
             L.oracle_quantize_block_bits.argtypes = [
-                vp, i64, i32, i32, i32, f32, f32, f32, i32, vp, vp, vp, vp, vp, vp,
+                vp, i64, i32, i32, i32, f32, f32, f32, i32, i32, vp, vp, vp, vp, vp, vp,
                 vp, vp, vp, vp, vp]
             L.oracle_dequant_block_bits.restype = i32
             L.oracle_dequant_block_bits.argtypes = [
-                vp, vp, vp, vp, vp, vp, i32, i32, i32, f32, f32, f32, i32, vp, i64]
+                vp, vp, vp, vp, vp, vp, i32, i32, i32, f32, f32, f32, i32, i32, vp, i64]
             L.oracle_quantize_bits.restype = i32
             L.oracle_quantize_bits.argtypes = [
-                vp, i64, i64, i64, i64, i64, i32, i32, i32, f32, f32, f32, i32,
+                vp, i64, i64, i64, i64, i64, i32, i32, i32, f32, f32, f32, i32, i32,
                 i64, i64, i64, vp, vp, vp, vp, vp, vp]
             L.oracle_dequant_bits.restype = i32
             L.oracle_dequant_bits.argtypes = [
                 vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, i32,
-                f32, f32, f32, i32, i64, i64, i64, vp]
+                f32, f32, f32, i32, i32, i64, i64, i64, vp]
             L.oracle_spec_verify.restype = i32
             L.oracle_spec_verify.argtypes = [vp, vp, vp, vp, f64, i32, i32,
                                              ctypes.POINTER(i32), ctypes.POINTER(i32)]
@@ -129,27 +129,37 @@ def level(k: int, alpha: float = 255.0, code_scale: float = CODE_SCALE) -> float
     return lib().oracle_level(k, alpha, code_scale)
 
 
-def code_max(anchor_bits: int = 4) -> int:
-    """Largest code whose anchor magnitude fits an anchor_bits-bit anchor
-    (a + b = 8): 2^7 - 2^(b-1), 120 for the paper's 4 + 4 split."""
-    return lib().oracle_code_max(anchor_bits)
+def residual_width(anchor_bits: int, residual_bits: int | None) -> int:
+    """Residual field width: 8 - a for a split of the 8-bit code unless given
+    (0 = a single a-bit stream, the paper's Lynx-INT4 / Lynx-INT8)."""
+    return 8 - anchor_bits if residual_bits is None else residual_bits
 
 
-def split(code_c: int, sign: int, anchor_bits: int = 4):
+def code_max(anchor_bits: int = 4, residual_bits: int | None = None) -> int:
+    """Largest code whose anchor magnitude fits an anchor_bits-bit anchor:
+    2^7 - 2^(b-1) for a split (120 for the paper's 4 + 4), 2^(a-1) - 1 for
+    a single stream."""
+    return lib().oracle_code_max(anchor_bits, residual_width(anchor_bits, residual_bits))
+
+
+def split(code_c: int, sign: int, anchor_bits: int = 4, residual_bits: int | None = None):
     """Algorithm 1 Stage 4 on one clipped code: returns (V_mag, Q_res, Q_anc)
     (the paper's 4 + 4 split by default)."""
     v, r, a = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
-    lib().oracle_split_bits(code_c, sign, anchor_bits, ctypes.byref(v), ctypes.byref(r),
-                            ctypes.byref(a))
+    lib().oracle_split_bits(code_c, sign, anchor_bits,
+                            residual_width(anchor_bits, residual_bits), ctypes.byref(v),
+                            ctypes.byref(r), ctypes.byref(a))
     return v.value, r.value, a.value
 
 
-def unsplit(anchor_field: int, residual_field: int | None, anchor_bits: int = 4):
+def unsplit(anchor_field: int, residual_field: int | None, anchor_bits: int = 4,
+            residual_bits: int | None = None):
     """Decoder side of Stage 4: (code, sign) from the anchor field (and the
     residual field for the full code)."""
     s = ctypes.c_int()
     c = lib().oracle_unsplit_bits(anchor_field, residual_field is not None,
-                                  residual_field or 0, anchor_bits, ctypes.byref(s))
+                                  residual_field or 0, anchor_bits,
+                                  residual_width(anchor_bits, residual_bits), ctypes.byref(s))
     return c, s.value
 
 
@@ -158,13 +168,14 @@ def unsplit(anchor_field: int, residual_field: int | None, anchor_bits: int = 4)
 class BlockResult:
     """Outputs of one oracle page block (plus optional intermediates)."""
 
-    def __init__(self, H, P, C, anchor_bits=4):
+    def __init__(self, H, P, C, anchor_bits=4, residual_bits=None):
         nch = P // C
         self.C, self.anchor_bits = C, anchor_bits
+        self.residual_bits = residual_width(anchor_bits, residual_bits)
         # chunk-tiled streams: [chunk][channel pair][run of 2C w-bit fields]
         # (for w = 4: [chunk][channel pair][token of the chunk])
         self.anchor = np.zeros((nch, H // 2, C * anchor_bits // 4), np.uint8)
-        self.residual = np.zeros((nch, H // 2, C * (8 - anchor_bits) // 4), np.uint8)
+        self.residual = np.zeros((nch, H // 2, C * self.residual_bits // 4), np.uint8)
         self.gamma_min = np.zeros(H, np.float32)
         self.gamma_scale = np.zeros(H, np.float32)
         self.mu = np.zeros((nch, H), np.float32)
@@ -177,14 +188,14 @@ class BlockResult:
 
 
 def quantize_block(x_bf16: np.ndarray, alpha=255.0, eps=1e-6, code_scale=CODE_SCALE,
-                   C=C_DEFAULT, anchor_bits=4) -> BlockResult:
+                   C=C_DEFAULT, anchor_bits=4, residual_bits=None) -> BlockResult:
     """Quantize one page block given token-major as uint16 bf16 bits [P][H]."""
     x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
     P, H = x.shape
-    r = BlockResult(H, P, C, anchor_bits)
+    r = BlockResult(H, P, C, anchor_bits, residual_bits)
     rc = lib().oracle_quantize_block_bits(
-        _ptr(x), H, H, P, C, alpha, eps, code_scale, anchor_bits, _ptr(r.anchor),
-        _ptr(r.residual), _ptr(r.gamma_min), _ptr(r.gamma_scale), _ptr(r.mu),
+        _ptr(x), H, H, P, C, alpha, eps, code_scale, anchor_bits, r.residual_bits,
+        _ptr(r.anchor), _ptr(r.residual) if r.residual_bits else None, _ptr(r.gamma_min), _ptr(r.gamma_scale), _ptr(r.mu),
         _ptr(r.sigma), _ptr(r.xn), _ptr(r.xcent), _ptr(r.xfinal),
         _ptr(r.code_raw), _ptr(r.sign))
     if rc:
@@ -194,7 +205,10 @@ def quantize_block(x_bf16: np.ndarray, alpha=255.0, eps=1e-6, code_scale=CODE_SC
 
 def dequant_block(r: BlockResult, full: bool, alpha=255.0, eps=1e-6,
                   code_scale=CODE_SCALE) -> np.ndarray:
-    """Reconstruct a block from its codes: anchor-only or anchor + residual."""
+    """Reconstruct a block from its codes: anchor-only or anchor + residual
+    (a single stream has no residual: its anchor is the whole code)."""
+    if full and not r.residual_bits:
+        raise ValueError("a single-stream code has no residual")
     nch, Hh = r.anchor.shape[:2]
     C = r.C
     P, H = nch * C, Hh * 2
@@ -202,7 +216,7 @@ def dequant_block(r: BlockResult, full: bool, alpha=255.0, eps=1e-6,
     rc = lib().oracle_dequant_block_bits(
         _ptr(r.anchor), _ptr(r.residual) if full else None, _ptr(r.gamma_min),
         _ptr(r.gamma_scale), _ptr(r.mu), _ptr(r.sigma), H, P, C, alpha, eps,
-        code_scale, r.anchor_bits, _ptr(out), H)
+        code_scale, r.anchor_bits, r.residual_bits, _ptr(out), H)
     if rc:
         raise ValueError("oracle_dequant_block_bits rejected the block")
     return out
@@ -213,11 +227,13 @@ def dequant_block(r: BlockResult, full: bool, alpha=255.0, eps=1e-6,
 class Codes:
     """Oracle outputs for a KV set of num_tensors [T][Ch] tensors."""
 
-    def __init__(self, nblocks, H=H_DEFAULT, P=P_DEFAULT, C=C_DEFAULT, anchor_bits=4):
+    def __init__(self, nblocks, H=H_DEFAULT, P=P_DEFAULT, C=C_DEFAULT, anchor_bits=4,
+                 residual_bits=None):
         self.nblocks = nblocks
         self.anchor_bits = anchor_bits
+        self.residual_bits = residual_width(anchor_bits, residual_bits)
         self.anchor = np.zeros((nblocks, P // C, H // 2, C * anchor_bits // 4), np.uint8)
-        self.residual = np.zeros((nblocks, P // C, H // 2, C * (8 - anchor_bits) // 4),
+        self.residual = np.zeros((nblocks, P // C, H // 2, C * self.residual_bits // 4),
                                  np.uint8)
         self.gamma_min = np.zeros((nblocks, H), np.float32)
         self.gamma_scale = np.zeros((nblocks, H), np.float32)
@@ -233,7 +249,8 @@ def _ranges(n, parts):
 
 def quantize(kv: np.ndarray, alpha=255.0, eps=1e-6, code_scale=CODE_SCALE,
              H=H_DEFAULT, P=P_DEFAULT, C=C_DEFAULT, threads=1,
-             blocks: tuple[int, int] | None = None, anchor_bits=4) -> Codes:
+             blocks: tuple[int, int] | None = None, anchor_bits=4,
+             residual_bits=None) -> Codes:
     """Quantize kv (uint16 bf16 bits, shape [num_tensors, T, Ch]).
 
     ``blocks=(b0, b1)`` restricts the work (and the returned arrays) to page
@@ -244,14 +261,15 @@ def quantize(kv: np.ndarray, alpha=255.0, eps=1e-6, code_scale=CODE_SCALE,
     nt, T, Ch = kv.shape
     nblocks = nt * (T // P) * (Ch // H)
     b0, b1 = blocks if blocks is not None else (0, nblocks)
-    out = Codes(b1 - b0, H, P, C, anchor_bits)
+    out = Codes(b1 - b0, H, P, C, anchor_bits, residual_bits)
     L = lib()
 
     def run(r):
         lo, hi = r
         rc = L.oracle_quantize_bits(
             _ptr(kv), nt, T * Ch, T, Ch, Ch, H, P, C, alpha, eps, code_scale,
-            anchor_bits, lo, hi, b0, _ptr(out.anchor), _ptr(out.residual),
+            anchor_bits, out.residual_bits, lo, hi, b0, _ptr(out.anchor),
+            _ptr(out.residual) if out.residual_bits else None,
             _ptr(out.gamma_min), _ptr(out.gamma_scale), _ptr(out.mu),
             _ptr(out.sigma))
         if rc:
@@ -278,6 +296,9 @@ def dequant(codes: Codes, shape, full: bool, alpha=255.0, eps=1e-6,
     nblocks = nt * (T // P) * (Ch // H)
     b0, b1 = blocks if blocks is not None else (0, nblocks)
     assert codes.nblocks == b1 - b0
+    rbits = getattr(codes, "residual_bits", 8 - getattr(codes, "anchor_bits", 4))
+    if full and not rbits:
+        raise ValueError("a single-stream code has no residual")
     out = np.zeros((nt, T, Ch), np.uint16)
     L = lib()
 
@@ -287,7 +308,7 @@ def dequant(codes: Codes, shape, full: bool, alpha=255.0, eps=1e-6,
             _ptr(codes.anchor), _ptr(codes.residual) if full else None,
             _ptr(codes.gamma_min), _ptr(codes.gamma_scale), _ptr(codes.mu),
             _ptr(codes.sigma), nt, T * Ch, T, Ch, Ch, H, P, C, alpha, eps,
-            code_scale, getattr(codes, "anchor_bits", 4), lo, hi, b0, _ptr(out))
+            code_scale, getattr(codes, "anchor_bits", 4), rbits, lo, hi, b0, _ptr(out))
         if rc:
             raise ValueError("oracle_dequant rejected the arguments")
 

@@ -47,7 +47,13 @@
  *     largest one whose anchor magnitude fits a bits, and the fields are
  *     packed as an LSB-first bit stream per (chunk, channel pair): value
  *     2 i + e (token i of the chunk, channel 2k + e) at bit w (2 i + e) of
- *     the pair's C w / 4 bytes.  For a = 4 this is the nibble layout above.
+ *     the pair's C w / 4 bytes.  For a = 4 this is the nibble layout above;
+ *   - the single-precision configurations of the paper's evaluation
+ *     (Lynx-INT4, Lynx-INT8: Algorithm 1 into one stream, no split) are
+ *     one a-bit field per value and no residual (b = 0): the code of
+ *     Eq. (3) with code_scale 2^(a-1) - 1 (7 or 127), its magnitude V = I
+ *     in the field, one's-complemented for a negative value as the anchor
+ *     is; the largest code is 2^(a-1) - 1.
  */
 #include <math.h>
 #include <stdint.h>
@@ -103,16 +109,24 @@ double oracle_code_real(float x_abs, float alpha, float code_scale)
            log1p((double)alpha);
 }
 
-/* Largest code whose anchor magnitude (I + 2^(b-1) - 1) >> b still fits an
- * a-bit two's-complement anchor (magnitude <= 2^(a-1) - 1 for either sign),
- * a + b = 8: 2^7 - 2^(b-1), i.e. 120 for the paper's 4 + 4 split. */
-static int valid_anchor_bits(int a) { return a >= 2 && a <= 7; }
-
-int oracle_code_max(int anchor_bits)
+/* Field widths: a anchor bits and b residual bits, either a split of the
+ * 8-bit code (a + b = 8) or a single stream of a-bit codes (b = 0). */
+static int valid_bits(int a, int b)
 {
-    if (!valid_anchor_bits(anchor_bits))
+    return (a + b == 8 && a >= 2 && a <= 7) || (b == 0 && a >= 2 && a <= 8);
+}
+
+/* Largest code whose anchor magnitude (I + bias) >> b still fits an a-bit
+ * two's-complement anchor (magnitude <= 2^(a-1) - 1 for either sign):
+ * 2^7 - 2^(b-1) for a split (120 for the paper's 4 + 4), 2^(a-1) - 1 for a
+ * single stream. */
+int oracle_code_max(int anchor_bits, int residual_bits)
+{
+    if (!valid_bits(anchor_bits, residual_bits))
         return -1;
-    return 128 - (1 << (8 - anchor_bits - 1));
+    if (residual_bits == 0)
+        return (1 << (anchor_bits - 1)) - 1;
+    return 128 - (1 << (residual_bits - 1));
 }
 
 /* Reconstruction level of code k, the inverse of Eq. (3)
@@ -128,15 +142,17 @@ float oracle_level(int k, float alpha, float code_scale)
 /* ------------------------------------------------------------ Stage 4 -- */
 
 /* Split-stream construction of one clipped code I with sign S (Algorithm
- * 1, Stage 4), for a anchor bits and b = 8 - a residual bits:
+ * 1, Stage 4), for a anchor bits and b residual bits:
  *   I_bias = I + 2^(b-1) - 1;  V_mag = I_bias >> b;  V_recon = V_mag << b;
  *   Q_res = V_recon - I;  Q_anc = V_mag * S + min(S, 0).
- * The paper's split (a = b = 4) has the bias +7. */
-void oracle_split_bits(int code, int sign, int anchor_bits, int *v_mag, int *q_res,
-                       int *q_anc)
+ * The paper's split (a = b = 4) has the bias +7; a single stream (b = 0)
+ * has no bias, V_mag = I and Q_res = 0. */
+void oracle_split_bits(int code, int sign, int anchor_bits, int residual_bits, int *v_mag,
+                       int *q_res, int *q_anc)
 {
-    int b = 8 - anchor_bits;
-    int i_bias = code + (1 << (b - 1)) - 1;
+    (void)anchor_bits;
+    int b = residual_bits;
+    int i_bias = code + (b > 0 ? (1 << (b - 1)) - 1 : 0);
     int v = i_bias >> b;
     int v_recon = v << b;
     *v_mag = v;
@@ -146,7 +162,7 @@ void oracle_split_bits(int code, int sign, int anchor_bits, int *v_mag, int *q_r
 
 void oracle_split(int code, int sign, int *v_mag, int *q_res, int *q_anc)
 {
-    oracle_split_bits(code, sign, 4, v_mag, q_res, q_anc);
+    oracle_split_bits(code, sign, 4, 4, v_mag, q_res, q_anc);
 }
 
 /* Inverse of the split: the code that the decoder rebuilds from an anchor
@@ -160,14 +176,14 @@ static int sext(unsigned field, int w)
 }
 
 int oracle_unsplit_bits(unsigned anc_field, int have_res, unsigned res_field,
-                        int anchor_bits, int *sign)
+                        int anchor_bits, int residual_bits, int *sign)
 {
-    int b = 8 - anchor_bits;
+    int b = residual_bits;
     int a = sext(anc_field, anchor_bits);
     int s = a < 0 ? -1 : 1;
     int v = a < 0 ? -a - 1 : a;
     int code = v << b;
-    if (have_res)
+    if (have_res && b > 0)
         code -= sext(res_field, b);
     if (code < 0)
         code = 0;
@@ -177,7 +193,7 @@ int oracle_unsplit_bits(unsigned anc_field, int have_res, unsigned res_field,
 
 int oracle_unsplit(unsigned anc_nib, int have_res, unsigned res_nib, int *sign)
 {
-    return oracle_unsplit_bits(anc_nib, have_res, res_nib, 4, sign);
+    return oracle_unsplit_bits(anc_nib, have_res, res_nib, 4, 4, sign);
 }
 
 /* Bit stream of one (chunk, channel pair) run: field f of width w at bit
@@ -232,7 +248,7 @@ static int is_pow2(int n) { return n > 0 && (n & (n - 1)) == 0; }
  */
 int oracle_quantize_block_bits(const uint16_t *x, int64_t row_stride, int H,
                                int P, int C, float alpha, float eps,
-                               float code_scale, int anchor_bits,
+                               float code_scale, int anchor_bits, int residual_bits,
                                uint8_t *anchor, uint8_t *residual,
                                float *gamma_min, float *gamma_scale, float *mu,
                                float *sigma, float *xn_out, float *xcent_out,
@@ -240,9 +256,9 @@ int oracle_quantize_block_bits(const uint16_t *x, int64_t row_stride, int H,
                                int8_t *sign_out)
 {
     if (H <= 0 || (H & 1) || P <= 0 || !is_pow2(C) || P % C || C % 4 ||
-        !valid_anchor_bits(anchor_bits))
+        !valid_bits(anchor_bits, residual_bits) || (residual_bits > 0 && !residual))
         return ORACLE_EINVAL;
-    const int code_max = oracle_code_max(anchor_bits);
+    const int code_max = oracle_code_max(anchor_bits, residual_bits);
     const int nchunk = P / C;
     float *xn = (float *)malloc(sizeof(float) * (size_t)P);
     float *xc = (float *)malloc(sizeof(float) * (size_t)P);
@@ -295,7 +311,8 @@ int oracle_quantize_block_bits(const uint16_t *x, int64_t row_stride, int H,
                 int s = xc[t] < 0.0f ? -1 : 1;
                 int code_c = code < code_max ? code : code_max;
                 int v, q_res, q_anc;
-                oracle_split_bits(code_c, s, anchor_bits, &v, &q_res, &q_anc);
+                oracle_split_bits(code_c, s, anchor_bits, residual_bits, &v, &q_res,
+                                  &q_anc);
                 qa[(size_t)t * H + c] = (int8_t)q_anc;
                 qr[(size_t)t * H + c] = (int8_t)q_res;
                 if (xfinal_out) xfinal_out[(size_t)c * P + t] = xf;
@@ -314,18 +331,20 @@ int oracle_quantize_block_bits(const uint16_t *x, int64_t row_stride, int H,
      * (j * (H / 2) + k) * C * w / 4; token i of the chunk and channel
      * 2k + e is field 2 i + e.  (For w = 4: byte i of the run, channel 2k
      * in the low nibble.) */
-    const int wa = anchor_bits, wr = 8 - anchor_bits;
+    const int wa = anchor_bits, wr = residual_bits;
     memset(anchor, 0, (size_t)P * H * wa / 8);
-    memset(residual, 0, (size_t)P * H * wr / 8);
+    if (wr > 0)
+        memset(residual, 0, (size_t)P * H * wr / 8);
     for (int t = 0; t < P; ++t) {
         const int j = t / C, i = t % C;
         for (int k = 0; k < H / 2; ++k) {
             uint8_t *ra = anchor + ((size_t)j * (H / 2) + k) * run_bytes(C, wa);
-            uint8_t *rr = residual + ((size_t)j * (H / 2) + k) * run_bytes(C, wr);
             for (int e = 0; e < 2; ++e) {
                 const int v = 2 * i + e;
                 put_bits(ra, wa * v, wa, (unsigned)qa[(size_t)t * H + 2 * k + e]);
-                put_bits(rr, wr * v, wr, (unsigned)qr[(size_t)t * H + 2 * k + e]);
+                if (wr > 0)
+                    put_bits(residual + ((size_t)j * (H / 2) + k) * run_bytes(C, wr), wr * v,
+                             wr, (unsigned)qr[(size_t)t * H + 2 * k + e]);
             }
         }
     }
@@ -342,7 +361,7 @@ int oracle_quantize_block_ex(const uint16_t *x, int64_t row_stride, int H,
                              float *xfinal_out, int32_t *code_raw_out,
                              int8_t *sign_out)
 {
-    return oracle_quantize_block_bits(x, row_stride, H, P, C, alpha, eps, code_scale, 4,
+    return oracle_quantize_block_bits(x, row_stride, H, P, C, alpha, eps, code_scale, 4, 4,
                                       anchor, residual, gamma_min, gamma_scale, mu, sigma,
                                       xn_out, xcent_out, xfinal_out, code_raw_out, sign_out);
 }
@@ -358,13 +377,13 @@ int oracle_dequant_block_bits(const uint8_t *anchor, const uint8_t *residual,
                               const float *gamma_min, const float *gamma_scale,
                               const float *mu, const float *sigma, int H, int P,
                               int C, float alpha, float eps, float code_scale,
-                              int anchor_bits, uint16_t *out,
+                              int anchor_bits, int residual_bits, uint16_t *out,
                               int64_t out_row_stride)
 {
     if (H <= 0 || (H & 1) || P <= 0 || C <= 0 || P % C || C % 4 ||
-        !valid_anchor_bits(anchor_bits))
+        !valid_bits(anchor_bits, residual_bits) || (residual_bits == 0 && residual))
         return ORACLE_EINVAL;
-    const int wa = anchor_bits, wr = 8 - anchor_bits;
+    const int wa = anchor_bits, wr = residual_bits;
     float lut[128];
     for (int k = 0; k < 128; ++k)
         lut[k] = oracle_level(k, alpha, code_scale);
@@ -378,7 +397,8 @@ int oracle_dequant_block_bits(const uint8_t *anchor, const uint8_t *residual,
             if (residual)
                 rn = get_bits(residual + run * run_bytes(C, wr), wr * v, wr);
             int s;
-            int code = oracle_unsplit_bits(an, residual != NULL, rn, anchor_bits, &s);
+            int code = oracle_unsplit_bits(an, residual != NULL, rn, anchor_bits,
+                                           residual_bits, &s);
             float m = lut[code];
             float xf = s < 0 ? -m : m;
             float d2 = sigma[j * H + c] + eps;
@@ -400,7 +420,7 @@ int oracle_dequant_block(const uint8_t *anchor, const uint8_t *residual,
                          uint16_t *out, int64_t out_row_stride)
 {
     return oracle_dequant_block_bits(anchor, residual, gamma_min, gamma_scale, mu, sigma, H,
-                                     P, C, alpha, eps, code_scale, 4, out, out_row_stride);
+                                     P, C, alpha, eps, code_scale, 4, 4, out, out_row_stride);
 }
 
 /* ------------------------------------------------------- whole tensors -- */
@@ -431,12 +451,12 @@ int oracle_quantize_bits(const uint16_t *kv, int64_t num_tensors,
                          int64_t tensor_stride, int64_t T, int64_t Ch,
                          int64_t row_stride, int H, int P, int C, float alpha,
                          float eps, float code_scale, int anchor_bits,
-                         int64_t block_begin, int64_t block_end,
+                         int residual_bits, int64_t block_begin, int64_t block_end,
                          int64_t out_first_block, uint8_t *anchor,
                          uint8_t *residual, float *gamma_min,
                          float *gamma_scale, float *mu, float *sigma)
 {
-    if (!valid_anchor_bits(anchor_bits))
+    if (!valid_bits(anchor_bits, residual_bits))
         return ORACLE_EINVAL;
     if (T % P || Ch % H || num_tensors < 0)
         return ORACLE_EINVAL;
@@ -445,7 +465,7 @@ int oracle_quantize_bits(const uint16_t *kv, int64_t num_tensors,
         out_first_block > block_begin)
         return ORACLE_EINVAL;
     const int64_t anchor_bytes = (int64_t)P * H * anchor_bits / 8;
-    const int64_t residual_bytes = (int64_t)P * H * (8 - anchor_bits) / 8;
+    const int64_t residual_bytes = (int64_t)P * H * residual_bits / 8;
     const int64_t chunk_meta = (int64_t)(P / C) * H;
     for (int64_t b = block_begin; b < block_end; ++b) {
         int64_t tensor, page, group;
@@ -454,8 +474,8 @@ int oracle_quantize_bits(const uint16_t *kv, int64_t num_tensors,
                             page * P * row_stride + group * H;
         const int64_t o = b - out_first_block;
         int rc = oracle_quantize_block_bits(
-            x, row_stride, H, P, C, alpha, eps, code_scale, anchor_bits,
-            anchor + o * anchor_bytes, residual + o * residual_bytes,
+            x, row_stride, H, P, C, alpha, eps, code_scale, anchor_bits, residual_bits,
+            anchor + o * anchor_bytes, residual ? residual + o * residual_bytes : NULL,
             gamma_min + o * H, gamma_scale + o * H, mu + o * chunk_meta,
             sigma + o * chunk_meta, NULL, NULL, NULL, NULL, NULL);
         if (rc)
@@ -474,7 +494,7 @@ int oracle_quantize(const uint16_t *kv, int64_t num_tensors,
                     float *sigma)
 {
     return oracle_quantize_bits(kv, num_tensors, tensor_stride, T, Ch, row_stride, H, P, C,
-                                alpha, eps, code_scale, 4, block_begin, block_end,
+                                alpha, eps, code_scale, 4, 4, block_begin, block_end,
                                 out_first_block, anchor, residual, gamma_min, gamma_scale,
                                 mu, sigma);
 }
@@ -485,10 +505,10 @@ int oracle_dequant_bits(const uint8_t *anchor, const uint8_t *residual,
                         int64_t tensor_stride, int64_t T, int64_t Ch,
                         int64_t row_stride, int H, int P, int C, float alpha,
                         float eps, float code_scale, int anchor_bits,
-                        int64_t block_begin, int64_t block_end,
+                        int residual_bits, int64_t block_begin, int64_t block_end,
                         int64_t in_first_block, uint16_t *out)
 {
-    if (!valid_anchor_bits(anchor_bits))
+    if (!valid_bits(anchor_bits, residual_bits))
         return ORACLE_EINVAL;
     if (T % P || Ch % H || num_tensors < 0)
         return ORACLE_EINVAL;
@@ -497,7 +517,7 @@ int oracle_dequant_bits(const uint8_t *anchor, const uint8_t *residual,
         in_first_block > block_begin)
         return ORACLE_EINVAL;
     const int64_t anchor_bytes = (int64_t)P * H * anchor_bits / 8;
-    const int64_t residual_bytes = (int64_t)P * H * (8 - anchor_bits) / 8;
+    const int64_t residual_bytes = (int64_t)P * H * residual_bits / 8;
     const int64_t chunk_meta = (int64_t)(P / C) * H;
     for (int64_t b = block_begin; b < block_end; ++b) {
         int64_t tensor, page, group;
@@ -508,8 +528,8 @@ int oracle_dequant_bits(const uint8_t *anchor, const uint8_t *residual,
         int rc = oracle_dequant_block_bits(
             anchor + i * anchor_bytes, residual ? residual + i * residual_bytes : NULL,
             gamma_min + i * H, gamma_scale + i * H, mu + i * chunk_meta,
-            sigma + i * chunk_meta, H, P, C, alpha, eps, code_scale, anchor_bits, o,
-            row_stride);
+            sigma + i * chunk_meta, H, P, C, alpha, eps, code_scale, anchor_bits,
+            residual_bits, o, row_stride);
         if (rc)
             return rc;
     }
@@ -526,7 +546,7 @@ int oracle_dequant(const uint8_t *anchor, const uint8_t *residual,
 {
     return oracle_dequant_bits(anchor, residual, gamma_min, gamma_scale, mu, sigma,
                                num_tensors, tensor_stride, T, Ch, row_stride, H, P, C, alpha,
-                               eps, code_scale, 4, block_begin, block_end, in_first_block,
+                               eps, code_scale, 4, 4, block_begin, block_end, in_first_block,
                                out);
 }
 

@@ -169,6 +169,6 @@ def test_fewer_anchor_bits_coarser_draft():
 
 def test_rejects_bad_split():
     x = bits(kvgen.CONFIGS["single_page"].make()[0])
-    for a in (0, 1, 8):
+    for a, b in ((0, None), (1, None), (1, 0), (9, 0), (5, 4), (4, 5), (3, 3)):
         with pytest.raises(ValueError):
-            oracle.quantize_block(x, anchor_bits=a)
+            oracle.quantize_block(x, anchor_bits=a, residual_bits=b)
