@@ -49,7 +49,9 @@
  *   [b][j][k] x 8 w of the block's 4096 w bytes: an LSB-first bit stream
  *   of 64 two's-complement w-bit fields, field 2 i + e (token 32 j + i,
  *   channel 2k + e) at bit w (2 i + e).  For w = 4 this is the nibble
- *   layout above.
+ *   layout above.  A single stream (residual_bits = 0) is the anchor layout
+ *   alone, each field the whole code: magnitude I, one's-complemented when
+ *   the value is negative.
  *   gamma_min, gamma_scale   float32 [nblocks][H]
  *   mu, sigma               float32 [nblocks][P/C][H]
  *
@@ -113,11 +115,16 @@ extern "C" {
  * carry (anchor magnitude (code + 7) >> 4 <= 7), so every |X_final| in
  * [0, 1] keeps its code; 127 (the 2^7 - 1 printed in Eq. (3)) is accepted and
  * then codes above 120 are clipped to 120.  page_tokens, chunk_tokens and
- * block_channels must be 256, 32 and 128.  anchor_bits (3..6, default 4 =
- * the paper's split) is the width a of the anchor field, 8 - a that of the
- * residual (the bias of Stage 4 is 2^(7 - a) - 1, +7 for a = 4); the
- * anchor and residual streams then take 4096 a and 4096 (8 - a) bytes per
- * block.  Only quantize and the two dequant calls accept a != 4. */
+ * block_channels must be 256, 32 and 128.  anchor_bits a and residual_bits
+ * b are the field widths (default 4 and 4 = the paper's split): a split of
+ * the 8-bit code has a = 3..6 and b = 8 - a (the bias of Stage 4 is
+ * 2^(b - 1) - 1, +7 for b = 4; codes above 128 - 2^(b - 1) are clipped);
+ * b = 0 with a = 4 or 8 is a single a-bit stream (the paper's Lynx-INT4 /
+ * Lynx-INT8 configurations, Section 5: Algorithm 1 into one precision, no
+ * split; set code_scale to 2^(a - 1) - 1 = 7 or 127, codes above that are
+ * clipped).  The anchor and residual streams take 4096 a and 4096 b bytes
+ * per block.  Only quantize and the two dequant calls accept other widths
+ * than 4 + 4. */
 typedef struct lynx_params {
     float alpha;
     float eps;
@@ -126,6 +133,7 @@ typedef struct lynx_params {
     int32_t chunk_tokens;
     int32_t block_channels;
     int32_t anchor_bits;
+    int32_t residual_bits;
 } lynx_params;
 
 /* Shape of a KV set (element strides, bf16 elements). */
@@ -146,7 +154,7 @@ typedef struct lynx_meta {
 } lynx_meta;
 
 /* Fills *p with alpha = 255, eps = 1e-6, code_scale = 120, P = 256,
- * C = 32, H = 128, anchor_bits = 4. */
+ * C = 32, H = 128, anchor_bits = residual_bits = 4. */
 void lynx_default_params(lynx_params *p);
 
 /* Number of page blocks of a shape, or a negative status if the shape is
@@ -156,7 +164,7 @@ int64_t lynx_num_blocks(const lynx_kv_shape *shape);
 /* Bytes of one stream (anchor or residual) and number of floats of each
  * metadata array, for a shape; 0 if the shape is invalid.
  * lynx_stream_bytes is the 4-bit stream of the paper's split;
- * lynx_field_stream_bytes the stream of field_bits-bit fields (1..7),
+ * lynx_field_stream_bytes the stream of field_bits-bit fields (1..8),
  * nblocks x 4096 x field_bits. */
 size_t lynx_stream_bytes(const lynx_kv_shape *shape);
 size_t lynx_field_stream_bytes(const lynx_kv_shape *shape, int field_bits);
@@ -172,8 +180,8 @@ uint64_t lynx_kv_bytes(int64_t k_factor, int64_t seq_len, int64_t hidden,
 /* The 128 compander thresholds the kernels use for `params` (NULL =
  * defaults): thr[k], k = 1..120, is the smallest binary32 magnitude whose
  * Eq. (3) value reaches k - 1/2 (so code(|x|) = #{k : |x| >= thr[k]});
- * thr[0] = 0 and thr[k] = +inf for codes above 120 (above the split's
- * largest code 128 - 2^(7 - anchor_bits) in general) or out of reach.  Host
+ * thr[0] = 0 and thr[k] = +inf for codes above 120 (above the largest
+ * storable code of the field widths in general) or out of reach.  Host
  * only, no GPU needed.  Returns LYNX_EINVAL for bad parameters. */
 int lynx_compander_thresholds(const lynx_params *params, float *thr128);
 
@@ -184,8 +192,10 @@ const char *lynx_status_string(int status);
 /*
  * Algorithm 1 on every page block of the KV set `kv` (bf16, layout given
  * by `shape`): writes anchor, residual (nblocks * 16384 bytes each; nblocks
- * * 4096 * anchor_bits and nblocks * 4096 * (8 - anchor_bits) for the other
- * splits) and the four metadata arrays.  `params` NULL means the defaults.
+ * * 4096 * anchor_bits and nblocks * 4096 * residual_bits for other field
+ * widths) and the four metadata arrays.  `params` NULL means the defaults.
+ * residual must be NULL exactly when residual_bits is 0 (a single stream),
+ * else LYNX_EINVAL.
  */
 int lynx_quantize_pages(const void *kv, const lynx_kv_shape *shape,
                         const lynx_params *params, uint8_t *anchor,
@@ -193,8 +203,9 @@ int lynx_quantize_pages(const void *kv, const lynx_kv_shape *shape,
 
 /*
  * Anchor phase: rebuilds every page block from the anchor stream and the
- * metadata (code = anchor magnitude << 4) into `out` (bf16, layout given by
- * `shape`; the shape's strides describe `out`).  meta.* are only read.
+ * metadata (code = anchor magnitude << residual_bits: << 4 for the paper's
+ * split, the whole code for a single stream) into `out` (bf16, layout given
+ * by `shape`; the shape's strides describe `out`).  meta.* are only read.
  */
 int lynx_dequant_anchor(const uint8_t *anchor, lynx_meta meta,
                         const lynx_kv_shape *shape, const lynx_params *params,
@@ -202,7 +213,8 @@ int lynx_dequant_anchor(const uint8_t *anchor, lynx_meta meta,
 
 /*
  * Residual phase: rebuilds every page block at the verification precision
- * from anchor + residual and the metadata into `out`.
+ * from anchor + residual and the metadata into `out`.  LYNX_EINVAL for a
+ * single stream (residual_bits = 0).
  */
 int lynx_dequant_full(const uint8_t *anchor, const uint8_t *residual,
                       lynx_meta meta, const lynx_kv_shape *shape,
@@ -255,8 +267,8 @@ size_t lynx_attn_workspace_bytes(int t_q, int num_q_heads, int num_kv_heads,
  *   workspace    >= lynx_attn_workspace_bytes(...) bytes of device memory,
  *                overwritten (split partials).
  * Scores, the softmax and the accumulation are binary32 (bf16 x bf16
- * products are exact).  t_q * g must be <= 64; params->anchor_bits must be
- * 4.  Errors as above.
+ * products are exact).  t_q * g must be <= 64; the field widths must be
+ * 4 + 4.  Errors as above.
  */
 int lynx_decode_attn_dequant(const void *q, int t_q, int num_q_heads,
                              const uint8_t *k_anchor, const uint8_t *k_residual,
@@ -309,7 +321,7 @@ typedef struct lynx_transfer_times {
  *                    anchor into kv_anchor;
  * then, once every object is rebuilt from its anchor, per object: after its
  * residual copy, rebuild it from anchor + residual into kv_full.
- *   kv, shape, params  as lynx_quantize_pages (anchor_bits must be 4);
+ *   kv, shape, params  as lynx_quantize_pages (field widths must be 4 + 4);
  *   tx, wire, rx       code buffers of the whole set: tx and rx device
  *                      memory, wire pinned host memory (or device memory);
  *   kv_anchor, kv_full device bf16 outputs laid out by shape;

@@ -121,16 +121,18 @@ struct Tables {
 };
 
 std::mutex g_mu;
-std::map<std::tuple<uint32_t, uint32_t, int>, Tables> g_cache;
+std::map<std::tuple<uint32_t, uint32_t, int, int>, Tables> g_cache;
 
 const Tables *tables_for(const lynx_params &p) {
     std::lock_guard<std::mutex> lock(g_mu);
-    auto key = std::make_tuple(f2u(p.alpha), f2u(p.code_scale), (int)p.anchor_bits);
+    auto key = std::make_tuple(f2u(p.alpha), f2u(p.code_scale), (int)p.anchor_bits,
+                               (int)p.residual_bits);
     auto it = g_cache.find(key);
     if (it != g_cache.end())
         return &it->second;
     Tables t;
-    if (!build_quant_tab(p.alpha, p.code_scale, code_max_of(p.anchor_bits), &t.q))
+    if (!build_quant_tab(p.alpha, p.code_scale, code_max_of(p.anchor_bits, p.residual_bits),
+                         &t.q))
         return nullptr;
     build_dequant_tab(p.alpha, p.code_scale, &t.d);
     return &g_cache.emplace(key, t).first->second;
@@ -153,7 +155,7 @@ int check_params(const lynx_params &p) {
         return LYNX_EINVAL;
     if (!(p.code_scale >= 1.0f) || !(p.code_scale <= 127.0f))
         return LYNX_EINVAL;
-    if (p.anchor_bits < kMinAnchorBits || p.anchor_bits > kMaxAnchorBits)
+    if (!valid_field_bits(p.anchor_bits, p.residual_bits))
         return LYNX_EINVAL;
     return LYNX_OK;
 }
@@ -216,7 +218,7 @@ int quantize_common(const void *kv, const lynx_kv_shape *shape, const lynx_param
         return LYNX_EINVAL;
     if (mode != kModePageStats && (!mu || !sigma))
         return LYNX_EINVAL;
-    if (mode == kModeQuantize && (!anchor || !residual))
+    if (mode == kModeQuantize && (!anchor || (p.residual_bits > 0) != (residual != nullptr)))
         return LYNX_EINVAL;
     for (const void *ptr : {(const void *)kv, (const void *)gmin, (const void *)gscale,
                             (const void *)mu, (const void *)sigma, (const void *)anchor,
@@ -233,7 +235,8 @@ int quantize_common(const void *kv, const lynx_kv_shape *shape, const lynx_param
         g.block0 = b0;
         g.nblocks = (nb - b0) < kMaxLaunchBlocks ? (nb - b0) : kMaxLaunchBlocks;
         rc = hip_status(launch_quantize((const uint16_t *)kv, g, tab, anchor, residual, gmin,
-                                        gscale, mu, sigma, mode, p.anchor_bits, stream));
+                                        gscale, mu, sigma, mode, p.anchor_bits,
+                                        p.residual_bits, stream));
         if (rc)
             return rc;
     }
@@ -254,6 +257,8 @@ int dequant_common(const uint8_t *anchor, const uint8_t *residual, lynx_meta met
         return LYNX_OK;
     if (!anchor || !out || !meta.gamma_min || !meta.gamma_scale || !meta.mu || !meta.sigma)
         return LYNX_EINVAL;
+    if (residual && p.residual_bits == 0)  // a single stream has no residual phase
+        return LYNX_EINVAL;
     for (const void *ptr : {(const void *)anchor, (const void *)residual, (const void *)out,
                             (const void *)meta.gamma_min, (const void *)meta.gamma_scale,
                             (const void *)meta.mu, (const void *)meta.sigma})
@@ -270,7 +275,7 @@ int dequant_common(const uint8_t *anchor, const uint8_t *residual, lynx_meta met
         g.nblocks = (nb - b0) < kMaxLaunchBlocks ? (nb - b0) : kMaxLaunchBlocks;
         rc = hip_status(launch_dequant(anchor, residual, meta.gamma_min, meta.gamma_scale,
                                        meta.mu, meta.sigma, g, tab, (uint16_t *)out,
-                                       p.anchor_bits, stream));
+                                       p.anchor_bits, p.residual_bits, stream));
         if (rc)
             return rc;
     }
@@ -334,7 +339,7 @@ struct EventSet {
     }
     ~EventSet() {
         for (hipEvent_t e : ev)
-            hipEventDestroy(e);
+            (void)hipEventDestroy(e);
     }
 };
 
@@ -385,6 +390,7 @@ void lynx_default_params(lynx_params *p) {
     p->chunk_tokens = kChunk;
     p->block_channels = kHead;
     p->anchor_bits = 4;
+    p->residual_bits = 4;
 }
 
 int64_t lynx_num_blocks(const lynx_kv_shape *shape) {
@@ -400,7 +406,7 @@ size_t lynx_stream_bytes(const lynx_kv_shape *shape) {
 
 size_t lynx_field_stream_bytes(const lynx_kv_shape *shape, int field_bits) {
     int64_t nb = lynx_num_blocks(shape);
-    if (nb < 0 || field_bits < 1 || field_bits > 7)
+    if (nb < 0 || field_bits < 1 || field_bits > 8)
         return 0;
     return (size_t)nb * (kPage * kHead / 8) * (size_t)field_bits;
 }
@@ -491,7 +497,7 @@ int lynx_decode_attn_dequant(const void *q, int t_q, int num_q_heads, const uint
     int rc = check_params(p);
     if (rc)
         return rc;
-    if (p.anchor_bits != 4)
+    if (p.anchor_bits != 4 || p.residual_bits != 4)
         return LYNX_EINVAL;
     if (head_dim != kHead || !(scale > 0.0f) || !(scale < 1e30f) ||
         (out_dtype != LYNX_OUT_BF16 && out_dtype != LYNX_OUT_F32))
@@ -575,7 +581,7 @@ int lynx_split_stream_transfer(const void *kv, const lynx_kv_shape *shape,
     int rc = check_params(p);
     if (rc)
         return rc;
-    if (p.anchor_bits != 4)
+    if (p.anchor_bits != 4 || p.residual_bits != 4)
         return LYNX_EINVAL;
     int64_t nb = 0;
     if ((rc = check_shape(shape, &nb)))
@@ -639,7 +645,7 @@ int lynx_split_stream_transfer(const void *kv, const lynx_kv_shape *shape,
         if (!copies_only)
             ok(launch_quantize((const uint16_t *)kv, g, qt, tx.anchor, tx.residual,
                                tx.meta.gamma_min, tx.meta.gamma_scale, tx.meta.mu, tx.meta.sigma,
-                               kModeQuantize, 4, sender));
+                               kModeQuantize, 4, 4, sender));
         ok(hipEventRecord(q[i], sender));
         // anchor queue: anchor + metadata over the wire
         ok(hipStreamWaitEvent(anchor_link, q[i], 0));
@@ -655,7 +661,7 @@ int lynx_split_stream_transfer(const void *kv, const lynx_kv_shape *shape,
         ok(hipStreamWaitEvent(receiver, a[i], 0));
         if (!copies_only)
             ok(launch_dequant(rx.anchor, nullptr, rx.meta.gamma_min, rx.meta.gamma_scale,
-                              rx.meta.mu, rx.meta.sigma, g, dt, (uint16_t *)kv_anchor, 4,
+                              rx.meta.mu, rx.meta.sigma, g, dt, (uint16_t *)kv_anchor, 4, 4,
                               receiver));
         if (i == 0)
             ok(hipEventRecord(t_da0, receiver));
@@ -674,7 +680,7 @@ int lynx_split_stream_transfer(const void *kv, const lynx_kv_shape *shape,
         ok(hipStreamWaitEvent(receiver, r[i], 0));
         if (!copies_only)
             ok(launch_dequant(rx.anchor, rx.residual, rx.meta.gamma_min, rx.meta.gamma_scale,
-                              rx.meta.mu, rx.meta.sigma, g, dt, (uint16_t *)kv_full, 4,
+                              rx.meta.mu, rx.meta.sigma, g, dt, (uint16_t *)kv_full, 4, 4,
                               receiver));
     }
     ok(hipEventRecord(t_df, receiver));

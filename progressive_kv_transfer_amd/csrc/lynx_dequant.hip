@@ -18,9 +18,10 @@
 // four 16-byte runs of the chunk-tiled streams (one per channel pair) and
 // writes 16-byte row pieces that 16 lanes join into one 256-byte row.
 // Workgroups are persistent and build the level table in LDS once.
-// The other splits of the 8-bit code (ABITS anchor bits, 8 - ABITS residual
-// bits) read the lane's fields from the per-(chunk, pair) bit-stream runs:
-// the lane's 16 tokens of a pair are ABITS (8 - ABITS) consecutive dwords.
+// Other field widths (ABITS anchor bits, RBITS residual bits: the other
+// splits of the 8-bit code, or RBITS = 0 for a single stream of whole codes)
+// read the lane's fields from the per-(chunk, pair) bit-stream runs: the
+// lane's 16 tokens of a pair are ABITS (RBITS) consecutive dwords.
 #include "lynx_recon.h"
 
 namespace lynx {
@@ -35,12 +36,11 @@ constexpr int kThreads = 256;
 // different entries spread over the LDS banks.
 constexpr int kCopies = 1;
 
-// Signed level S * L[code] of table entry t for a anchor bits: t's low a
-// bits are the anchor field, the next 8 - a the residual field (full), as
-// signed_level does for a = 4.
+// Signed level S * L[code] of table entry t for a anchor bits and b residual
+// bits: t's low a bits are the anchor field, the next b the residual field
+// (full), as signed_level does for a = b = 4.
 __device__ __forceinline__ float signed_level_bits(const DequantTab &tab, int t, bool full,
-                                                   int abits) {
-    const int bbits = 8 - abits;
+                                                   int abits, int bbits) {
     const int af = t & ((1 << abits) - 1);
     const int av = af >= (1 << (abits - 1)) ? af - (1 << abits) : af;
     const int v = av < 0 ? -av - 1 : av;
@@ -65,13 +65,15 @@ __device__ __forceinline__ uint32_t get_field(const uint32_t *w, int v) {
     return f & ((1u << W) - 1u);
 }
 
-template <bool FULL, int ABITS>
+template <bool FULL, int ABITS, int RBITS>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(
     const uint8_t *__restrict__ anchor, const uint8_t *__restrict__ residual,
     const float *__restrict__ gmin, const float *__restrict__ gscale,
     const float *__restrict__ mu, const float *__restrict__ sigma, Geometry g,
     const DequantTab tab, uint16_t *__restrict__ out) {
-    constexpr int kBits = 8 - ABITS;
+    constexpr int kBits = RBITS;
+    constexpr bool kNibbles = ABITS == 4 && RBITS == 4;
+    static_assert(!FULL || RBITS > 0, "a single stream has no residual phase");
     constexpr int kLut = FULL ? 256 : (1 << ABITS);
     constexpr int kCop = FULL ? kCopies : 1;
     __shared__ float s_lut[kLut * kCop];
@@ -86,8 +88,8 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
 
     // Signed level of every (anchor nibble, residual nibble) pair.
     for (int e = tid; e < kLut * kCop; e += kThreads)
-        s_lut[e] = ABITS == 4 ? signed_level(tab, e / kCop, FULL)
-                              : signed_level_bits(tab, e / kCop, FULL, ABITS);
+        s_lut[e] = kNibbles ? signed_level(tab, e / kCop, FULL)
+                            : signed_level_bits(tab, e / kCop, FULL, ABITS, RBITS);
     __syncthreads();
     const float *lut = s_lut + (lane % kCop);
 
@@ -106,8 +108,8 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
         // successive loads, so these are ordinary (cached) loads.  Other
         // splits: the pair's run of 8 w bytes, dwords w (tg & 1) .. + w - 1.
         u32x4 A[4], R[4];
-        uint32_t Aw[4][ABITS == 4 ? 1 : ABITS], Rw[4][ABITS == 4 ? 1 : kBits];
-        if constexpr (ABITS == 4) {
+        uint32_t Aw[4][kNibbles ? 1 : ABITS], Rw[4][kNibbles || kBits == 0 ? 1 : kBits];
+        if constexpr (kNibbles) {
             const int64_t coff = b * (kPage * kHead / 2) + j * (kHead / 2 * kChunk) +
                                  (4 * cg) * kChunk + 16 * (tg & 1);
 #pragma unroll
@@ -121,15 +123,18 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
                                                     (int64_t)(j * (kHead / 2) + 4 * cg) *
                                                         (8 * ABITS)) +
                                  ABITS * (tg & 1);
-            const uint32_t *rr = (const uint32_t *)(residual + b * (kPage * kHead / 8 * kBits) +
-                                                    (int64_t)(j * (kHead / 2) + 4 * cg) *
-                                                        (8 * kBits)) +
-                                 kBits * (tg & 1);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
 #pragma unroll
                 for (int d = 0; d < ABITS; ++d) Aw[k][d] = ar[k * 2 * ABITS + d];
-                if (FULL)
+            }
+            if constexpr (FULL) {
+                const uint32_t *rr =
+                    (const uint32_t *)(residual + b * (kPage * kHead / 8 * kBits) +
+                                       (int64_t)(j * (kHead / 2) + 4 * cg) * (8 * kBits)) +
+                    kBits * (tg & 1);
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
 #pragma unroll
                     for (int d = 0; d < kBits; ++d) Rw[k][d] = rr[k * 2 * kBits + d];
             }
@@ -154,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
             uint32_t ev[4], od[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                if (ABITS != 4) {
+                if (!kNibbles) {
                     ev[k] = od[k] = 0u;
                 } else if (FULL) {
                     ev[k] = (A[k][h] & 0x0f0f0f0fu) | ((R[k][h] << 4) & 0xf0f0f0f0u);
@@ -173,13 +178,13 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
                     for (int o = 0; o < 2; ++o) {
                         const int e = 2 * k + o;
                         uint32_t idx;
-                        if constexpr (ABITS == 4) {
+                        if constexpr (kNibbles) {
                             idx = ((o ? od[k] : ev[k]) >> (8 * i)) & 0xffu;
                         } else {
                             // field of token 4h + i, channel 2k + o of the run
                             const int v = 2 * (4 * h + i) + o;
                             idx = get_field<ABITS>(Aw[k], v);
-                            if (FULL)
+                            if constexpr (FULL)
                                 idx |= get_field<kBits>(Rw[k], v) << ABITS;
                         }
                         y[e] = reconstruct(lut[idx * kCop], d2[e], um[e], d1[e], gm[e]);
@@ -199,46 +204,61 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
 
 }  // namespace
 
-template <bool FULL, int ABITS>
+template <bool FULL, int ABITS, int RBITS>
 static hipError_t launch_one(const uint8_t *anchor, const uint8_t *residual,
                              const float *gmin, const float *gscale, const float *mu,
                              const float *sigma, const Geometry &g, const DequantTab &tab,
                              uint16_t *out, hipStream_t stream) {
     Geometry gl = g;
     gl.grid_wgs = g.nblocks;
-    hipLaunchKernelGGL((dequant_kernel<FULL, ABITS>), dim3((unsigned)gl.grid_wgs),
+    hipLaunchKernelGGL((dequant_kernel<FULL, ABITS, RBITS>), dim3((unsigned)gl.grid_wgs),
                        dim3(kThreads), 0, stream, anchor, residual, gmin, gscale, mu, sigma, gl,
                        tab, out);
     return hipGetLastError();
 }
 
-template <int ABITS>
+template <int ABITS, int RBITS>
 static hipError_t launch_split(const uint8_t *anchor, const uint8_t *residual,
                                const float *gmin, const float *gscale, const float *mu,
                                const float *sigma, const Geometry &g, const DequantTab &tab,
                                uint16_t *out, hipStream_t stream) {
-    if (residual)
-        return launch_one<true, ABITS>(anchor, residual, gmin, gscale, mu, sigma, g, tab, out,
-                                       stream);
-    return launch_one<false, ABITS>(anchor, residual, gmin, gscale, mu, sigma, g, tab, out,
-                                    stream);
+    if constexpr (RBITS > 0) {
+        if (residual)
+            return launch_one<true, ABITS, RBITS>(anchor, residual, gmin, gscale, mu, sigma, g,
+                                                  tab, out, stream);
+    } else {
+        if (residual)
+            return hipErrorInvalidValue;
+    }
+    return launch_one<false, ABITS, RBITS>(anchor, residual, gmin, gscale, mu, sigma, g, tab,
+                                           out, stream);
 }
 
 hipError_t launch_dequant(const uint8_t *anchor, const uint8_t *residual, const float *gmin,
                           const float *gscale, const float *mu, const float *sigma,
                           const Geometry &g, const DequantTab &tab, uint16_t *out,
-                          int anchor_bits, hipStream_t stream) {
+                          int anchor_bits, int residual_bits, hipStream_t stream) {
     if (g.nblocks == 0)
         return hipSuccess;
-    switch (anchor_bits) {
-    case 3:
-        return launch_split<3>(anchor, residual, gmin, gscale, mu, sigma, g, tab, out, stream);
-    case 4:
-        return launch_split<4>(anchor, residual, gmin, gscale, mu, sigma, g, tab, out, stream);
-    case 5:
-        return launch_split<5>(anchor, residual, gmin, gscale, mu, sigma, g, tab, out, stream);
-    case 6:
-        return launch_split<6>(anchor, residual, gmin, gscale, mu, sigma, g, tab, out, stream);
+    switch (anchor_bits * 16 + residual_bits) {
+    case 3 * 16 + 5:
+        return launch_split<3, 5>(anchor, residual, gmin, gscale, mu, sigma, g, tab, out,
+                                  stream);
+    case 4 * 16 + 4:
+        return launch_split<4, 4>(anchor, residual, gmin, gscale, mu, sigma, g, tab, out,
+                                  stream);
+    case 5 * 16 + 3:
+        return launch_split<5, 3>(anchor, residual, gmin, gscale, mu, sigma, g, tab, out,
+                                  stream);
+    case 6 * 16 + 2:
+        return launch_split<6, 2>(anchor, residual, gmin, gscale, mu, sigma, g, tab, out,
+                                  stream);
+    case 4 * 16 + 0:
+        return launch_split<4, 0>(anchor, residual, gmin, gscale, mu, sigma, g, tab, out,
+                                  stream);
+    case 8 * 16 + 0:
+        return launch_split<8, 0>(anchor, residual, gmin, gscale, mu, sigma, g, tab, out,
+                                  stream);
     default:
         return hipErrorInvalidValue;
     }

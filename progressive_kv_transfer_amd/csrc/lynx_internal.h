@@ -12,12 +12,20 @@ constexpr int kPage = 256;      // P: tokens per page block
 constexpr int kChunk = 32;      // C: tokens per chunk
 constexpr int kHead = 128;      // H: channels per page block
 constexpr int kChunks = kPage / kChunk;
-// Splits of the 8-bit code: a anchor bits and 8 - a residual bits (the
-// paper's split is a = 4).  The largest code whose anchor magnitude
-// (code + 2^(7-a) - 1) >> (8 - a) fits a two's-complement bits is
-// 128 - 2^(7-a) (120 for a = 4).
+// Field widths: a anchor bits and b residual bits.  Splits of the 8-bit code
+// have a + b = 8 (the paper's split is a = 4, a = 3..6 are built); a single
+// stream has b = 0 (a = 4 or 8: the paper's Lynx-INT4 / Lynx-INT8).  The
+// largest code whose anchor magnitude (code + bias) >> b fits a
+// two's-complement bits is 128 - 2^(b-1) for a split (120 for 4 + 4) and
+// 2^(a-1) - 1 for a single stream.
 constexpr int kMinAnchorBits = 3, kMaxAnchorBits = 6;
-constexpr int code_max_of(int anchor_bits) { return 128 - (1 << (7 - anchor_bits)); }
+constexpr bool valid_field_bits(int a, int b) {
+    return (a + b == 8 && a >= kMinAnchorBits && a <= kMaxAnchorBits) ||
+           (b == 0 && (a == 4 || a == 8));
+}
+constexpr int code_max_of(int a, int b) {
+    return b == 0 ? (1 << (a - 1)) - 1 : 128 - (1 << (b - 1));
+}
 constexpr int kMaxBuckets = 1792;  // 14 KiB: with the 32 KiB stage, 3 workgroups per CU
 
 // Compander tables, built once per (alpha, code_scale) on the host and
@@ -64,12 +72,12 @@ enum StatsMode : int { kModeQuantize = 0, kModePageStats = 1, kModeBlockStats = 
 hipError_t launch_quantize(const uint16_t *kv, const Geometry &g, const QuantTab &tab,
                            uint8_t *anchor, uint8_t *residual, float *gmin, float *gscale,
                            float *mu, float *sigma, int mode, int anchor_bits,
-                           hipStream_t stream);
+                           int residual_bits, hipStream_t stream);
 
 hipError_t launch_dequant(const uint8_t *anchor, const uint8_t *residual, const float *gmin,
                           const float *gscale, const float *mu, const float *sigma,
                           const Geometry &g, const DequantTab &tab, uint16_t *out,
-                          int anchor_bits, hipStream_t stream);
+                          int anchor_bits, int residual_bits, hipStream_t stream);
 
 // Argument block of the fused dequant + attention kernels.
 struct AttnArgs {

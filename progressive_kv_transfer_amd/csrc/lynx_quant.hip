@@ -93,9 +93,10 @@ __device__ __forceinline__ void put_field(uint32_t *w, int v, uint32_t f) {
 }
 
 // SH16: the compander buckets are the upper 16 bits of the magnitude, so the
-// table address is one v_mad_u32_u16 (high half x 8 + base).  ABITS: width
-// of the anchor field (4 = the paper's split; the residual has 8 - ABITS).
-template <int MODE, bool SH16, int ABITS>
+// table address is one v_mad_u32_u16 (high half x 8 + base).  ABITS, RBITS:
+// widths of the anchor and residual fields (4 + 4 = the paper's split;
+// RBITS = 0 is a single stream of whole codes).
+template <int MODE, bool SH16, int ABITS, int RBITS>
 __global__ __launch_bounds__(kThreads) void quant_kernel(
     const uint16_t *__restrict__ kv, Geometry g, const QuantTab tab,
     uint8_t *__restrict__ anchor, uint8_t *__restrict__ residual, float *__restrict__ gmin_io,
@@ -110,10 +111,13 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
 
     // Global stores every wave issues per block after its staging loads:
     // mu and sigma (2), then at least 4 for the anchor and residual words
-    // (4 with the paper's split, 8 with the others).  Page statistics alone
-    // store from waves 0 and 1 only.
-    constexpr int kBits = 8 - ABITS;              // residual field width
-    constexpr uint32_t kBias = (1u << (kBits - 1)) - 1u;  // Stage 4 bias (+7 at 4 + 4)
+    // (4 with the paper's split, ABITS + RBITS >= 4 otherwise).  Page
+    // statistics alone store from waves 0 and 1 only.
+    constexpr int kBits = RBITS;  // residual field width
+    // Stage 4 bias (+7 at 4 + 4; none for a single stream)
+    constexpr uint32_t kBias = kBits > 0 ? (1u << (kBits - 1)) - 1u : 0u;
+    constexpr bool kNibbles = ABITS == 4 && RBITS == 4;
+    static_assert(ABITS + RBITS >= 4, "fewer stores than the wait counts assume");
     constexpr int kStoresAfterStage =
         MODE == kModeQuantize ? 6 : MODE == kModeBlockStats ? 2 : 0;
     const int tid = (int)__builtin_amdgcn_workitem_id_x();
@@ -121,11 +125,14 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
     const int j = tid / kPairs;        // chunk: tokens 32 j .. 32 j + 31
     const int wave = tid >> 6;         // = j
 
-    // Compander table into LDS, once per workgroup.
+    // Compander table into LDS, once per workgroup.  Above code 127 (the top
+    // of a single 8-bit stream) there is no next threshold: +inf, which no
+    // clamped magnitude reaches.
     if (MODE == kModeQuantize) {
         for (int i = tid; i < tab.nbuckets; i += kThreads) {
             uint32_t c = tab.bucket_code[i];
-            s_tab[i] = u32x2{__float_as_uint(tab.thr[c + 1]), c + kBias};
+            const uint32_t next = c + 1 < 128 ? __float_as_uint(tab.thr[c + 1]) : 0x7f800000u;
+            s_tab[i] = u32x2{next, c + kBias};
         }
     }
     typedef __attribute__((address_space(3))) const u32x2 lds_u32x2;
@@ -366,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
             u32x2 ent = *(lds_u32x2 *)(uintptr_t)addr;
             return ent[1] + (mb >= ent[0] ? 1u : 0u);
         };
-        if constexpr (ABITS == 4) {
+        if constexpr (kNibbles) {
             u32x4 av[2], rv[2];
 #pragma unroll
             for (int q = 0; q < 8; ++q) {  // tokens 4q .. 4q+3
@@ -410,12 +417,14 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
             ro[0] = rv[0];
             ro[1] = rv[1];
         } else {
-            // Other splits: field 2 i + e (token i, channel 2p + e) of the
+            // Other widths: field 2 i + e (token i, channel 2p + e) of the
             // lane's run at bit w (2 i + e); the anchor field is the
             // magnitude J >> b, one's-complemented for a negative quotient,
-            // the residual (J ^ bias) mod 2^b = (-code) mod 2^b.
-            constexpr uint32_t kMaskA = (1u << ABITS) - 1u, kMaskR = (1u << kBits) - 1u;
-            uint32_t aw[2 * ABITS], rw[2 * kBits];
+            // the residual (J ^ bias) mod 2^b = (-code) mod 2^b.  A single
+            // stream (b = 0) stores the whole code in the anchor field.
+            constexpr uint32_t kMaskA = (1u << ABITS) - 1u;
+            constexpr uint32_t kMaskR = kBits > 0 ? (1u << kBits) - 1u : 0u;
+            uint32_t aw[2 * ABITS], rw[kBits > 0 ? 2 * kBits : 1];
 #pragma unroll
             for (int d = 0; d < 2 * ABITS; ++d) aw[d] = 0u;
 #pragma unroll
@@ -427,7 +436,8 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
                     const uint32_t J = code_j(x[i][e]);
                     const uint32_t neg = (uint32_t)((int32_t)__float_as_uint(x[i][e]) >> 31);
                     put_field<ABITS>(aw, 2 * i + e, ((J >> kBits) ^ neg) & kMaskA);
-                    put_field<kBits>(rw, 2 * i + e, (J ^ kBias) & kMaskR);
+                    if constexpr (kBits > 0)
+                        put_field<kBits>(rw, 2 * i + e, (J ^ kBias) & kMaskR);
                 }
             // Run of 8 w bytes per (chunk, pair), 4096 w bytes per block.
             const int64_t aoff = b * (kPage * kHead / 8 * ABITS) +
@@ -448,7 +458,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
 
 // Workgroups resident on the device (per kernel variant), cached per device.
 static int resident_workgroups(const void *kernel, int slot, int threads) {
-    static int cache[64][10];
+    static int cache[64][14];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
         return 1024;
@@ -461,63 +471,69 @@ static int resident_workgroups(const void *kernel, int slot, int threads) {
     return cache[dev][slot];
 }
 
-template <int MODE, bool SH16, int ABITS>
+template <int MODE, bool SH16, int ABITS, int RBITS>
 static hipError_t launch_variant(int slot, const uint16_t *kv, const Geometry &g,
                                  const QuantTab &tab, uint8_t *anchor, uint8_t *residual,
                                  float *gmin, float *gscale, float *mu, float *sigma,
                                  hipStream_t stream) {
-    const int64_t res =
-        resident_workgroups((const void *)quant_kernel<MODE, SH16, ABITS>, slot, kThreads);
+    const int64_t res = resident_workgroups(
+        (const void *)quant_kernel<MODE, SH16, ABITS, RBITS>, slot, kThreads);
     Geometry gl = g;
     gl.grid_wgs = g.nblocks < res ? g.nblocks : res;
-    hipLaunchKernelGGL((quant_kernel<MODE, SH16, ABITS>), dim3((unsigned)gl.grid_wgs),
+    hipLaunchKernelGGL((quant_kernel<MODE, SH16, ABITS, RBITS>), dim3((unsigned)gl.grid_wgs),
                        dim3(kThreads), 0, stream, kv, gl, tab, anchor, residual, gmin, gscale,
                        mu, sigma);
     return hipGetLastError();
 }
 
-template <int ABITS>
+template <int ABITS, int RBITS>
 static hipError_t launch_split(int slot, const uint16_t *kv, const Geometry &g,
                                const QuantTab &tab, uint8_t *anchor, uint8_t *residual,
                                float *gmin, float *gscale, float *mu, float *sigma,
                                hipStream_t stream) {
     if (tab.shift == 16)
-        return launch_variant<kModeQuantize, true, ABITS>(slot, kv, g, tab, anchor, residual,
-                                                          gmin, gscale, mu, sigma, stream);
-    return launch_variant<kModeQuantize, false, ABITS>(slot + 1, kv, g, tab, anchor, residual,
-                                                       gmin, gscale, mu, sigma, stream);
+        return launch_variant<kModeQuantize, true, ABITS, RBITS>(
+            slot, kv, g, tab, anchor, residual, gmin, gscale, mu, sigma, stream);
+    return launch_variant<kModeQuantize, false, ABITS, RBITS>(
+        slot + 1, kv, g, tab, anchor, residual, gmin, gscale, mu, sigma, stream);
 }
 
 hipError_t launch_quantize(const uint16_t *kv, const Geometry &g, const QuantTab &tab,
                            uint8_t *anchor, uint8_t *residual, float *gmin, float *gscale,
                            float *mu, float *sigma, int mode, int anchor_bits,
-                           hipStream_t stream) {
+                           int residual_bits, hipStream_t stream) {
     if (g.nblocks == 0)
         return hipSuccess;
     switch (mode) {
     case kModeQuantize:
-        switch (anchor_bits) {
-        case 3:
-            return launch_split<3>(4, kv, g, tab, anchor, residual, gmin, gscale, mu, sigma,
-                                   stream);
-        case 4:
-            return launch_split<4>(0, kv, g, tab, anchor, residual, gmin, gscale, mu, sigma,
-                                   stream);
-        case 5:
-            return launch_split<5>(6, kv, g, tab, anchor, residual, gmin, gscale, mu, sigma,
-                                   stream);
-        case 6:
-            return launch_split<6>(8, kv, g, tab, anchor, residual, gmin, gscale, mu, sigma,
-                                   stream);
+        switch (anchor_bits * 16 + residual_bits) {
+        case 3 * 16 + 5:
+            return launch_split<3, 5>(4, kv, g, tab, anchor, residual, gmin, gscale, mu, sigma,
+                                      stream);
+        case 4 * 16 + 4:
+            return launch_split<4, 4>(0, kv, g, tab, anchor, residual, gmin, gscale, mu, sigma,
+                                      stream);
+        case 5 * 16 + 3:
+            return launch_split<5, 3>(6, kv, g, tab, anchor, residual, gmin, gscale, mu, sigma,
+                                      stream);
+        case 6 * 16 + 2:
+            return launch_split<6, 2>(8, kv, g, tab, anchor, residual, gmin, gscale, mu, sigma,
+                                      stream);
+        case 4 * 16 + 0:
+            return launch_split<4, 0>(10, kv, g, tab, anchor, residual, gmin, gscale, mu,
+                                      sigma, stream);
+        case 8 * 16 + 0:
+            return launch_split<8, 0>(12, kv, g, tab, anchor, residual, gmin, gscale, mu,
+                                      sigma, stream);
         default:
             return hipErrorInvalidValue;
         }
     case kModePageStats:
-        return launch_variant<kModePageStats, false, 4>(2, kv, g, tab, anchor, residual, gmin,
-                                                        gscale, mu, sigma, stream);
+        return launch_variant<kModePageStats, false, 4, 4>(2, kv, g, tab, anchor, residual,
+                                                           gmin, gscale, mu, sigma, stream);
     default:
-        return launch_variant<kModeBlockStats, false, 4>(3, kv, g, tab, anchor, residual, gmin,
-                                                         gscale, mu, sigma, stream);
+        return launch_variant<kModeBlockStats, false, 4, 4>(3, kv, g, tab, anchor, residual,
+                                                            gmin, gscale, mu, sigma, stream);
     }
 }
 

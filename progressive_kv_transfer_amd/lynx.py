@@ -33,7 +33,7 @@ class lynx_params(ctypes.Structure):
     _fields_ = [("alpha", ctypes.c_float), ("eps", ctypes.c_float),
                 ("code_scale", ctypes.c_float), ("page_tokens", ctypes.c_int32),
                 ("chunk_tokens", ctypes.c_int32), ("block_channels", ctypes.c_int32),
-                ("anchor_bits", ctypes.c_int32)]
+                ("anchor_bits", ctypes.c_int32), ("residual_bits", ctypes.c_int32)]
 
 
 class lynx_kv_shape(ctypes.Structure):
@@ -134,18 +134,25 @@ def _check(fn, rc):
         raise LynxError(fn, rc, lib().lynx_status_string(rc).decode())
 
 
-def params(alpha=255.0, eps=1e-6, code_scale=120.0, anchor_bits=4) -> lynx_params:
-    """Method parameters; anchor_bits = width of the anchor field (4 = the
-    paper's split, 3..6 for the other splits of the 8-bit code)."""
+def params(alpha=255.0, eps=1e-6, code_scale=120.0, anchor_bits=4,
+           residual_bits=None) -> lynx_params:
+    """Method parameters; anchor_bits, residual_bits = widths of the anchor
+    and residual fields: 4 + 4 is the paper's split, 3..6 + 8 - a the other
+    splits of the 8-bit code (residual_bits None means 8 - anchor_bits), and
+    residual_bits = 0 with anchor_bits 4 or 8 a single stream (the paper's
+    Lynx-INT4 / Lynx-INT8, with code_scale 7 / 127)."""
     p = lynx_params()
     lib().lynx_default_params(ctypes.byref(p))
     p.alpha, p.eps, p.code_scale, p.anchor_bits = alpha, eps, code_scale, anchor_bits
+    p.residual_bits = 8 - anchor_bits if residual_bits is None else residual_bits
     return p
 
 
-def code_max(anchor_bits: int = 4) -> int:
-    """Largest code of the split: 128 - 2^(7 - anchor_bits) (120 for 4 + 4)."""
-    return 128 - (1 << (7 - anchor_bits))
+def code_max(anchor_bits: int = 4, residual_bits: int | None = None) -> int:
+    """Largest storable code: 128 - 2^(b - 1) for a split (120 for 4 + 4),
+    2^(a - 1) - 1 for a single stream (b = 0)."""
+    b = 8 - anchor_bits if residual_bits is None else residual_bits
+    return (1 << (anchor_bits - 1)) - 1 if b == 0 else 128 - (1 << (b - 1))
 
 
 def shape_of(kv: torch.Tensor) -> lynx_kv_shape:
@@ -208,17 +215,20 @@ class Codes:
                 self.sigma)
 
 
-def alloc_codes(nblocks: int, device, pin_memory: bool = False, anchor_bits: int = 4) -> Codes:
+def alloc_codes(nblocks: int, device, pin_memory: bool = False, anchor_bits: int = 4,
+                residual_bits: int | None = None) -> Codes:
     """Code buffers for nblocks page blocks on `device`; on the CPU with
     pin_memory=True they are pinned host memory (a transfer's wire).  The
     streams hold [block][chunk][channel pair][run of 8 w bytes] with
-    w = anchor_bits for the anchor, 8 - anchor_bits for the residual (for
-    w = 4 the run is the pair's 32 tokens, one byte each)."""
+    w = anchor_bits for the anchor, residual_bits (default 8 - anchor_bits)
+    for the residual (for w = 4 the run is the pair's 32 tokens, one byte
+    each); a single stream (residual_bits 0) has an empty residual."""
+    b = 8 - anchor_bits if residual_bits is None else residual_bits
     u8 = dict(dtype=torch.uint8, device=device, pin_memory=pin_memory)
     f32 = dict(dtype=torch.float32, device=device, pin_memory=pin_memory)
     tile = (nblocks, PAGE_TOKENS // CHUNK_TOKENS, BLOCK_CHANNELS // 2)
     return Codes(torch.empty(tile + (8 * anchor_bits,), **u8),
-                 torch.empty(tile + (8 * (8 - anchor_bits),), **u8),
+                 torch.empty(tile + (8 * b,), **u8),
                  torch.empty((nblocks, BLOCK_CHANNELS), **f32),
                  torch.empty((nblocks, BLOCK_CHANNELS), **f32),
                  torch.empty((nblocks, PAGE_TOKENS // CHUNK_TOKENS, BLOCK_CHANNELS), **f32),
@@ -245,11 +255,14 @@ def quantize_pages(kv: torch.Tensor, p: lynx_params | None = None,
         raise ValueError("KV must be bfloat16")
     sh = shape_of(kv)
     nb = num_blocks(sh)
-    codes = out if out is not None else alloc_codes(nb, kv.device,
-                                                    anchor_bits=p.anchor_bits if p else 4)
+    codes = out if out is not None else alloc_codes(
+        nb, kv.device, anchor_bits=p.anchor_bits if p else 4,
+        residual_bits=p.residual_bits if p else 4)
+    single = p is not None and p.residual_bits == 0
     _check("lynx_quantize_pages", lib().lynx_quantize_pages(
         kv.data_ptr(), ctypes.byref(sh), ctypes.byref(p) if p else None,
-        codes.anchor.data_ptr(), codes.residual.data_ptr(), codes.meta(), _stream(stream)))
+        codes.anchor.data_ptr(), None if single else codes.residual.data_ptr(), codes.meta(),
+        _stream(stream)))
     return codes
 
 

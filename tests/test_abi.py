@@ -323,10 +323,10 @@ def test_split_parameters_and_stream_sizes():
     assert p.anchor_bits == 4
     sh = lynx.lynx_kv_shape(1, 256 * 128, 256, 128, 128)
     assert L.lynx_stream_bytes(ctypes.byref(sh)) == 16384
-    for bits_ in range(1, 8):
+    for bits_ in range(1, 9):
         assert L.lynx_field_stream_bytes(ctypes.byref(sh), bits_) == 4096 * bits_
     assert L.lynx_field_stream_bytes(ctypes.byref(sh), 0) == 0
-    assert L.lynx_field_stream_bytes(ctypes.byref(sh), 8) == 0
+    assert L.lynx_field_stream_bytes(ctypes.byref(sh), 9) == 0
     thr = np.zeros(128, np.float32)
     for a, top in ((3, 112), (4, 120), (5, 124), (6, 126)):
         q = lynx.params(code_scale=127.0, anchor_bits=a)
@@ -348,3 +348,39 @@ def test_split_parameters_and_stream_sizes():
     assert L.lynx_split_stream_transfer(FAKE, ctypes.byref(sh), ctypes.byref(q5), 1, c, c, c,
                                         FAKE, FAKE, 0, None, None, None, None,
                                         ctypes.byref(t)) == -1
+
+
+def test_single_stream_parameters():
+    """residual_bits = 0 with anchor_bits 4 or 8 (Lynx-INT4 / Lynx-INT8) is
+    accepted by the codec calls with no residual buffer; the compander tops
+    out at 2^(a-1) - 1; a residual buffer, the residual phase, attention and
+    the transfer are refused, and so are widths that are neither a split of
+    the 8-bit code nor a built single stream."""
+    L = lynx.lib()
+    sh = lynx.lynx_kv_shape(1, 256 * 128, 256, 128, 128)
+    m = lynx.lynx_meta(FAKE, FAKE, FAKE, FAKE)
+    thr = np.zeros(128, np.float32)
+    for a, cs in ((4, 7.0), (8, 127.0)):
+        q = lynx.params(code_scale=cs, anchor_bits=a, residual_bits=0)
+        assert q.residual_bits == 0
+        assert L.lynx_compander_thresholds(ctypes.byref(q), thr.ctypes.data) == 0
+        top = (1 << (a - 1)) - 1
+        assert lynx.code_max(a, 0) == top
+        assert np.isfinite(thr[top]) and np.all(np.isinf(thr[top + 1:])), a
+        # a residual buffer for a single stream is an argument error
+        assert L.lynx_quantize_pages(FAKE, ctypes.byref(sh), ctypes.byref(q), FAKE, FAKE, m,
+                                     None) == -1
+        assert L.lynx_dequant_full(FAKE, FAKE, m, ctypes.byref(sh), ctypes.byref(q), FAKE,
+                                   None) == -1
+        assert L.lynx_decode_attn_dequant(FAKE, 1, 8, FAKE, None, m, FAKE, None, m, 256, 1,
+                                          128, 0.1, 0, ctypes.byref(q), FAKE, 0, FAKE,
+                                          1 << 20, None) == -1
+    # the paper's split needs its residual buffer
+    q44 = lynx.params()
+    assert L.lynx_quantize_pages(FAKE, ctypes.byref(sh), ctypes.byref(q44), FAKE, None, m,
+                                 None) == -1
+    for a, b in ((4, 5), (8, 4), (5, 0), (3, 0), (6, 0), (2, 6), (7, 1), (4, 3)):
+        q = lynx.params(anchor_bits=a, residual_bits=b)
+        assert L.lynx_compander_thresholds(ctypes.byref(q), thr.ctypes.data) == -1, (a, b)
+        assert L.lynx_quantize_pages(FAKE, ctypes.byref(sh), ctypes.byref(q), FAKE, FAKE, m,
+                                     None) == -1, (a, b)
