@@ -21,9 +21,10 @@ blocks): the link alone and the pipelined quantize -> anchor link ->
 residual link -> rebuild, and how much of the codec time the pipeline hides.
 
 `split_variants` reports the other splits of the 8-bit code (3 + 5, 5 + 3,
-6 + 2 beside the paper's 4 + 4) on the same set: stream bytes, kernel
-times and the reconstruction error (NMSE) of the anchor alone and of the
-full code.
+6 + 2 beside the paper's 4 + 4) and the single streams of the paper's
+Lynx-INT4 and Lynx-INT8 (4 + 0, 8 + 0) on the same set: stream bytes,
+kernel times and the reconstruction error (NMSE) of the anchor alone and of
+the full code.
 
 `verify` reports the speculative verification (lynx_spec_verify) of 8
 drafts over a 151936-token vocabulary: time per call and logit bytes per
@@ -330,25 +331,29 @@ def measure_verify(torch, kvgen, lynx, calls: int = 200, sets: int = 32):
             "input_sets": sets}
 
 
-SPLITS = (3, 4, 5, 6)  # anchor bits of the splits of the 8-bit code (4 = the paper's)
+# (anchor bits, residual bits): the splits of the 8-bit code (4 + 4 = the
+# paper's) and the single streams of the paper's Lynx-INT4 / Lynx-INT8
+FIELD_WIDTHS = ((3, 5), (4, 4), (5, 3), (6, 2), (4, 0), (8, 0))
 
 
 def measure_splits(torch, lynx, kv, out, reps: int = 5, acc_tensors: int = 8):
-    """The splits of the 8-bit code on the same set, each at its own code
-    range (128 - 2^(7 - a), nothing clipped): bytes per element of the two
-    streams (+ metadata), kernel times (HIP events, average of `reps`
-    launches, best of 3 rounds), and
-    the reconstruction error of the first `acc_tensors` tensors as NMSE =
+    """The splits of the 8-bit code and the single streams (the paper's
+    Lynx-INT4 / Lynx-INT8) on the same set, each at its own code range
+    (128 - 2^(b - 1) for a split, 2^(a - 1) - 1 for a single stream,
+    nothing clipped): bytes per element of the streams (+ metadata), kernel
+    times (HIP events, average of `reps` launches, best of 3 rounds), and the
+    reconstruction error of the first `acc_tensors` tensors as NMSE =
     sum (x^ - x)^2 / sum x^2 for the anchor alone and for anchor + residual."""
     stream = torch.cuda.current_stream()
     nb = kv.numel() // (256 * 128)
     res = {}
-    for a in SPLITS:
-        p = lynx.params(code_scale=float(lynx.code_max(a)), anchor_bits=a)
-        codes = lynx.alloc_codes(nb, "cuda", anchor_bits=a)
+    for a, b in FIELD_WIDTHS:
+        p = lynx.params(code_scale=float(lynx.code_max(a, b)), anchor_bits=a, residual_bits=b)
+        codes = lynx.alloc_codes(nb, "cuda", anchor_bits=a, residual_bits=b)
         calls = {"quantize": lambda: lynx.quantize_pages(kv, p, out=codes, stream=stream),
-                 "dequant_anchor": lambda: lynx.dequant_anchor(codes, out, p, stream=stream),
-                 "dequant_full": lambda: lynx.dequant_full(codes, out, p, stream=stream)}
+                 "dequant_anchor": lambda: lynx.dequant_anchor(codes, out, p, stream=stream)}
+        if b:
+            calls["dequant_full"] = lambda: lynx.dequant_full(codes, out, p, stream=stream)
         times = {}
         for name, fn in calls.items():
             fn()
@@ -364,7 +369,7 @@ def measure_splits(torch, lynx, kv, out, reps: int = 5, acc_tensors: int = 8):
                 best = min(best, e0.elapsed_time(e1) / reps)
             times[name + "_ms"] = round(best, 4)
         err = {}
-        for full in (False, True):
+        for full in (False, True) if b else (False,):
             (lynx.dequant_full if full else lynx.dequant_anchor)(codes, out, p, stream=stream)
             num = den = 0.0
             for t in range(acc_tensors):
@@ -372,10 +377,10 @@ def measure_splits(torch, lynx, kv, out, reps: int = 5, acc_tensors: int = 8):
                 num += float(((out[t].float() - x) ** 2).sum())
                 den += float((x ** 2).sum())
             err["full_nmse" if full else "anchor_nmse"] = float(f"{num / den:.4g}")
-        res[f"{a}+{8 - a}"] = {"code_scale": p.code_scale,
-                               "anchor_bytes_per_elem": a / 8,
-                               "residual_bytes_per_elem": (8 - a) / 8,
-                               "metadata_bytes_per_elem": 0.28125, **times, **err}
+        res[f"{a}+{b}"] = {"code_scale": p.code_scale,
+                           "anchor_bytes_per_elem": a / 8,
+                           "residual_bytes_per_elem": b / 8,
+                           "metadata_bytes_per_elem": 0.28125, **times, **err}
         del codes
     torch.cuda.synchronize()
     return {"workload": WORKLOAD, "accuracy_tensors": acc_tensors, "splits": res}
