@@ -82,14 +82,14 @@ def lib():
                                               ctypes.POINTER(i32)]
             L.oracle_quantize_block_bits.restype = i32
             L.oracle_quantize_block_bits.argtypes = [
-                vp, i64, i32, i32, i32, f32, f32, f32, i32, i32, vp, vp, vp, vp, vp, vp,
-                vp, vp, vp, vp, vp]
+                vp, i64, i32, i32, i32, f32, f32, f32, i32, i32, i32, vp, vp, vp, vp, vp,
+                vp, vp, vp, vp, vp, vp]
             L.oracle_dequant_block_bits.restype = i32
             L.oracle_dequant_block_bits.argtypes = [
                 vp, vp, vp, vp, vp, vp, i32, i32, i32, f32, f32, f32, i32, i32, vp, i64]
             L.oracle_quantize_bits.restype = i32
             L.oracle_quantize_bits.argtypes = [
-                vp, i64, i64, i64, i64, i64, i32, i32, i32, f32, f32, f32, i32, i32,
+                vp, i64, i64, i64, i64, i64, i32, i32, i32, f32, f32, f32, i32, i32, i32,
                 i64, i64, i64, vp, vp, vp, vp, vp, vp]
             L.oracle_dequant_bits.restype = i32
             L.oracle_dequant_bits.argtypes = [
@@ -188,14 +188,17 @@ class BlockResult:
 
 
 def quantize_block(x_bf16: np.ndarray, alpha=255.0, eps=1e-6, code_scale=CODE_SCALE,
-                   C=C_DEFAULT, anchor_bits=4, residual_bits=None) -> BlockResult:
-    """Quantize one page block given token-major as uint16 bf16 bits [P][H]."""
+                   C=C_DEFAULT, anchor_bits=4, residual_bits=None,
+                   meta_bits=32) -> BlockResult:
+    """Quantize one page block given token-major as uint16 bf16 bits [P][H].
+    meta_bits = 16: the statistics are rounded to bfloat16 where they are
+    produced (their float32 arrays then hold bfloat16 values)."""
     x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
     P, H = x.shape
     r = BlockResult(H, P, C, anchor_bits, residual_bits)
     rc = lib().oracle_quantize_block_bits(
         _ptr(x), H, H, P, C, alpha, eps, code_scale, anchor_bits, r.residual_bits,
-        _ptr(r.anchor), _ptr(r.residual) if r.residual_bits else None, _ptr(r.gamma_min), _ptr(r.gamma_scale), _ptr(r.mu),
+        meta_bits, _ptr(r.anchor), _ptr(r.residual) if r.residual_bits else None, _ptr(r.gamma_min), _ptr(r.gamma_scale), _ptr(r.mu),
         _ptr(r.sigma), _ptr(r.xn), _ptr(r.xcent), _ptr(r.xfinal),
         _ptr(r.code_raw), _ptr(r.sign))
     if rc:
@@ -250,7 +253,7 @@ def _ranges(n, parts):
 def quantize(kv: np.ndarray, alpha=255.0, eps=1e-6, code_scale=CODE_SCALE,
              H=H_DEFAULT, P=P_DEFAULT, C=C_DEFAULT, threads=1,
              blocks: tuple[int, int] | None = None, anchor_bits=4,
-             residual_bits=None) -> Codes:
+             residual_bits=None, meta_bits=32) -> Codes:
     """Quantize kv (uint16 bf16 bits, shape [num_tensors, T, Ch]).
 
     ``blocks=(b0, b1)`` restricts the work (and the returned arrays) to page
@@ -268,7 +271,7 @@ def quantize(kv: np.ndarray, alpha=255.0, eps=1e-6, code_scale=CODE_SCALE,
         lo, hi = r
         rc = L.oracle_quantize_bits(
             _ptr(kv), nt, T * Ch, T, Ch, Ch, H, P, C, alpha, eps, code_scale,
-            anchor_bits, out.residual_bits, lo, hi, b0, _ptr(out.anchor),
+            anchor_bits, out.residual_bits, meta_bits, lo, hi, b0, _ptr(out.anchor),
             _ptr(out.residual) if out.residual_bits else None,
             _ptr(out.gamma_min), _ptr(out.gamma_scale), _ptr(out.mu),
             _ptr(out.sigma))

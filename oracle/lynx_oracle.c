@@ -53,7 +53,13 @@
  *     one a-bit field per value and no residual (b = 0): the code of
  *     Eq. (3) with code_scale 2^(a-1) - 1 (7 or 127), its magnitude V = I
  *     in the field, one's-complemented for a negative value as the anchor
- *     is; the largest code is 2^(a-1) - 1.
+ *     is; the largest code is 2^(a-1) - 1;
+ *   - bfloat16 metadata (meta_bits = 16): every statistic is rounded to a
+ *     bfloat16 value where Algorithm 1 produces it and the rounded value is
+ *     used from there on, so that the decoder inverts what the encoder did:
+ *     gamma_min needs no rounding (a minimum of bfloat16 inputs), gamma_scale
+ *     and sigma are rounded up (so X_norm <= 1 and |X_final| <= 1 still
+ *     hold), mu to nearest (ties to even).
  */
 #include <math.h>
 #include <stdint.h>
@@ -82,6 +88,24 @@ static uint16_t f32_to_bf16_rne(float f)
         return (uint16_t)((u >> 16) | 0x0040u);
     u += 0x7fffu + ((u >> 16) & 1u);
     return (uint16_t)(u >> 16);
+}
+
+/* The smallest bfloat16 value >= f, for f >= 0 (bf16 metadata: a scale
+ * rounded up never makes a normalised value exceed 1). */
+static float bf16_ceil_nonneg(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if (u & 0xffffu)
+        u = (u & 0xffff0000u) + 0x10000u; /* next bfloat16 above |f| */
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* f rounded to the nearest bfloat16 value (ties to even), as binary32. */
+static float bf16_nearest(float f)
+{
+    return bf16_to_f32(f32_to_bf16_rne(f));
 }
 
 /* ------------------------------------------------------- Eq. (3), Round -- */
@@ -249,16 +273,18 @@ static int is_pow2(int n) { return n > 0 && (n & (n - 1)) == 0; }
 int oracle_quantize_block_bits(const uint16_t *x, int64_t row_stride, int H,
                                int P, int C, float alpha, float eps,
                                float code_scale, int anchor_bits, int residual_bits,
-                               uint8_t *anchor, uint8_t *residual,
+                               int meta_bits, uint8_t *anchor, uint8_t *residual,
                                float *gamma_min, float *gamma_scale, float *mu,
                                float *sigma, float *xn_out, float *xcent_out,
                                float *xfinal_out, int32_t *code_raw_out,
                                int8_t *sign_out)
 {
     if (H <= 0 || (H & 1) || P <= 0 || !is_pow2(C) || P % C || C % 4 ||
-        !valid_bits(anchor_bits, residual_bits) || (residual_bits > 0 && !residual))
+        !valid_bits(anchor_bits, residual_bits) || (residual_bits > 0 && !residual) ||
+        (meta_bits != 32 && meta_bits != 16))
         return ORACLE_EINVAL;
     const int code_max = oracle_code_max(anchor_bits, residual_bits);
+    const int m16 = meta_bits == 16;
     const int nchunk = P / C;
     float *xn = (float *)malloc(sizeof(float) * (size_t)P);
     float *xc = (float *)malloc(sizeof(float) * (size_t)P);
@@ -280,6 +306,8 @@ int oracle_quantize_block_bits(const uint16_t *x, int64_t row_stride, int H,
         }
         mn = mn + 0.0f;
         float gscale = mx - mn;
+        if (m16)
+            gscale = bf16_ceil_nonneg(gscale);
         float d1 = gscale + eps;
         gamma_min[c] = mn;
         gamma_scale[c] = gscale;
@@ -293,12 +321,16 @@ int oracle_quantize_block_bits(const uint16_t *x, int64_t row_stride, int H,
         for (int j = 0; j < nchunk; ++j) {
             const float *blk = xn + j * C;
             float m = tree_sum(blk, C) / (float)C;
+            if (m16)
+                m = bf16_nearest(m);
             float sg = 0.0f;
             for (int i = 0; i < C; ++i) {
                 xc[j * C + i] = blk[i] - m;
                 float a = fabsf(xc[j * C + i]);
                 if (a > sg) sg = a;
             }
+            if (m16)
+                sg = bf16_ceil_nonneg(sg);
             mu[j * H + c] = m;
             sigma[j * H + c] = sg;
             float d2 = sg + eps;
@@ -362,7 +394,7 @@ int oracle_quantize_block_ex(const uint16_t *x, int64_t row_stride, int H,
                              int8_t *sign_out)
 {
     return oracle_quantize_block_bits(x, row_stride, H, P, C, alpha, eps, code_scale, 4, 4,
-                                      anchor, residual, gamma_min, gamma_scale, mu, sigma,
+                                      32, anchor, residual, gamma_min, gamma_scale, mu, sigma,
                                       xn_out, xcent_out, xfinal_out, code_raw_out, sign_out);
 }
 
@@ -451,8 +483,8 @@ int oracle_quantize_bits(const uint16_t *kv, int64_t num_tensors,
                          int64_t tensor_stride, int64_t T, int64_t Ch,
                          int64_t row_stride, int H, int P, int C, float alpha,
                          float eps, float code_scale, int anchor_bits,
-                         int residual_bits, int64_t block_begin, int64_t block_end,
-                         int64_t out_first_block, uint8_t *anchor,
+                         int residual_bits, int meta_bits, int64_t block_begin,
+                         int64_t block_end, int64_t out_first_block, uint8_t *anchor,
                          uint8_t *residual, float *gamma_min,
                          float *gamma_scale, float *mu, float *sigma)
 {
@@ -475,7 +507,7 @@ int oracle_quantize_bits(const uint16_t *kv, int64_t num_tensors,
         const int64_t o = b - out_first_block;
         int rc = oracle_quantize_block_bits(
             x, row_stride, H, P, C, alpha, eps, code_scale, anchor_bits, residual_bits,
-            anchor + o * anchor_bytes, residual ? residual + o * residual_bytes : NULL,
+            meta_bits, anchor + o * anchor_bytes, residual ? residual + o * residual_bytes : NULL,
             gamma_min + o * H, gamma_scale + o * H, mu + o * chunk_meta,
             sigma + o * chunk_meta, NULL, NULL, NULL, NULL, NULL);
         if (rc)
@@ -494,7 +526,7 @@ int oracle_quantize(const uint16_t *kv, int64_t num_tensors,
                     float *sigma)
 {
     return oracle_quantize_bits(kv, num_tensors, tensor_stride, T, Ch, row_stride, H, P, C,
-                                alpha, eps, code_scale, 4, 4, block_begin, block_end,
+                                alpha, eps, code_scale, 4, 4, 32, block_begin, block_end,
                                 out_first_block, anchor, residual, gamma_min, gamma_scale,
                                 mu, sigma);
 }
