@@ -54,6 +54,7 @@
  *   the value is negative.
  *   gamma_min, gamma_scale   float32 [nblocks][H]
  *   mu, sigma               float32 [nblocks][P/C][H]
+ *   (bfloat16 bit patterns instead of float32 with meta_bits = 16)
  *
  * Numerics: binary32 with one IEEE round-to-nearest-even rounding per step
  * of Algorithm 1 (no contraction); the compander code is the exact
@@ -124,7 +125,13 @@ extern "C" {
  * split; set code_scale to 2^(a - 1) - 1 = 7 or 127, codes above that are
  * clipped).  The anchor and residual streams take 4096 a and 4096 b bytes
  * per block.  Only quantize and the two dequant calls accept other widths
- * than 4 + 4. */
+ * than 4 + 4.  meta_bits is 32 (binary32 metadata, default) or 16: bfloat16
+ * metadata for the 4 + 4 split, each statistic rounded where Algorithm 1
+ * produces it and used rounded from there on (gamma_scale and sigma up,
+ * mu to nearest; gamma_min is already a bfloat16 value); the four lynx_meta
+ * pointers then address arrays of bfloat16 bit patterns (uint16) with the
+ * same element counts, half the bytes.  Only lynx_quantize_pages and the two
+ * dequant calls accept 16. */
 typedef struct lynx_params {
     float alpha;
     float eps;
@@ -134,6 +141,7 @@ typedef struct lynx_params {
     int32_t block_channels;
     int32_t anchor_bits;
     int32_t residual_bits;
+    int32_t meta_bits;
 } lynx_params;
 
 /* Shape of a KV set (element strides, bf16 elements). */
@@ -154,7 +162,7 @@ typedef struct lynx_meta {
 } lynx_meta;
 
 /* Fills *p with alpha = 255, eps = 1e-6, code_scale = 120, P = 256,
- * C = 32, H = 128, anchor_bits = residual_bits = 4. */
+ * C = 32, H = 128, anchor_bits = residual_bits = 4, meta_bits = 32. */
 void lynx_default_params(lynx_params *p);
 
 /* Number of page blocks of a shape, or a negative status if the shape is
@@ -233,6 +241,7 @@ int lynx_page_stats(const void *kv, const lynx_kv_shape *shape,
  * Algorithm 1 Stage 2 statistics alone, given the Stage 1 statistics
  * (read from gamma_min / gamma_scale): mu (balanced pairwise tree mean of
  * the 32 normalised values) and sigma = max |X - mu| of every chunk.
+ * Both statistics calls write binary32 (meta_bits must be 32).
  */
 int lynx_block_stats(const void *kv, const lynx_kv_shape *shape,
                      const lynx_params *params, const float *gamma_min,

@@ -157,6 +157,10 @@ int check_params(const lynx_params &p) {
         return LYNX_EINVAL;
     if (!valid_field_bits(p.anchor_bits, p.residual_bits))
         return LYNX_EINVAL;
+    // bfloat16 metadata is built for the paper's 4 + 4 split
+    if (p.meta_bits != 32 &&
+        !(p.meta_bits == 16 && p.anchor_bits == 4 && p.residual_bits == 4))
+        return LYNX_EINVAL;
     return LYNX_OK;
 }
 
@@ -220,6 +224,8 @@ int quantize_common(const void *kv, const lynx_kv_shape *shape, const lynx_param
         return LYNX_EINVAL;
     if (mode == kModeQuantize && (!anchor || (p.residual_bits > 0) != (residual != nullptr)))
         return LYNX_EINVAL;
+    if (mode != kModeQuantize && p.meta_bits != 32)  // the stats calls write binary32
+        return LYNX_EINVAL;
     for (const void *ptr : {(const void *)kv, (const void *)gmin, (const void *)gscale,
                             (const void *)mu, (const void *)sigma, (const void *)anchor,
                             (const void *)residual})
@@ -236,7 +242,7 @@ int quantize_common(const void *kv, const lynx_kv_shape *shape, const lynx_param
         g.nblocks = (nb - b0) < kMaxLaunchBlocks ? (nb - b0) : kMaxLaunchBlocks;
         rc = hip_status(launch_quantize((const uint16_t *)kv, g, tab, anchor, residual, gmin,
                                         gscale, mu, sigma, mode, p.anchor_bits,
-                                        p.residual_bits, stream));
+                                        p.residual_bits, p.meta_bits, stream));
         if (rc)
             return rc;
     }
@@ -275,7 +281,7 @@ int dequant_common(const uint8_t *anchor, const uint8_t *residual, lynx_meta met
         g.nblocks = (nb - b0) < kMaxLaunchBlocks ? (nb - b0) : kMaxLaunchBlocks;
         rc = hip_status(launch_dequant(anchor, residual, meta.gamma_min, meta.gamma_scale,
                                        meta.mu, meta.sigma, g, tab, (uint16_t *)out,
-                                       p.anchor_bits, p.residual_bits, stream));
+                                       p.anchor_bits, p.residual_bits, p.meta_bits, stream));
         if (rc)
             return rc;
     }
@@ -391,6 +397,7 @@ void lynx_default_params(lynx_params *p) {
     p->block_channels = kHead;
     p->anchor_bits = 4;
     p->residual_bits = 4;
+    p->meta_bits = 32;
 }
 
 int64_t lynx_num_blocks(const lynx_kv_shape *shape) {
@@ -497,7 +504,7 @@ int lynx_decode_attn_dequant(const void *q, int t_q, int num_q_heads, const uint
     int rc = check_params(p);
     if (rc)
         return rc;
-    if (p.anchor_bits != 4 || p.residual_bits != 4)
+    if (p.anchor_bits != 4 || p.residual_bits != 4 || p.meta_bits != 32)
         return LYNX_EINVAL;
     if (head_dim != kHead || !(scale > 0.0f) || !(scale < 1e30f) ||
         (out_dtype != LYNX_OUT_BF16 && out_dtype != LYNX_OUT_F32))
@@ -581,7 +588,7 @@ int lynx_split_stream_transfer(const void *kv, const lynx_kv_shape *shape,
     int rc = check_params(p);
     if (rc)
         return rc;
-    if (p.anchor_bits != 4 || p.residual_bits != 4)
+    if (p.anchor_bits != 4 || p.residual_bits != 4 || p.meta_bits != 32)
         return LYNX_EINVAL;
     int64_t nb = 0;
     if ((rc = check_shape(shape, &nb)))
@@ -645,7 +652,7 @@ int lynx_split_stream_transfer(const void *kv, const lynx_kv_shape *shape,
         if (!copies_only)
             ok(launch_quantize((const uint16_t *)kv, g, qt, tx.anchor, tx.residual,
                                tx.meta.gamma_min, tx.meta.gamma_scale, tx.meta.mu, tx.meta.sigma,
-                               kModeQuantize, 4, 4, sender));
+                               kModeQuantize, 4, 4, 32, sender));
         ok(hipEventRecord(q[i], sender));
         // anchor queue: anchor + metadata over the wire
         ok(hipStreamWaitEvent(anchor_link, q[i], 0));
@@ -662,7 +669,7 @@ int lynx_split_stream_transfer(const void *kv, const lynx_kv_shape *shape,
         if (!copies_only)
             ok(launch_dequant(rx.anchor, nullptr, rx.meta.gamma_min, rx.meta.gamma_scale,
                               rx.meta.mu, rx.meta.sigma, g, dt, (uint16_t *)kv_anchor, 4, 4,
-                              receiver));
+                              32, receiver));
         if (i == 0)
             ok(hipEventRecord(t_da0, receiver));
     }
@@ -681,7 +688,7 @@ int lynx_split_stream_transfer(const void *kv, const lynx_kv_shape *shape,
         if (!copies_only)
             ok(launch_dequant(rx.anchor, rx.residual, rx.meta.gamma_min, rx.meta.gamma_scale,
                               rx.meta.mu, rx.meta.sigma, g, dt, (uint16_t *)kv_full, 4, 4,
-                              receiver));
+                              32, receiver));
     }
     ok(hipEventRecord(t_df, receiver));
     // Blocking: every stream drains before the events go away.

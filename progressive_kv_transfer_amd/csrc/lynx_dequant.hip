@@ -65,7 +65,8 @@ __device__ __forceinline__ uint32_t get_field(const uint32_t *w, int v) {
     return f & ((1u << W) - 1u);
 }
 
-template <bool FULL, int ABITS, int RBITS>
+// M16: bfloat16 metadata (the four arrays hold bfloat16 bit patterns).
+template <bool FULL, int ABITS, int RBITS, bool M16 = false>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(
     const uint8_t *__restrict__ anchor, const uint8_t *__restrict__ residual,
     const float *__restrict__ gmin, const float *__restrict__ gscale,
@@ -139,12 +140,30 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
                     for (int d = 0; d < kBits; ++d) Rw[k][d] = rr[k * 2 * kBits + d];
             }
         }
-        const float4 *gm4 = (const float4 *)(gmin + b * kHead + cg * 8);
-        const float4 *gs4 = (const float4 *)(gscale + b * kHead + cg * 8);
-        const float4 *mu4 = (const float4 *)(mu + b * (kChunks * kHead) + j * kHead + cg * 8);
-        const float4 *sg4 = (const float4 *)(sigma + b * (kChunks * kHead) + j * kHead + cg * 8);
-        const float4 m0 = gm4[0], m1 = gm4[1], c0 = gs4[0], c1 = gs4[1];
-        const float4 u0 = mu4[0], u1 = mu4[1], q0 = sg4[0], q1 = sg4[1];
+        float4 m0, m1, c0, c1, u0, u1, q0, q1;
+        const int64_t goff = b * kHead + cg * 8;
+        const int64_t coff8 = b * (kChunks * kHead) + j * kHead + cg * 8;
+        if constexpr (M16) {
+            // 8 channels = 16 bytes of bfloat16 per array
+            auto widen = [](const float *base, int64_t off, float4 &lo, float4 &hi) {
+                const u32x4 w = *(const u32x4 *)((const uint16_t *)base + off);
+                lo = make_float4(__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+                                 __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u));
+                hi = make_float4(__uint_as_float(w[2] << 16), __uint_as_float(w[2] & 0xffff0000u),
+                                 __uint_as_float(w[3] << 16), __uint_as_float(w[3] & 0xffff0000u));
+            };
+            widen(gmin, goff, m0, m1);
+            widen(gscale, goff, c0, c1);
+            widen(mu, coff8, u0, u1);
+            widen(sigma, coff8, q0, q1);
+        } else {
+            const float4 *gm4 = (const float4 *)(gmin + goff);
+            const float4 *gs4 = (const float4 *)(gscale + goff);
+            const float4 *mu4 = (const float4 *)(mu + coff8);
+            const float4 *sg4 = (const float4 *)(sigma + coff8);
+            m0 = gm4[0], m1 = gm4[1], c0 = gs4[0], c1 = gs4[1];
+            u0 = mu4[0], u1 = mu4[1], q0 = sg4[0], q1 = sg4[1];
+        }
         const float gm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
         const float um[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
         const float d1[8] = {c0.x + tab.eps, c0.y + tab.eps, c0.z + tab.eps, c0.w + tab.eps,
@@ -204,42 +223,49 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
 
 }  // namespace
 
-template <bool FULL, int ABITS, int RBITS>
+template <bool FULL, int ABITS, int RBITS, bool M16>
 static hipError_t launch_one(const uint8_t *anchor, const uint8_t *residual,
                              const float *gmin, const float *gscale, const float *mu,
                              const float *sigma, const Geometry &g, const DequantTab &tab,
                              uint16_t *out, hipStream_t stream) {
     Geometry gl = g;
     gl.grid_wgs = g.nblocks;
-    hipLaunchKernelGGL((dequant_kernel<FULL, ABITS, RBITS>), dim3((unsigned)gl.grid_wgs),
+    hipLaunchKernelGGL((dequant_kernel<FULL, ABITS, RBITS, M16>), dim3((unsigned)gl.grid_wgs),
                        dim3(kThreads), 0, stream, anchor, residual, gmin, gscale, mu, sigma, gl,
                        tab, out);
     return hipGetLastError();
 }
 
-template <int ABITS, int RBITS>
+template <int ABITS, int RBITS, bool M16 = false>
 static hipError_t launch_split(const uint8_t *anchor, const uint8_t *residual,
                                const float *gmin, const float *gscale, const float *mu,
                                const float *sigma, const Geometry &g, const DequantTab &tab,
                                uint16_t *out, hipStream_t stream) {
     if constexpr (RBITS > 0) {
         if (residual)
-            return launch_one<true, ABITS, RBITS>(anchor, residual, gmin, gscale, mu, sigma, g,
-                                                  tab, out, stream);
+            return launch_one<true, ABITS, RBITS, M16>(anchor, residual, gmin, gscale, mu,
+                                                       sigma, g, tab, out, stream);
     } else {
         if (residual)
             return hipErrorInvalidValue;
     }
-    return launch_one<false, ABITS, RBITS>(anchor, residual, gmin, gscale, mu, sigma, g, tab,
-                                           out, stream);
+    return launch_one<false, ABITS, RBITS, M16>(anchor, residual, gmin, gscale, mu, sigma, g,
+                                                tab, out, stream);
 }
 
 hipError_t launch_dequant(const uint8_t *anchor, const uint8_t *residual, const float *gmin,
                           const float *gscale, const float *mu, const float *sigma,
                           const Geometry &g, const DequantTab &tab, uint16_t *out,
-                          int anchor_bits, int residual_bits, hipStream_t stream) {
+                          int anchor_bits, int residual_bits, int meta_bits,
+                          hipStream_t stream) {
     if (g.nblocks == 0)
         return hipSuccess;
+    if (meta_bits == 16) {
+        if (anchor_bits != 4 || residual_bits != 4)
+            return hipErrorInvalidValue;
+        return launch_split<4, 4, true>(anchor, residual, gmin, gscale, mu, sigma, g, tab, out,
+                                        stream);
+    }
     switch (anchor_bits * 16 + residual_bits) {
     case 3 * 16 + 5:
         return launch_split<3, 5>(anchor, residual, gmin, gscale, mu, sigma, g, tab, out,

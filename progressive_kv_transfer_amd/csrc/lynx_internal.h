@@ -72,12 +72,13 @@ enum StatsMode : int { kModeQuantize = 0, kModePageStats = 1, kModeBlockStats = 
 hipError_t launch_quantize(const uint16_t *kv, const Geometry &g, const QuantTab &tab,
                            uint8_t *anchor, uint8_t *residual, float *gmin, float *gscale,
                            float *mu, float *sigma, int mode, int anchor_bits,
-                           int residual_bits, hipStream_t stream);
+                           int residual_bits, int meta_bits, hipStream_t stream);
 
 hipError_t launch_dequant(const uint8_t *anchor, const uint8_t *residual, const float *gmin,
                           const float *gscale, const float *mu, const float *sigma,
                           const Geometry &g, const DequantTab &tab, uint16_t *out,
-                          int anchor_bits, int residual_bits, hipStream_t stream);
+                          int anchor_bits, int residual_bits, int meta_bits,
+                          hipStream_t stream);
 
 // Argument block of the fused dequant + attention kernels.
 struct AttnArgs {

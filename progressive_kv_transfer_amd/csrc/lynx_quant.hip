@@ -50,6 +50,19 @@ __device__ __forceinline__ float div_fast(float a, float d, float r) {
     return __builtin_fmaf(e, r, q);
 }
 
+// bfloat16 metadata: a non-negative scale rounded up to the next bfloat16
+// value (a normalised value then stays <= 1), and a value rounded to the
+// nearest bfloat16 (ties to even), both returned as binary32.
+__device__ __forceinline__ float bf16_up(float x) {
+    uint32_t u = __float_as_uint(x);
+    u = (u & 0xffffu) ? (u | 0xffffu) + 1u : u;
+    return __uint_as_float(u);
+}
+__device__ __forceinline__ float bf16_rne(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return __uint_as_float((u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u);
+}
+
 constexpr float kTiny100 = 0x1p-100f;
 constexpr float kTiny125 = 0x1p-125f;
 constexpr float kHuge125 = 0x1p125f;
@@ -95,8 +108,11 @@ __device__ __forceinline__ void put_field(uint32_t *w, int v, uint32_t f) {
 // SH16: the compander buckets are the upper 16 bits of the magnitude, so the
 // table address is one v_mad_u32_u16 (high half x 8 + base).  ABITS, RBITS:
 // widths of the anchor and residual fields (4 + 4 = the paper's split;
-// RBITS = 0 is a single stream of whole codes).
-template <int MODE, bool SH16, int ABITS, int RBITS>
+// RBITS = 0 is a single stream of whole codes).  M16: bfloat16 metadata:
+// gamma_scale and sigma rounded up and mu to nearest where they are
+// produced, the rounded values used from there on and stored as bfloat16
+// (the metadata pointers then address uint16 arrays).
+template <int MODE, bool SH16, int ABITS, int RBITS, bool M16 = false>
 __global__ __launch_bounds__(kThreads) void quant_kernel(
     const uint16_t *__restrict__ kv, Geometry g, const QuantTab tab,
     uint8_t *__restrict__ anchor, uint8_t *__restrict__ residual, float *__restrict__ gmin_io,
@@ -266,10 +282,16 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
                     a = fminf(a, mn[w * kHead]);
                     m = fmaxf(m, mx[w * kHead]);
                 }
-                gmin = a + 0.0f;  // canonical +0 for a zero minimum
+                gmin = a + 0.0f;  // canonical +0 for a zero minimum (a bf16 value)
                 gsc = m - gmin;
-                gmin_io[meta0 + tid] = gmin;
-                gscale_io[meta0 + tid] = gsc;
+                if (M16) {
+                    gsc = bf16_up(gsc);
+                    ((uint16_t *)gmin_io)[meta0 + tid] = (uint16_t)(__float_as_uint(gmin) >> 16);
+                    ((uint16_t *)gscale_io)[meta0 + tid] = (uint16_t)(__float_as_uint(gsc) >> 16);
+                } else {
+                    gmin_io[meta0 + tid] = gmin;
+                    gscale_io[meta0 + tid] = gsc;
+                }
             }
             float d1 = gsc + tab.eps;
             float r1 = __fdiv_rn(1.0f, d1);
@@ -320,16 +342,25 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
             for (int k = 0; k < 4; ++k) t4[k] = t8[2 * k] + t8[2 * k + 1];
             float s32 = (t4[0] + t4[1]) + (t4[2] + t4[3]);
             mu[e] = s32 * 0.03125f;
+            if (M16)
+                mu[e] = bf16_rne(mu[e]);
             float m = 0.0f;
 #pragma unroll
             for (int i = 0; i < kChunk; ++i) {
                 x[i][e] = x[i][e] - mu[e];
                 m = fmaxf(m, fabsf(x[i][e]));
             }
-            sg[e] = m;
+            sg[e] = M16 ? bf16_up(m) : m;
         }
-        *(float2 *)(mu_out + cmeta0 + 2 * p) = make_float2(mu[0], mu[1]);
-        *(float2 *)(sigma_out + cmeta0 + 2 * p) = make_float2(sg[0], sg[1]);
+        if (M16) {
+            *(uint32_t *)((uint16_t *)mu_out + cmeta0 + 2 * p) =
+                (__float_as_uint(mu[0]) >> 16) | (__float_as_uint(mu[1]) & 0xffff0000u);
+            *(uint32_t *)((uint16_t *)sigma_out + cmeta0 + 2 * p) =
+                (__float_as_uint(sg[0]) >> 16) | (__float_as_uint(sg[1]) & 0xffff0000u);
+        } else {
+            *(float2 *)(mu_out + cmeta0 + 2 * p) = make_float2(mu[0], mu[1]);
+            *(float2 *)(sigma_out + cmeta0 + 2 * p) = make_float2(sg[0], sg[1]);
+        }
         if (MODE == kModeBlockStats)
             continue;
 
@@ -458,7 +489,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
 
 // Workgroups resident on the device (per kernel variant), cached per device.
 static int resident_workgroups(const void *kernel, int slot, int threads) {
-    static int cache[64][14];
+    static int cache[64][16];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
         return 1024;
@@ -471,39 +502,45 @@ static int resident_workgroups(const void *kernel, int slot, int threads) {
     return cache[dev][slot];
 }
 
-template <int MODE, bool SH16, int ABITS, int RBITS>
+template <int MODE, bool SH16, int ABITS, int RBITS, bool M16 = false>
 static hipError_t launch_variant(int slot, const uint16_t *kv, const Geometry &g,
                                  const QuantTab &tab, uint8_t *anchor, uint8_t *residual,
                                  float *gmin, float *gscale, float *mu, float *sigma,
                                  hipStream_t stream) {
     const int64_t res = resident_workgroups(
-        (const void *)quant_kernel<MODE, SH16, ABITS, RBITS>, slot, kThreads);
+        (const void *)quant_kernel<MODE, SH16, ABITS, RBITS, M16>, slot, kThreads);
     Geometry gl = g;
     gl.grid_wgs = g.nblocks < res ? g.nblocks : res;
-    hipLaunchKernelGGL((quant_kernel<MODE, SH16, ABITS, RBITS>), dim3((unsigned)gl.grid_wgs),
+    hipLaunchKernelGGL((quant_kernel<MODE, SH16, ABITS, RBITS, M16>), dim3((unsigned)gl.grid_wgs),
                        dim3(kThreads), 0, stream, kv, gl, tab, anchor, residual, gmin, gscale,
                        mu, sigma);
     return hipGetLastError();
 }
 
-template <int ABITS, int RBITS>
+template <int ABITS, int RBITS, bool M16 = false>
 static hipError_t launch_split(int slot, const uint16_t *kv, const Geometry &g,
                                const QuantTab &tab, uint8_t *anchor, uint8_t *residual,
                                float *gmin, float *gscale, float *mu, float *sigma,
                                hipStream_t stream) {
     if (tab.shift == 16)
-        return launch_variant<kModeQuantize, true, ABITS, RBITS>(
+        return launch_variant<kModeQuantize, true, ABITS, RBITS, M16>(
             slot, kv, g, tab, anchor, residual, gmin, gscale, mu, sigma, stream);
-    return launch_variant<kModeQuantize, false, ABITS, RBITS>(
+    return launch_variant<kModeQuantize, false, ABITS, RBITS, M16>(
         slot + 1, kv, g, tab, anchor, residual, gmin, gscale, mu, sigma, stream);
 }
 
 hipError_t launch_quantize(const uint16_t *kv, const Geometry &g, const QuantTab &tab,
                            uint8_t *anchor, uint8_t *residual, float *gmin, float *gscale,
                            float *mu, float *sigma, int mode, int anchor_bits,
-                           int residual_bits, hipStream_t stream) {
+                           int residual_bits, int meta_bits, hipStream_t stream) {
     if (g.nblocks == 0)
         return hipSuccess;
+    if (meta_bits == 16) {
+        if (mode != kModeQuantize || anchor_bits != 4 || residual_bits != 4)
+            return hipErrorInvalidValue;
+        return launch_split<4, 4, true>(14, kv, g, tab, anchor, residual, gmin, gscale, mu,
+                                        sigma, stream);
+    }
     switch (mode) {
     case kModeQuantize:
         switch (anchor_bits * 16 + residual_bits) {

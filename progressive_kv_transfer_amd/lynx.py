@@ -33,7 +33,8 @@ class lynx_params(ctypes.Structure):
     _fields_ = [("alpha", ctypes.c_float), ("eps", ctypes.c_float),
                 ("code_scale", ctypes.c_float), ("page_tokens", ctypes.c_int32),
                 ("chunk_tokens", ctypes.c_int32), ("block_channels", ctypes.c_int32),
-                ("anchor_bits", ctypes.c_int32), ("residual_bits", ctypes.c_int32)]
+                ("anchor_bits", ctypes.c_int32), ("residual_bits", ctypes.c_int32),
+                ("meta_bits", ctypes.c_int32)]
 
 
 class lynx_kv_shape(ctypes.Structure):
@@ -135,16 +136,18 @@ def _check(fn, rc):
 
 
 def params(alpha=255.0, eps=1e-6, code_scale=120.0, anchor_bits=4,
-           residual_bits=None) -> lynx_params:
+           residual_bits=None, meta_bits=32) -> lynx_params:
     """Method parameters; anchor_bits, residual_bits = widths of the anchor
     and residual fields: 4 + 4 is the paper's split, 3..6 + 8 - a the other
     splits of the 8-bit code (residual_bits None means 8 - anchor_bits), and
     residual_bits = 0 with anchor_bits 4 or 8 a single stream (the paper's
-    Lynx-INT4 / Lynx-INT8, with code_scale 7 / 127)."""
+    Lynx-INT4 / Lynx-INT8, with code_scale 7 / 127); meta_bits = 16 keeps the
+    metadata in bfloat16 (4 + 4 only)."""
     p = lynx_params()
     lib().lynx_default_params(ctypes.byref(p))
     p.alpha, p.eps, p.code_scale, p.anchor_bits = alpha, eps, code_scale, anchor_bits
     p.residual_bits = 8 - anchor_bits if residual_bits is None else residual_bits
+    p.meta_bits = meta_bits
     return p
 
 
@@ -216,16 +219,18 @@ class Codes:
 
 
 def alloc_codes(nblocks: int, device, pin_memory: bool = False, anchor_bits: int = 4,
-                residual_bits: int | None = None) -> Codes:
+                residual_bits: int | None = None, meta_bits: int = 32) -> Codes:
     """Code buffers for nblocks page blocks on `device`; on the CPU with
     pin_memory=True they are pinned host memory (a transfer's wire).  The
     streams hold [block][chunk][channel pair][run of 8 w bytes] with
     w = anchor_bits for the anchor, residual_bits (default 8 - anchor_bits)
     for the residual (for w = 4 the run is the pair's 32 tokens, one byte
-    each); a single stream (residual_bits 0) has an empty residual."""
+    each); a single stream (residual_bits 0) has an empty residual; with
+    meta_bits = 16 the metadata tensors are bfloat16."""
     b = 8 - anchor_bits if residual_bits is None else residual_bits
     u8 = dict(dtype=torch.uint8, device=device, pin_memory=pin_memory)
-    f32 = dict(dtype=torch.float32, device=device, pin_memory=pin_memory)
+    f32 = dict(dtype=torch.bfloat16 if meta_bits == 16 else torch.float32, device=device,
+               pin_memory=pin_memory)
     tile = (nblocks, PAGE_TOKENS // CHUNK_TOKENS, BLOCK_CHANNELS // 2)
     return Codes(torch.empty(tile + (8 * anchor_bits,), **u8),
                  torch.empty(tile + (8 * b,), **u8),
@@ -257,7 +262,7 @@ def quantize_pages(kv: torch.Tensor, p: lynx_params | None = None,
     nb = num_blocks(sh)
     codes = out if out is not None else alloc_codes(
         nb, kv.device, anchor_bits=p.anchor_bits if p else 4,
-        residual_bits=p.residual_bits if p else 4)
+        residual_bits=p.residual_bits if p else 4, meta_bits=p.meta_bits if p else 32)
     single = p is not None and p.residual_bits == 0
     _check("lynx_quantize_pages", lib().lynx_quantize_pages(
         kv.data_ptr(), ctypes.byref(sh), ctypes.byref(p) if p else None,

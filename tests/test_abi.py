@@ -384,3 +384,34 @@ def test_single_stream_parameters():
         assert L.lynx_compander_thresholds(ctypes.byref(q), thr.ctypes.data) == -1, (a, b)
         assert L.lynx_quantize_pages(FAKE, ctypes.byref(sh), ctypes.byref(q), FAKE, FAKE, m,
                                      None) == -1, (a, b)
+
+
+def test_bf16_metadata_parameters():
+    """meta_bits: 32 by default, 16 accepted by the codec calls for the 4 + 4
+    split only, refused by the statistics calls, attention and the
+    transfer, and any other width refused."""
+    L = lynx.lib()
+    sh = lynx.lynx_kv_shape(1, 256 * 128, 256, 128, 128)
+    m = lynx.lynx_meta(FAKE, FAKE, FAKE, FAKE)
+    thr = np.zeros(128, np.float32)
+    assert lynx.params().meta_bits == 32
+    q16 = lynx.params(meta_bits=16)
+    assert L.lynx_compander_thresholds(ctypes.byref(q16), thr.ctypes.data) == 0
+    for bad in (lynx.params(meta_bits=8), lynx.params(meta_bits=64),
+                lynx.params(meta_bits=16, anchor_bits=5),
+                lynx.params(meta_bits=16, code_scale=127.0, anchor_bits=8, residual_bits=0)):
+        assert L.lynx_compander_thresholds(ctypes.byref(bad), thr.ctypes.data) == -1
+        assert L.lynx_quantize_pages(FAKE, ctypes.byref(sh), ctypes.byref(bad), FAKE, FAKE, m,
+                                     None) == -1
+    assert L.lynx_page_stats(FAKE, ctypes.byref(sh), ctypes.byref(q16), FAKE, FAKE,
+                             None) == -1
+    assert L.lynx_block_stats(FAKE, ctypes.byref(sh), ctypes.byref(q16), FAKE, FAKE, FAKE,
+                              FAKE, None) == -1
+    assert L.lynx_decode_attn_dequant(FAKE, 1, 8, FAKE, FAKE, m, FAKE, FAKE, m, 256, 1, 128,
+                                      0.1, 0, ctypes.byref(q16), FAKE, 0, FAKE, 1 << 20,
+                                      None) == -1
+    c = lynx.lynx_codes(FAKE, FAKE, m)
+    t = lynx.lynx_transfer_times()
+    assert L.lynx_split_stream_transfer(FAKE, ctypes.byref(sh), ctypes.byref(q16), 1, c, c, c,
+                                        FAKE, FAKE, 0, None, None, None, None,
+                                        ctypes.byref(t)) == -1
