@@ -21,10 +21,10 @@ blocks): the link alone and the pipelined quantize -> anchor link ->
 residual link -> rebuild, and how much of the codec time the pipeline hides.
 
 `split_variants` reports the other splits of the 8-bit code (3 + 5, 5 + 3,
-6 + 2 beside the paper's 4 + 4) and the single streams of the paper's
-Lynx-INT4 and Lynx-INT8 (4 + 0, 8 + 0) on the same set: stream bytes,
-kernel times and the reconstruction error (NMSE) of the anchor alone and of
-the full code.
+6 + 2 beside the paper's 4 + 4), the single streams of the paper's
+Lynx-INT4 and Lynx-INT8 (4 + 0, 8 + 0) and the 4 + 4 split with bfloat16
+metadata on the same set: stream bytes, kernel times and the
+reconstruction error (NMSE) of the anchor alone and of the full code.
 
 `verify` reports the speculative verification (lynx_spec_verify) of 8
 drafts over a 151936-token vocabulary: time per call and logit bytes per
@@ -331,9 +331,11 @@ def measure_verify(torch, kvgen, lynx, calls: int = 200, sets: int = 32):
             "input_sets": sets}
 
 
-# (anchor bits, residual bits): the splits of the 8-bit code (4 + 4 = the
-# paper's) and the single streams of the paper's Lynx-INT4 / Lynx-INT8
-FIELD_WIDTHS = ((3, 5), (4, 4), (5, 3), (6, 2), (4, 0), (8, 0))
+# (anchor bits, residual bits, metadata bits): the splits of the 8-bit code
+# (4 + 4 = the paper's), the single streams of the paper's Lynx-INT4 /
+# Lynx-INT8, and the paper's split with bfloat16 metadata
+FORMATS = ((3, 5, 32), (4, 4, 32), (5, 3, 32), (6, 2, 32), (4, 0, 32), (8, 0, 32),
+           (4, 4, 16))
 
 
 def measure_splits(torch, lynx, kv, out, reps: int = 5, acc_tensors: int = 8):
@@ -347,9 +349,10 @@ def measure_splits(torch, lynx, kv, out, reps: int = 5, acc_tensors: int = 8):
     stream = torch.cuda.current_stream()
     nb = kv.numel() // (256 * 128)
     res = {}
-    for a, b in FIELD_WIDTHS:
-        p = lynx.params(code_scale=float(lynx.code_max(a, b)), anchor_bits=a, residual_bits=b)
-        codes = lynx.alloc_codes(nb, "cuda", anchor_bits=a, residual_bits=b)
+    for a, b, mb in FORMATS:
+        p = lynx.params(code_scale=float(lynx.code_max(a, b)), anchor_bits=a, residual_bits=b,
+                        meta_bits=mb)
+        codes = lynx.alloc_codes(nb, "cuda", anchor_bits=a, residual_bits=b, meta_bits=mb)
         calls = {"quantize": lambda: lynx.quantize_pages(kv, p, out=codes, stream=stream),
                  "dequant_anchor": lambda: lynx.dequant_anchor(codes, out, p, stream=stream)}
         if b:
@@ -377,10 +380,10 @@ def measure_splits(torch, lynx, kv, out, reps: int = 5, acc_tensors: int = 8):
                 num += float(((out[t].float() - x) ** 2).sum())
                 den += float((x ** 2).sum())
             err["full_nmse" if full else "anchor_nmse"] = float(f"{num / den:.4g}")
-        res[f"{a}+{b}"] = {"code_scale": p.code_scale,
-                           "anchor_bytes_per_elem": a / 8,
-                           "residual_bytes_per_elem": b / 8,
-                           "metadata_bytes_per_elem": 0.28125, **times, **err}
+        res[f"{a}+{b}" + ("" if mb == 32 else "/bf16-metadata")] = {
+            "code_scale": p.code_scale, "anchor_bytes_per_elem": a / 8,
+            "residual_bytes_per_elem": b / 8, "metadata_bytes_per_elem": 0.28125 * mb / 32,
+            **times, **err}
         del codes
     torch.cuda.synchronize()
     return {"workload": WORKLOAD, "accuracy_tensors": acc_tensors, "splits": res}
