@@ -27,10 +27,10 @@ _CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 CODEC_SOURCES = ("lynx_quant.hip", "lynx_dequant.hip", "lynx_recon.h", "lynx_internal.h")
 # kernel symbol -> (name, algorithmic HBM bytes per bf16 element)
 CODEC_KERNELS = {
-    "lynx::quant_kernel<0, true, 4>": ("quantize", 2.0 + 0.5 + 0.5 + 0.28125),
-    "lynx::quant_kernel<0, false, 4>": ("quantize", 2.0 + 0.5 + 0.5 + 0.28125),
-    "lynx::dequant_kernel<false, 4>": ("dequant_anchor", 0.5 + 0.28125 + 2.0),
-    "lynx::dequant_kernel<true, 4>": ("dequant_full", 0.5 + 0.5 + 0.28125 + 2.0),
+    "lynx::quant_kernel<0, true, 4, 4, false>": ("quantize", 2.0 + 0.5 + 0.5 + 0.28125),
+    "lynx::quant_kernel<0, false, 4, 4, false>": ("quantize", 2.0 + 0.5 + 0.5 + 0.28125),
+    "lynx::dequant_kernel<false, 4, 4, false>": ("dequant_anchor", 0.5 + 0.28125 + 2.0),
+    "lynx::dequant_kernel<true, 4, 4, false>": ("dequant_full", 0.5 + 0.5 + 0.28125 + 2.0),
 }
 COPY_BYTES = 1 << 30
 
