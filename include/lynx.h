@@ -321,15 +321,19 @@ typedef struct lynx_transfer_times {
  * the Residual arrives).
  *
  * The set's page blocks (block order of the layouts above) are cut into
- * objects of object_blocks blocks.  Per object i:
+ * objects of object_blocks blocks.  The wire has two hops, out (tx ->
+ * wire) and in (wire -> rx), one stream each, so the two directions of the
+ * link run at once.  Per object i:
  *   sender stream:   quantize the object into tx;
- *   anchor_link:     after it, copy its anchor and metadata tx -> wire -> rx;
- *   residual_link:   after the anchor copy of the same object, copy its
- *                    residual tx -> wire -> rx;
- *   receiver stream: after the anchor copy, rebuild the object from the
- *                    anchor into kv_anchor;
- * then, once every object is rebuilt from its anchor, per object: after its
- * residual copy, rebuild it from anchor + residual into kv_full.
+ *   link_out:        after it, copy its anchor and metadata tx -> wire;
+ *   link_in:         after that, copy them wire -> rx;
+ *   receiver stream: after that, rebuild the object from the anchor into
+ *                    kv_anchor;
+ * and only after every object's anchor copy on the same link stream (the
+ * anchor queue is drained first on both hops), per object: its residual
+ * tx -> wire on link_out, wire -> rx on link_in, and once every object is
+ * rebuilt from its anchor, its rebuild from anchor + residual into
+ * kv_full on the receiver stream.
  *   kv, shape, params  as lynx_quantize_pages (field widths must be 4 + 4);
  *   tx, wire, rx       code buffers of the whole set: tx and rx device
  *                      memory, wire pinned host memory (or device memory);
@@ -345,8 +349,8 @@ int lynx_split_stream_transfer(const void *kv, const lynx_kv_shape *shape,
                                const lynx_params *params, int64_t object_blocks,
                                lynx_codes tx, lynx_codes wire, lynx_codes rx,
                                void *kv_anchor, void *kv_full, int flags,
-                               hipStream_t sender, hipStream_t anchor_link,
-                               hipStream_t residual_link, hipStream_t receiver,
+                               hipStream_t sender, hipStream_t link_out,
+                               hipStream_t link_in, hipStream_t receiver,
                                lynx_transfer_times *times);
 
 /* Workspace bytes of lynx_spec_verify (0 for invalid sizes).  Host only. */

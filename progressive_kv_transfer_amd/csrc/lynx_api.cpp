@@ -581,8 +581,8 @@ int lynx_block_stats(const void *kv, const lynx_kv_shape *shape, const lynx_para
 int lynx_split_stream_transfer(const void *kv, const lynx_kv_shape *shape,
                                const lynx_params *params, int64_t object_blocks, lynx_codes tx,
                                lynx_codes wire, lynx_codes rx, void *kv_anchor, void *kv_full,
-                               int flags, hipStream_t sender, hipStream_t anchor_link,
-                               hipStream_t residual_link, hipStream_t receiver,
+                               int flags, hipStream_t sender, hipStream_t link_out,
+                               hipStream_t link_in, hipStream_t receiver,
                                lynx_transfer_times *times) {
     const lynx_params p = resolve(params);
     int rc = check_params(p);
@@ -624,10 +624,14 @@ int lynx_split_stream_transfer(const void *kv, const lynx_kv_shape *shape,
     hipEvent_t start = es.make(true), t_q = es.make(true), t_a = es.make(true),
                t_r = es.make(true), t_da0 = es.make(true), t_da = es.make(true),
                t_df = es.make(true);
-    std::vector<hipEvent_t> q(nobj), a(nobj), r(nobj);
+    // per object: quantized, anchor out of tx, anchor in rx, residual out,
+    // residual in rx
+    std::vector<hipEvent_t> q(nobj), ao(nobj), a(nobj), ro(nobj), r(nobj);
     for (int64_t i = 0; i < nobj; ++i) {
         q[i] = es.make(false);
+        ao[i] = es.make(false);
         a[i] = es.make(false);
+        ro[i] = es.make(false);
         r[i] = es.make(false);
     }
     if (es.err != hipSuccess)
@@ -639,31 +643,36 @@ int lynx_split_stream_transfer(const void *kv, const lynx_kv_shape *shape,
             err = e;
         return err == hipSuccess;
     };
-    ok(hipEventRecord(start, sender));
-    for (hipStream_t s : {anchor_link, residual_link, receiver})
-        ok(hipStreamWaitEvent(s, start, 0));
-    for (int64_t i = 0; i < nobj && err == hipSuccess; ++i) {
-        const int64_t b0 = i * object_blocks;
-        const int64_t n = (nb - b0) < object_blocks ? (nb - b0) : object_blocks;
-        Geometry g = g0;
+    auto object = [&](int64_t i, Geometry &g, int64_t &b0, int64_t &n) {
+        b0 = i * object_blocks;
+        n = (nb - b0) < object_blocks ? (nb - b0) : object_blocks;
+        g = g0;
         g.block0 = b0;
         g.nblocks = n;
-        // serializer: quantize object i (object i + 1 then overlaps its sending)
+    };
+    ok(hipEventRecord(start, sender));
+    for (hipStream_t s : {link_out, link_in, receiver})
+        ok(hipStreamWaitEvent(s, start, 0));
+    // Anchor queue.  Each link stream carries every anchor + metadata copy
+    // before any residual copy (stream order is the strict priority of the
+    // anchor queue); the outbound hop (tx -> wire) of object i + 1 overlaps
+    // the inbound hop (wire -> rx) of object i, and the quantization of
+    // object i + 1 overlaps the sending of object i.
+    for (int64_t i = 0; i < nobj && err == hipSuccess; ++i) {
+        Geometry g;
+        int64_t b0, n;
+        object(i, g, b0, n);
         if (!copies_only)
             ok(launch_quantize((const uint16_t *)kv, g, qt, tx.anchor, tx.residual,
                                tx.meta.gamma_min, tx.meta.gamma_scale, tx.meta.mu, tx.meta.sigma,
                                kModeQuantize, 4, 4, 32, sender));
         ok(hipEventRecord(q[i], sender));
-        // anchor queue: anchor + metadata over the wire
-        ok(hipStreamWaitEvent(anchor_link, q[i], 0));
-        ok(copy_anchor_meta(tx, wire, b0, n, anchor_link));
-        ok(copy_anchor_meta(wire, rx, b0, n, anchor_link));
-        ok(hipEventRecord(a[i], anchor_link));
-        // residual queue: only behind the anchor of the same object
-        ok(hipStreamWaitEvent(residual_link, a[i], 0));
-        ok(copy_residual(tx, wire, b0, n, residual_link));
-        ok(copy_residual(wire, rx, b0, n, residual_link));
-        ok(hipEventRecord(r[i], residual_link));
+        ok(hipStreamWaitEvent(link_out, q[i], 0));
+        ok(copy_anchor_meta(tx, wire, b0, n, link_out));
+        ok(hipEventRecord(ao[i], link_out));
+        ok(hipStreamWaitEvent(link_in, ao[i], 0));
+        ok(copy_anchor_meta(wire, rx, b0, n, link_in));
+        ok(hipEventRecord(a[i], link_in));
         // deserializer, anchor phase
         ok(hipStreamWaitEvent(receiver, a[i], 0));
         if (!copies_only)
@@ -674,16 +683,25 @@ int lynx_split_stream_transfer(const void *kv, const lynx_kv_shape *shape,
             ok(hipEventRecord(t_da0, receiver));
     }
     ok(hipEventRecord(t_q, sender));
-    ok(hipEventRecord(t_a, anchor_link));
-    ok(hipEventRecord(t_r, residual_link));
+    ok(hipEventRecord(t_a, link_in));
     ok(hipEventRecord(t_da, receiver));
+    // Residual queue: behind the whole anchor queue on both hops.
+    for (int64_t i = 0; i < nobj && err == hipSuccess; ++i) {
+        Geometry g;
+        int64_t b0, n;
+        object(i, g, b0, n);
+        ok(copy_residual(tx, wire, b0, n, link_out));
+        ok(hipEventRecord(ro[i], link_out));
+        ok(hipStreamWaitEvent(link_in, ro[i], 0));
+        ok(copy_residual(wire, rx, b0, n, link_in));
+        ok(hipEventRecord(r[i], link_in));
+    }
+    ok(hipEventRecord(t_r, link_in));
     // deserializer, residual phase (after the whole anchor phase)
     for (int64_t i = 0; i < nobj && err == hipSuccess; ++i) {
-        const int64_t b0 = i * object_blocks;
-        const int64_t n = (nb - b0) < object_blocks ? (nb - b0) : object_blocks;
-        Geometry g = g0;
-        g.block0 = b0;
-        g.nblocks = n;
+        Geometry g;
+        int64_t b0, n;
+        object(i, g, b0, n);
         ok(hipStreamWaitEvent(receiver, r[i], 0));
         if (!copies_only)
             ok(launch_dequant(rx.anchor, rx.residual, rx.meta.gamma_min, rx.meta.gamma_scale,
@@ -692,7 +710,7 @@ int lynx_split_stream_transfer(const void *kv, const lynx_kv_shape *shape,
     }
     ok(hipEventRecord(t_df, receiver));
     // Blocking: every stream drains before the events go away.
-    for (hipStream_t s : {sender, anchor_link, residual_link, receiver}) {
+    for (hipStream_t s : {sender, link_out, link_in, receiver}) {
         const hipError_t e = hipStreamSynchronize(s);
         if (err == hipSuccess)
             err = e;

@@ -383,8 +383,8 @@ def split_stream_transfer(kv: torch.Tensor | None, shape: lynx_kv_shape, object_
                           kv_full: torch.Tensor | None = None, copies_only: bool = False,
                           p: lynx_params | None = None, streams=None) -> dict:
     """lynx_split_stream_transfer (blocking); returns the milestones in ms.
-    streams: (sender, anchor_link, residual_link, receiver), default four new
-    streams of default priority."""
+    streams: (sender, link_out, link_in, receiver), default four new streams
+    of default priority."""
     for c in (tx, rx):
         _require_cuda(*c.tensors())
     if streams is None:
