@@ -17,8 +17,9 @@ of the same workload on this host.
 
 `transfer` reports the split-stream transfer of the same set through
 pinned host memory (lynx_split_stream_transfer, objects of 4096 page
-blocks): the link alone and the pipelined quantize -> anchor link ->
-residual link -> rebuild, and how much of the codec time the pipeline hides.
+blocks, the anchor queue drained first on both hops): the link alone and
+the pipelined quantize -> link out -> link in -> rebuild, as medians of
+alternating runs, and how much of the codec time the pipeline hides.
 
 `split_variants` reports the other splits of the 8-bit code (3 + 5, 5 + 3,
 6 + 2 beside the paper's 4 + 4), the single streams of the paper's
