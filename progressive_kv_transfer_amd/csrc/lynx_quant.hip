@@ -120,7 +120,14 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
     __shared__ float2 s_min[kChunks][kPairs];
     __shared__ float2 s_max[kChunks][kPairs];
     __shared__ float4 s_ch[kHead];  // gamma_min, d1, r1, slow flag
-    __shared__ u32x2 s_tab[MODE == kModeQuantize ? kMaxBuckets : 1];
+    // Compander table, one entry per bucket.  SH16: one word,
+    // ((J_base + 1) << 24) - t, where t is the low half of the bucket's
+    // threshold (the magnitudes of a bucket share its upper half) or 0x10000
+    // if the next threshold lies beyond the bucket, so that adding a
+    // magnitude's low half leaves J = code + bias in the top byte.
+    // Otherwise two words: (next threshold, J_base).
+    __shared__ __attribute__((aligned(8)))
+    uint32_t s_tab[MODE == kModeQuantize ? (SH16 ? kMaxBuckets : 2 * kMaxBuckets) : 1];
     // Staged rows of the coming blocks, per buffer and wave: the 32 token
     // rows of its chunk x 128 channels, token-major.
     __shared__ uint32_t s_stage[kDepth][kWaves][kChunk * kPairs];
@@ -148,14 +155,22 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
         for (int i = tid; i < tab.nbuckets; i += kThreads) {
             uint32_t c = tab.bucket_code[i];
             const uint32_t next = c + 1 < 128 ? __float_as_uint(tab.thr[c + 1]) : 0x7f800000u;
-            s_tab[i] = u32x2{next, c + kBias};
+            if (SH16) {
+                const uint32_t lo = (next >> 16) == (uint32_t)(tab.bucket_lo + i) ? (next & 0xffffu)
+                                                                                : 0x10000u;
+                s_tab[i] = ((c + kBias + 1u) << 24) - lo;
+            } else {
+                s_tab[2 * i] = next;
+                s_tab[2 * i + 1] = c + kBias;
+            }
         }
     }
     typedef __attribute__((address_space(3))) const u32x2 lds_u32x2;
+    typedef __attribute__((address_space(3))) const uint32_t lds_u32;
     const float mag_lo = __uint_as_float((uint32_t)tab.bucket_lo << tab.shift);
     const uint32_t sh = (uint32_t)tab.shift;
-    const uint32_t tab_base = (uint32_t)(uintptr_t)(lds_u32x2 *)s_tab -
-                              (uint32_t)tab.bucket_lo * (uint32_t)sizeof(u32x2);
+    const uint32_t tab_base = (uint32_t)(uintptr_t)(lds_u32 *)s_tab -
+                              (uint32_t)tab.bucket_lo * (SH16 ? 4u : 8u);
     const uint32_t row_bytes = (uint32_t)g.row_stride * 2u;
     const int64_t nblocks = g.nblocks;
     // Staging load of lane l: 16 bytes (channels 8 (l % 16) .. + 7) of
@@ -391,34 +406,53 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
         // since that bucket starts below the first threshold, and
         // non-finite inputs stay inside the table).  The bucket offset is
         // folded into the LDS base address.
-        // J = code + bias of Stage 4 for one quotient.
-        auto code_j = [&](float xq) {
+        // J = code + bias of Stage 4 for one quotient, in the top byte (the
+        // low bytes are not part of it): SH16, one v_add of the magnitude's
+        // low half (SDWA word select) to the table word; otherwise the
+        // threshold compare.
+        auto jtop = [&](float xq) -> uint32_t {
             float m = __builtin_amdgcn_fmed3f(fabsf(xq), mag_lo, 1.0f);
             uint32_t mb = __float_as_uint(m);
             uint32_t addr;
-            if (SH16)
-                asm("v_mad_u32_u16 %0, %1, 8, %2 op_sel:[1,0,0,0]"
+            if constexpr (SH16) {
+                asm("v_mad_u32_u16 %0, %1, 4, %2 op_sel:[1,0,0,0]"
                     : "=v"(addr) : "v"(mb), "s"(tab_base));
-            else
+                const uint32_t ent = *(lds_u32 *)(uintptr_t)addr;
+                uint32_t t;
+                asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD "
+                    "src0_sel:DWORD src1_sel:WORD_0"
+                    : "=v"(t) : "v"(ent), "v"(mb));
+                return t;
+            } else {
                 asm("v_lshl_add_u32 %0, %1, 3, %2" : "=v"(addr) : "v"(mb >> sh), "s"(tab_base));
-            u32x2 ent = *(lds_u32x2 *)(uintptr_t)addr;
-            return ent[1] + (mb >= ent[0] ? 1u : 0u);
+                u32x2 ent = *(lds_u32x2 *)(uintptr_t)addr;
+                return (ent[1] + (mb >= ent[0] ? 1u : 0u)) << 24;
+            }
         };
+        auto code_j = [&](float xq) { return jtop(xq) >> 24; };
         if constexpr (kNibbles) {
             u32x4 av[2], rv[2];
 #pragma unroll
             for (int q = 0; q < 8; ++q) {  // tokens 4q .. 4q+3
-                uint32_t J[4][2];
+                uint32_t T[4][2];
 #pragma unroll
                 for (int k = 0; k < 4; ++k)
 #pragma unroll
                     for (int e = 0; e < 2; ++e)
                         // J = code + 7: high nibble = anchor magnitude
                         // (code + 7) >> 4, low nibble ^ 7 = residual (-code) mod 16.
-                        J[k][e] = code_j(x[4 * q + k][e]);
+                        T[k][e] = jtop(x[4 * q + k][e]);
                 // byte k of w0 / w1 = J of channel 2p / 2p+1 at token 4q + k
-                uint32_t w0 = J[0][0] | (J[1][0] << 8) | (J[2][0] << 16) | (J[3][0] << 24);
-                uint32_t w1 = J[0][1] | (J[1][1] << 8) | (J[2][1] << 16) | (J[3][1] << 24);
+                // (the top bytes gathered by v_perm: 0x0c0c0703 takes byte 3
+                // of each source into bytes 0 and 1, 0x05040100 joins two
+                // such halves)
+                auto gather = [](uint32_t t0, uint32_t t1, uint32_t t2, uint32_t t3) {
+                    return __builtin_amdgcn_perm(__builtin_amdgcn_perm(t3, t2, 0x0c0c0703u),
+                                                 __builtin_amdgcn_perm(t1, t0, 0x0c0c0703u),
+                                                 0x05040100u);
+                };
+                uint32_t w0 = gather(T[0][0], T[1][0], T[2][0], T[3][0]);
+                uint32_t w1 = gather(T[0][1], T[1][1], T[2][1], T[3][1]);
                 uint32_t a = ((w0 >> 4) & 0x0f0f0f0fu) | (w1 & 0xf0f0f0f0u);
                 uint32_t r = ((w0 & 0x0f0f0f0fu) | ((w1 << 4) & 0xf0f0f0f0u)) ^ 0x77777777u;
                 // Sign bits of the quotients replicated to bytes (v_perm
