@@ -27,6 +27,10 @@ Lynx-INT4 and Lynx-INT8 (4 + 0, 8 + 0) and the 4 + 4 split with bfloat16
 metadata on the same set: stream bytes, kernel times and the
 reconstruction error (NMSE) of the anchor alone and of the full code.
 
+`large_set` reports the three codec kernels over the whole 23.5 GiB
+Qwen3-235B-A22B-shaped KV set at 128K context, resident in HBM, one launch
+each per pass.
+
 `verify` reports the speculative verification (lynx_spec_verify) of 8
 drafts over a 151936-token vocabulary: time per call and logit bytes per
 second.
@@ -391,6 +395,46 @@ def measure_splits(torch, lynx, kv, out, reps: int = 5, acc_tensors: int = 8):
     return {"workload": WORKLOAD, "accuracy_tensors": acc_tensors, "splits": res}
 
 
+LARGE_WORKLOAD = "qwen3_235b_128k"
+
+
+def measure_large(torch, kvgen, lynx, reps: int = 5):
+    """The Qwen3-235B-A22B-shaped set at 128K context (94 layers x {K, V} x
+    131072 tokens x 512 channels, 23.5 GiB of bf16) resident on the GPU:
+    quantize + split and both reconstructions over the whole set in one
+    launch each, HIP events around `reps` launches after one warm-up, with
+    the step's algorithmic bytes per element."""
+    cfg = kvgen.CONFIGS[LARGE_WORKLOAD]
+    kv = cfg.make("cuda")
+    n_elem = kv.numel()
+    nb = n_elem // (256 * 128)
+    codes = lynx.alloc_codes(nb, "cuda")
+    out = torch.empty_like(kv)
+    p = lynx.params()
+    stream = torch.cuda.current_stream()
+    calls = {"quantize": lambda: lynx.quantize_pages(kv, p, out=codes, stream=stream),
+             "dequant_anchor": lambda: lynx.dequant_anchor(codes, out, p, stream=stream),
+             "dequant_full": lambda: lynx.dequant_full(codes, out, p, stream=stream)}
+    res = {}
+    for name, fn in calls.items():
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        algo = BYTES_PER_ELEM[name] * n_elem / (ms * 1e-3) / 1e9
+        res[name] = {"ms": round(ms, 4), "bf16_GBps": round(2.0 * n_elem / (ms * 1e-3) / 1e9, 1),
+                     "algo_GBps": round(algo, 1), "hbm_frac": round(algo / HBM_PEAK_GBPS, 4)}
+    del kv, codes, out
+    torch.cuda.empty_cache()
+    return {"workload": LARGE_WORKLOAD, "kv_bf16_bytes": 2 * n_elem, "blocks": nb,
+            "launches_timed": reps, "kernels": res}
+
+
 TRANSFER_OBJECT_BLOCKS = 4096  # 256 MiB of bf16 KV per transfer object (16 objects)
 TRANSFER_REPS = 5              # alternating link-only / pipeline runs (medians reported)
 
@@ -468,6 +512,7 @@ def main():
     ap.add_argument("--hbm-probe", action="store_true")
     ap.add_argument("--no-attention", action="store_true")
     ap.add_argument("--no-transfer", action="store_true")
+    ap.add_argument("--no-large", action="store_true")
     ap.add_argument("--attention-only", action="store_true")
     ap.add_argument("--attention-calls", type=int, default=50)
     ap.add_argument("--attention-case", default=None,
@@ -591,6 +636,8 @@ def main():
         out["attention"] = measure_attention(torch, kvgen, lynx, args.attention_calls, 5)
     if not args.profile_run:
         out["verify"] = measure_verify(torch, kvgen, lynx)
+    if not args.no_large and not args.profile_run:
+        out["large_set"] = measure_large(torch, kvgen, lynx)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = run_cpu_baseline(cfg, kv, args.cpu_budget)
     print(json.dumps(out), flush=True)
