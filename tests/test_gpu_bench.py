@@ -1,0 +1,36 @@
+"""bench.py on the GPU: one short run (2 timed steps) prints exactly one
+JSON line with the fields of the measurement contract."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_bench_json_line():
+    print("[gpu-bench] bench.py --steps 2 --warmup 1 (short sections)", flush=True)
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "2",
+                        "--warmup", "1", "--no-cpu-baseline", "--no-attention",
+                        "--no-transfer", "--no-large"],
+                       capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stdout.splitlines() if l.strip()]
+    assert len(lines) == 1
+    d = json.loads(lines[0])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+                "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+                "roofline", "kernels"):
+        assert key in d, key
+    assert d["n_gpus"] == 1 and d["steps"] == 2 and d["warmup"] == 1
+    assert d["value"] > 0 and d["ms_per_step"] > 0 and d["higher_is_better"] is True
+    assert d["unit"] == "GB/s" and d["config"]["workload"] == "qwen32b_16k"
+    rl = d["roofline"]
+    assert rl["bound"] == "hbm" and rl["unit"] == "GB/s" and rl["peak"] == 8000.0
+    assert abs(rl["frac"] - rl["achieved"] / rl["peak"]) < 1e-3
+    assert rl["traffic"] is None or rl["traffic"] > 0.9 * rl["algorithmic_bytes_per_launch"]
+    assert set(d["kernels"]) == {"quantize", "dequant_anchor", "dequant_full"}
+    assert "split_variants" in d and "verify" in d
