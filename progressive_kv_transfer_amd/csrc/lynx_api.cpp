@@ -29,11 +29,6 @@ uint32_t f2u(float f) {
     memcpy(&u, &f, 4);
     return u;
 }
-float u2f(uint32_t u) {
-    float f;
-    memcpy(&f, &u, 4);
-    return f;
-}
 
 // ---------------------------------------------------------------- tables --
 

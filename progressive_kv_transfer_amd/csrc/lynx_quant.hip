@@ -32,6 +32,8 @@
 // worst-case significands and on 1.2e10 random operand pairs).  Operands
 // outside that range are detected per channel (Stage 1) and per chunk
 // (Stage 2) from the statistics and divided with an IEEE division instead.
+#include <atomic>
+
 #include "lynx_internal.h"
 
 namespace lynx {
@@ -521,19 +523,28 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
 
 }  // namespace
 
-// Workgroups resident on the device (per kernel variant), cached per device.
+// Workgroups resident on the device (per kernel variant), cached per device
+// (host threads may race to fill an entry; they store the same value).  The
+// persistent kernels are correct with any grid; 1024 is used, and nothing
+// cached, when the runtime cannot tell.
 static int resident_workgroups(const void *kernel, int slot, int threads) {
-    static int cache[64][16];
+    static std::atomic<int> cache[64][16];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
         return 1024;
-    if (cache[dev][slot] == 0) {
+    int v = cache[dev][slot].load(std::memory_order_relaxed);
+    if (v == 0) {
         int cus = 0, per_cu = 0;
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0);
-        cache[dev][slot] = (cus > 0 ? cus : 256) * (per_cu > 0 ? per_cu : 1);
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) !=
+                hipSuccess ||
+            cus <= 0 || per_cu <= 0)
+            return 1024;
+        v = cus * per_cu;
+        cache[dev][slot].store(v, std::memory_order_relaxed);
     }
-    return cache[dev][slot];
+    return v;
 }
 
 template <int MODE, bool SH16, int ABITS, int RBITS, bool M16 = false>
