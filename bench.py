@@ -116,8 +116,21 @@ def cpu_threads() -> int:
     return max(1, min(16, n))
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def run_cpu_baseline(cfg, kv_dev, budget_s: float):
-    """Oracle quantize + both dequants, tensor by tensor, until ~budget_s."""
+    """Oracle quantize + both dequants, tensor by tensor, until ~budget_s, on
+    a pool of threads over page blocks; then the same steps on one thread
+    over the first 256 blocks of the first tensor."""
     import oracle
     from progressive_kv_transfer_amd import kvgen
 
@@ -136,10 +149,26 @@ def run_cpu_baseline(cfg, kv_dev, budget_s: float):
         if t_total >= budget_s:
             break
     gbps = 2.0 * elems / t_total / 1e9
+
+    one_blocks = 256
+    xb = kvgen.bf16_bits(kv_dev[0:1])
+    t0 = time.perf_counter()
+    c = oracle.quantize(xb, threads=1, blocks=(0, one_blocks))
+    oracle.dequant(c, xb.shape, False, threads=1, blocks=(0, one_blocks))
+    oracle.dequant(c, xb.shape, True, threads=1, blocks=(0, one_blocks))
+    t_one = time.perf_counter() - t0
+    one_elems = one_blocks * 32768
     return {"value": round(gbps, 4), "unit": "GB/s", "cores": th, "kind": "oracle",
             "sample": (f"first {done} of {kv_dev.shape[0]} tensors (K/V of layers "
                        f"0..{(done - 1) // 2}) of {cfg.name}: {elems} elements, "
-                       f"{t_total:.1f} s wall, quantize + anchor dequant + full dequant")}
+                       f"{t_total:.1f} s wall, quantize + anchor dequant + full dequant"),
+            "cpu_model": cpu_model(), "wall_s": round(t_total, 2),
+            "elements_per_s": round(elems / t_total, 1),
+            "single_thread": {"value": round(2.0 * one_elems / t_one / 1e9, 4),
+                              "unit": "GB/s", "elements": one_elems,
+                              "wall_s": round(t_one, 2),
+                              "elements_per_s": round(one_elems / t_one, 1),
+                              "sample": f"page blocks 0..{one_blocks - 1} of tensor 0"}}
 
 
 def copy_probe(timed: bool = False):
@@ -585,9 +614,13 @@ def main():
             per[n].append(ev[i].elapsed_time(ev[i + 1]))
     kern = {}
     for n in names:
+        # the mean matches the profiler's average duration; the median and
+        # the minimum show the spread over the timed steps
         ms = sum(per[n]) / len(per[n])
         algo = BYTES_PER_ELEM[n] * n_elem / (ms * 1e-3) / 1e9
-        kern[n] = {"ms": round(ms, 4), "bf16_GBps": round(2.0 * n_elem / (ms * 1e-3) / 1e9, 1),
+        kern[n] = {"ms": round(ms, 4), "ms_median": round(statistics.median(per[n]), 4),
+                   "ms_min": round(min(per[n]), 4),
+                   "bf16_GBps": round(2.0 * n_elem / (ms * 1e-3) / 1e9, 1),
                    "algo_GBps": round(algo, 1), "hbm_frac": round(algo / HBM_PEAK_GBPS, 4)}
     ms_step = wall / args.steps * 1e3
     value = 2.0 * n_elem / (wall / args.steps) / 1e9

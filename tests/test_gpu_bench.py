@@ -12,9 +12,10 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def test_bench_json_line():
-    print("[gpu-bench] bench.py --steps 2 --warmup 1 (short sections)", flush=True)
+    print("[gpu-bench] bench.py --steps 2 --warmup 1 (short sections, short CPU baseline)",
+          flush=True)
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "2",
-                        "--warmup", "1", "--no-cpu-baseline", "--no-attention",
+                        "--warmup", "1", "--cpu-budget", "0.5", "--no-attention",
                         "--no-transfer", "--no-large"],
                        capture_output=True, text=True, timeout=240)
     assert r.returncode == 0, r.stderr[-2000:]
@@ -34,3 +35,10 @@ def test_bench_json_line():
     assert rl["traffic"] is None or rl["traffic"] > 0.9 * rl["algorithmic_bytes_per_launch"]
     assert set(d["kernels"]) == {"quantize", "dequant_anchor", "dequant_full"}
     assert "split_variants" in d and "verify" in d
+    for k in d["kernels"].values():
+        assert 0 < k["ms_min"] <= k["ms_median"] and k["ms"] > 0
+    cb = d["cpu_baseline"]
+    assert cb["kind"] == "oracle" and cb["unit"] == "GB/s" and cb["value"] > 0
+    assert cb["cores"] >= 1 and cb["elements_per_s"] > 0 and cb["cpu_model"]
+    st = cb["single_thread"]
+    assert st["value"] > 0 and st["elements"] == 256 * 32768
