@@ -321,7 +321,8 @@ typedef struct lynx_transfer_times {
  * the Residual arrives).
  *
  * The set's page blocks (block order of the layouts above) are cut into
- * objects of object_blocks blocks.  The wire has two hops, out (tx ->
+ * objects of object_blocks blocks (1 .. 2^22, at most 4096 objects; else
+ * LYNX_EINVAL).  The wire has two hops, out (tx ->
  * wire) and in (wire -> rx), one stream each, so the two directions of the
  * link run at once.  Per object i:
  *   sender stream:   quantize the object into tx;

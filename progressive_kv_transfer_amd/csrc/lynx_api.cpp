@@ -588,7 +588,9 @@ int lynx_split_stream_transfer(const void *kv, const lynx_kv_shape *shape,
     int64_t nb = 0;
     if ((rc = check_shape(shape, &nb)))
         return rc;
-    if (object_blocks <= 0 || (flags & ~LYNX_TRANSFER_COPIES_ONLY))
+    // one launch per object: at most kMaxLaunchBlocks blocks each
+    if (object_blocks <= 0 || object_blocks > kMaxLaunchBlocks ||
+        (flags & ~LYNX_TRANSFER_COPIES_ONLY))
         return LYNX_EINVAL;
     const bool copies_only = (flags & LYNX_TRANSFER_COPIES_ONLY) != 0;
     if (times)

@@ -252,6 +252,49 @@ def _require_cuda(*ts):
             raise ValueError("lynx calls take device tensors")
 
 
+def _fields(p: lynx_params | None):
+    """(anchor_bits, residual_bits, metadata dtype) of p (None = defaults)."""
+    if p is None:
+        return 4, 4, torch.float32
+    return p.anchor_bits, p.residual_bits, \
+        torch.bfloat16 if p.meta_bits == 16 else torch.float32
+
+
+def _check_codes(fn: str, codes: Codes, nblocks: int, p: lynx_params | None = None,
+                 residual: bool = True, device: bool = True):
+    """The library writes and reads code buffers through bare pointers: make
+    sure each one is a dense tensor of the right type that holds nblocks
+    page blocks (on the device unless device=False: a transfer's wire may be
+    pinned host memory)."""
+    a, b, mdt = _fields(p)
+    need = [("anchor", codes.anchor, torch.uint8, nblocks * 4096 * a),
+            ("gamma_min", codes.gamma_min, mdt, nblocks * BLOCK_CHANNELS),
+            ("gamma_scale", codes.gamma_scale, mdt, nblocks * BLOCK_CHANNELS),
+            ("mu", codes.mu, mdt, nblocks * 8 * BLOCK_CHANNELS),
+            ("sigma", codes.sigma, mdt, nblocks * 8 * BLOCK_CHANNELS)]
+    if residual and b:
+        need.append(("residual", codes.residual, torch.uint8, nblocks * 4096 * b))
+    for name, t, dt, n in need:
+        if device and not t.is_cuda:
+            raise ValueError(f"{fn}: {name} must be a device tensor")
+        if t.dtype != dt or not t.is_contiguous():
+            raise ValueError(f"{fn}: {name} must be a contiguous {dt} tensor")
+        if t.numel() < n:
+            raise ValueError(f"{fn}: {name} holds {t.numel()} elements, "
+                             f"{n} needed for {nblocks} page blocks")
+
+
+def _check_kv(fn: str, name: str, t: torch.Tensor, shape: lynx_kv_shape):
+    """A bf16 device tensor whose memory covers every element `shape` addresses."""
+    if not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous():
+        raise ValueError(f"{fn}: {name} must be a contiguous bf16 device tensor")
+    if shape.num_tensors > 0 and shape.num_tokens > 0 and shape.num_channels > 0:
+        extent = ((shape.num_tensors - 1) * shape.tensor_stride +
+                  (shape.num_tokens - 1) * shape.row_stride + shape.num_channels)
+        if t.numel() < extent:
+            raise ValueError(f"{fn}: {name} holds {t.numel()} elements, {extent} addressed")
+
+
 def quantize_pages(kv: torch.Tensor, p: lynx_params | None = None,
                    out: Codes | None = None, stream=None) -> Codes:
     """lynx_quantize_pages on a bf16 [num_tensors, T, Ch] device tensor."""
@@ -263,6 +306,7 @@ def quantize_pages(kv: torch.Tensor, p: lynx_params | None = None,
     codes = out if out is not None else alloc_codes(
         nb, kv.device, anchor_bits=p.anchor_bits if p else 4,
         residual_bits=p.residual_bits if p else 4, meta_bits=p.meta_bits if p else 32)
+    _check_codes("quantize_pages", codes, nb, p)
     single = p is not None and p.residual_bits == 0
     _check("lynx_quantize_pages", lib().lynx_quantize_pages(
         kv.data_ptr(), ctypes.byref(sh), ctypes.byref(p) if p else None,
@@ -275,7 +319,10 @@ def dequant_anchor(codes: Codes, out: torch.Tensor, p: lynx_params | None = None
                    stream=None) -> torch.Tensor:
     """lynx_dequant_anchor into a bf16 [num_tensors, T, Ch] device tensor."""
     _require_cuda(out)
+    if out.dtype != torch.bfloat16:
+        raise ValueError("dequant_anchor: out must be bfloat16")
     sh = shape_of(out)
+    _check_codes("dequant_anchor", codes, num_blocks(sh), p, residual=False)
     _check("lynx_dequant_anchor", lib().lynx_dequant_anchor(
         codes.anchor.data_ptr(), codes.meta(), ctypes.byref(sh),
         ctypes.byref(p) if p else None, out.data_ptr(), _stream(stream)))
@@ -286,7 +333,10 @@ def dequant_full(codes: Codes, out: torch.Tensor, p: lynx_params | None = None,
                  stream=None) -> torch.Tensor:
     """lynx_dequant_full into a bf16 [num_tensors, T, Ch] device tensor."""
     _require_cuda(out)
+    if out.dtype != torch.bfloat16:
+        raise ValueError("dequant_full: out must be bfloat16")
     sh = shape_of(out)
+    _check_codes("dequant_full", codes, num_blocks(sh), p)
     _check("lynx_dequant_full", lib().lynx_dequant_full(
         codes.anchor.data_ptr(), codes.residual.data_ptr(), codes.meta(), ctypes.byref(sh),
         ctypes.byref(p) if p else None, out.data_ptr(), _stream(stream)))
@@ -366,6 +416,14 @@ def decode_attn_dequant(q: torch.Tensor, k: CodeView, v: CodeView, ctx_len: int,
             or not out.is_contiguous():
         raise ValueError("out must be a contiguous bf16 or float32 tensor shaped like q")
     code = OUT_F32 if out.dtype == torch.float32 else OUT_BF16
+    if ctx_len > 0 and ctx_len % PAGE_TOKENS == 0 and num_kv_heads > 0:
+        # (other sizes are refused by the library)
+        nb = ctx_len // PAGE_TOKENS * num_kv_heads
+        for name, view in (("k", k), ("v", v)):
+            if not 0 <= view.b0 <= view.b1 or view.b1 - view.b0 != nb:
+                raise ValueError(f"decode_attn_dequant: the {name} view must hold the {nb} "
+                                 f"page blocks of a [{ctx_len}, {num_kv_heads} x 128] tensor")
+            _check_codes("decode_attn_dequant", view.codes, view.b1, p, residual=view.full)
     need = attn_workspace_bytes(t_q, nqh, num_kv_heads, ctx_len)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
@@ -385,8 +443,15 @@ def split_stream_transfer(kv: torch.Tensor | None, shape: lynx_kv_shape, object_
     """lynx_split_stream_transfer (blocking); returns the milestones in ms.
     streams: (sender, link_out, link_in, receiver), default four new streams
     of default priority."""
-    for c in (tx, rx):
-        _require_cuda(*c.tensors())
+    nb = num_blocks(shape)
+    for name, c in (("tx", tx), ("rx", rx)):
+        _check_codes(f"split_stream_transfer ({name})", c, nb, p)
+    _check_codes("split_stream_transfer (wire)", wire, nb, p, device=False)
+    if not copies_only:
+        for name, t in (("kv", kv), ("kv_anchor", kv_anchor), ("kv_full", kv_full)):
+            if t is None:
+                raise ValueError(f"split_stream_transfer: {name} is required")
+            _check_kv("split_stream_transfer", name, t, shape)
     if streams is None:
         streams = tuple(torch.cuda.Stream() for _ in range(4))
     t = lynx_transfer_times()
@@ -409,15 +474,24 @@ def spec_verify(draft_logits: torch.Tensor, target_logits: torch.Tensor, tokens:
     """lynx_spec_verify: float32 logits [T, V] / [T + 1, V], int32 tokens [T],
     float64 uniforms [T] on the device; returns int32 [2] (accepted drafts,
     next token) on the device."""
-    _require_cuda(target_logits)
+    _require_cuda(draft_logits, target_logits, tokens, u_accept)
+    if target_logits.dim() != 2:
+        raise ValueError("spec_verify: target_logits must be [T + 1, V]")
     t_draft, vocab = target_logits.shape[0] - 1, target_logits.shape[1]
     for x, dt in ((draft_logits, torch.float32), (target_logits, torch.float32),
                   (tokens, torch.int32), (u_accept, torch.float64)):
         if x.dtype != dt or not x.is_contiguous():
             raise ValueError("spec_verify: contiguous float32 logits, int32 tokens and "
                              "float64 uniforms expected")
+    if draft_logits.numel() != t_draft * vocab or tokens.numel() != t_draft \
+            or u_accept.numel() != t_draft:
+        raise ValueError(f"spec_verify: draft_logits [{t_draft}, {vocab}], tokens and "
+                         f"u_accept [{t_draft}] expected")
     if out is None:
         out = torch.empty(2, dtype=torch.int32, device=target_logits.device)
+    _require_cuda(out)
+    if out.dtype != torch.int32 or out.numel() < 2 or not out.is_contiguous():
+        raise ValueError("spec_verify: out must be a contiguous int32 tensor of 2 elements")
     if workspace is None:
         workspace = torch.empty(max(spec_verify_workspace_bytes(t_draft, vocab), 16),
                                 dtype=torch.uint8, device=target_logits.device)

@@ -250,7 +250,7 @@ def _codes(ptr=FAKE):
 
 
 @pytest.mark.parametrize("case,expect", [
-    ("object_blocks", -1), ("flags", -1), ("null_wire", -1), ("misaligned_rx", -1),
+    ("object_blocks", -1), ("huge_objects", -1), ("flags", -1), ("null_wire", -1), ("misaligned_rx", -1),
     ("misaligned_kv", -2), ("null_out", -1), ("too_many_objects", -1), ("tokens", -2),
     ("params", -1)])
 def test_transfer_argument_errors(case, expect):
@@ -262,6 +262,8 @@ def test_transfer_argument_errors(case, expect):
     tx, wire, rx = _codes(), _codes(), _codes()
     if case == "object_blocks":
         ob = 0
+    elif case == "huge_objects":
+        ob = (1 << 22) + 1  # one launch per object: over the grid limit
     elif case == "flags":
         flags = 2
     elif case == "null_wire":

@@ -91,18 +91,49 @@ def test_other_geometries(t_q, n_qh, n_kvh):
 
 
 def test_attention_argument_errors():
-    kv = torch.stack([kvgen.kv_tensor(730 + i, 256, 128, [], True, DEV) for i in range(2)])
+    # two tensors of 256 tokens x 2 KV heads: 2 page blocks each
+    kv = torch.stack([kvgen.kv_tensor(730 + i, 256, 256, [], True, DEV) for i in range(2)])
     codes = lynx.quantize_pages(kv)
-    k = lynx.CodeView(codes, 0, 1)
-    v = lynx.CodeView(codes, 1, 2)
+    k = lynx.CodeView(codes, 0, 2)
+    v = lynx.CodeView(codes, 2, 4)
     q = kvgen.queries(731, 1, 2, device=DEV)
     with pytest.raises(lynx.LynxError):   # 3 q-heads over 2 KV heads is not GQA
         lynx.decode_attn_dequant(kvgen.queries(732, 1, 3, device=DEV), k, v, 256, 2, 0.1)
     with pytest.raises(lynx.LynxError):   # too small a workspace
-        lynx.decode_attn_dequant(q, k, v, 256, 1, 0.1,
+        lynx.decode_attn_dequant(q, k, v, 256, 2, 0.1,
                                  workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
     with pytest.raises(lynx.LynxError):   # context not a multiple of 256
-        lynx.decode_attn_dequant(q, k, v, 200, 1, 0.1)
+        lynx.decode_attn_dequant(q, k, v, 200, 2, 0.1)
+    # refused by the binding before any launch: views that do not hold the
+    # context's page blocks, or that reach past their code buffers
+    with pytest.raises(ValueError):
+        lynx.decode_attn_dequant(q, lynx.CodeView(codes, 0, 1), v, 256, 2, 0.1)
+    with pytest.raises(ValueError):
+        lynx.decode_attn_dequant(q, k, lynx.CodeView(codes, 3, 5), 256, 2, 0.1)
+
+
+def test_binding_refuses_short_buffers():
+    """Code buffers too small for the KV shape, of the wrong type or on the
+    host, and non-bf16 outputs are refused before any launch."""
+    kv = torch.stack([kvgen.kv_tensor(740 + i, 512, 256, [], True, DEV) for i in range(2)])
+    nb = 8
+    with pytest.raises(ValueError):
+        lynx.quantize_pages(kv, out=lynx.alloc_codes(nb - 1, DEV))
+    codes = lynx.quantize_pages(kv)
+    with pytest.raises(ValueError):
+        lynx.dequant_anchor(codes, torch.empty(kv.shape, dtype=torch.float32, device=DEV))
+    with pytest.raises(ValueError):
+        lynx.dequant_full(lynx.alloc_codes(nb - 1, DEV), torch.empty_like(kv))
+    host = lynx.alloc_codes(nb, "cpu")
+    with pytest.raises(ValueError):
+        lynx.dequant_full(host, torch.empty_like(kv))
+    bad = lynx.alloc_codes(nb, DEV)
+    bad.mu = bad.mu.to(torch.float64)
+    with pytest.raises(ValueError):
+        lynx.quantize_pages(kv, out=bad)
+    # the right buffers still work
+    out = lynx.dequant_full(codes, torch.empty_like(kv))
+    assert torch.isfinite(out.float()).all()
 
 
 @pytest.mark.parametrize("name,full", [("decode_attn_32k", False), ("decode_attn_32k", True),
