@@ -86,6 +86,40 @@ def test_edge_pages():
     full_check(kv)
 
 
+def test_non_finite_values_stay_in_their_block():
+    """NaN and +-Inf in three of eight page blocks (outputs unspecified
+    there): every launch completes and the other blocks' codes, metadata and
+    reconstructions equal the oracle's on the clean set bit for bit (page
+    blocks are independent; the compander clamps every magnitude into its
+    table)."""
+    announce("non-finite values in blocks 0, 3, 5 of 8")
+    clean = torch.stack([kvgen.kv_tensor(610 + i, 512, 256, [7], True, DEV)
+                         for i in range(2)])
+    kv = clean.clone()
+    kv[0, 5, 3] = float("nan")                    # block 0: tensor 0, page 0, head 0
+    kv[0, 256 + 17, 128 + 9] = float("inf")       # block 3: tensor 0, page 1, head 1
+    kv[1, 40:72, 128 + 100] = float("-inf")       # block 5: tensor 1, page 0, head 1
+    kv[1, 44, 128 + 3] = float("nan")
+    codes, out_a, out_f = run_gpu(kv)
+    xb = bits(clean)
+    ref = oracle.quantize(xb, threads=8)
+    keep = [1, 2, 4, 6, 7]
+    nb = 8
+    for name in ("anchor", "residual", "gamma_min", "gamma_scale", "mu", "sigma"):
+        g = host(getattr(codes, name)).reshape(nb, -1)[keep]
+        r = np.asarray(getattr(ref, name)).reshape(nb, -1)[keep]
+        assert np.array_equal(g, r), name
+    for full, out in ((False, out_a), (True, out_f)):
+        rd = oracle.dequant(ref, xb.shape, full, threads=8)
+        got = bits(out)
+        for b in keep:
+            t, rest = divmod(b, 4)
+            page, head = divmod(rest, 2)
+            rows = slice(256 * page, 256 * page + 256)
+            cols = slice(128 * head, 128 * head + 128)
+            np.testing.assert_array_equal(got[t, rows, cols], rd[t, rows, cols])
+
+
 def test_strided_multi_block_set():
     """3 tensors x 5 pages x 3 heads inside padded rows and tensors; the
     padding of the dequant outputs is left untouched."""

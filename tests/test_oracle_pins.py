@@ -466,3 +466,23 @@ def test_small_geometry():
         x = torch.from_numpy(vals).to(torch.bfloat16)
         check_error_bound(bits(x), True)
         check_error_bound(bits(x), False)
+
+
+def test_non_finite_values_stay_in_their_block():
+    """Page blocks are quantized independently (Algorithm 1's statistics are
+    per page and per chunk): NaN / Inf in one block changes nothing in the
+    others (4 blocks; block 1 = page 0, head 1 and block 2 = page 1, head 0
+    are poisoned)."""
+    clean = kvgen.kv_tensor(620, 512, 256, [7], True, "cpu")[None]
+    kv = clean.clone()
+    kv[0, 9, 128 + 4] = float("nan")
+    kv[0, 256 + 30:256 + 40, 17] = float("-inf")
+    kv[0, 256 + 3, 100] = float("inf")
+    ref = oracle.quantize(bits(clean))
+    poi = oracle.quantize(bits(kv))
+    for name in ("anchor", "residual", "gamma_min", "gamma_scale", "mu", "sigma"):
+        r = np.asarray(getattr(ref, name)).reshape(4, -1)
+        p = np.asarray(getattr(poi, name)).reshape(4, -1)
+        assert np.array_equal(r[[0, 3]], p[[0, 3]]), name
+    assert not np.array_equal(np.asarray(ref.mu).reshape(4, -1)[1],
+                              np.asarray(poi.mu).reshape(4, -1)[1])
