@@ -56,6 +56,7 @@ import argparse
 import json
 import statistics
 import os
+import subprocess
 import sys
 import time
 
@@ -202,10 +203,20 @@ def copy_probe(timed: bool = False):
 
         t = timeit(lambda: b.copy_(a))
         out["copy_GBps"] = round(2 * 2 * m / t / 1e9, 1)
-        t = timeit(lambda: torch.sum(a, dtype=torch.int64))
-        out["read_GBps"] = round(2 * m / t / 1e9, 1)
         t = timeit(lambda: b.fill_(3))
         out["write_GBps"] = round(2 * m / t / 1e9, 1)
+        del a, b
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        # plain HIP streams of several read / write mixes (a child process)
+        from progressive_kv_transfer_amd import build as B
+        if not os.path.exists(B.PROBE):
+            raise RuntimeError(f"{B.PROBE} is not built: run "
+                               "`python -m progressive_kv_transfer_amd.build`")
+        r = subprocess.run([B.PROBE], capture_output=True, text=True, timeout=300)
+        if r.returncode != 0:
+            raise RuntimeError("stream probe failed: " + r.stderr[-2000:])
+        out["streams"] = [json.loads(l) for l in r.stdout.splitlines() if l.strip()]
     print(json.dumps(out))
 
 

@@ -73,6 +73,20 @@ def build(verbose: bool = False, isa_dir: str | None = None) -> str:
     return LIB
 
 
+PROBE_SRC = os.path.join(CSRC, "stream_ceiling.hip")
+PROBE = os.path.join(PKG, "stream_ceiling")
+
+
+def build_stream_probe(verbose: bool = False) -> str:
+    """Compile the stand-alone streaming-ceiling probe (run by
+    `bench.py --hbm-probe`; not part of the library)."""
+    out = PROBE + ".tmp%d" % os.getpid()
+    _run([HIPCC, "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-Xclang", "-target-feature",
+          "-Xclang", "-packed-fp32-ops", PROBE_SRC, "-o", out], verbose, cwd=PKG)
+    os.replace(out, PROBE)
+    return PROBE
+
+
 def _run(cmd, verbose, cwd):
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -90,3 +104,4 @@ if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv,
                 isa_dir=(sys.argv[sys.argv.index("--isa") + 1]
                          if "--isa" in sys.argv else None)))
+    print(build_stream_probe(verbose="-v" in sys.argv))
