@@ -35,6 +35,9 @@ each per pass.
 drafts over a 151936-token vocabulary: time per call and logit bytes per
 second.
 
+`single_page` reports the latency of each codec kernel on the single-page
+workload (one K and one V page block), over 2048 rotating copies.
+
 `attention` reports, beside the step, the fused dequant + attention calls
 (lynx_decode_attn_dequant) on their own workloads: decode (1 query token,
 64 q-heads over 8 KV heads, 32768 tokens; anchor-only and full codes) and
@@ -48,7 +51,7 @@ and QK + PV flops per second.
     python bench.py --profile-run      # the codec steps only, for rocprofv3
     python bench.py --attention-only [--attention-case NAME]   # attention calls only
     python bench.py --copy-probe       # plain 1 GiB copy, PMC scale factor
-    python bench.py --hbm-probe        # timed copy / read / write bandwidths
+    python bench.py --hbm-probe        # plain streaming ceilings (torch + csrc/stream_ceiling.hip)
 """
 from __future__ import annotations
 
@@ -319,6 +322,63 @@ def measure_attention(torch, kvgen, lynx, calls: int, warmup: int, only=None):
         del views, copies
     built.clear()
     torch.cuda.synchronize()
+    return res
+
+
+def measure_single_page(torch, kvgen, lynx, copies: int = 2048):
+    """The single-page workload (one K and one V page block, 2 x 256 x 128):
+    latency of each codec kernel per call, cycling over `copies` copies of
+    input and outputs (more bytes than the last-level cache), from a HIP
+    graph of the calls replayed (device time; every replay must reproduce
+    the eager outputs bit for bit) and issued one by one (eager)."""
+    cfg = kvgen.CONFIGS["single_page"]
+    base = cfg.make("cuda")
+    kvs = base.unsqueeze(0).repeat(copies, 1, 1, 1)
+    nb = base.numel() // 32768
+    codes = [lynx.alloc_codes(nb, "cuda") for _ in range(copies)]
+    outs = torch.empty_like(kvs)
+    p = lynx.params()
+    stream = torch.cuda.current_stream()
+    calls = {
+        "quantize": lambda i, s: lynx.quantize_pages(kvs[i], p, out=codes[i], stream=s),
+        "dequant_anchor": lambda i, s: lynx.dequant_anchor(codes[i], outs[i], p, stream=s),
+        "dequant_full": lambda i, s: lynx.dequant_full(codes[i], outs[i], p, stream=s),
+    }
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {"workload": cfg.name, "blocks": nb, "copies": copies,
+           "us_per_call": {}, "us_per_call_eager": {}}
+    for name, fn in calls.items():
+        for i in range(copies):
+            fn(i, stream)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(copies):
+            fn(i, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res["us_per_call_eager"][name] = round(e0.elapsed_time(e1) / copies * 1e3, 2)
+        ref = (torch.cat([c.anchor.view(-1) for c in codes[:4]]).clone(), outs[:4].clone())
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.graph(graph, stream=cap):
+            for i in range(copies):
+                fn(i, cap)
+        stream.wait_stream(cap)
+        times = []
+        for r in range(3):
+            torch.cuda.synchronize()
+            e0.record(stream)
+            graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / copies * 1e3)
+            got = (torch.cat([c.anchor.view(-1) for c in codes[:4]]), outs[:4])
+            if not (torch.equal(got[0], ref[0]) and
+                    torch.equal(got[1].view(torch.int16), ref[1].view(torch.int16))):
+                raise RuntimeError(f"single page {name}: graph replay {r} differs")
+        del graph
+        res["us_per_call"][name] = round(min(times), 2)
     return res
 
 
@@ -680,6 +740,7 @@ def main():
         out["attention"] = measure_attention(torch, kvgen, lynx, args.attention_calls, 5)
     if not args.profile_run:
         out["verify"] = measure_verify(torch, kvgen, lynx)
+        out["single_page"] = measure_single_page(torch, kvgen, lynx)
     if not args.no_large and not args.profile_run:
         out["large_set"] = measure_large(torch, kvgen, lynx)
     if not args.no_cpu_baseline:

@@ -35,6 +35,9 @@ def test_bench_json_line():
     assert rl["traffic"] is None or rl["traffic"] > 0.9 * rl["algorithmic_bytes_per_launch"]
     assert set(d["kernels"]) == {"quantize", "dequant_anchor", "dequant_full"}
     assert "split_variants" in d and "verify" in d
+    sp = d["single_page"]
+    assert sp["blocks"] == 2 and set(sp["us_per_call"]) == set(d["kernels"])
+    assert all(v > 0 for v in sp["us_per_call"].values())
     for k in d["kernels"].values():
         assert 0 < k["ms_min"] <= k["ms_median"] and k["ms"] > 0
     cb = d["cpu_baseline"]
