@@ -115,22 +115,33 @@ struct Tables {
     DequantTab d;
 };
 
+// Tables per (alpha, code_scale, field widths), built on first use.  The
+// cache is bounded (emptied when full; a caller sweeping parameters rebuilds
+// tables, never grows memory) and hands out copies, so no caller holds a
+// reference into it.
+constexpr size_t kMaxCachedTables = 64;
 std::mutex g_mu;
 std::map<std::tuple<uint32_t, uint32_t, int, int>, Tables> g_cache;
 
-const Tables *tables_for(const lynx_params &p) {
+bool tables_for(const lynx_params &p, Tables *out) {
     std::lock_guard<std::mutex> lock(g_mu);
     auto key = std::make_tuple(f2u(p.alpha), f2u(p.code_scale), (int)p.anchor_bits,
                                (int)p.residual_bits);
     auto it = g_cache.find(key);
-    if (it != g_cache.end())
-        return &it->second;
+    if (it != g_cache.end()) {
+        *out = it->second;
+        return true;
+    }
     Tables t;
     if (!build_quant_tab(p.alpha, p.code_scale, code_max_of(p.anchor_bits, p.residual_bits),
                          &t.q))
-        return nullptr;
+        return false;
     build_dequant_tab(p.alpha, p.code_scale, &t.d);
-    return &g_cache.emplace(key, t).first->second;
+    if (g_cache.size() >= kMaxCachedTables)
+        g_cache.clear();
+    g_cache.emplace(key, t);
+    *out = t;
+    return true;
 }
 
 // ------------------------------------------------------------ validation --
@@ -226,10 +237,10 @@ int quantize_common(const void *kv, const lynx_kv_shape *shape, const lynx_param
                             (const void *)residual})
         if (ptr && !aligned16(ptr))
             return LYNX_ESHAPE;
-    const Tables *t = tables_for(p);
-    if (!t)
+    Tables t;
+    if (!tables_for(p, &t))
         return LYNX_EINVAL;
-    QuantTab tab = t->q;
+    QuantTab tab = t.q;
     tab.eps = p.eps;
     Geometry g = geometry(shape, nb);
     for (int64_t b0 = 0; b0 < nb; b0 += kMaxLaunchBlocks) {
@@ -265,10 +276,10 @@ int dequant_common(const uint8_t *anchor, const uint8_t *residual, lynx_meta met
                             (const void *)meta.mu, (const void *)meta.sigma})
         if (ptr && !aligned16(ptr))
             return LYNX_ESHAPE;
-    const Tables *t = tables_for(p);
-    if (!t)
+    Tables t;
+    if (!tables_for(p, &t))
         return LYNX_EINVAL;
-    DequantTab tab = t->d;
+    DequantTab tab = t.d;
     tab.eps = p.eps;
     Geometry g = geometry(shape, nb);
     for (int64_t b0 = 0; b0 < nb; b0 += kMaxLaunchBlocks) {
@@ -441,10 +452,10 @@ int lynx_compander_thresholds(const lynx_params *params, float *thr128) {
     const lynx_params p = resolve(params);
     if (!thr128 || check_params(p))
         return LYNX_EINVAL;
-    const Tables *t = tables_for(p);
-    if (!t)
+    Tables t;
+    if (!tables_for(p, &t))
         return LYNX_EINVAL;
-    memcpy(thr128, t->q.thr, sizeof t->q.thr);
+    memcpy(thr128, t.q.thr, sizeof t.q.thr);
     return LYNX_OK;
 }
 
@@ -524,10 +535,10 @@ int lynx_decode_attn_dequant(const void *q, int t_q, int num_q_heads, const uint
                             (const void *)v_meta.sigma})
         if (ptr && !aligned16(ptr))
             return LYNX_ESHAPE;
-    const Tables *t = tables_for(p);
-    if (!t)
+    Tables t;
+    if (!tables_for(p, &t))
         return LYNX_EINVAL;
-    DequantTab tab = t->d;
+    DequantTab tab = t.d;
     tab.eps = p.eps;
     AttnArgs a;
     a.q = (const uint16_t *)q;
@@ -608,12 +619,12 @@ int lynx_split_stream_transfer(const void *kv, const lynx_kv_shape *shape,
         if (!aligned16(kv) || !aligned16(kv_anchor) || !aligned16(kv_full))
             return LYNX_ESHAPE;
     }
-    const Tables *t = tables_for(p);
-    if (!t)
+    Tables t;
+    if (!tables_for(p, &t))
         return LYNX_EINVAL;
-    QuantTab qt = t->q;
+    QuantTab qt = t.q;
     qt.eps = p.eps;
-    DequantTab dt = t->d;
+    DequantTab dt = t.d;
     dt.eps = p.eps;
     const Geometry g0 = geometry(shape, nb);
 

@@ -417,3 +417,18 @@ def test_bf16_metadata_parameters():
     assert L.lynx_split_stream_transfer(FAKE, ctypes.byref(sh), ctypes.byref(q16), 1, c, c, c,
                                         FAKE, FAKE, 0, None, None, None, None,
                                         ctypes.byref(t)) == -1
+
+
+def test_table_cache_is_bounded_and_stable():
+    """More parameter sets than the table cache holds: the tables are
+    rebuilt after eviction and come out identical (host only)."""
+    first = lynx.compander_thresholds(lynx.params(alpha=255.0))
+    seen = {}
+    for i in range(150):
+        a = 10.0 + 7.25 * i
+        seen[a] = lynx.compander_thresholds(lynx.params(alpha=a))
+    again = lynx.compander_thresholds(lynx.params(alpha=255.0))
+    assert np.array_equal(first.view(np.uint32), again.view(np.uint32))
+    for a in (10.0, 10.0 + 7.25 * 149):
+        assert np.array_equal(seen[a].view(np.uint32),
+                              lynx.compander_thresholds(lynx.params(alpha=a)).view(np.uint32))
