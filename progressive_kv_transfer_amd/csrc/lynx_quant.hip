@@ -153,16 +153,32 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
     // Compander table into LDS, once per workgroup.  Above code 127 (the top
     // of a single 8-bit stream) there is no next threshold: +inf, which no
     // clamped magnitude reaches.
+    // All of a lane's bucket codes are loaded first, then their thresholds:
+    // two dependent loads per lane instead of two per bucket.
     if (MODE == kModeQuantize) {
-        for (int i = tid; i < tab.nbuckets; i += kThreads) {
-            uint32_t c = tab.bucket_code[i];
-            const uint32_t next = c + 1 < 128 ? __float_as_uint(tab.thr[c + 1]) : 0x7f800000u;
+        constexpr int kPer = (kMaxBuckets + kThreads - 1) / kThreads;
+        uint32_t code[kPer], next[kPer];
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const int i = tid + k * kThreads;
+            code[k] = i < tab.nbuckets ? tab.bucket_code[i] : 0u;
+        }
+#pragma unroll
+        for (int k = 0; k < kPer; ++k)
+            next[k] = code[k] + 1 < 128 ? __float_as_uint(tab.thr[code[k] + 1]) : 0x7f800000u;
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const int i = tid + k * kThreads;
+            if (i >= tab.nbuckets)
+                break;
+            const uint32_t c = code[k];
             if (SH16) {
-                const uint32_t lo = (next >> 16) == (uint32_t)(tab.bucket_lo + i) ? (next & 0xffffu)
-                                                                                : 0x10000u;
+                const uint32_t lo = (next[k] >> 16) == (uint32_t)(tab.bucket_lo + i)
+                                        ? (next[k] & 0xffffu)
+                                        : 0x10000u;
                 s_tab[i] = ((c + kBias + 1u) << 24) - lo;
             } else {
-                s_tab[2 * i] = next;
+                s_tab[2 * i] = next[k];
                 s_tab[2 * i + 1] = c + kBias;
             }
         }
