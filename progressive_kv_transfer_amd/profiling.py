@@ -4,6 +4,7 @@
     python -m progressive_kv_transfer_amd.profiling pmc RESULTS_DB [--match lynx]
     python -m progressive_kv_transfer_amd.profiling traffic FETCH_DB WRITE_DB \
         COPY_FETCH_DB COPY_WRITE_DB --elements N [--title T]
+    python -m progressive_kv_transfer_amd.profiling copies RESULTS_DB
 
 `trace` prints, per kernel, the number of dispatches and the average,
 minimum and maximum duration (from the kernel-trace table); `pmc` prints, per
@@ -11,7 +12,9 @@ kernel and counter (rocprofv3 --pmc), the per-dispatch value averaged over
 the dispatches; `traffic` turns FETCH_SIZE / WRITE_SIZE passes over the codec
 kernels (and over a plain 1 GiB copy, which fixes the counters' scale) into
 HBM bytes per launch against the algorithmic bytes of N bf16 elements, as a
-markdown table plus the JSON block that bench.py reads.
+markdown table plus the JSON block that bench.py reads; `copies` summarises
+the host <-> device copies of a --memory-copy-trace run and the runtime's
+shader blit copies.
 """
 from __future__ import annotations
 
@@ -139,9 +142,31 @@ cd $R && python3 -m progressive_kv_transfer_amd.profiling traffic \\
 """
 
 
+def copies(db: str):
+    """Host <-> device copies of a --memory-copy-trace run, by direction and
+    size (>= 32 MiB = big), and the runtime's shader blit copies
+    (`__amd_rocclr_copyBuffer` dispatches) by duration."""
+    c = sqlite3.connect(db)
+    names = [r[0] for r in c.execute("select name from sqlite_master")]
+    agents = (dict(c.execute("select id, type from rocpd_info_agent").fetchall())
+              if "rocpd_info_agent" in names else {})
+    groups = {}
+    for src, dst, size, dur in c.execute(
+            "select src_agent_id, dst_agent_id, size, end - start from rocpd_memory_copy"):
+        k = (agents.get(src, src), agents.get(dst, dst), "big" if size >= 32 << 20 else "small")
+        g = groups.setdefault(k, [0, 0, 0])
+        g[0] += 1
+        g[1] += size
+        g[2] += dur
+    blits = [d for (d,) in c.execute(
+        "select k.end - k.start from rocpd_kernel_dispatch k join rocpd_info_kernel_symbol s "
+        "on k.kernel_id = s.id where s.kernel_name like '%copyBuffer%'")]
+    return groups, blits
+
+
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("mode", choices=["trace", "pmc", "traffic"])
+    ap.add_argument("mode", choices=["trace", "pmc", "traffic", "copies"])
     ap.add_argument("db", nargs="+")
     ap.add_argument("--match", default=None)
     ap.add_argument("--elements", type=int, default=1 << 31)
@@ -154,6 +179,19 @@ def main():
         print(traffic(*a.db, a.elements, a.title, TRAFFIC_COMMAND), end="")
         return
     a.db = a.db[0]
+    if a.mode == "copies":
+        groups, blits = copies(a.db)
+        print("| from | to | size | copies | GB | avg us | GB/s while copying |")
+        print("|---|---|---|---|---|---|---|")
+        for (src, dst, cls), (n, b, t) in sorted(groups.items(), key=str):
+            print(f"| {src} | {dst} | {cls} | {n} | {b / 1e9:.2f} | {t / n / 1e3:.1f} | "
+                  f"{b / t if t else 0.0:.1f} |")
+        print()
+        print("| shader blit copies | dispatches | under 100 us | 100 us - 1 ms | over 1 ms |")
+        print("|---|---|---|---|---|")
+        print(f"| __amd_rocclr_copyBuffer | {len(blits)} | {sum(d <= 1e5 for d in blits)} | "
+              f"{sum(1e5 < d <= 1e6 for d in blits)} | {sum(d > 1e6 for d in blits)} |")
+        return
     if a.mode == "trace":
         print("| kernel | dispatches | avg us | min us | max us |")
         print("|---|---|---|---|---|")
