@@ -536,7 +536,7 @@ def measure_large(torch, kvgen, lynx, reps: int = 5):
 
 
 TRANSFER_OBJECT_BLOCKS = 4096  # 256 MiB of bf16 KV per transfer object (16 objects)
-TRANSFER_REPS = 5              # alternating link-only / pipeline runs (medians reported)
+TRANSFER_REPS = 9              # alternating link-only / pipeline runs (medians reported)
 
 
 def measure_transfer(torch, lynx, kv, codes, out_a, out_f, kern_ms):
