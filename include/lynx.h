@@ -79,7 +79,10 @@
  * before launching anything and returns a status code; on an error nothing
  * is launched and no output is written.  Successful calls are asynchronous
  * on `stream` (NULL = the default stream): results are visible once the
- * stream is synchronised.  Device pointers must be 16-byte aligned, row and
+ * stream is synchronised.  Apart from the blocking
+ * lynx_split_stream_transfer, a call only enqueues kernels on `stream` (no
+ * allocation, memset, copy or synchronisation), so it may be recorded into a
+ * HIP graph and replayed.  Device pointers must be 16-byte aligned, row and
  * tensor strides multiples of 8 elements.
  */
 #ifndef LYNX_H
