@@ -674,15 +674,20 @@ int lynx_split_stream_transfer(const void *kv, const lynx_kv_shape *shape,
             ok(launch_quantize((const uint16_t *)kv, g, qt, tx.anchor, tx.residual,
                                tx.meta.gamma_min, tx.meta.gamma_scale, tx.meta.mu, tx.meta.sigma,
                                kModeQuantize, 4, 4, 32, sender));
-        ok(hipEventRecord(q[i], sender));
-        ok(hipStreamWaitEvent(link_out, q[i], 0));
+        // the last object's events are the timed milestones themselves, so
+        // each milestone is ordered by the same waits as the work it marks
+        const bool last = i + 1 == nobj;
+        const hipEvent_t qe = last ? t_q : q[i];
+        ok(hipEventRecord(qe, sender));
+        ok(hipStreamWaitEvent(link_out, qe, 0));
         ok(copy_anchor_meta(tx, wire, b0, n, link_out));
         ok(hipEventRecord(ao[i], link_out));
         ok(hipStreamWaitEvent(link_in, ao[i], 0));
         ok(copy_anchor_meta(wire, rx, b0, n, link_in));
-        ok(hipEventRecord(a[i], link_in));
+        const hipEvent_t ae = last ? t_a : a[i];
+        ok(hipEventRecord(ae, link_in));
         // deserializer, anchor phase
-        ok(hipStreamWaitEvent(receiver, a[i], 0));
+        ok(hipStreamWaitEvent(receiver, ae, 0));
         if (!copies_only)
             ok(launch_dequant(rx.anchor, nullptr, rx.meta.gamma_min, rx.meta.gamma_scale,
                               rx.meta.mu, rx.meta.sigma, g, dt, (uint16_t *)kv_anchor, 4, 4,
@@ -690,8 +695,6 @@ int lynx_split_stream_transfer(const void *kv, const lynx_kv_shape *shape,
         if (i == 0)
             ok(hipEventRecord(t_da0, receiver));
     }
-    ok(hipEventRecord(t_q, sender));
-    ok(hipEventRecord(t_a, link_in));
     ok(hipEventRecord(t_da, receiver));
     // Residual queue: behind the whole anchor queue on both hops.
     for (int64_t i = 0; i < nobj && err == hipSuccess; ++i) {
@@ -702,15 +705,14 @@ int lynx_split_stream_transfer(const void *kv, const lynx_kv_shape *shape,
         ok(hipEventRecord(ro[i], link_out));
         ok(hipStreamWaitEvent(link_in, ro[i], 0));
         ok(copy_residual(wire, rx, b0, n, link_in));
-        ok(hipEventRecord(r[i], link_in));
+        ok(hipEventRecord(i + 1 == nobj ? t_r : r[i], link_in));
     }
-    ok(hipEventRecord(t_r, link_in));
     // deserializer, residual phase (after the whole anchor phase)
     for (int64_t i = 0; i < nobj && err == hipSuccess; ++i) {
         Geometry g;
         int64_t b0, n;
         object(i, g, b0, n);
-        ok(hipStreamWaitEvent(receiver, r[i], 0));
+        ok(hipStreamWaitEvent(receiver, i + 1 == nobj ? t_r : r[i], 0));
         if (!copies_only)
             ok(launch_dequant(rx.anchor, rx.residual, rx.meta.gamma_min, rx.meta.gamma_scale,
                               rx.meta.mu, rx.meta.sigma, g, dt, (uint16_t *)kv_full, 4, 4,
