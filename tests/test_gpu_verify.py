@@ -65,6 +65,8 @@ def test_invalid_draft_token_is_rejected():
     tokens[2] = 300  # out of range: rejected at position 2 without a read
     k, tok = run_gpu(draft, target, tokens, u, us)
     assert k == 2
-    # the correction at an identical draft/target row has no residual mass:
-    # the fallback is the last token with positive weight, none here -> -1
-    assert tok == -1 or 0 <= tok < 300
+    # the correction at position 2 draws from max(0, p - q) of identical
+    # draft and target rows (noise 0): no token carries weight, and the
+    # library's contract for a correction without mass is token -1
+    assert torch.equal(draft[2], target[2])
+    assert tok == -1
