@@ -23,7 +23,8 @@
  * reason in the design notes of the repository):
  *   - axis=1 of X in R^{H x P} is the token axis: statistics are per channel;
  *   - one epsilon for both stages;
- *   - gamma_min is canonicalised with "+ 0.0f" (turns -0 into +0);
+ *   - gamma_min, gamma_scale and mu are canonicalised with "+ 0.0f" (turns
+ *     -0 into +0), so every stored statistic has one bit pattern;
  *   - the 32-token mean is a balanced pairwise tree sum, then / C;
  *   - S = Sign(X_cent), with +0 and -0 counted as non-negative;
  *   - Round is round-half-up of the real value Y;
@@ -118,6 +119,12 @@ int oracle_code(float x_abs, float alpha, float code_scale)
 {
     double y = (double)code_scale * log1p((double)alpha * (double)x_abs) /
                log1p((double)alpha);
+    /* Only non-finite inputs (unspecified codes) leave [0, code_scale]:
+     * keep the integer conversion defined for them. */
+    if (!(y >= 0.0))
+        return 0;
+    if (y > 1.0e9)
+        return 1000000000;
     double fl = floor(y);
     int i = (int)fl;
     if (y - fl >= 0.5)
@@ -305,7 +312,7 @@ int oracle_quantize_block_bits(const uint16_t *x, int64_t row_stride, int H,
             if (v > mx) mx = v;
         }
         mn = mn + 0.0f;
-        float gscale = mx - mn;
+        float gscale = (mx - mn) + 0.0f;
         if (m16)
             gscale = bf16_ceil_nonneg(gscale);
         float d1 = gscale + eps;
@@ -320,7 +327,7 @@ int oracle_quantize_block_bits(const uint16_t *x, int64_t row_stride, int H,
         /* Stage 2: per-channel, chunk-wise isolation. */
         for (int j = 0; j < nchunk; ++j) {
             const float *blk = xn + j * C;
-            float m = tree_sum(blk, C) / (float)C;
+            float m = tree_sum(blk, C) / (float)C + 0.0f;
             if (m16)
                 m = bf16_nearest(m);
             float sg = 0.0f;

@@ -315,8 +315,9 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
                     a = fminf(a, mn[w * kHead]);
                     m = fmaxf(m, mx[w * kHead]);
                 }
-                gmin = a + 0.0f;  // canonical +0 for a zero minimum (a bf16 value)
-                gsc = m - gmin;
+                // canonical +0 for a zero minimum (a bf16 value) and scale
+                gmin = a + 0.0f;
+                gsc = (m - gmin) + 0.0f;
                 if (M16) {
                     gsc = bf16_up(gsc);
                     ((uint16_t *)gmin_io)[meta0 + tid] = (uint16_t)(__float_as_uint(gmin) >> 16);
@@ -374,7 +375,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
 #pragma unroll
             for (int k = 0; k < 4; ++k) t4[k] = t8[2 * k] + t8[2 * k + 1];
             float s32 = (t4[0] + t4[1]) + (t4[2] + t4[3]);
-            mu[e] = s32 * 0.03125f;
+            mu[e] = s32 * 0.03125f + 0.0f;  // canonical +0 for a zero mean
             if (M16)
                 mu[e] = bf16_rne(mu[e]);
             float m = 0.0f;

@@ -204,7 +204,11 @@ def edge_pages(seed: int = 7) -> dict[str, torch.Tensor]:
     huge_range        : 1e30 and 1e-30 in the same channel;
     large_same_sign   : magnitudes up to 1e38, all positive;
     all_negative      : strictly negative Laplacian page;
-    zeros             : all +0.
+    zeros             : all +0;
+    mixed_sign_zeros  : every value +0 or -0: channels whose first token is
+                        -0 and the rest +0, all -0 channels, channels with
+                        whole -0 chunks among +0 chunks, and channels with
+                        scattered -0 plus one small positive value.
     """
     g = torch.Generator()
     g.manual_seed(int(seed))
@@ -237,6 +241,15 @@ def edge_pages(seed: int = 7) -> dict[str, torch.Tensor]:
     out["large_same_sign"] = _bf16_from_f32(lap.abs() * 2.0e37 + 1.0e30)
     out["all_negative"] = _bf16_from_f32(-(lap.abs() + 0.01))
     out["zeros"] = _bf16_from_f32(torch.zeros((P, H)))
+    mz = torch.zeros((P, H))
+    mz[0, 0:32] = -0.0
+    mz[:, 32:64] = -0.0
+    chunk_odd = ((torch.arange(P) // CHUNK) % 2 == 1)[:, None]
+    mz[:, 64:96] = torch.where(chunk_odd, torch.tensor(-0.0), torch.tensor(0.0))
+    mz[:, 96:128] = torch.where(torch.rand((P, 32), generator=g) < 0.5,
+                                torch.tensor(-0.0), torch.tensor(0.0))
+    mz[100, 96:128] = 2.0e-3
+    out["mixed_sign_zeros"] = _bf16_from_f32(mz)
     return out
 
 

@@ -42,7 +42,8 @@ def check(kv, a, code_scale, alpha=255.0):
     nb = ref.nblocks
     np.testing.assert_array_equal(host(codes.anchor).reshape(nb, -1), ref.anchor.reshape(nb, -1))
     for name in ("gamma_min", "gamma_scale", "mu", "sigma"):
-        assert np.array_equal(host(getattr(codes, name)), getattr(ref, name)), name
+        assert np.array_equal(host(getattr(codes, name)).view(np.uint32),
+                              getattr(ref, name).view(np.uint32)), name
     np.testing.assert_array_equal(
         bits(out), oracle.dequant(ref, xb.shape, False, alpha=alpha, code_scale=code_scale,
                                   threads=8))

@@ -203,8 +203,11 @@ def test_stage1_invariants(name):
     x = bits(PAGES[name])
     r = oracle.quantize_block(x)
     xf = bf16_to_f32(x)  # [P][H]
-    assert np.array_equal(r.gamma_min, xf.min(axis=0) + F32(0.0))
-    assert np.array_equal(r.gamma_scale, xf.max(axis=0) - r.gamma_min)
+    # bit patterns: a zero minimum and a zero range are the canonical +0
+    u32 = lambda a: np.ascontiguousarray(a, np.float32).view(np.uint32)
+    assert np.array_equal(u32(r.gamma_min), u32(xf.min(axis=0) + F32(0.0)))
+    assert np.array_equal(u32(r.gamma_scale),
+                          u32((xf.max(axis=0) - r.gamma_min) + F32(0.0)))
     assert np.all(r.xn >= 0.0) and np.all(r.xn <= 1.0)
     for c in range(x.shape[1]):
         col = xf[:, c]
@@ -231,6 +234,7 @@ def test_stage2_invariants(name):
             exact = sum(Fraction(float(v)) for v in xn) / 32
             bound = 6 * 2.0 ** -24 * float(np.abs(xn).max())
             assert abs(float(mu) - float(exact)) <= bound
+            assert not (mu == 0.0 and np.signbit(mu))  # a zero mean is +0
             xc = r.xcent[c, sl]
             assert np.array_equal(xc, xn - F32(mu))
             sg = r.sigma[j, c]
@@ -240,6 +244,25 @@ def test_stage2_invariants(name):
             assert np.abs(xfin).max() == F32(sg) / (F32(sg) + F32(1e-6))
             assert np.all((xfin < 0) == (xc < 0))
             assert np.all((r.sign[c, sl] < 0) == (xc < 0))
+
+
+def test_zero_statistics_are_positive_zero():
+    """A page of signed zeros: every stored statistic is +0 bit for bit
+    (gamma_min, gamma_scale and mu carry one canonical zero, whatever the
+    mix of +0 and -0 inputs or the order of the minimum / maximum), every
+    code is 0 and both reconstructions give +0 or -0 only."""
+    x = bits(PAGES["mixed_sign_zeros"])
+    r = oracle.quantize_block(x)
+    for a in (r.gamma_min, r.gamma_scale, r.mu, r.sigma)[:3]:
+        assert not np.any(np.signbit(a) & (a == 0.0))
+    assert np.all(r.sigma >= 0.0) and not np.any(np.signbit(r.sigma))
+    # channels 0-95 hold zeros only: all statistics exactly +0
+    for a in (r.gamma_min[:96], r.gamma_scale[:96], r.mu[:, :96], r.sigma[:, :96]):
+        assert np.all(np.ascontiguousarray(a).view(np.uint32) == 0)
+    assert np.all(r.code_raw[:96] == 0)
+    for full in (False, True):
+        out = bf16_to_f32(oracle.dequant_block(r, full))
+        assert np.all(out[:, :96] == 0.0)
 
 
 def test_stage2_chunk_locality():
