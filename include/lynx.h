@@ -83,7 +83,9 @@
  * lynx_split_stream_transfer, a call only enqueues kernels on `stream` (no
  * allocation, memset, copy or synchronisation), so it may be recorded into a
  * HIP graph and replayed.  Device pointers must be 16-byte aligned, row and
- * tensor strides multiples of 8 elements.
+ * tensor strides multiples of 8 elements, and row_stride at most 4210744
+ * elements (a page block's 256 rows are addressed with 32-bit byte offsets;
+ * larger strides give LYNX_ESHAPE).
  */
 #ifndef LYNX_H
 #define LYNX_H

@@ -24,6 +24,12 @@ thread_local std::string g_hip_error;
 // work-items (blocks x 512) must stay below 2^32.
 constexpr int64_t kMaxLaunchBlocks = int64_t(1) << 22;
 
+// Largest row stride (elements): the quantize kernel addresses a page
+// block's 256 rows through one buffer resource with 32-bit byte offsets
+// below 2^31 - 1, up to 255 rows of 2 row_stride bytes plus one 256-byte
+// row (4210744 is the largest multiple of 8 below this).
+constexpr int64_t kMaxRowStride = (int64_t(0x7fffffff) - 256) / 510;
+
 uint32_t f2u(float f) {
     uint32_t u;
     memcpy(&u, &f, 4);
@@ -178,7 +184,7 @@ int check_shape(const lynx_kv_shape *s, int64_t *nblocks) {
         return LYNX_EINVAL;
     if (s->num_tokens % kPage || s->num_channels % kHead)
         return LYNX_ESHAPE;
-    if (s->row_stride < s->num_channels || s->row_stride % 8)
+    if (s->row_stride < s->num_channels || s->row_stride % 8 || s->row_stride > kMaxRowStride)
         return LYNX_ESHAPE;
     if (s->num_tensors > 1 &&
         (s->tensor_stride % 8 || s->tensor_stride < s->num_tokens * s->row_stride))

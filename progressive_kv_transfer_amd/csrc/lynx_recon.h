@@ -1,8 +1,11 @@
-// Reconstruction arithmetic shared by the dequant and the fused attention
-// kernels, so both produce the same bf16 K^ / V^ bit for bit: the inverse of
+// Reconstruction arithmetic of the dequant kernels: the inverse of
 // Algorithm 1 of "Lynx: Progressive Speculative Quantization for
 // accelerating KV Transfer in Long-Context Inference" (Eq. (4); the anchor
-// level V << 4 of the reading notes' worked example).
+// level V << 4 of the reading notes' worked example).  The fused attention
+// kernels share only the signed level table (signed_level) and the bf16
+// rounding (pack_bf16): they fold Eq. (4) into one fused multiply-add per
+// element, so their K^ / V^ may differ from lynx_dequant_* by one bf16 unit
+// on rare elements (rounding order, not a different level).
 #pragma once
 
 #include "lynx_internal.h"

@@ -343,11 +343,45 @@ def dequant_full(codes: Codes, out: torch.Tensor, p: lynx_params | None = None,
     return out
 
 
+def _blocks_of(sh: lynx_kv_shape) -> int:
+    """Page blocks of a shape, computed here (no library call); shapes the
+    library refuses count as 0 blocks and are left to its status code."""
+    if min(sh.num_tensors, sh.num_tokens, sh.num_channels) < 0 or \
+            sh.num_tokens % PAGE_TOKENS or sh.num_channels % BLOCK_CHANNELS:
+        return 0
+    return sh.num_tensors * (sh.num_tokens // PAGE_TOKENS) * (sh.num_channels // BLOCK_CHANNELS)
+
+
+def _check_stats(fn: str, kv: torch.Tensor, arrays, p: lynx_params | None):
+    """The statistics calls: a bf16 KV set and float32 arrays (binary32
+    metadata only) of at least the listed element counts per page block, all
+    on the device; checked before any library call (types and sizes first,
+    then placement)."""
+    if kv.dtype != torch.bfloat16:
+        raise ValueError(f"{fn}: kv must be bfloat16")
+    # the shape comes from the view's own strides, so it addresses only the
+    # view's elements
+    sh = shape_of(kv)
+    if p is not None and p.meta_bits != 32:
+        raise ValueError(f"{fn}: the statistics calls write binary32 metadata")
+    nb = _blocks_of(sh)
+    for name, t, per_block in arrays:
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"{fn}: {name} must be a contiguous float32 tensor")
+        if t.numel() < nb * per_block:
+            raise ValueError(f"{fn}: {name} holds {t.numel()} elements, "
+                             f"{nb * per_block} needed for {nb} page blocks")
+    for name, t in [("kv", kv)] + [(n, t) for n, t, _ in arrays]:
+        if not t.is_cuda:
+            raise ValueError(f"{fn}: {name} must be a device tensor")
+    return sh
+
+
 def page_stats(kv: torch.Tensor, gamma_min: torch.Tensor, gamma_scale: torch.Tensor,
                p: lynx_params | None = None, stream=None):
     """lynx_page_stats (Stage 1 statistics only)."""
-    _require_cuda(kv, gamma_min, gamma_scale)
-    sh = shape_of(kv)
+    sh = _check_stats("page_stats", kv, (("gamma_min", gamma_min, BLOCK_CHANNELS),
+                                         ("gamma_scale", gamma_scale, BLOCK_CHANNELS)), p)
     _check("lynx_page_stats", lib().lynx_page_stats(
         kv.data_ptr(), ctypes.byref(sh), ctypes.byref(p) if p else None,
         gamma_min.data_ptr(), gamma_scale.data_ptr(), _stream(stream)))
@@ -357,8 +391,10 @@ def block_stats(kv: torch.Tensor, gamma_min: torch.Tensor, gamma_scale: torch.Te
                 mu: torch.Tensor, sigma: torch.Tensor, p: lynx_params | None = None,
                 stream=None):
     """lynx_block_stats (Stage 2 statistics given Stage 1's)."""
-    _require_cuda(kv, gamma_min, gamma_scale, mu, sigma)
-    sh = shape_of(kv)
+    chunk = PAGE_TOKENS // CHUNK_TOKENS * BLOCK_CHANNELS
+    sh = _check_stats("block_stats", kv, (("gamma_min", gamma_min, BLOCK_CHANNELS),
+                                          ("gamma_scale", gamma_scale, BLOCK_CHANNELS),
+                                          ("mu", mu, chunk), ("sigma", sigma, chunk)), p)
     _check("lynx_block_stats", lib().lynx_block_stats(
         kv.data_ptr(), ctypes.byref(sh), ctypes.byref(p) if p else None,
         gamma_min.data_ptr(), gamma_scale.data_ptr(), mu.data_ptr(), sigma.data_ptr(),
@@ -424,9 +460,13 @@ def decode_attn_dequant(q: torch.Tensor, k: CodeView, v: CodeView, ctx_len: int,
                 raise ValueError(f"decode_attn_dequant: the {name} view must hold the {nb} "
                                  f"page blocks of a [{ctx_len}, {num_kv_heads} x 128] tensor")
             _check_codes("decode_attn_dequant", view.codes, view.b1, p, residual=view.full)
+    _require_cuda(out)
     need = attn_workspace_bytes(t_q, nqh, num_kv_heads, ctx_len)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _require_cuda(workspace)
+    if not workspace.is_contiguous():
+        raise ValueError("decode_attn_dequant: workspace must be a contiguous device tensor")
     _check("lynx_decode_attn_dequant", lib().lynx_decode_attn_dequant(
         q.data_ptr(), t_q, nqh, k.anchor(), k.residual(), k.meta(), v.anchor(), v.residual(),
         v.meta(), ctx_len, num_kv_heads, hd, scale, int(causal_tail),
@@ -495,6 +535,9 @@ def spec_verify(draft_logits: torch.Tensor, target_logits: torch.Tensor, tokens:
     if workspace is None:
         workspace = torch.empty(max(spec_verify_workspace_bytes(t_draft, vocab), 16),
                                 dtype=torch.uint8, device=target_logits.device)
+    _require_cuda(workspace)
+    if not workspace.is_contiguous():
+        raise ValueError("spec_verify: workspace must be a contiguous device tensor")
     _check("lynx_spec_verify", lib().lynx_spec_verify(
         draft_logits.data_ptr(), target_logits.data_ptr(), tokens.data_ptr(),
         u_accept.data_ptr(), float(u_sample), t_draft, vocab, out.data_ptr(),

@@ -107,6 +107,7 @@ def _meta(ptr=FAKE):
 
 @pytest.mark.parametrize("case,expect", [
     ("tokens", -2), ("channels", -2), ("row_stride", -2), ("row_stride_small", -2),
+    ("row_stride_huge", -2),
     ("tensor_stride", -2), ("negative", -1), ("alpha", -1), ("alpha_nan", -1),
     ("eps", -1), ("page", -1), ("chunk", -1), ("null_kv", -1), ("null_anchor", -1),
     ("misaligned", -2), ("code_scale", -1)])
@@ -124,6 +125,9 @@ def test_quantize_argument_errors(case, expect):
         s = _shape(rs=132)
     elif case == "row_stride_small":
         s = _shape(rs=64)
+    elif case == "row_stride_huge":
+        # the first multiple of 8 above the 32-bit row addressing limit
+        s = _shape(rs=4210752)
     elif case == "tensor_stride":
         s = _shape(nt=2, ts=1000)
     elif case == "negative":
@@ -165,6 +169,10 @@ def test_dequant_and_stats_argument_errors():
     assert L.lynx_page_stats(FAKE, ctypes.byref(s), ctypes.byref(p), None, FAKE, None) == -1
     assert L.lynx_block_stats(FAKE, ctypes.byref(s), None, FAKE, FAKE, None, FAKE,
                               None) == -1
+    huge = _shape(rs=4210752)
+    assert L.lynx_dequant_anchor(FAKE, _meta(), ctypes.byref(huge), None, FAKE, None) == -2
+    assert L.lynx_page_stats(FAKE, ctypes.byref(huge), None, FAKE, FAKE, None) == -2
+    assert L.lynx_num_blocks(ctypes.byref(huge)) == -2
     bad = lynx.params(eps=0.0)
     assert L.lynx_page_stats(FAKE, ctypes.byref(s), ctypes.byref(bad), FAKE, FAKE,
                              None) == -1
