@@ -26,11 +26,22 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "lynx_oracle.c")
-_LIB = os.path.join(_HERE, "liblynx_oracle.so")
 
 # Plain scalar build: no FMA contraction, no fast-math, SSE binary32.
 CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
           "-fno-fast-math", "-fno-unsafe-math-optimizations", "-Wall"]
+
+# LYNX_ORACLE_SANITIZE=1 selects a separate build of the same source with
+# AddressSanitizer and UndefinedBehaviorSanitizer (every report fatal), for
+# running the CPU test suite under the sanitizers.  Python itself is not
+# instrumented, so that run preloads the ASan runtime:
+#   LD_PRELOAD=$(gcc -print-file-name=libasan.so) \
+#   ASAN_OPTIONS=detect_leaks=0 LYNX_ORACLE_SANITIZE=1 \
+#   python -m pytest tests -m "not gpu"
+SANITIZE = os.environ.get("LYNX_ORACLE_SANITIZE", "") == "1"
+SAN_FLAGS = ["-fsanitize=address,undefined,float-cast-overflow", "-fno-sanitize-recover=all",
+             "-fno-omit-frame-pointer", "-g"]
+_LIB = os.path.join(_HERE, "liblynx_oracle_san.so" if SANITIZE else "liblynx_oracle.so")
 
 _lock = threading.Lock()
 _lib = None
@@ -50,7 +61,8 @@ def build(force: bool = True) -> str:
             os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
         return _LIB
     tmp = _LIB + ".tmp%d" % os.getpid()
-    subprocess.check_call(["gcc", *CFLAGS, "-o", tmp, _SRC, "-lm"])
+    subprocess.check_call(["gcc", *CFLAGS, *(SAN_FLAGS if SANITIZE else []), "-o", tmp,
+                           _SRC, "-lm"])
     os.replace(tmp, _LIB)
     return _LIB
 
