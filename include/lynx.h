@@ -104,6 +104,8 @@ extern "C" {
 #define LYNX_EINVAL (-1) /* null pointer, negative size, bad parameter     */
 #define LYNX_ESHAPE (-2) /* tokens % 256, channels % 128, stride or align   */
 #define LYNX_EHIP (-3)   /* a HIP call or launch failed (see status string) */
+#define LYNX_ESCRATCH (-4) /* more than LYNX_ATTN_SCRATCH_BYTES of scratch
+                              needed (lynx_decode_attn_dequant_noalloc)     */
 
 /* Geometry fixed by the GPU kernels. */
 #define LYNX_PAGE_TOKENS 256
@@ -293,6 +295,38 @@ int lynx_decode_attn_dequant(const void *q, int t_q, int num_q_heads,
                              const lynx_params *params, void *out,
                              int out_dtype, void *workspace,
                              size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of the fixed device scratch of lynx_decode_attn_dequant_noalloc. */
+#define LYNX_ATTN_SCRATCH_BYTES (24u << 20)
+
+/*
+ * For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): lynx_decode_attn_dequant
+ * without a workspace argument.  Same arguments, results and errors, bit
+ * for bit the same output; the split partials go to a fixed device array of
+ * LYNX_ATTN_SCRATCH_BYTES (24 MiB) inside the library instead, and the call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine;
+ * the caller passes q, the codes and out).  Each GPU the library runs on
+ * holds its own copy of the array from the first call on that device until
+ * the process ends.  The first call on a device looks up that device's
+ * array address (with the device current).  Calls whose partials need more
+ * than the array holds (lynx_attn_workspace_bytes(...) above
+ * LYNX_ATTN_SCRATCH_BYTES, which takes 64 query rows per KV head and more
+ * than 128 KV heads) return LYNX_ESCRATCH before launching anything.  Every call on
+ * one GPU shares that GPU's array and leaves its partials there (every
+ * partial a call reads was written by the same call, so nothing needs
+ * clearing): calls that overlap on one GPU (on different streams, or from
+ * different host threads) race on it and must be serialised by the caller.
+ */
+int lynx_decode_attn_dequant_noalloc(const void *q, int t_q, int num_q_heads,
+                                     const uint8_t *k_anchor,
+                                     const uint8_t *k_residual, lynx_meta k_meta,
+                                     const uint8_t *v_anchor,
+                                     const uint8_t *v_residual, lynx_meta v_meta,
+                                     int64_t ctx_len, int num_kv_heads,
+                                     int head_dim, float scale, int causal_tail,
+                                     const lynx_params *params, void *out,
+                                     int out_dtype, hipStream_t stream);
 
 /* Streams and metadata of a KV set in one memory space (device memory or
  * pinned host memory), layouts as above. */

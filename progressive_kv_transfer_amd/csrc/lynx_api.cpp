@@ -475,6 +475,9 @@ const char *lynx_status_string(int status) {
         return "invalid shape (tokens % 256, channels % 128, stride or 16-byte alignment)";
     case LYNX_EHIP:
         return g_hip_error.empty() ? "HIP error" : g_hip_error.c_str();
+    case LYNX_ESCRATCH:
+        return "the call needs more than the library's fixed device scratch "
+               "(LYNX_ATTN_SCRATCH_BYTES); use the entry point that takes a workspace";
     default:
         return "unknown status";
     }
@@ -505,13 +508,20 @@ size_t lynx_attn_workspace_bytes(int t_q, int num_q_heads, int num_kv_heads, int
     return attn_plan(t_q, num_q_heads, num_kv_heads, ctx_len, &pl) ? 0 : pl.ws_bytes;
 }
 
-int lynx_decode_attn_dequant(const void *q, int t_q, int num_q_heads, const uint8_t *k_anchor,
-                             const uint8_t *k_residual, lynx_meta k_meta,
-                             const uint8_t *v_anchor, const uint8_t *v_residual,
-                             lynx_meta v_meta, int64_t ctx_len, int num_kv_heads, int head_dim,
-                             float scale, int causal_tail, const lynx_params *params, void *out,
-                             int out_dtype, void *workspace, size_t workspace_bytes,
-                             hipStream_t stream) {
+}  // extern "C"
+
+static_assert(kAttnScratchBytes == LYNX_ATTN_SCRATCH_BYTES, "scratch size of lynx.h");
+
+namespace {
+
+// Both attention entry points: the partials go to the caller's workspace,
+// or (use_scratch) to the library's fixed device scratch.
+int attn_common(const void *q, int t_q, int num_q_heads, const uint8_t *k_anchor,
+                const uint8_t *k_residual, lynx_meta k_meta, const uint8_t *v_anchor,
+                const uint8_t *v_residual, lynx_meta v_meta, int64_t ctx_len,
+                int num_kv_heads, int head_dim, float scale, int causal_tail,
+                const lynx_params *params, void *out, int out_dtype, void *workspace,
+                size_t workspace_bytes, bool use_scratch, hipStream_t stream) {
     const lynx_params p = resolve(params);
     int rc = check_params(p);
     if (rc)
@@ -526,12 +536,12 @@ int lynx_decode_attn_dequant(const void *q, int t_q, int num_q_heads, const uint
         return rc;
     if (causal_tail && ctx_len < t_q)
         return LYNX_EINVAL;
-    if (!q || !out || !workspace || !k_anchor || !v_anchor || !k_meta.gamma_min ||
-        !k_meta.gamma_scale || !k_meta.mu || !k_meta.sigma || !v_meta.gamma_min ||
-        !v_meta.gamma_scale || !v_meta.mu || !v_meta.sigma)
+    if (!q || !out || (!use_scratch && !workspace) || !k_anchor || !v_anchor ||
+        !k_meta.gamma_min || !k_meta.gamma_scale || !k_meta.mu || !k_meta.sigma ||
+        !v_meta.gamma_min || !v_meta.gamma_scale || !v_meta.mu || !v_meta.sigma)
         return LYNX_EINVAL;
-    if (workspace_bytes < pl.ws_bytes)
-        return LYNX_EINVAL;
+    if (use_scratch ? pl.ws_bytes > kAttnScratchBytes : workspace_bytes < pl.ws_bytes)
+        return use_scratch ? LYNX_ESCRATCH : LYNX_EINVAL;
     for (const void *ptr : {(const void *)q, (const void *)out, (const void *)workspace, (const void *)k_anchor,
                             (const void *)k_residual, (const void *)v_anchor,
                             (const void *)v_residual, (const void *)k_meta.gamma_min,
@@ -560,7 +570,14 @@ int lynx_decode_attn_dequant(const void *q, int t_q, int num_q_heads, const uint
     a.v_gsc = v_meta.gamma_scale;
     a.v_mu = v_meta.mu;
     a.v_sg = v_meta.sigma;
-    a.ws = (float *)workspace;
+    if (use_scratch) {
+        float *ws = nullptr;
+        if ((rc = hip_status(attn_scratch(&ws))))
+            return rc;
+        a.ws = ws;
+    } else {
+        a.ws = (float *)workspace;
+    }
     a.out = out;
     a.out_f32 = out_dtype == LYNX_OUT_F32 ? 1 : 0;
     a.ctx = ctx_len;
@@ -575,6 +592,34 @@ int lynx_decode_attn_dequant(const void *q, int t_q, int num_q_heads, const uint
     a.causal = causal_tail ? 1 : 0;
     a.qk_scale_log2 = (float)((double)scale * 1.4426950408889634);
     return hip_status(launch_attention(a, tab, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int lynx_decode_attn_dequant(const void *q, int t_q, int num_q_heads, const uint8_t *k_anchor,
+                             const uint8_t *k_residual, lynx_meta k_meta,
+                             const uint8_t *v_anchor, const uint8_t *v_residual,
+                             lynx_meta v_meta, int64_t ctx_len, int num_kv_heads, int head_dim,
+                             float scale, int causal_tail, const lynx_params *params, void *out,
+                             int out_dtype, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+    return attn_common(q, t_q, num_q_heads, k_anchor, k_residual, k_meta, v_anchor, v_residual,
+                       v_meta, ctx_len, num_kv_heads, head_dim, scale, causal_tail, params, out,
+                       out_dtype, workspace, workspace_bytes, false, stream);
+}
+
+int lynx_decode_attn_dequant_noalloc(const void *q, int t_q, int num_q_heads,
+                                     const uint8_t *k_anchor, const uint8_t *k_residual,
+                                     lynx_meta k_meta, const uint8_t *v_anchor,
+                                     const uint8_t *v_residual, lynx_meta v_meta,
+                                     int64_t ctx_len, int num_kv_heads, int head_dim,
+                                     float scale, int causal_tail, const lynx_params *params,
+                                     void *out, int out_dtype, hipStream_t stream) {
+    return attn_common(q, t_q, num_q_heads, k_anchor, k_residual, k_meta, v_anchor, v_residual,
+                       v_meta, ctx_len, num_kv_heads, head_dim, scale, causal_tail, params, out,
+                       out_dtype, nullptr, 0, true, stream);
 }
 
 int lynx_page_stats(const void *kv, const lynx_kv_shape *shape, const lynx_params *params,

@@ -31,9 +31,19 @@
 // which skips most output rescales.  At the end the waves of a row tile are
 // merged in LDS and each live row leaves one partial (max, sum, output) per
 // split in the workspace; attn_combine_kernel merges the splits.
+#include <mutex>
+
 #include "lynx_recon.h"
 
 namespace lynx {
+
+// Fixed device scratch of the allocation-free attention entry point: the
+// split partials live here instead of in a caller's workspace.  Each GPU the
+// library runs on holds its own copy until the process ends.  In host code
+// the name is only a stand-in: its device address comes from
+// hipGetSymbolAddress, looked up once per device (attn_scratch below).
+static __device__ __align__(256) float scratch[kAttnScratchBytes / sizeof(float)];
+
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -545,6 +555,31 @@ hipError_t launch_tiles(const AttnArgs &a, const DequantTab &tab, hipStream_t st
 
 int attn_row_tiles(int rows) {
     return rows < 1 ? -1 : rows <= 16 ? 1 : rows <= 32 ? 2 : rows <= 64 ? 4 : -1;
+}
+
+hipError_t attn_scratch(float **ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static float *per_device[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!per_device[dev]) {
+        // the current device is `dev`: the address is that device's copy
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        if (!p)
+            return hipErrorInvalidSymbol;
+        per_device[dev] = (float *)p;
+    }
+    *ptr = per_device[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_attention(const AttnArgs &a, const DequantTab &tab, hipStream_t stream) {

@@ -98,6 +98,11 @@ struct AttnArgs {
 };
 int attn_row_tiles(int rows);  // tiles of 16 query rows, -1 if rows > 64
 hipError_t launch_attention(const AttnArgs &a, const DequantTab &tab, hipStream_t stream);
+// Bytes of the fixed device scratch of lynx_decode_attn_dequant_noalloc
+// (LYNX_ATTN_SCRATCH_BYTES of lynx.h) and its device address on the current
+// device (looked up once per device).
+constexpr size_t kAttnScratchBytes = size_t(24) << 20;
+hipError_t attn_scratch(float **ptr);
 
 // Speculative verification (lynx_verify.hip).
 constexpr int kVerifyChunk = 2048;    // tokens per statistics workgroup

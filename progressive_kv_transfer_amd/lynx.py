@@ -20,7 +20,9 @@ PAGE_TOKENS = 256
 CHUNK_TOKENS = 32
 BLOCK_CHANNELS = 128
 OUT_BF16, OUT_F32 = 0, 1  # lynx_decode_attn_dequant output element types
-STATUS = {0: "LYNX_OK", -1: "LYNX_EINVAL", -2: "LYNX_ESHAPE", -3: "LYNX_EHIP"}
+STATUS = {0: "LYNX_OK", -1: "LYNX_EINVAL", -2: "LYNX_ESHAPE", -3: "LYNX_EHIP",
+          -4: "LYNX_ESCRATCH"}
+ATTN_SCRATCH_BYTES = 24 << 20  # LYNX_ATTN_SCRATCH_BYTES
 
 
 class LynxError(RuntimeError):
@@ -68,6 +70,7 @@ EXPORTS = ["lynx_default_params", "lynx_num_blocks", "lynx_stream_bytes",
            "lynx_status_string", "lynx_compander_thresholds", "lynx_quantize_pages", "lynx_dequant_anchor",
            "lynx_dequant_full", "lynx_page_stats", "lynx_block_stats",
            "lynx_attn_workspace_bytes", "lynx_decode_attn_dequant",
+           "lynx_decode_attn_dequant_noalloc",
            "lynx_split_stream_transfer", "lynx_spec_verify_workspace_bytes",
            "lynx_spec_verify"]
 
@@ -115,6 +118,9 @@ def lib():
                                                lynx_meta, i64, i32, i32, ctypes.c_float, i32,
                                                P(lynx_params), vp, i32, vp, ctypes.c_size_t,
                                                vp]
+        L.lynx_decode_attn_dequant_noalloc.argtypes = [
+            vp, i32, i32, vp, vp, lynx_meta, vp, vp, lynx_meta, i64, i32, i32,
+            ctypes.c_float, i32, P(lynx_params), vp, i32, vp]
         L.lynx_split_stream_transfer.argtypes = [vp, P(lynx_kv_shape), P(lynx_params), i64,
                                                  lynx_codes, lynx_codes, lynx_codes, vp, vp,
                                                  i32, vp, vp, vp, vp, P(lynx_transfer_times)]
@@ -124,6 +130,7 @@ def lib():
                                        ctypes.c_size_t, vp]
         for f in ("lynx_quantize_pages", "lynx_dequant_anchor", "lynx_dequant_full",
                   "lynx_page_stats", "lynx_block_stats", "lynx_decode_attn_dequant",
+                  "lynx_decode_attn_dequant_noalloc",
                   "lynx_split_stream_transfer", "lynx_spec_verify"):
             getattr(L, f).restype = i32
         _lib = L
@@ -472,6 +479,38 @@ def decode_attn_dequant(q: torch.Tensor, k: CodeView, v: CodeView, ctx_len: int,
         v.meta(), ctx_len, num_kv_heads, hd, scale, int(causal_tail),
         ctypes.byref(p) if p else None, out.data_ptr(), code, workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def decode_attn_dequant_noalloc(q: torch.Tensor, k: CodeView, v: CodeView, ctx_len: int,
+                                num_kv_heads: int, scale: float, out: torch.Tensor,
+                                causal_tail: bool = False, p: lynx_params | None = None,
+                                stream=None) -> torch.Tensor:
+    """lynx_decode_attn_dequant_noalloc: decode_attn_dequant with the split
+    partials in the library's fixed device scratch.  Nothing is allocated,
+    here or in the library: the caller passes `out` (bf16 or float32 shaped
+    like q)."""
+    _require_cuda(q, out)
+    if q.dtype != torch.bfloat16 or q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous bf16 [t_q, num_q_heads, head_dim] tensor")
+    t_q, nqh, hd = q.shape
+    if out.dtype not in (torch.bfloat16, torch.float32) or out.shape != q.shape \
+            or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 or float32 tensor shaped like q")
+    code = OUT_F32 if out.dtype == torch.float32 else OUT_BF16
+    if ctx_len > 0 and ctx_len % PAGE_TOKENS == 0 and num_kv_heads > 0:
+        nb = ctx_len // PAGE_TOKENS * num_kv_heads
+        for name, view in (("k", k), ("v", v)):
+            if not 0 <= view.b0 <= view.b1 or view.b1 - view.b0 != nb:
+                raise ValueError(f"decode_attn_dequant_noalloc: the {name} view must hold the "
+                                 f"{nb} page blocks of a [{ctx_len}, {num_kv_heads} x 128] "
+                                 f"tensor")
+            _check_codes("decode_attn_dequant_noalloc", view.codes, view.b1, p,
+                         residual=view.full)
+    _check("lynx_decode_attn_dequant_noalloc", lib().lynx_decode_attn_dequant_noalloc(
+        q.data_ptr(), t_q, nqh, k.anchor(), k.residual(), k.meta(), v.anchor(), v.residual(),
+        v.meta(), ctx_len, num_kv_heads, hd, scale, int(causal_tail),
+        ctypes.byref(p) if p else None, out.data_ptr(), code, _stream(stream)))
     return out
 
 

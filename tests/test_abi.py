@@ -257,6 +257,29 @@ def _codes(ptr=FAKE):
     return c
 
 
+def test_noalloc_attention_refuses_beyond_its_scratch():
+    """lynx_decode_attn_dequant_noalloc: partials of more than
+    LYNX_ATTN_SCRATCH_BYTES are refused with LYNX_ESCRATCH before any
+    launch; other argument errors as the workspace entry point."""
+    L = lynx.lib()
+    # 8 drafts x 8 query heads per KV head = 64 rows, 1024 KV heads: one split
+    # of 64 partials of (2 + 128) floats per KV head
+    need = lynx.attn_workspace_bytes(8, 8192, 1024, 256)
+    assert need == 1024 * 64 * 130 * 4 > lynx.ATTN_SCRATCH_BYTES
+    args = lambda t_q, nqh, nkvh, ctx: (FAKE, t_q, nqh, FAKE, FAKE, _meta(), FAKE, FAKE,
+                                        _meta(), ctx, nkvh, 128, 0.088, 0, None, FAKE, 0, None)
+    rc = L.lynx_decode_attn_dequant_noalloc(*args(8, 8192, 1024, 256))
+    assert rc == -4 and "scratch" in L.lynx_status_string(rc).decode()
+    assert L.lynx_decode_attn_dequant_noalloc(*args(1, 64, 8, 300)) == -2
+    assert L.lynx_decode_attn_dequant_noalloc(*args(9, 64, 8, 256)) == -1  # 72 rows
+    a = list(args(1, 64, 8, 256))
+    a[15] = None  # out
+    assert L.lynx_decode_attn_dequant_noalloc(*a) == -1
+    # every size the decode and verify workloads use fits
+    assert lynx.attn_workspace_bytes(1, 64, 8, 32768) <= lynx.ATTN_SCRATCH_BYTES
+    assert lynx.attn_workspace_bytes(8, 32, 4, 131072) <= lynx.ATTN_SCRATCH_BYTES
+
+
 @pytest.mark.parametrize("case,expect", [
     ("object_blocks", -1), ("huge_objects", -1), ("flags", -1), ("null_wire", -1), ("misaligned_rx", -1),
     ("misaligned_kv", -2), ("null_out", -1), ("too_many_objects", -1), ("tokens", -2),
