@@ -112,23 +112,38 @@ def load_counters():
     return t.get("quantize")
 
 
+# Host threads of one GPU's share of a GPU machine (the box runs one job per GPU
+# and gives each 16 host threads, whatever os.cpu_count() reports).
+CPU_SHARE = 16
+
+
 def cpu_threads() -> int:
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
         n = os.cpu_count() or 1
-    return max(1, min(16, n))
+    return max(1, min(CPU_SHARE, n))
 
 
 def cpu_model() -> str:
+    """The host CPU as /proc/cpuinfo names it: model name, vendor, family /
+    model / stepping and the number of logical CPUs listed."""
+    fields, n = {}, 0
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                k, _, v = line.partition(":")
+                k = k.strip()
+                if k == "processor":
+                    n += 1
+                if k in ("model name", "vendor_id", "cpu family", "model", "stepping") \
+                        and k not in fields:
+                    fields[k] = v.strip()
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    return (f"{fields.get('model name', 'unknown')} ({fields.get('vendor_id', '?')}, family "
+            f"{fields.get('cpu family', '?')} model {fields.get('model', '?')} stepping "
+            f"{fields.get('stepping', '?')}; {n} logical CPUs listed)")
 
 
 def run_cpu_baseline(cfg, kv_dev, budget_s: float):
@@ -162,7 +177,13 @@ def run_cpu_baseline(cfg, kv_dev, budget_s: float):
     oracle.dequant(c, xb.shape, True, threads=1, blocks=(0, one_blocks))
     t_one = time.perf_counter() - t0
     one_elems = one_blocks * 32768
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = None
     return {"value": round(gbps, 4), "unit": "GB/s", "cores": th, "kind": "oracle",
+            "host_threads": {"os_cpu_count": os.cpu_count(), "affinity": affinity,
+                             "used": th, "share_per_gpu": CPU_SHARE},
             "sample": (f"first {done} of {kv_dev.shape[0]} tensors (K/V of layers "
                        f"0..{(done - 1) // 2}) of {cfg.name}: {elems} elements, "
                        f"{t_total:.1f} s wall, quantize + anchor dequant + full dequant"),
@@ -539,18 +560,25 @@ TRANSFER_OBJECT_BLOCKS = 4096  # 256 MiB of bf16 KV per transfer object (16 obje
 TRANSFER_REPS = 9              # alternating link-only / pipeline runs (medians reported)
 
 
-def measure_transfer(torch, lynx, kv, codes, out_a, out_f, kern_ms):
+def measure_transfer(torch, lynx, kv, codes, out_a, out_f, kern_ms, layout):
     """Split-stream transfer of the whole set through pinned host memory:
     the link alone (codes already made) and the full pipeline (quantize,
-    two link streams, rebuild from anchor, refine)."""
+    two link streams, rebuild from anchor, refine).  layout: the code
+    layout (packed = the pages' transmission buffer, one copy per hop for an
+    object's anchor + metadata; separate = stream and four metadata arrays,
+    five copies)."""
     shape = lynx.shape_of(kv)
     nb = lynx.num_blocks(shape)
-    rx = lynx.alloc_codes(nb, "cuda")
-    wire = lynx.alloc_codes(nb, "cpu", pin_memory=True)
+    p = lynx.params(layout=layout)
+    if layout == lynx.LAYOUT_PACKED:
+        codes = lynx.quantize_pages(kv, p)
+    rx = lynx.alloc_codes(nb, "cuda", layout=layout)
+    wire = lynx.alloc_codes(nb, "cpu", pin_memory=True, layout=layout)
     streams = tuple(torch.cuda.Stream() for _ in range(4))
     # Raw PCIe rates of one 1 GiB pinned copy each way (the link's floor).
     pcie = {}
-    for name, src, dst in (("d2h", codes.anchor, wire.anchor), ("h2d", wire.anchor, rx.anchor)):
+    for name, src, dst in (("d2h", codes.residual, wire.residual),
+                           ("h2d", wire.residual, rx.residual)):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         with torch.cuda.stream(streams[1]):
             for rep in range(2):
@@ -560,7 +588,7 @@ def measure_transfer(torch, lynx, kv, codes, out_a, out_f, kern_ms):
         streams[1].synchronize()
         pcie[name] = src.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
     ob = TRANSFER_OBJECT_BLOCKS
-    lynx.split_stream_transfer(None, shape, ob, codes, wire, rx, copies_only=True,
+    lynx.split_stream_transfer(None, shape, ob, codes, wire, rx, copies_only=True, p=p,
                                streams=streams)  # warm-up
     # Pinned copies of ~90 ms vary by a few ms from run to run, more than the
     # codec time whose hiding is measured: alternate link-only and pipeline
@@ -568,9 +596,9 @@ def measure_transfer(torch, lynx, kv, codes, out_a, out_f, kern_ms):
     links, pipes = [], []
     for _ in range(TRANSFER_REPS):
         links.append(lynx.split_stream_transfer(None, shape, ob, codes, wire, rx,
-                                                copies_only=True, streams=streams))
+                                                copies_only=True, p=p, streams=streams))
         pipes.append(lynx.split_stream_transfer(kv, shape, ob, codes, wire, rx, out_a, out_f,
-                                                streams=streams))
+                                                p=p, streams=streams))
     link = {k: statistics.median(r[k] for r in links) for k in links[0]}
     pipe = {k: statistics.median(r[k] for r in pipes) for k in pipes[0]}
     anchor_bytes = nb * (16384 + 9216)
@@ -580,6 +608,8 @@ def measure_transfer(torch, lynx, kv, codes, out_a, out_f, kern_ms):
     del rx, wire
     return {
         "workload": WORKLOAD, "object_blocks": ob, "objects": -(-nb // ob),
+        "layout": "packed" if layout == lynx.LAYOUT_PACKED else "separate",
+        "copies_per_object_per_hop": 2 if layout == lynx.LAYOUT_PACKED else 6,
         "wire": "pinned host memory (device -> host -> device per object)",
         "pcie_GBps": {k: round(v, 1) for k, v in pcie.items()},
         "link_floor_ms": round((anchor_bytes + residual_bytes) / 1e9 / min(pcie.values()) * 1e3,
@@ -731,8 +761,13 @@ def main():
         "kernels": kern,
     }
     if not args.no_transfer and not args.profile_run:
-        out["transfer"] = measure_transfer(torch, lynx, kv, codes, out_a, out_f,
-                                           {n: kern[n]["ms"] for n in names})
+        kms = {n: kern[n]["ms"] for n in names}
+        # the pages' transmission buffer (anchor + scalars per block, one copy
+        # per hop and object), then the separate arrays for comparison
+        out["transfer"] = measure_transfer(torch, lynx, kv, codes, out_a, out_f, kms,
+                                           lynx.LAYOUT_PACKED)
+        out["transfer_separate"] = measure_transfer(torch, lynx, kv, codes, out_a, out_f, kms,
+                                                    lynx.LAYOUT_SEPARATE)
     if not args.profile_run:
         out["split_variants"] = measure_splits(torch, lynx, kv, out_a)
     if not args.no_attention and not args.profile_run:

@@ -149,7 +149,28 @@ typedef struct lynx_params {
     int32_t anchor_bits;
     int32_t residual_bits;
     int32_t meta_bits;
+    int32_t layout;
 } lynx_params;
+
+/* Code layouts (lynx_params.layout).
+ *   LYNX_LAYOUT_SEPARATE (default): the anchor stream and the four metadata
+ *     arrays are separate buffers (the layouts at the top of this file).
+ *   LYNX_LAYOUT_PACKED: the transmission buffer of the paper's Section 4.2
+ *     (prefill workflow, step 3) and Section 5 ("Compression Kernel"): the
+ *     anchor of every page block followed immediately by its scalars.  The
+ *     `anchor` buffer then holds one record per block, back to back, of
+ *     lynx_anchor_block_bytes(params) bytes: the block's 4096 a bytes of
+ *     anchor stream, then its gamma_min[128], gamma_scale[128],
+ *     mu[8][128] and sigma[8][128] (binary32, or bfloat16 with
+ *     meta_bits = 16): 25600 bytes per block for the paper's 4 + 4 split.
+ *     A run of blocks is one contiguous byte range, so a KV object's anchor
+ *     and metadata move in one copy.  Every lynx_meta argument must then be
+ *     all NULL (LYNX_EINVAL otherwise).  The residual stream is unchanged.
+ *     Accepted by lynx_quantize_pages, the two dequant calls, the two
+ *     attention calls and lynx_split_stream_transfer; the statistics calls
+ *     refuse it. */
+#define LYNX_LAYOUT_SEPARATE 0
+#define LYNX_LAYOUT_PACKED 1
 
 /* Shape of a KV set (element strides, bf16 elements). */
 typedef struct lynx_kv_shape {
@@ -169,7 +190,8 @@ typedef struct lynx_meta {
 } lynx_meta;
 
 /* Fills *p with alpha = 255, eps = 1e-6, code_scale = 120, P = 256,
- * C = 32, H = 128, anchor_bits = residual_bits = 4, meta_bits = 32. */
+ * C = 32, H = 128, anchor_bits = residual_bits = 4, meta_bits = 32,
+ * layout = LYNX_LAYOUT_SEPARATE. */
 void lynx_default_params(lynx_params *p);
 
 /* Number of page blocks of a shape, or a negative status if the shape is
@@ -184,6 +206,12 @@ int64_t lynx_num_blocks(const lynx_kv_shape *shape);
 size_t lynx_stream_bytes(const lynx_kv_shape *shape);
 size_t lynx_field_stream_bytes(const lynx_kv_shape *shape, int field_bits);
 size_t lynx_gamma_floats(const lynx_kv_shape *shape);
+
+/* Bytes per page block of the anchor-side buffer for `params` (NULL =
+ * defaults): 4096 anchor_bits (separate layout), or the packed record of the
+ * anchor stream and the metadata (4096 anchor_bits + 2304 meta_bits / 8).
+ * 0 for invalid parameters.  Host only. */
+size_t lynx_anchor_block_bytes(const lynx_params *params);
 size_t lynx_chunk_floats(const lynx_kv_shape *shape);
 
 /* Eq. (1) of the paper (Section 2.2): Size_KV = K_factor * L * D *

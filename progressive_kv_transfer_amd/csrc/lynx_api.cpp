@@ -173,7 +173,48 @@ int check_params(const lynx_params &p) {
     if (p.meta_bits != 32 &&
         !(p.meta_bits == 16 && p.anchor_bits == 4 && p.residual_bits == 4))
         return LYNX_EINVAL;
+    if (p.layout != LYNX_LAYOUT_SEPARATE && p.layout != LYNX_LAYOUT_PACKED)
+        return LYNX_EINVAL;
     return LYNX_OK;
+}
+
+// Bytes per page block of the anchor stream, of the metadata, and of the
+// anchor-side buffer in the params' layout (the packed record is the anchor
+// stream followed by gamma_min, gamma_scale, mu and sigma).
+int64_t stream_block_bytes(const lynx_params &p) { return (int64_t)kPage * kHead / 8 * p.anchor_bits; }
+int64_t meta_block_bytes(const lynx_params &p) {
+    return (int64_t)(2 * kHead + 2 * kChunks * kHead) * (p.meta_bits / 8);
+}
+int64_t anchor_block_bytes(const lynx_params &p) {
+    return stream_block_bytes(p) + (p.layout == LYNX_LAYOUT_PACKED ? meta_block_bytes(p) : 0);
+}
+
+// Metadata pointers of a packed anchor-side buffer (block 0's record).
+lynx_meta packed_meta(const lynx_params &p, const uint8_t *records) {
+    const int64_t e = p.meta_bits / 8;
+    uint8_t *g0 = const_cast<uint8_t *>(records) + stream_block_bytes(p);
+    lynx_meta m;
+    m.gamma_min = (float *)g0;
+    m.gamma_scale = (float *)(g0 + kHead * e);
+    m.mu = (float *)(g0 + 2 * kHead * e);
+    m.sigma = (float *)(g0 + (2 * kHead + kChunks * kHead) * e);
+    return m;
+}
+
+// The metadata pointers a call works with: as given (separate layout), or
+// inside the anchor-side buffer (packed layout, where the caller passes
+// NULL metadata pointers).  False if the caller's pointers do not fit the
+// layout.
+bool resolve_meta(const lynx_params &p, const uint8_t *anchor, lynx_meta in, lynx_meta *out) {
+    const bool none = !in.gamma_min && !in.gamma_scale && !in.mu && !in.sigma;
+    if (p.layout == LYNX_LAYOUT_PACKED) {
+        if (!none || !anchor)
+            return false;
+        *out = packed_meta(p, anchor);
+        return true;
+    }
+    *out = in;
+    return true;
 }
 
 int check_shape(const lynx_kv_shape *s, int64_t *nblocks) {
@@ -200,7 +241,7 @@ int check_shape(const lynx_kv_shape *s, int64_t *nblocks) {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-Geometry geometry(const lynx_kv_shape *s, int64_t nblocks) {
+Geometry geometry(const lynx_kv_shape *s, int64_t nblocks, const lynx_params &p) {
     Geometry g;
     g.tensor_stride = s->tensor_stride;
     g.row_stride = s->row_stride;
@@ -208,6 +249,14 @@ Geometry geometry(const lynx_kv_shape *s, int64_t nblocks) {
     g.heads = (int32_t)(s->num_channels / kHead);
     g.nblocks = nblocks;
     g.block0 = 0;
+    g.grid_wgs = 0;
+    g.astride = anchor_block_bytes(p);
+    if (p.layout == LYNX_LAYOUT_PACKED) {
+        g.gstride = g.cstride = anchor_block_bytes(p) / (p.meta_bits / 8);
+    } else {
+        g.gstride = kHead;
+        g.cstride = kChunks * kHead;
+    }
     return g;
 }
 
@@ -228,8 +277,19 @@ int quantize_common(const void *kv, const lynx_kv_shape *shape, const lynx_param
     int64_t nb = 0;
     if ((rc = check_shape(shape, &nb)))
         return rc;
+    if (mode != kModeQuantize && p.layout != LYNX_LAYOUT_SEPARATE)
+        return LYNX_EINVAL;  // the statistics calls write separate arrays
     if (nb == 0)
         return LYNX_OK;
+    if (mode == kModeQuantize) {
+        lynx_meta m = {gmin, gscale, mu, sigma};
+        if (!resolve_meta(p, anchor, m, &m))
+            return LYNX_EINVAL;
+        gmin = m.gamma_min;
+        gscale = m.gamma_scale;
+        mu = m.mu;
+        sigma = m.sigma;
+    }
     if (!kv || !gmin || !gscale)
         return LYNX_EINVAL;
     if (mode != kModePageStats && (!mu || !sigma))
@@ -248,7 +308,7 @@ int quantize_common(const void *kv, const lynx_kv_shape *shape, const lynx_param
         return LYNX_EINVAL;
     QuantTab tab = t.q;
     tab.eps = p.eps;
-    Geometry g = geometry(shape, nb);
+    Geometry g = geometry(shape, nb, p);
     for (int64_t b0 = 0; b0 < nb; b0 += kMaxLaunchBlocks) {
         g.block0 = b0;
         g.nblocks = (nb - b0) < kMaxLaunchBlocks ? (nb - b0) : kMaxLaunchBlocks;
@@ -273,6 +333,8 @@ int dequant_common(const uint8_t *anchor, const uint8_t *residual, lynx_meta met
         return rc;
     if (nb == 0)
         return LYNX_OK;
+    if (!resolve_meta(p, anchor, meta, &meta))
+        return LYNX_EINVAL;
     if (!anchor || !out || !meta.gamma_min || !meta.gamma_scale || !meta.mu || !meta.sigma)
         return LYNX_EINVAL;
     if (residual && p.residual_bits == 0)  // a single stream has no residual phase
@@ -287,7 +349,7 @@ int dequant_common(const uint8_t *anchor, const uint8_t *residual, lynx_meta met
         return LYNX_EINVAL;
     DequantTab tab = t.d;
     tab.eps = p.eps;
-    Geometry g = geometry(shape, nb);
+    Geometry g = geometry(shape, nb, p);
     for (int64_t b0 = 0; b0 < nb; b0 += kMaxLaunchBlocks) {
         g.block0 = b0;
         g.nblocks = (nb - b0) < kMaxLaunchBlocks ? (nb - b0) : kMaxLaunchBlocks;
@@ -362,9 +424,15 @@ struct EventSet {
 };
 
 // Anchor stream + metadata (or the residual stream) of blocks [b0, b0 + n)
-// from one code set to another.
-hipError_t copy_anchor_meta(const lynx_codes &src, const lynx_codes &dst, int64_t b0, int64_t n,
-                            hipStream_t s) {
+// from one code set to another: with the packed layout one copy of the
+// blocks' records, otherwise the stream and the four metadata arrays.
+hipError_t copy_anchor_meta(const lynx_params &p, const lynx_codes &src, const lynx_codes &dst,
+                            int64_t b0, int64_t n, hipStream_t s) {
+    if (p.layout == LYNX_LAYOUT_PACKED) {
+        const size_t rec = (size_t)anchor_block_bytes(p);
+        return hipMemcpyAsync(dst.anchor + b0 * rec, src.anchor + b0 * rec, n * rec,
+                              hipMemcpyDefault, s);
+    }
     const size_t stream_b = (size_t)kPage * kHead / 2, gam = kHead, chk = (size_t)kChunks * kHead;
     hipError_t e = hipMemcpyAsync(dst.anchor + b0 * stream_b, src.anchor + b0 * stream_b,
                                   n * stream_b, hipMemcpyDefault, s);
@@ -385,9 +453,11 @@ hipError_t copy_residual(const lynx_codes &src, const lynx_codes &dst, int64_t b
                           n * stream_b, hipMemcpyDefault, s);
 }
 
-bool codes_ok(const lynx_codes &c) {
-    const void *ptrs[6] = {c.anchor, c.residual, c.meta.gamma_min, c.meta.gamma_scale,
-                           c.meta.mu, c.meta.sigma};
+bool codes_ok(const lynx_params &p, const lynx_codes &c) {
+    lynx_meta m;
+    if (!resolve_meta(p, c.anchor, c.meta, &m))
+        return false;
+    const void *ptrs[6] = {c.anchor, c.residual, m.gamma_min, m.gamma_scale, m.mu, m.sigma};
     for (const void *q : ptrs)
         if (!q || !aligned16(q))
             return false;
@@ -410,6 +480,7 @@ void lynx_default_params(lynx_params *p) {
     p->anchor_bits = 4;
     p->residual_bits = 4;
     p->meta_bits = 32;
+    p->layout = LYNX_LAYOUT_SEPARATE;
 }
 
 int64_t lynx_num_blocks(const lynx_kv_shape *shape) {
@@ -428,6 +499,11 @@ size_t lynx_field_stream_bytes(const lynx_kv_shape *shape, int field_bits) {
     if (nb < 0 || field_bits < 1 || field_bits > 8)
         return 0;
     return (size_t)nb * (kPage * kHead / 8) * (size_t)field_bits;
+}
+
+size_t lynx_anchor_block_bytes(const lynx_params *params) {
+    const lynx_params p = resolve(params);
+    return check_params(p) ? 0 : (size_t)anchor_block_bytes(p);
 }
 
 size_t lynx_gamma_floats(const lynx_kv_shape *shape) {
@@ -536,6 +612,8 @@ int attn_common(const void *q, int t_q, int num_q_heads, const uint8_t *k_anchor
         return rc;
     if (causal_tail && ctx_len < t_q)
         return LYNX_EINVAL;
+    if (!resolve_meta(p, k_anchor, k_meta, &k_meta) || !resolve_meta(p, v_anchor, v_meta, &v_meta))
+        return LYNX_EINVAL;
     if (!q || !out || (!use_scratch && !workspace) || !k_anchor || !v_anchor ||
         !k_meta.gamma_min || !k_meta.gamma_scale || !k_meta.mu || !k_meta.sigma ||
         !v_meta.gamma_min || !v_meta.gamma_scale || !v_meta.mu || !v_meta.sigma)
@@ -580,6 +658,14 @@ int attn_common(const void *q, int t_q, int num_q_heads, const uint8_t *k_anchor
     }
     a.out = out;
     a.out_f32 = out_dtype == LYNX_OUT_F32 ? 1 : 0;
+    {
+        const lynx_kv_shape one = {1, 0, ctx_len, (int64_t)num_kv_heads * kHead,
+                                   (int64_t)num_kv_heads * kHead};
+        const Geometry gs = geometry(&one, 0, p);
+        a.astride = gs.astride;
+        a.gstride = gs.gstride;
+        a.cstride = gs.cstride;
+    }
     a.ctx = ctx_len;
     a.n_qh = num_q_heads;
     a.n_kvh = num_kv_heads;
@@ -662,8 +748,12 @@ int lynx_split_stream_transfer(const void *kv, const lynx_kv_shape *shape,
     const int64_t nobj = (nb + object_blocks - 1) / object_blocks;
     if (nobj > kMaxTransferObjects)
         return LYNX_EINVAL;
-    if (!codes_ok(tx) || !codes_ok(wire) || !codes_ok(rx))
+    if (!codes_ok(p, tx) || !codes_ok(p, wire) || !codes_ok(p, rx))
         return LYNX_EINVAL;
+    if (p.layout == LYNX_LAYOUT_PACKED) {  // the kernels take the derived pointers
+        resolve_meta(p, tx.anchor, tx.meta, &tx.meta);
+        resolve_meta(p, rx.anchor, rx.meta, &rx.meta);
+    }
     if (!copies_only) {
         if (!kv || !kv_anchor || !kv_full)
             return LYNX_EINVAL;
@@ -677,7 +767,7 @@ int lynx_split_stream_transfer(const void *kv, const lynx_kv_shape *shape,
     qt.eps = p.eps;
     DequantTab dt = t.d;
     dt.eps = p.eps;
-    const Geometry g0 = geometry(shape, nb);
+    const Geometry g0 = geometry(shape, nb, p);
 
     EventSet es;
     hipEvent_t start = es.make(true), t_q = es.make(true), t_a = es.make(true),
@@ -731,10 +821,10 @@ int lynx_split_stream_transfer(const void *kv, const lynx_kv_shape *shape,
         const hipEvent_t qe = last ? t_q : q[i];
         ok(hipEventRecord(qe, sender));
         ok(hipStreamWaitEvent(link_out, qe, 0));
-        ok(copy_anchor_meta(tx, wire, b0, n, link_out));
+        ok(copy_anchor_meta(p, tx, wire, b0, n, link_out));
         ok(hipEventRecord(ao[i], link_out));
         ok(hipStreamWaitEvent(link_in, ao[i], 0));
-        ok(copy_anchor_meta(wire, rx, b0, n, link_in));
+        ok(copy_anchor_meta(p, wire, rx, b0, n, link_in));
         const hipEvent_t ae = last ? t_a : a[i];
         ok(hipEventRecord(ae, link_in));
         // deserializer, anchor phase

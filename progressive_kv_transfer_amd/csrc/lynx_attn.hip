@@ -83,22 +83,24 @@ __device__ __forceinline__ Affine fold(const LaneCodes &L, float eps) {
 
 __device__ __forceinline__ void load_codes(const uint8_t *anc, const uint8_t *res,
                                            const float *gmin, const float *gsc, const float *mu,
-                                           const float *sg, int64_t b, int j, int p,
-                                           LaneCodes &L) {
-    const int64_t coff = b * (kPage * kHead / 2) + j * (kHead / 2 * kChunk) + p * kChunk;
-    L.a0 = *(const u32x4 *)(anc + coff);
-    L.a1 = *(const u32x4 *)(anc + coff + 16);
+                                           const float *sg, const AttnArgs &a, int64_t b, int j,
+                                           int p, LaneCodes &L) {
+    const int64_t toff = j * (kHead / 2 * kChunk) + p * kChunk;
+    const int64_t aoff = b * a.astride + toff;
+    const int64_t roff = b * (kPage * kHead / 2) + toff;
+    L.a0 = *(const u32x4 *)(anc + aoff);
+    L.a1 = *(const u32x4 *)(anc + aoff + 16);
     if (res) {
-        L.r0 = *(const u32x4 *)(res + coff);
-        L.r1 = *(const u32x4 *)(res + coff + 16);
+        L.r0 = *(const u32x4 *)(res + roff);
+        L.r1 = *(const u32x4 *)(res + roff + 16);
     } else {
         L.r0 = u32x4{0u, 0u, 0u, 0u};
         L.r1 = u32x4{0u, 0u, 0u, 0u};
     }
-    L.gm = *(const float2 *)(gmin + b * kHead + 2 * p);
-    L.gs = *(const float2 *)(gsc + b * kHead + 2 * p);
-    L.mu = *(const float2 *)(mu + b * (kChunks * kHead) + j * kHead + 2 * p);
-    L.sg = *(const float2 *)(sg + b * (kChunks * kHead) + j * kHead + 2 * p);
+    L.gm = *(const float2 *)(gmin + b * a.gstride + 2 * p);
+    L.gs = *(const float2 *)(gsc + b * a.gstride + 2 * p);
+    L.mu = *(const float2 *)(mu + b * a.cstride + j * kHead + 2 * p);
+    L.sg = *(const float2 *)(sg + b * a.cstride + j * kHead + 2 * p);
 }
 
 // Byte i of w shifted left by S (an SDWA byte select: one instruction).
@@ -312,8 +314,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(AttnArgs 
     if (st0 < st1) {
         const int64_t b = (int64_t)(st0 >> 1) * a.n_kvh + kvh;
         const int j = (st0 & 1) * 4 + c_fill;
-        load_codes(a.k_anc, a.k_res, a.k_gmin, a.k_gsc, a.k_mu, a.k_sg, b, j, p, ck);
-        load_codes(a.v_anc, a.v_res, a.v_gmin, a.v_gsc, a.v_mu, a.v_sg, b, j, p, cv);
+        load_codes(a.k_anc, a.k_res, a.k_gmin, a.k_gsc, a.k_mu, a.k_sg, a, b, j, p, ck);
+        load_codes(a.v_anc, a.v_res, a.v_gmin, a.v_gsc, a.v_mu, a.v_sg, a, b, j, p, cv);
     }
     __syncthreads();  // s_lut
 
@@ -329,8 +331,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(AttnArgs 
         if (st + 1 < st1) {
             const int64_t b = (int64_t)((st + 1) >> 1) * a.n_kvh + kvh;
             const int j = ((st + 1) & 1) * 4 + c_fill;
-            load_codes(a.k_anc, a.k_res, a.k_gmin, a.k_gsc, a.k_mu, a.k_sg, b, j, p, ck);
-            load_codes(a.v_anc, a.v_res, a.v_gmin, a.v_gsc, a.v_mu, a.v_sg, b, j, p, cv);
+            load_codes(a.k_anc, a.k_res, a.k_gmin, a.k_gsc, a.k_mu, a.k_sg, a, b, j, p, ck);
+            load_codes(a.v_anc, a.v_res, a.v_gmin, a.v_gsc, a.v_mu, a.v_sg, a, b, j, p, cv);
         }
         step_sync<RT>();
 

@@ -130,7 +130,7 @@ __global__ __launch_bounds__(64 * kWaves) void dequant_kernel(
         // in each stream: ABITS (RBITS) x 8 bytes.
         uint32_t aw[2 * ABITS], rw[kBits > 0 ? 2 * kBits : 1];
         {
-            const u32x4 *ap = (const u32x4 *)(anchor + b * (kPage * kHead / 8 * ABITS) +
+            const u32x4 *ap = (const u32x4 *)(anchor + b * g.astride +
                                              (int64_t)(j * (kHead / 2) + p) * (8 * ABITS));
 #pragma unroll
             for (int d = 0; d < ABITS / 2; ++d) {
@@ -161,8 +161,8 @@ __global__ __launch_bounds__(64 * kWaves) void dequant_kernel(
         }
         float gm[2], um[2], d1[2], d2[2];
         {
-            const int64_t goff = b * kHead + 2 * p;
-            const int64_t coff = b * (kChunks * kHead) + j * kHead + 2 * p;
+            const int64_t goff = b * g.gstride + 2 * p;
+            const int64_t coff = b * g.cstride + j * kHead + 2 * p;
             if constexpr (M16) {
                 auto lo = [](uint32_t w) { return __uint_as_float(w << 16); };
                 auto hi = [](uint32_t w) { return __uint_as_float(w & 0xffff0000u); };

@@ -62,6 +62,14 @@ struct Geometry {
     int64_t nblocks;        // blocks in this launch
     int64_t block0;         // global index of the launch's first block
     int64_t grid_wgs;       // workgroups of a persistent launch
+    // Per-block strides of the code buffers: bytes of the anchor-side buffer
+    // (the anchor stream alone, or with the packed layout the block's whole
+    // record: anchor stream then gamma_min, gamma_scale, mu, sigma), and
+    // elements of the gamma_min / gamma_scale and mu / sigma arrays.  The
+    // residual stream always has 4096 b bytes per block.
+    int64_t astride;
+    int64_t gstride;
+    int64_t cstride;
 };
 
 // Block and lane indices come from the amdgcn intrinsics: the kernels are
@@ -87,6 +95,7 @@ struct AttnArgs {
     const float *k_gmin, *k_gsc, *k_mu, *k_sg;
     const float *v_gmin, *v_gsc, *v_mu, *v_sg;
     float *ws;      // partials [split][kv head][row][2 + 128]
+    int64_t astride, gstride, cstride;  // per-block strides of K and V codes
     void *out;      // [t_q][n_qh][128], bf16 or binary32
     int64_t ctx;    // context tokens (multiple of 256)
     int n_qh, n_kvh, group, t_q;

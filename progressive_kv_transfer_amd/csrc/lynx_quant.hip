@@ -235,8 +235,8 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
     for (int64_t u = wg0; u < nblocks; u += g.grid_wgs, ++n) {
         const int64_t b = g.block0 + u;
         const int buf = n % kDepth;
-        const int64_t meta0 = b * kHead;
-        const int64_t cmeta0 = b * (kChunks * kHead) + j * kHead;
+        const int64_t meta0 = b * g.gstride;
+        const int64_t cmeta0 = b * g.cstride + j * kHead;
         // Address of the block staged during this one, computed here where
         // few registers are live (the empty asm keeps it from being sunk to
         // its use).
@@ -491,10 +491,9 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
                 rv[q >> 2][q & 3] = r;
             }
             // 32 contiguous bytes per stream: [chunk j][pair][token of chunk]
-            const int64_t coff = b * (kPage * kHead / 2) + j * (kHead / 2 * kChunk) +
-                                 p * kChunk;
-            u32x4 *ao = (u32x4 *)(anchor + coff);
-            u32x4 *ro = (u32x4 *)(residual + coff);
+            const int64_t toff = j * (kHead / 2 * kChunk) + p * kChunk;
+            u32x4 *ao = (u32x4 *)(anchor + b * g.astride + toff);
+            u32x4 *ro = (u32x4 *)(residual + b * (kPage * kHead / 2) + toff);
             // Ordinary stores: the streams are read again by the dequant kernels.
             ao[0] = av[0];
             ao[1] = av[1];
@@ -524,8 +523,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
                         put_field<kBits>(rw, 2 * i + e, (J ^ kBias) & kMaskR);
                 }
             // Run of 8 w bytes per (chunk, pair), 4096 w bytes per block.
-            const int64_t aoff = b * (kPage * kHead / 8 * ABITS) +
-                                 (int64_t)(j * (kHead / 2) + p) * (8 * ABITS);
+            const int64_t aoff = b * g.astride + (int64_t)(j * (kHead / 2) + p) * (8 * ABITS);
             const int64_t roff = b * (kPage * kHead / 8 * kBits) +
                                  (int64_t)(j * (kHead / 2) + p) * (8 * kBits);
             u32x2 *ao = (u32x2 *)(anchor + aoff);

@@ -36,7 +36,7 @@ class lynx_params(ctypes.Structure):
                 ("code_scale", ctypes.c_float), ("page_tokens", ctypes.c_int32),
                 ("chunk_tokens", ctypes.c_int32), ("block_channels", ctypes.c_int32),
                 ("anchor_bits", ctypes.c_int32), ("residual_bits", ctypes.c_int32),
-                ("meta_bits", ctypes.c_int32)]
+                ("meta_bits", ctypes.c_int32), ("layout", ctypes.c_int32)]
 
 
 class lynx_kv_shape(ctypes.Structure):
@@ -62,11 +62,13 @@ class lynx_transfer_times(ctypes.Structure):
 
 
 TRANSFER_COPIES_ONLY = 1
+LAYOUT_SEPARATE, LAYOUT_PACKED = 0, 1  # lynx_params.layout
 
 # Every symbol include/lynx.h declares.
 EXPORTS = ["lynx_default_params", "lynx_num_blocks", "lynx_stream_bytes",
            "lynx_field_stream_bytes",
-           "lynx_gamma_floats", "lynx_chunk_floats", "lynx_kv_bytes",
+           "lynx_gamma_floats", "lynx_chunk_floats", "lynx_anchor_block_bytes",
+           "lynx_kv_bytes",
            "lynx_status_string", "lynx_compander_thresholds", "lynx_quantize_pages", "lynx_dequant_anchor",
            "lynx_dequant_full", "lynx_page_stats", "lynx_block_stats",
            "lynx_attn_workspace_bytes", "lynx_decode_attn_dequant",
@@ -95,6 +97,8 @@ def lib():
         for f in ("lynx_stream_bytes", "lynx_gamma_floats", "lynx_chunk_floats"):
             getattr(L, f).argtypes = [P(lynx_kv_shape)]
             getattr(L, f).restype = ctypes.c_size_t
+        L.lynx_anchor_block_bytes.argtypes = [P(lynx_params)]
+        L.lynx_anchor_block_bytes.restype = ctypes.c_size_t
         L.lynx_field_stream_bytes.argtypes = [P(lynx_kv_shape), i32]
         L.lynx_field_stream_bytes.restype = ctypes.c_size_t
         L.lynx_kv_bytes.argtypes = [i64] * 5
@@ -143,19 +147,30 @@ def _check(fn, rc):
 
 
 def params(alpha=255.0, eps=1e-6, code_scale=120.0, anchor_bits=4,
-           residual_bits=None, meta_bits=32) -> lynx_params:
+           residual_bits=None, meta_bits=32, layout=LAYOUT_SEPARATE) -> lynx_params:
     """Method parameters; anchor_bits, residual_bits = widths of the anchor
     and residual fields: 4 + 4 is the paper's split, 3..6 + 8 - a the other
     splits of the 8-bit code (residual_bits None means 8 - anchor_bits), and
     residual_bits = 0 with anchor_bits 4 or 8 a single stream (the paper's
     Lynx-INT4 / Lynx-INT8, with code_scale 7 / 127); meta_bits = 16 keeps the
-    metadata in bfloat16 (4 + 4 only)."""
+    metadata in bfloat16 (4 + 4 only); layout = LAYOUT_PACKED stores each
+    block's anchor stream followed by its metadata in one record."""
     p = lynx_params()
     lib().lynx_default_params(ctypes.byref(p))
     p.alpha, p.eps, p.code_scale, p.anchor_bits = alpha, eps, code_scale, anchor_bits
     p.residual_bits = 8 - anchor_bits if residual_bits is None else residual_bits
     p.meta_bits = meta_bits
+    p.layout = layout
     return p
+
+
+def anchor_block_bytes(p: lynx_params | None = None) -> int:
+    """Bytes per page block of the anchor-side buffer (the packed record
+    with LAYOUT_PACKED)."""
+    n = int(lib().lynx_anchor_block_bytes(ctypes.byref(p) if p else None))
+    if n == 0:
+        raise ValueError("anchor_block_bytes: invalid parameters")
+    return n
 
 
 def code_max(anchor_bits: int = 4, residual_bits: int | None = None) -> int:
@@ -200,23 +215,35 @@ def num_blocks(shape: lynx_kv_shape) -> int:
 
 @dataclass
 class Codes:
-    """Device buffers of one quantized KV set (layouts of include/lynx.h)."""
+    """Device buffers of one quantized KV set (layouts of include/lynx.h).
+    With the packed layout `records` is the anchor-side buffer (one record
+    of anchor stream + metadata per block) and `anchor` and the four
+    metadata tensors are views into it."""
     anchor: torch.Tensor       # uint8 [nblocks, 8 chunks, 64 channel pairs, 32 tokens]
     residual: torch.Tensor     # uint8 [nblocks, 8, 64, 32]
     gamma_min: torch.Tensor    # float32 [nblocks, 128]
     gamma_scale: torch.Tensor  # float32 [nblocks, 128]
     mu: torch.Tensor           # float32 [nblocks, 8, 128]
     sigma: torch.Tensor        # float32 [nblocks, 8, 128]
+    records: torch.Tensor | None = None  # uint8 [nblocks, record bytes] (packed)
+
+    @property
+    def packed(self) -> bool:
+        return self.records is not None
+
+    def anchor_ptr(self) -> int:
+        return (self.records if self.packed else self.anchor).data_ptr()
 
     def meta(self) -> lynx_meta:
-        m = lynx_meta()
-        m.gamma_min, m.gamma_scale = self.gamma_min.data_ptr(), self.gamma_scale.data_ptr()
-        m.mu, m.sigma = self.mu.data_ptr(), self.sigma.data_ptr()
+        m = lynx_meta()  # all NULL with the packed layout
+        if not self.packed:
+            m.gamma_min, m.gamma_scale = self.gamma_min.data_ptr(), self.gamma_scale.data_ptr()
+            m.mu, m.sigma = self.mu.data_ptr(), self.sigma.data_ptr()
         return m
 
     def c_struct(self) -> lynx_codes:
         c = lynx_codes()
-        c.anchor, c.residual = self.anchor.data_ptr(), self.residual.data_ptr()
+        c.anchor, c.residual = self.anchor_ptr(), self.residual.data_ptr()
         c.meta = self.meta()
         return c
 
@@ -226,7 +253,8 @@ class Codes:
 
 
 def alloc_codes(nblocks: int, device, pin_memory: bool = False, anchor_bits: int = 4,
-                residual_bits: int | None = None, meta_bits: int = 32) -> Codes:
+                residual_bits: int | None = None, meta_bits: int = 32,
+                layout: int = LAYOUT_SEPARATE) -> Codes:
     """Code buffers for nblocks page blocks on `device`; on the CPU with
     pin_memory=True they are pinned host memory (a transfer's wire).  The
     streams hold [block][chunk][channel pair][run of 8 w bytes] with
@@ -239,6 +267,19 @@ def alloc_codes(nblocks: int, device, pin_memory: bool = False, anchor_bits: int
     f32 = dict(dtype=torch.bfloat16 if meta_bits == 16 else torch.float32, device=device,
                pin_memory=pin_memory)
     tile = (nblocks, PAGE_TOKENS // CHUNK_TOKENS, BLOCK_CHANNELS // 2)
+    if layout == LAYOUT_PACKED:
+        mdt = f32["dtype"]
+        esz = 2 if meta_bits == 16 else 4
+        sbytes = 4096 * anchor_bits
+        rec = sbytes + 2304 * esz
+        records = torch.empty((nblocks, rec), **u8)
+        meta = records.view(mdt)  # [nblocks, rec / esz]
+        m0 = sbytes // esz
+        return Codes(records[:, :sbytes].view(tile + (8 * anchor_bits,)),
+                     torch.empty(tile + (8 * b,), **u8),
+                     meta[:, m0:m0 + 128], meta[:, m0 + 128:m0 + 256],
+                     meta[:, m0 + 256:m0 + 1280].view(nblocks, 8, 128),
+                     meta[:, m0 + 1280:m0 + 2304].view(nblocks, 8, 128), records)
     return Codes(torch.empty(tile + (8 * anchor_bits,), **u8),
                  torch.empty(tile + (8 * b,), **u8),
                  torch.empty((nblocks, BLOCK_CHANNELS), **f32),
@@ -274,11 +315,18 @@ def _check_codes(fn: str, codes: Codes, nblocks: int, p: lynx_params | None = No
     page blocks (on the device unless device=False: a transfer's wire may be
     pinned host memory)."""
     a, b, mdt = _fields(p)
-    need = [("anchor", codes.anchor, torch.uint8, nblocks * 4096 * a),
-            ("gamma_min", codes.gamma_min, mdt, nblocks * BLOCK_CHANNELS),
-            ("gamma_scale", codes.gamma_scale, mdt, nblocks * BLOCK_CHANNELS),
-            ("mu", codes.mu, mdt, nblocks * 8 * BLOCK_CHANNELS),
-            ("sigma", codes.sigma, mdt, nblocks * 8 * BLOCK_CHANNELS)]
+    packed = p is not None and p.layout == LAYOUT_PACKED
+    if packed != codes.packed:
+        raise ValueError(f"{fn}: the code buffers' layout differs from the parameters' "
+                         f"({'packed' if packed else 'separate'} expected)")
+    if packed:
+        need = [("records", codes.records, torch.uint8, nblocks * anchor_block_bytes(p))]
+    else:
+        need = [("anchor", codes.anchor, torch.uint8, nblocks * 4096 * a),
+                ("gamma_min", codes.gamma_min, mdt, nblocks * BLOCK_CHANNELS),
+                ("gamma_scale", codes.gamma_scale, mdt, nblocks * BLOCK_CHANNELS),
+                ("mu", codes.mu, mdt, nblocks * 8 * BLOCK_CHANNELS),
+                ("sigma", codes.sigma, mdt, nblocks * 8 * BLOCK_CHANNELS)]
     if residual and b:
         need.append(("residual", codes.residual, torch.uint8, nblocks * 4096 * b))
     for name, t, dt, n in need:
@@ -312,12 +360,13 @@ def quantize_pages(kv: torch.Tensor, p: lynx_params | None = None,
     nb = num_blocks(sh)
     codes = out if out is not None else alloc_codes(
         nb, kv.device, anchor_bits=p.anchor_bits if p else 4,
-        residual_bits=p.residual_bits if p else 4, meta_bits=p.meta_bits if p else 32)
+        residual_bits=p.residual_bits if p else 4, meta_bits=p.meta_bits if p else 32,
+        layout=p.layout if p else LAYOUT_SEPARATE)
     _check_codes("quantize_pages", codes, nb, p)
     single = p is not None and p.residual_bits == 0
     _check("lynx_quantize_pages", lib().lynx_quantize_pages(
         kv.data_ptr(), ctypes.byref(sh), ctypes.byref(p) if p else None,
-        codes.anchor.data_ptr(), None if single else codes.residual.data_ptr(), codes.meta(),
+        codes.anchor_ptr(), None if single else codes.residual.data_ptr(), codes.meta(),
         _stream(stream)))
     return codes
 
@@ -331,7 +380,7 @@ def dequant_anchor(codes: Codes, out: torch.Tensor, p: lynx_params | None = None
     sh = shape_of(out)
     _check_codes("dequant_anchor", codes, num_blocks(sh), p, residual=False)
     _check("lynx_dequant_anchor", lib().lynx_dequant_anchor(
-        codes.anchor.data_ptr(), codes.meta(), ctypes.byref(sh),
+        codes.anchor_ptr(), codes.meta(), ctypes.byref(sh),
         ctypes.byref(p) if p else None, out.data_ptr(), _stream(stream)))
     return out
 
@@ -345,7 +394,7 @@ def dequant_full(codes: Codes, out: torch.Tensor, p: lynx_params | None = None,
     sh = shape_of(out)
     _check_codes("dequant_full", codes, num_blocks(sh), p)
     _check("lynx_dequant_full", lib().lynx_dequant_full(
-        codes.anchor.data_ptr(), codes.residual.data_ptr(), codes.meta(), ctypes.byref(sh),
+        codes.anchor_ptr(), codes.residual.data_ptr(), codes.meta(), ctypes.byref(sh),
         ctypes.byref(p) if p else None, out.data_ptr(), _stream(stream)))
     return out
 
@@ -421,6 +470,8 @@ class CodeView:
         return t.data_ptr() + self.b0 * per_block * t.element_size()
 
     def anchor(self) -> int:
+        if self.codes.packed:
+            return self._ptr(self.codes.records, self.codes.records[0].numel())
         return self._ptr(self.codes.anchor, self.codes.anchor[0].numel())
 
     def residual(self):
@@ -430,6 +481,8 @@ class CodeView:
     def meta(self) -> lynx_meta:
         c = self.codes
         m = lynx_meta()
+        if c.packed:
+            return m  # all NULL: the metadata sits in the records
         m.gamma_min = self._ptr(c.gamma_min, c.gamma_min[0].numel())
         m.gamma_scale = self._ptr(c.gamma_scale, c.gamma_scale[0].numel())
         m.mu = self._ptr(c.mu, c.mu[0].numel())

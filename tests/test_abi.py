@@ -257,6 +257,35 @@ def _codes(ptr=FAKE):
     return c
 
 
+def test_packed_layout_sizes_and_errors():
+    """LYNX_LAYOUT_PACKED: records of 4096 a + 2304 meta_bits / 8 bytes per
+    block (25600 for the paper's 4 + 4 split: 16 KiB anchor + 9 KiB
+    scalars); metadata pointers must be NULL; the statistics calls refuse it;
+    an unknown layout is refused."""
+    L = lynx.lib()
+    assert lynx.anchor_block_bytes() == 16384
+    for a, mb, want in ((4, 32, 25600), (4, 16, 20992), (3, 32, 21504), (6, 32, 33792),
+                        (5, 32, 29696)):
+        assert lynx.anchor_block_bytes(lynx.params(anchor_bits=a, meta_bits=mb,
+                                                   layout=lynx.LAYOUT_PACKED)) == want
+        assert want % 16 == 0
+    p = lynx.params(layout=lynx.LAYOUT_PACKED)
+    s = _shape()
+    # metadata pointers given with the packed layout
+    assert L.lynx_quantize_pages(FAKE, ctypes.byref(s), ctypes.byref(p), FAKE, FAKE, _meta(),
+                                 None) == -1
+    assert L.lynx_dequant_anchor(FAKE, _meta(), ctypes.byref(s), ctypes.byref(p), FAKE,
+                                 None) == -1
+    assert L.lynx_page_stats(FAKE, ctypes.byref(s), ctypes.byref(p), FAKE, FAKE, None) == -1
+    assert L.lynx_block_stats(FAKE, ctypes.byref(s), ctypes.byref(p), FAKE, FAKE, FAKE, FAKE,
+                              None) == -1
+    bad = lynx.params()
+    bad.layout = 2
+    assert L.lynx_quantize_pages(FAKE, ctypes.byref(s), ctypes.byref(bad), FAKE, FAKE,
+                                 _meta(), None) == -1
+    assert L.lynx_anchor_block_bytes(ctypes.byref(bad)) == 0
+
+
 def test_noalloc_attention_refuses_beyond_its_scratch():
     """lynx_decode_attn_dequant_noalloc: partials of more than
     LYNX_ATTN_SCRATCH_BYTES are refused with LYNX_ESCRATCH before any
