@@ -110,6 +110,21 @@ bool build_quant_tab(float alpha, float code_scale, int code_max, QuantTab *t) {
     return false;
 }
 
+// The quantize kernel's table entries of a 16-bit-shift bucket table (the
+// form QuantTab::word describes); bias is the Stage 4 offset of the split.
+void build_table_words(int residual_bits, QuantTab *t) {
+    if (t->shift != 16)
+        return;
+    const uint32_t bias = residual_bits > 0 ? (1u << (residual_bits - 1)) - 1u : 0u;
+    for (int i = 0; i < t->nbuckets; ++i) {
+        const uint32_t c = t->bucket_code[i];
+        const uint32_t next = c + 1 < 128 ? f2u(t->thr[c + 1]) : f2u(INFINITY);
+        const uint32_t lo =
+            (next >> 16) == (uint32_t)(t->bucket_lo + i) ? (next & 0xffffu) : 0x10000u;
+        t->word[i] = ((c + bias + 1u) << 24) - lo;
+    }
+}
+
 void build_dequant_tab(float alpha, float code_scale, DequantTab *t) {
     const double l1pa = log1p((double)alpha);
     for (int k = 0; k < 128; ++k)
@@ -142,6 +157,7 @@ bool tables_for(const lynx_params &p, Tables *out) {
     if (!build_quant_tab(p.alpha, p.code_scale, code_max_of(p.anchor_bits, p.residual_bits),
                          &t.q))
         return false;
+    build_table_words(p.residual_bits, &t.q);
     build_dequant_tab(p.alpha, p.code_scale, &t.d);
     if (g_cache.size() >= kMaxCachedTables)
         g_cache.clear();

@@ -25,6 +25,7 @@
 // this layout took the anchor dequant from 1.12 to 1.04 ms and the full one
 // from 1.32 to 1.24 ms against the earlier one-block-per-workgroup kernel
 // (16-byte row pieces).
+#include "lynx_device.h"
 #include "lynx_recon.h"
 
 namespace lynx {
@@ -60,15 +61,6 @@ __device__ __forceinline__ uint32_t get_field(const uint32_t *w, int v) {
     if (s + W > 32)
         f |= w[d + 1] << (32 - s);
     return f & ((1u << W) - 1u);
-}
-
-// Workgroup u of a launch of n workgroups, reordered so that the hardware's
-// round-robin deal of workgroups to the 8 XCDs (u % 8) gives XCD x the
-// contiguous run [x q + min(x, r), ...) (q = n / 8, r = n % 8): the
-// workgroups of one XCD work on neighbouring rows.  A bijection of [0, n).
-__device__ __forceinline__ int64_t xcd_unit(int64_t u, int64_t n) {
-    const int64_t q = n >> 3, r = n & 7, x = u & 7, i = u >> 3;
-    return x * q + (x < r ? x : r) + i;
 }
 
 constexpr int kWaves = 8;  // waves per workgroup = (head, chunk) items

@@ -26,7 +26,7 @@ constexpr bool valid_field_bits(int a, int b) {
 constexpr int code_max_of(int a, int b) {
     return b == 0 ? (1 << (a - 1)) - 1 : 128 - (1 << (b - 1));
 }
-constexpr int kMaxBuckets = 1792;  // 14 KiB: with the 32 KiB stage, 3 workgroups per CU
+constexpr int kMaxBuckets = 1792;  // 7 KiB of SH16 table words in LDS and in the kernel argument
 
 // Compander tables, built once per (alpha, code_scale) on the host and
 // passed by value as a kernel argument.
@@ -38,9 +38,17 @@ constexpr int kMaxBuckets = 1792;  // 14 KiB: with the 32 KiB stage, 3 workgroup
 // Bucket index of a magnitude m is bits(m) >> shift, clamped to
 // [bucket_lo, bucket_lo + nbuckets - 1]; every bucket holds at most one
 // threshold, so code(m) = bucket_code[i] + (m >= thr[bucket_code[i] + 1]).
+//
+// word[i] (shift = 16 only): the quantize kernel's table entry of bucket i,
+// ((bucket_code[i] + bias + 1) << 24) - t, where bias is the Stage 4 offset
+// of the field split and t the low half of thr[bucket_code[i] + 1] if that
+// threshold lies in bucket i (the magnitudes of a bucket share their upper
+// half), else 0x10000; adding a magnitude's low half to the entry leaves
+// code + bias in the top byte.  Entries past nbuckets are zero.
 struct QuantTab {
     float thr[128];
     uint8_t bucket_code[kMaxBuckets];
+    uint32_t word[kMaxBuckets];
     int32_t bucket_lo;
     int32_t nbuckets;
     int32_t shift;
@@ -61,7 +69,7 @@ struct Geometry {
     int32_t heads;          // 128-channel groups per tensor
     int64_t nblocks;        // blocks in this launch
     int64_t block0;         // global index of the launch's first block
-    int64_t grid_wgs;       // workgroups of a persistent launch
+    int64_t grid_wgs;       // workgroups of a launch whose kernel loops over blocks
     // Per-block strides of the code buffers: bytes of the anchor-side buffer
     // (the anchor stream alone, or with the packed layout the block's whole
     // record: anchor stream then gamma_min, gamma_scale, mu, sigma), and
