@@ -16,17 +16,20 @@
 //
 // One workgroup per block, grid = blocks, dealt to the 8 XCDs in contiguous
 // runs (neighbouring blocks share DRAM rows).  A workgroup first requests
-// its block's rows: buffer loads of 16 bytes per lane, four whole 256-byte
-// block rows per instruction, straight into LDS (buffer_load_dwordx4 ...
-// lds), each wave the 32 rows of its chunk.  While they are in flight the
-// compander table arrives in LDS the same way: its entries are built on the
-// host and travel in the kernel argument, so a workgroup copies 7 KiB
-// instead of computing them.  The kernel stays within 128 VGPRs, so two
-// workgroups (16 waves) share a compute unit and one computes while the
-// other's rows stream in: the rare IEEE divisions are taken per group of 4
-// tokens behind a wave-uniform branch (a wide unrolled slow path would set
-// the register budget), and the chunk minima / maxima meet in LDS as
-// bfloat16 halves (the inputs are bfloat16, so this is exact).
+// its block's rows straight into registers: 4 bytes (the lane's channel
+// pair) of each of its chunk's 32 rows, one whole 256-byte block row per
+// wave instruction.  While they are in flight the compander table arrives
+// in LDS by buffer loads into LDS (buffer_load_dwordx4 ... lds): its
+// entries are built on the host and travel in the kernel argument, so a
+// workgroup copies 7 KiB instead of computing them.  The kernel stays within
+// 128 VGPRs and 13 KiB of LDS, so two workgroups (16 waves) share a compute
+// unit and one computes while the other's rows stream in: the rare IEEE
+// divisions are taken per group of 4 tokens behind a wave-uniform branch (a
+// wide unrolled slow path would set the register budget), and the chunk
+// minima / maxima meet in LDS as bfloat16 halves (the inputs are bfloat16,
+// so this is exact).  Staging the rows through LDS with 16-byte loads
+// measured slower (1.41 against 1.36 ms on a 4 GiB set), as did
+// nontemporal loads and ordinary code stores.
 // The anchor and residual bytes of a lane are 32 contiguous bytes of the
 // chunk-tiled stream layout, so a wave writes 2 KiB of each stream that no
 // other workgroup touches.
@@ -82,7 +85,6 @@ constexpr float kMuTiny = 0x1p-74f;
 constexpr int kPairs = kHead / 2;            // channel pairs per block (lanes per chunk)
 constexpr int kThreads = kPairs * kChunks;   // 512
 constexpr int kWaves = kThreads / 64;        // 8, one per chunk
-constexpr int kStageLoads = kChunk / 4;      // 16-byte loads per wave and block
 constexpr int kGroups = kChunk / 4;          // token groups of the division branches
 
 // Workgroup barrier over LDS traffic only: each wave waits for its own LDS
@@ -148,9 +150,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     // (QuantTab::word).  Otherwise two words: (next threshold, J_base).
     __shared__ __attribute__((aligned(16)))
     uint32_t s_tab[MODE == kModeQuantize ? (SH16 ? kMaxBuckets : 2 * kMaxBuckets) : 1];
-    // The block's rows per wave: the 32 token rows of its chunk x 128
-    // channels, token-major.
-    __shared__ __attribute__((aligned(16))) uint32_t s_stage[kWaves][kChunk * kPairs];
 
     constexpr int kBits = RBITS;  // residual field width
     // Stage 4 bias (+7 at 4 + 4; none for a single stream)
@@ -172,28 +171,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     typedef __attribute__((address_space(3))) const u32x2 lds_u32x2;
     typedef __attribute__((address_space(3))) const uint32_t lds_u32;
 
-    // ---- the block's rows into LDS --------------------------------------
-    // Load k of lane l: 16 bytes (channels 8 (l % 16) .. + 7) of token row
-    // 4 k + l / 16 of the wave's chunk; one 1 KiB LDS row group per load.
+    // ---- the block's rows into registers ---------------------------------
+    // Row i of the lane's chunk: the 4 bytes of its channel pair (one whole
+    // 256-byte block row per wave instruction), all 32 requested at once.
+    uint32_t raw[kChunk];
     {
         const int64_t tp = b / g.heads;
         const uint16_t *bp = kv + (tp / g.pages) * g.tensor_stride +
                              (int64_t)(tp % g.pages) * kPage * g.row_stride +
                              (b % g.heads) * kHead;
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(bp, 0x7fffffff);
-        const uint32_t voff = (uint32_t)(wave * kChunk + (lane >> 4)) * row_bytes +
-                              (uint32_t)(lane & 15) * 16u;
-        const uint32_t group_bytes = 4u * row_bytes;
-        uint32_t soff = 0;
-        uint32_t lds = __builtin_amdgcn_readfirstlane(
-            (uint32_t)(uintptr_t)(lds_void *)&s_stage[wave][0]);
+        const uint8_t *rp = (const uint8_t *)bp + (int64_t)(kChunk * j) * row_bytes + 4 * p;
 #pragma unroll
-        for (int k = 0; k < kStageLoads; ++k) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(uintptr_t)lds, 16, voff,
-                                                     soff, 0, 0);
-            asm volatile("s_add_u32 %0, %0, %1" : "+s"(soff) : "s"(group_bytes));
-            asm volatile("s_add_u32 %0, %0, 0x400" : "+s"(lds));
-        }
+        for (int i = 0; i < kChunk; ++i)
+            raw[i] = *(const uint32_t *)(rp + (int64_t)i * row_bytes);
     }
 
     // ---- compander table into LDS ---------------------------------------
@@ -245,19 +235,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     const uint32_t tab_base = (uint32_t)(uintptr_t)(lds_u32 *)s_tab -
                               (uint32_t)tab.bucket_lo * (SH16 ? 4u : 8u);
 
-    // ---- 32 token rows x 2 channels (4 B per row) from the stage ---------
-    // The wave's own loads (rows and table words) have landed in LDS.
+    // ---- 32 token rows x 2 channels --------------------------------------
+    // The wave's own loads (rows, and table words into LDS) have landed.
     vm_wait_all();
     float x[kChunk][2];
-    {
-        uint32_t raw[kChunk];
 #pragma unroll
-        for (int i = 0; i < kChunk; ++i) raw[i] = s_stage[wave][i * kPairs + p];
-#pragma unroll
-        for (int i = 0; i < kChunk; ++i) {
-            x[i][0] = bf16_lo(raw[i]);
-            x[i][1] = bf16_hi(raw[i]);
-        }
+    for (int i = 0; i < kChunk; ++i) {
+        x[i][0] = bf16_lo(raw[i]);
+        x[i][1] = bf16_hi(raw[i]);
     }
 
     // ---- phase 1: page statistics ----------------------------------------
@@ -479,11 +464,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
         const int64_t toff = j * (kHead / 2 * kChunk) + p * kChunk;
         u32x4 *ao = (u32x4 *)(anchor + b * g.astride + toff);
         u32x4 *ro = (u32x4 *)(residual + b * (kPage * kHead / 2) + toff);
-        // Ordinary stores: the streams are read again by the dequant kernels.
-        ao[0] = av[0];
-        ao[1] = av[1];
-        ro[0] = rv[0];
-        ro[1] = rv[1];
+        // Nontemporal stores (measured faster than ordinary ones here).
+        __builtin_nontemporal_store(av[0], ao);
+        __builtin_nontemporal_store(av[1], ao + 1);
+        __builtin_nontemporal_store(rv[0], ro);
+        __builtin_nontemporal_store(rv[1], ro + 1);
     } else {
         // Other widths: field 2 i + e (token i, channel 2p + e) of the lane's
         // run at bit w (2 i + e); the anchor field is the magnitude J >> b,
