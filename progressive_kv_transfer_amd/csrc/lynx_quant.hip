@@ -174,16 +174,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     // ---- the block's rows into registers ---------------------------------
     // Row i of the lane's chunk: the 4 bytes of its channel pair (one whole
     // 256-byte block row per wave instruction), all 32 requested at once.
+    // Buffer loads: the row offset is a scalar (no per-lane address
+    // arithmetic); every offset stays below 255 row_bytes + 256 < 2^31.
     uint32_t raw[kChunk];
     {
         const int64_t tp = b / g.heads;
         const uint16_t *bp = kv + (tp / g.pages) * g.tensor_stride +
                              (int64_t)(tp % g.pages) * kPage * g.row_stride +
                              (b % g.heads) * kHead;
-        const uint8_t *rp = (const uint8_t *)bp + (int64_t)(kChunk * j) * row_bytes + 4 * p;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(bp, 0x7fffffff);
+        const uint32_t voff = (uint32_t)(kChunk * j) * row_bytes + 4u * (uint32_t)p;
 #pragma unroll
         for (int i = 0; i < kChunk; ++i)
-            raw[i] = *(const uint32_t *)(rp + (int64_t)i * row_bytes);
+            raw[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff, (uint32_t)i * row_bytes, 0);
     }
 
     // ---- compander table into LDS ---------------------------------------
