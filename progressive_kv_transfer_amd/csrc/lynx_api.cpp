@@ -6,6 +6,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
 #include <map>
 #include <mutex>
 #include <string>
@@ -379,10 +380,12 @@ int dequant_common(const uint8_t *anchor, const uint8_t *residual, lynx_meta met
 }
 
 // Split-KV plan of an attention call: query rows per KV head, splits of the
-// context into runs of 128-token steps (about two resident workgroups per
-// compute unit in total) and the workspace of their partials.
+// context (about two resident workgroups per compute unit in total) and the
+// workspace of their partials.  Up to 16 rows the decode kernel takes runs
+// of 32-token chunks (a multiple of its 8 waves), beyond that the tile
+// kernel runs of 128-token steps.
 struct AttnPlan {
-    int rows, pages, splits, sps;
+    int rows, pages, splits, sps, cps;
     size_t ws_bytes;
 };
 
@@ -396,15 +399,26 @@ int attn_plan(int t_q, int n_qh, int n_kvh, int64_t ctx, AttnPlan *pl) {
         return LYNX_EINVAL;
     pl->rows = (int)rows;
     pl->pages = (int)(ctx / kPage);
-    const int64_t steps = ctx / 128;
     const int64_t target_wgs = 512;
-    int64_t sps = (steps * n_kvh + target_wgs - 1) / target_wgs;
-    if (sps < 1)
-        sps = 1;
-    if (sps > steps)
-        sps = steps;
-    pl->sps = (int)sps;
-    pl->splits = (int)((steps + sps - 1) / sps);
+    pl->sps = pl->cps = 0;
+    if (rows <= 16) {
+        const int64_t chunks = ctx / kChunk;
+        int64_t cps = (chunks * n_kvh + target_wgs - 1) / target_wgs;
+        cps = (cps + 7) / 8 * 8;
+        if (cps > chunks)
+            cps = chunks;  // a multiple of 8: chunks is
+        pl->cps = (int)cps;
+        pl->splits = (int)((chunks + cps - 1) / cps);
+    } else {
+        const int64_t steps = ctx / 128;
+        int64_t sps = (steps * n_kvh + target_wgs - 1) / target_wgs;
+        if (sps < 1)
+            sps = 1;
+        if (sps > steps)
+            sps = steps;
+        pl->sps = (int)sps;
+        pl->splits = (int)((steps + sps - 1) / sps);
+    }
     pl->ws_bytes = (size_t)pl->splits * n_kvh * pl->rows * (2 + kHead) * sizeof(float);
     return LYNX_OK;
 }
@@ -691,6 +705,7 @@ int attn_common(const void *q, int t_q, int num_q_heads, const uint8_t *k_anchor
     a.pages = pl.pages;
     a.splits = pl.splits;
     a.steps_per_split = pl.sps;
+    a.chunks_per_split = pl.cps;
     a.causal = causal_tail ? 1 : 0;
     a.qk_scale_log2 = (float)((double)scale * 1.4426950408889634);
     return hip_status(launch_attention(a, tab, stream));

@@ -443,102 +443,469 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(AttnArgs 
     }
 }
 
-// Sum / max over the 64 lanes of a wave.
+// ---------------------------------------------------------------------------
+// Decode kernel (at most 16 query rows per KV head, one row tile): no K^ or
+// V^ tiles in LDS.  Each wave walks 32-token chunks on its own; every lane
+// loads the 32 code bytes of channel pair `lane` of each stream (two 16-byte
+// loads) and the MFMA operands are rebuilt in registers:
+//   K^ (A of S^T = K^ Q^T, 8 channels of one token per lane): the codes go
+//     through a 2 KiB LDS stage per stream ([pair][8 dwords], the two
+//     halves of a pair's row swapped for pairs with bit 2 set, so that the
+//     reads below hit distinct banks); lane (r16 = 4 qa + qi, g) reads, per
+//     k-block m and token half tt, the dword of pair 16 m + 4 g + qi at
+//     tokens 16 tt + 4 qa .. + 3, and a 4 x 4 byte transpose across the
+//     lanes of a quad (two DPP moves, two v_perm) leaves it the 4 pairs
+//     16 m + 4 g .. + 3 (channels 32 m + 8 g .. + 7) of token 16 tt + r16.
+//   V^ (A of O^T += V^T P^T, 8 tokens of one channel per lane): a 4 x 4
+//     dword transpose across the lane quarters (permlane32 / permlane16
+//     swaps) gives lane (r16, g) the dwords of pair 16 m + r16 at tokens
+//     4 g .. + 3 and 16 + 4 g .. + 3, the token order of the P^T operand;
+//     one pair gives the rows of two 16-channel tiles (its even and its odd
+//     channel).
+// The per-(chunk, channel) affine of Eq. (4) goes through a 2 KiB LDS table
+// per wave (one float4 per channel pair), the level tables sit at LDS
+// address 0 as in the tile kernel.  At the end the waves merge in LDS and
+// one partial per live row and split goes to the workspace for
+// attn_combine_kernel (merging the splits inside this kernel, by the last
+// workgroups to finish, measured slower: partials visible across the XCDs'
+// L2 caches cost either whole-cache write-backs or coherent-level loads,
+// more than the second launch).
+constexpr int kDecWaves = 8;
+constexpr int kDecThreads = 64 * kDecWaves;
+
+// Codes of one chunk (pair `lane`: tokens 0-15 in .0, 16-31 in .1) and the
+// metadata of pair `lane`.  With both tensors at full precision the V codes
+// are requested after the scores (all four streams at once would spill).
+template <bool KF, bool VF>
+struct DecCodes {
+    u32x4 ka[2], va[2];
+    u32x4 kr[KF ? 2 : 1], vr[VF ? 2 : 1];
+    float2 kgm, kgs, kmu, ksg, vgm, vgs, vmu, vsg;
+};
+
+template <bool KF, bool VF>
+__device__ __forceinline__ void dec_load_k(const AttnArgs &a, int64_t b, int j, int lane,
+                                           DecCodes<KF, VF> &c) {
+    const int64_t go = b * a.gstride + 2 * lane;
+    const int64_t co = b * a.cstride + j * kHead + 2 * lane;
+    c.kgm = *(const float2 *)(a.k_gmin + go);
+    c.kgs = *(const float2 *)(a.k_gsc + go);
+    c.kmu = *(const float2 *)(a.k_mu + co);
+    c.ksg = *(const float2 *)(a.k_sg + co);
+    c.vgm = *(const float2 *)(a.v_gmin + go);
+    c.vgs = *(const float2 *)(a.v_gsc + go);
+    c.vmu = *(const float2 *)(a.v_mu + co);
+    c.vsg = *(const float2 *)(a.v_sg + co);
+    const int64_t ab = b * a.astride + j * (kHead / 2 * kChunk) + lane * kChunk;
+    const int64_t rb = b * (kPage * kHead / 2) + j * (kHead / 2 * kChunk) + lane * kChunk;
+    c.ka[0] = *(const u32x4 *)(a.k_anc + ab);
+    c.ka[1] = *(const u32x4 *)(a.k_anc + ab + 16);
+    if constexpr (KF) {
+        c.kr[0] = *(const u32x4 *)(a.k_res + rb);
+        c.kr[1] = *(const u32x4 *)(a.k_res + rb + 16);
+    }
+}
+
+template <bool KF, bool VF>
+__device__ __forceinline__ void dec_load_v(const AttnArgs &a, int64_t b, int j, int lane,
+                                           DecCodes<KF, VF> &c) {
+    const int64_t ab = b * a.astride + j * (kHead / 2 * kChunk) + lane * kChunk;
+    const int64_t rb = b * (kPage * kHead / 2) + j * (kHead / 2 * kChunk) + lane * kChunk;
+    c.va[0] = *(const u32x4 *)(a.v_anc + ab);
+    c.va[1] = *(const u32x4 *)(a.v_anc + ab + 16);
+    if constexpr (VF) {
+        c.vr[0] = *(const u32x4 *)(a.v_res + rb);
+        c.vr[1] = *(const u32x4 *)(a.v_res + rb + 16);
+    }
+}
+
+// 4 x 4 byte transpose across the lanes of a quad: lane qi ends with byte
+// qi of each lane of its quad (byte k from lane k).  Stage 1 swaps half
+// words with lane qi ^ 2, stage 2 bytes with lane qi ^ 1; sel1 / sel2 are
+// the lane's v_perm selectors (perm(a, b, s) takes bytes 0-3 from b, 4-7
+// from a).
+__device__ __forceinline__ uint32_t quad_transpose(uint32_t x, uint32_t sel1, uint32_t sel2) {
+    uint32_t y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4e, 0xf, 0xf, false);
+    x = __builtin_amdgcn_perm(y, x, sel1);
+    y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xb1, 0xf, 0xf, false);
+    return __builtin_amdgcn_perm(y, x, sel2);
+}
+
+// 4 x 4 dword transpose across the lane quarters: lane (r16, x) ends with
+// d[q] = the d[x] lane (r16, q) held (stage 1 swaps with the other half of
+// the wave, stage 2 with the neighbouring quarter).
+__device__ __forceinline__ void quarter_transpose(uint32_t d[4]) {
+    auto s02 = __builtin_amdgcn_permlane32_swap(d[0], d[2], false, false);
+    auto s13 = __builtin_amdgcn_permlane32_swap(d[1], d[3], false, false);
+    auto s01 = __builtin_amdgcn_permlane16_swap(s02[0], s13[0], false, false);
+    auto s23 = __builtin_amdgcn_permlane16_swap(s02[1], s13[1], false, false);
+    d[0] = s01[0];
+    d[1] = s01[1];
+    d[2] = s23[0];
+    d[3] = s23[1];
+}
+
+// V operand dwords of a stream: out[2 m + h] = pair 16 m + r16, tokens
+// 16 h + 4 g .. + 3.
+__device__ __forceinline__ void v_operand_words(const u32x4 w[2], uint32_t out[8]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        uint32_t d[4] = {w[h][0], w[h][1], w[h][2], w[h][3]};
+        quarter_transpose(d);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) out[2 * m + h] = d[m];
+    }
+}
+
+// Eq. (4) folded for both channels of a pair: (a_lo, a_hi, b_lo, b_hi).
+__device__ __forceinline__ float4 dec_affine(float2 gm, float2 gs, float2 mu, float2 sg,
+                                             float eps) {
+    const float d1x = gs.x + eps, d1y = gs.y + eps;
+    return make_float4((sg.x + eps) * d1x, (sg.y + eps) * d1y, __builtin_fmaf(mu.x, d1x, gm.x),
+                       __builtin_fmaf(mu.y, d1y, gm.y));
+}
+
+// Levels of the two channels of code byte i of the anchor word A (and, for
+// full codes, of the combined words X, Y): .x channel 2P, .y channel 2P + 1.
+template <bool FULL>
+__device__ __forceinline__ float2 dec_levels(uint32_t X, uint32_t Y, uint32_t A, int i,
+                                             const Luts &t) {
+    if constexpr (FULL) {
+        return make_float2(*(const float *)((const char *)t.lut + byte_shl<2>(X, i)),
+                           *(const float *)((const char *)t.lut + byte_shl<2>(Y, i)));
+    } else {
+        return *(const float2 *)((const char *)t.lut2 + byte_shl<3>(A, i));
+    }
+}
+
+template <bool KF, bool VF>  // K / V rebuilt from anchor + residual
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4))) void
+attn_decode_kernel(AttnArgs a, const DequantTab tab) {
+    constexpr int kMergeFloats = kDecWaves * 16 * kMergeRow;
+    struct PerWave {
+        float4 affk[64], affv[64];  // affine of each pair, K then V
+        uint32_t ka[64 * 8];        // K codes [pair][8 dwords], halves swapped for pair bit 2
+        uint32_t kr[KF ? 64 * 8 : 1];
+    };
+    struct Lds {
+        float lut[256];
+        float2 lut2[256];
+        union {
+            PerWave w[kDecWaves];
+            float merge[kMergeFloats];  // [wave][16 rows][kMergeRow]
+        } u;
+    };
+    __shared__ Lds lds;
+
+    const int tid = (int)__builtin_amdgcn_workitem_id_x();
+    const int wg = (int)__builtin_amdgcn_workgroup_id_x();
+    const int kvh = wg % a.n_kvh;
+    const int split = wg / a.n_kvh;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int r16 = lane & 15;
+    const int g = lane >> 4;
+    const int qi = r16 & 3;
+    const int qa = r16 >> 2;
+
+    if (tid < 256) {
+        lds.lut[tid] = signed_level(tab, ((tid & 15) << 4) | (tid >> 4), true);
+        lds.lut2[tid] = make_float2(signed_level(tab, tid & 15, false),
+                                    signed_level(tab, tid >> 4, false));
+    }
+    const Luts luts = {lds.lut, lds.lut2};
+    PerWave &pw = lds.u.w[wave];
+
+    // quad-transpose selectors of this lane
+    const uint32_t sel1 = qi < 2 ? 0x05040100u : 0x03020706u;
+    const uint32_t sel2 = (qi & 1) ? 0x03070105u : 0x06020400u;
+    // K stage: this lane's pair row (halves swapped for pair bit 2), and
+    // the dword it reads for k-block m, token half tt: pair 16 m + 4 g + qi,
+    // dword (4 tt + qa) ^ (4 (g & 1)) (pair bit 2 = g & 1)
+    const int kw_lo = lane * 8 + 4 * ((lane >> 2) & 1);
+    const int kw_hi = lane * 8 + 4 * (((lane >> 2) & 1) ^ 1);
+    const int kr_base = (4 * g + qi) * 8 + qa;
+
+    // Query row h = r16 of this lane (both products), dead rows are zero.
+    const int h = r16;
+    const bool live = h < a.rows;
+    bf16x8 qreg[4];
+    {
+        const int r = live ? h / a.group : 0;
+        const int qh = live ? kvh * a.group + h % a.group : 0;
+        const uint16_t *qp = a.q + ((int64_t)r * a.n_qh + qh) * kHead + 8 * g;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const u32x4 v = live ? *(const u32x4 *)(qp + 32 * kb) : u32x4{0u, 0u, 0u, 0u};
+            qreg[kb] = as_bf16x8(v);
+        }
+    }
+    const int64_t limit =
+        a.causal ? a.ctx - a.t_q + (live ? h / a.group : a.t_q - 1) : a.ctx - 1;
+    const float cs = a.qk_scale_log2;
+    const float lazy = kLazyLog2 / cs;
+
+    float m_run = -INFINITY;
+    float l_run = 0.0f;
+    f32x4 o[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) o[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // Chunks of this split: wave w takes c0 + w, c0 + w + 8, ...
+    const int64_t chunks = a.ctx / kChunk;
+    const int64_t c0 = (int64_t)split * a.chunks_per_split;
+    const int64_t c1 = min(chunks, c0 + a.chunks_per_split);
+    __syncthreads();  // level tables
+
+    for (int64_t c = c0 + wave; c < c1; c += kDecWaves) {
+        const int64_t b = (c >> 3) * a.n_kvh + kvh;
+        const int j = (int)(c & 7);
+        DecCodes<KF, VF> cd;
+        dec_load_k<KF, VF>(a, b, j, lane, cd);
+        if constexpr (!(KF && VF))
+            dec_load_v<KF, VF>(a, b, j, lane, cd);
+        // This wave's own LDS region (a wave's LDS accesses execute in
+        // program order): affine tables and the K stage of the chunk.
+        pw.affk[lane] = dec_affine(cd.kgm, cd.kgs, cd.kmu, cd.ksg, tab.eps);
+        pw.affv[lane] = dec_affine(cd.vgm, cd.vgs, cd.vmu, cd.vsg, tab.eps);
+        *(u32x4 *)&pw.ka[kw_lo] = cd.ka[0];
+        *(u32x4 *)&pw.ka[kw_hi] = cd.ka[1];
+        if constexpr (KF) {
+            *(u32x4 *)&pw.kr[kw_lo] = cd.kr[0];
+            *(u32x4 *)&pw.kr[kw_hi] = cd.kr[1];
+        }
+        asm volatile("" ::: "memory");
+
+        // ---- S^T = K^ Q^T ------------------------------------------------
+        f32x4 s[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            uint32_t A[2], X[2] = {0u, 0u}, Y[2] = {0u, 0u};
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                const int idx = m * 128 + kr_base + ((4 * tt) ^ (4 * (g & 1)));
+                A[tt] = quad_transpose(pw.ka[idx], sel1, sel2);
+                if constexpr (KF) {
+                    const uint32_t R = quad_transpose(pw.kr[idx], sel1, sel2);
+                    X[tt] = ((A[tt] << 4) & 0xf0f0f0f0u) | (R & 0x0f0f0f0fu);
+                    Y[tt] = (A[tt] & 0xf0f0f0f0u) | ((R >> 4) & 0x0f0f0f0fu);
+                }
+            }
+            u32x4 op[2];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const float4 af = pw.affk[16 * m + 4 * g + jj];  // channels 32m + 8g + 2jj, +1
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) {
+                    const float2 lv = dec_levels<KF>(X[tt], Y[tt], A[tt], jj, luts);
+                    op[tt][jj] = pack_bf16(__builtin_fmaf(lv.x, af.x, af.z),
+                                           __builtin_fmaf(lv.y, af.y, af.w));
+                }
+            }
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+                s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(op[tt]), qreg[m], s[tt],
+                                                               0, 0, 0);
+        }
+        if constexpr (KF && VF)  // both full: V codes after the scores (registers)
+            dec_load_v<KF, VF>(a, b, j, lane, cd);
+        const int64_t tok0 = c * kChunk;
+        if (tok0 + kChunk - 1 > a.ctx - a.t_q) {  // uniform
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (tok0 + 16 * tt + 4 * g + e > limit) s[tt][e] = -INFINITY;
+        }
+        float mc = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                         fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+        mc = row_max4(mc);
+        const bool grow = mc > m_run + lazy;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+            const float corr = grow ? __builtin_amdgcn_exp2f((m_run - mc) * cs) : 1.0f;
+            l_run *= corr;
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) o[mt] *= corr;
+            m_run = grow ? mc : m_run;
+        }
+        const float base = m_run == -INFINITY ? 0.0f : m_run * cs;
+        float pr[8];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                pr[4 * tt + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tt][e], cs, -base));
+                l_run += pr[4 * tt + e];
+            }
+        // P^T operands: k-slot 8g + e' <-> token 16 (e' / 4) + 4g + e' % 4.
+        u32x4 hi, lo;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t hw = pack_bf16(pr[2 * i], pr[2 * i + 1]);
+            hi[i] = hw;
+            lo[i] = pack_bf16(pr[2 * i] - __uint_as_float(hw << 16),
+                              pr[2 * i + 1] - __uint_as_float(hw & 0xffff0000u));
+        }
+        const bf16x8 phi = as_bf16x8(hi), plo = as_bf16x8(lo);
+
+        // ---- O^T += V^T P^T ----------------------------------------------
+        // Tile 2m: rows = channels 2 (16 m + rho); tile 2m + 1: 2 (16 m + rho) + 1.
+        uint32_t va[8], vr[8];
+        v_operand_words(cd.va, va);
+        if constexpr (VF)
+            v_operand_words(cd.vr, vr);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const float4 af = pw.affv[16 * m + r16];
+            float ve[8], vo[8];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const uint32_t A = va[2 * m + hh];
+                uint32_t X = 0, Y = 0;
+                if constexpr (VF) {
+                    const uint32_t R = vr[2 * m + hh];
+                    X = ((A << 4) & 0xf0f0f0f0u) | (R & 0x0f0f0f0fu);
+                    Y = (A & 0xf0f0f0f0u) | ((R >> 4) & 0x0f0f0f0fu);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float2 lv = dec_levels<VF>(X, Y, A, e, luts);
+                    ve[4 * hh + e] = __builtin_fmaf(lv.x, af.x, af.z);
+                    vo[4 * hh + e] = __builtin_fmaf(lv.y, af.y, af.w);
+                }
+            }
+            const bf16x8 aeven = as_bf16x8(u32x4{pack_bf16(ve[0], ve[1]), pack_bf16(ve[2], ve[3]),
+                                                 pack_bf16(ve[4], ve[5]), pack_bf16(ve[6], ve[7])});
+            const bf16x8 aodd = as_bf16x8(u32x4{pack_bf16(vo[0], vo[1]), pack_bf16(vo[2], vo[3]),
+                                                pack_bf16(vo[4], vo[5]), pack_bf16(vo[6], vo[7])});
+            o[2 * m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aeven, phi, o[2 * m], 0, 0, 0);
+            o[2 * m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aeven, plo, o[2 * m], 0, 0, 0);
+            o[2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aodd, phi, o[2 * m + 1], 0, 0, 0);
+            o[2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aodd, plo, o[2 * m + 1], 0, 0, 0);
+        }
+        asm volatile("" ::: "memory");  // the wave's LDS region is rewritten by the next chunk
+    }
+    __syncthreads();  // the merge area overlaps every wave's region
+
+    // Merge the 8 waves in LDS, then one partial per live row.
+    const float l_row = row_sum4(l_run);
+    float *sm = lds.u.merge;
+    {
+        float *row = sm + (wave * 16 + r16) * kMergeRow;
+        if (g == 0) {
+            row[0] = m_run == -INFINITY ? -INFINITY : m_run * cs;
+            row[1] = l_row;
+        }
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                row[4 + 2 * (16 * (mt >> 1) + 4 * g + e) + (mt & 1)] = o[mt][e];
+    }
+    __syncthreads();
+    float *part = a.ws + ((int64_t)split * a.n_kvh + kvh) * a.rows * kPartial;
+    for (int idx = tid; idx < a.rows * kHead; idx += kDecThreads) {
+        const int hr = idx >> 7, ch = idx & (kHead - 1);
+        float M = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < kDecWaves; ++k) M = fmaxf(M, sm[(k * 16 + hr) * kMergeRow]);
+        float l = 0.0f, acc = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kDecWaves; ++k) {
+            const float *row = sm + (k * 16 + hr) * kMergeRow;
+            const float w = row[0] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(row[0] - M);
+            l = __builtin_fmaf(row[1], w, l);
+            acc = __builtin_fmaf(row[4 + ch], w, acc);
+        }
+        float *dst = part + hr * kPartial;
+        if (ch == 0) {
+            dst[0] = M;
+            dst[1] = l;
+        }
+        dst[2 + ch] = acc;
+    }
+
+}
+
+// Maximum over the 64 lanes of a wave.
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
     for (int d = 32; d > 0; d >>= 1) x = fmaxf(x, __shfl_xor(x, d, 64));
     return x;
 }
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int d = 32; d > 0; d >>= 1) x += __shfl_xor(x, d, 64);
-    return x;
-}
 
-// One workgroup of 256 lanes per (kv head, live row) merges the split
-// partials: the maximum M over the splits, then lane t takes the items
-// (split s, channel quarter t % 4) for s = t / 4, t / 4 + 64, ... (up to 64
-// splits this is a single round of loads), weights them by 2^(m_s - M), and
-// the 64 lanes of each quarter are summed through LDS.
-__global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(AttnArgs a) {
-    __shared__ float s_red[2][kAttnThreads / 64];
-    __shared__ float s_acc[64][4 * 33];
+// One wave per (KV head, live row, quarter of the 128 channels) merges the
+// split partials: lane s takes splits s, s + 64, ... (its max, sum and the
+// 32 outputs of the quarter, loaded together), the wave agrees on the
+// maximum M, weights each split by 2^(m_s - M), and the 64 lanes' weighted
+// sums meet through LDS, summed in split order per lane slot.
+constexpr int kCombineThreads = 64;
+
+__global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs a) {
+    __shared__ float s_acc[32][65];
+    __shared__ float s_l[64];
     const int wg = (int)__builtin_amdgcn_workgroup_id_x();
-    const int kvh = wg % a.n_kvh;
-    const int h = wg / a.n_kvh;
-    const int tid = (int)__builtin_amdgcn_workitem_id_x();
-    const int wave = tid >> 6;
+    const int cq = wg & 3;
+    const int kvh = (wg >> 2) % a.n_kvh;
+    const int h = (wg >> 2) / a.n_kvh;
+    const int lane = (int)__builtin_amdgcn_workitem_id_x();
     const int64_t split_stride = (int64_t)a.n_kvh * a.rows * kPartial;
     const float *base = a.ws + ((int64_t)kvh * a.rows + h) * kPartial;
 
-    // Lane t holds split t / 4, channel quarter t % 4 (its max, sum and 32
-    // outputs loaded together); splits beyond 64 are read in later passes.
-    const int cq = tid & 3;
-    const int s_first = tid >> 2;
-    float m0 = -INFINITY, l0 = 0.0f;
+    float m = -INFINITY;
+    for (int sp = lane; sp < a.splits; sp += 64) m = fmaxf(m, base[sp * split_stride]);
+    const float M = wave_max(m);
+    float l = 0.0f;
     float acc[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) acc[i] = 0.0f;
-    if (s_first < a.splits) {
-        const float *pt = base + s_first * split_stride;
-        m0 = pt[0];
-        l0 = pt[1];
-#pragma unroll
-        for (int i = 0; i < 32; i += 2) {
-            const float2 v = *(const float2 *)(pt + 2 + 32 * cq + i);
-            acc[i] = v.x;
-            acc[i + 1] = v.y;
-        }
-    }
-    float m = m0;
-    for (int s = s_first + kAttnThreads / 4; s < a.splits; s += kAttnThreads / 4)
-        m = fmaxf(m, base[s * split_stride]);
-    m = wave_max(m);
-    if ((tid & 63) == 0) s_red[0][wave] = m;
-    __syncthreads();
-    const float M = fmaxf(fmaxf(s_red[0][0], s_red[0][1]), fmaxf(s_red[0][2], s_red[0][3]));
-
-    const float w0 = m0 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m0 - M);
-    float l = cq == 0 ? l0 * w0 : 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) acc[i] *= w0;
-    for (int s = s_first + kAttnThreads / 4; s < a.splits; s += kAttnThreads / 4) {
-        const float *pt = base + s * split_stride;
+    for (int sp = lane; sp < a.splits; sp += 64) {
+        const float *pt = base + sp * split_stride;
         const float ms = pt[0];
         const float w = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
-        if (cq == 0) l = __builtin_fmaf(pt[1], w, l);
+        l = __builtin_fmaf(pt[1], w, l);
+        // rows of 130 floats: the outputs are 8-byte aligned
+        const float2 *po = (const float2 *)(pt + 2 + 32 * cq);
 #pragma unroll
-        for (int i = 0; i < 32; i += 2) {
-            const float2 v = *(const float2 *)(pt + 2 + 32 * cq + i);
-            acc[i] = __builtin_fmaf(v.x, w, acc[i]);
-            acc[i + 1] = __builtin_fmaf(v.y, w, acc[i + 1]);
+        for (int i = 0; i < 16; ++i) {
+            const float2 v = po[i];
+            acc[2 * i] = __builtin_fmaf(v.x, w, acc[2 * i]);
+            acc[2 * i + 1] = __builtin_fmaf(v.y, w, acc[2 * i + 1]);
         }
     }
-    l = wave_sum(l);
-    if ((tid & 63) == 0) s_red[1][wave] = l;
-
 #pragma unroll
-    for (int i = 0; i < 32; ++i) s_acc[tid >> 2][cq * 33 + i] = acc[i];
+    for (int i = 0; i < 32; ++i) s_acc[i][lane] = acc[i];
+    s_l[lane] = l;
     __syncthreads();
-    const int c = tid & (kHead - 1), half = tid >> 7;
-    float y = 0.0f;
-    for (int k = half; k < 64; k += 2) y += s_acc[k][(c >> 5) * 33 + (c & 31)];
-    __syncthreads();
-    if (half == 1) s_acc[0][c] = y;
-    __syncthreads();
-    if (half == 0) {
-        y += s_acc[0][c];
-        const float lt = s_red[1][0] + s_red[1][1] + s_red[1][2] + s_red[1][3];
+    if (lane < 32) {
+        float y = 0.0f, lt = 0.0f;
+#pragma unroll 8
+        for (int k = 0; k < 64; ++k) {
+            y += s_acc[lane][k];
+            lt += s_l[k];
+        }
         const float o = lt > 0.0f ? y / lt : 0.0f;
         const int r = h / a.group;
         const int qh = kvh * a.group + h % a.group;
-        const int64_t at = ((int64_t)r * a.n_qh + qh) * kHead + c;
+        const int64_t at = ((int64_t)r * a.n_qh + qh) * kHead + 32 * cq + lane;
         if (a.out_f32)
             ((float *)a.out)[at] = o;
         else
             ((uint16_t *)a.out)[at] = (uint16_t)(pack_bf16(o, 0.0f) & 0xffffu);
     }
+}
+
+template <bool KF, bool VF>
+hipError_t launch_decode(const AttnArgs &a, const DequantTab &tab, hipStream_t stream) {
+    hipLaunchKernelGGL((attn_decode_kernel<KF, VF>), dim3((unsigned)(a.n_kvh * a.splits)),
+                       dim3(kDecThreads), 0, stream, a, tab);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(a.n_kvh * a.rows * 4)),
+                       dim3(kCombineThreads), 0, stream, a);
+    return hipGetLastError();
 }
 
 template <int RT>
@@ -548,8 +915,8 @@ hipError_t launch_tiles(const AttnArgs &a, const DequantTab &tab, hipStream_t st
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(a.n_kvh * a.rows)),
-                       dim3(kAttnThreads), 0, stream, a);
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(a.n_kvh * a.rows * 4)),
+                       dim3(kCombineThreads), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -587,7 +954,11 @@ hipError_t attn_scratch(float **ptr) {
 hipError_t launch_attention(const AttnArgs &a, const DequantTab &tab, hipStream_t stream) {
     switch (attn_row_tiles(a.rows)) {
     case 1:
-        return launch_tiles<1>(a, tab, stream);
+        if (a.k_res)
+            return a.v_res ? launch_decode<true, true>(a, tab, stream)
+                           : launch_decode<true, false>(a, tab, stream);
+        return a.v_res ? launch_decode<false, true>(a, tab, stream)
+                       : launch_decode<false, false>(a, tab, stream);
     case 2:
         return launch_tiles<2>(a, tab, stream);
     case 4:

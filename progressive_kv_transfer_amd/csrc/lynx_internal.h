@@ -108,7 +108,9 @@ struct AttnArgs {
     int64_t ctx;    // context tokens (multiple of 256)
     int n_qh, n_kvh, group, t_q;
     int rows;       // t_q * group
-    int pages, splits, steps_per_split;  // steps of 128 tokens
+    int pages, splits;
+    int steps_per_split;   // tile kernel (more than 16 rows): steps of 128 tokens
+    int chunks_per_split;  // decode kernel (at most 16 rows): 32-token chunks
     int causal;
     int out_f32;
     float qk_scale_log2;  // scale * log2(e)

@@ -190,17 +190,22 @@ def test_empty_shapes_are_no_ops():
 
 
 def test_attention_workspace_sizes():
-    """Split-KV workspace: splits x KV heads x query rows x (2 + 128) floats,
-    splits cutting the context into runs of 128-token steps so that about 512
-    workgroups run."""
+    """Split-KV workspace: partials of splits x KV heads x query rows x
+    (2 + 128) floats.  Up to 16 rows per KV head (the decode kernel) the
+    splits are runs of 32-token chunks, a multiple of 8, about 512
+    workgroups in all; beyond 16 rows (the tile kernel) runs of 128-token
+    steps."""
     ws = lynx.attn_workspace_bytes
-    # decode, 64 q-heads over 8 KV heads at 32K: 8 rows, 256 steps, 4 per split
-    assert ws(1, 64, 8, 32768) == 64 * 8 * 8 * 130 * 4
+    per = lambda nkvh, rows: nkvh * rows * 130 * 4
+    # decode, 64 q-heads over 8 KV heads at 32K: 8 rows, 1024 chunks, 16 per split
+    assert ws(1, 64, 8, 32768) == 64 * per(8, 8)
     # verify, 8 drafts x 32 q-heads over 4 KV heads at 128K: 64 rows, 8 steps per split
-    assert ws(8, 32, 4, 131072) == 128 * 4 * 64 * 130 * 4
-    # small contexts: one step per split
-    assert ws(3, 8, 4, 1024) == 8 * 4 * 6 * 130 * 4
-    assert ws(5, 8, 4, 1024) == 8 * 4 * 10 * 130 * 4
+    assert ws(8, 32, 4, 131072) == 128 * per(4, 64)
+    # small contexts: 32 chunks in splits of 8 chunks
+    assert ws(3, 8, 4, 1024) == 4 * per(4, 6)
+    assert ws(5, 8, 4, 1024) == 4 * per(4, 10)
+    # 17 rows and more: the tile kernel's steps, one per split
+    assert ws(3, 24, 4, 1024) == 8 * per(4, 18)
     # invalid plans report 0
     assert ws(9, 64, 8, 32768) == 0      # 72 rows per KV head
     assert ws(1, 6, 4, 1024) == 0        # not grouped-query
