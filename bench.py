@@ -50,6 +50,7 @@ and QK + PV flops per second.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --profile-run      # the codec steps only, for rocprofv3
     python bench.py --attention-only [--attention-case NAME]   # attention calls only
+    python bench.py --large-only       # the 23.5 GiB set's three kernels only
     python bench.py --copy-probe       # plain 1 GiB copy, PMC scale factor
     python bench.py --hbm-probe        # plain streaming ceilings (torch + csrc/stream_ceiling.hip)
 """
@@ -519,7 +520,7 @@ def measure_splits(torch, lynx, kv, out, reps: int = 5, acc_tensors: int = 8):
 LARGE_WORKLOAD = "qwen3_235b_128k"
 
 
-def measure_large(torch, kvgen, lynx, reps: int = 5):
+def measure_large(torch, kvgen, lynx, reps: int = 10):
     """The Qwen3-235B-A22B-shaped set at 128K context (94 layers x {K, V} x
     131072 tokens x 512 channels, 23.5 GiB of bf16) resident on the GPU:
     quantize + split and both reconstructions over the whole set in one
@@ -644,6 +645,7 @@ def main():
     ap.add_argument("--no-transfer", action="store_true")
     ap.add_argument("--no-large", action="store_true")
     ap.add_argument("--attention-only", action="store_true")
+    ap.add_argument("--large-only", action="store_true")
     ap.add_argument("--attention-calls", type=int, default=50)
     ap.add_argument("--attention-case", default=None,
                     choices=[c[0] for c in ATTENTION_CASES])
@@ -666,6 +668,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     lynx.lib()
+    if args.large_only:
+        print(json.dumps({"large_set": measure_large(torch, kvgen, lynx)}), flush=True)
+        return
     if args.attention_only:
         print(json.dumps({"attention": measure_attention(
             torch, kvgen, lynx, args.attention_calls, 5, args.attention_case)}), flush=True)

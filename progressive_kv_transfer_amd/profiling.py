@@ -27,7 +27,8 @@ import statistics
 
 _CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 # Sources of the codec kernels whose traffic the committed summary describes.
-CODEC_SOURCES = ("lynx_quant.hip", "lynx_dequant.hip", "lynx_recon.h", "lynx_internal.h")
+CODEC_SOURCES = ("lynx_quant.hip", "lynx_dequant.hip", "lynx_recon.h", "lynx_internal.h",
+                 "lynx_device.h")
 # kernel symbol -> (name, algorithmic HBM bytes per bf16 element)
 CODEC_KERNELS = {
     "lynx::quant_kernel<0, true, 4, 4, false>": ("quantize", 2.0 + 0.5 + 0.5 + 0.28125),
