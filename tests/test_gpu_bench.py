@@ -32,7 +32,10 @@ def test_bench_json_line():
     rl = d["roofline"]
     assert rl["bound"] == "hbm" and rl["unit"] == "GB/s" and rl["peak"] == 8000.0
     assert abs(rl["frac"] - rl["achieved"] / rl["peak"]) < 1e-3
-    assert rl["traffic"] is None or rl["traffic"] > 0.9 * rl["algorithmic_bytes_per_launch"]
+    # measured HBM bytes (committed counter summary of the same kernel
+    # sources) within 5% of the algorithmic bytes, or null when stale
+    assert rl["traffic"] is None or (
+        abs(rl["traffic"] / rl["algorithmic_bytes_per_launch"] - 1.0) <= 0.05)
     assert set(d["kernels"]) == {"quantize", "dequant_anchor", "dequant_full"}
     assert "split_variants" in d and "verify" in d
     sp = d["single_page"]
