@@ -90,6 +90,25 @@ def test_other_geometries(t_q, n_qh, n_kvh):
     run_case(kv, q, n_kvh, t_q, True, False, t_q > 1)
 
 
+@pytest.mark.parametrize("full_k,full_v", [(False, True), (True, False)])
+def test_decode_kernel_mixed_precision_16_rows(full_k, full_v):
+    """The decode kernel at its largest row count (2 queries x group 8 = 16
+    rows), causal, with K and V at different precisions, on 5 pages (a
+    context that is not a power of two)."""
+    announce(f"decode kernel 16 rows full_k={full_k} full_v={full_v}")
+    kv = torch.stack([kvgen.kv_tensor(730 + i, 1280, 256, [5], True, DEV) for i in range(2)])
+    q = kvgen.queries(731, 2, 16, device=DEV)
+    run_case(kv, q, 2, 2, full_k, full_v, True)
+
+
+def test_decode_kernel_group_16_one_head():
+    """One KV head shared by 16 query heads (16 rows, one query token)."""
+    announce("decode kernel group 16, one KV head")
+    kv = torch.stack([kvgen.kv_tensor(740 + i, 768, 128, [2], True, DEV) for i in range(2)])
+    q = kvgen.queries(741, 1, 16, device=DEV)
+    run_case(kv, q, 1, 1, False, False, False)
+
+
 def test_attention_argument_errors():
     # two tensors of 256 tokens x 2 KV heads: 2 page blocks each
     kv = torch.stack([kvgen.kv_tensor(730 + i, 256, 256, [], True, DEV) for i in range(2)])
