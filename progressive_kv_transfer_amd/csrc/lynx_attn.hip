@@ -827,68 +827,97 @@ attn_decode_kernel(AttnArgs a, const DequantTab tab) {
 
 }
 
-// Maximum over the 64 lanes of a wave.
+// Sum / max over the 64 lanes of a wave.
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
     for (int d = 32; d > 0; d >>= 1) x = fmaxf(x, __shfl_xor(x, d, 64));
     return x;
 }
 
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) x += __shfl_xor(x, d, 64);
+    return x;
+}
 
-// One wave per (KV head, live row, quarter of the 128 channels) merges the
-// split partials: lane s takes splits s, s + 64, ... (its max, sum and the
-// 32 outputs of the quarter, loaded together), the wave agrees on the
-// maximum M, weights each split by 2^(m_s - M), and the 64 lanes' weighted
-// sums meet through LDS, summed in split order per lane slot.
-constexpr int kCombineThreads = 64;
-
-__global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs a) {
-    __shared__ float s_acc[32][65];
-    __shared__ float s_l[64];
+// One workgroup of 256 lanes per (kv head, live row) merges the split
+// partials: the maximum M over the splits, then lane t takes the items
+// (split s, channel quarter t % 4) for s = t / 4, t / 4 + 64, ... (up to 64
+// splits this is a single round of loads), weights them by 2^(m_s - M), and
+// the 64 lanes of each quarter are summed through LDS.
+__global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(AttnArgs a) {
+    __shared__ float s_red[2][kAttnThreads / 64];
+    __shared__ float s_acc[64][4 * 33];
     const int wg = (int)__builtin_amdgcn_workgroup_id_x();
-    const int cq = wg & 3;
-    const int kvh = (wg >> 2) % a.n_kvh;
-    const int h = (wg >> 2) / a.n_kvh;
-    const int lane = (int)__builtin_amdgcn_workitem_id_x();
+    const int kvh = wg % a.n_kvh;
+    const int h = wg / a.n_kvh;
+    const int tid = (int)__builtin_amdgcn_workitem_id_x();
+    const int wave = tid >> 6;
     const int64_t split_stride = (int64_t)a.n_kvh * a.rows * kPartial;
     const float *base = a.ws + ((int64_t)kvh * a.rows + h) * kPartial;
 
-    float m = -INFINITY;
-    for (int sp = lane; sp < a.splits; sp += 64) m = fmaxf(m, base[sp * split_stride]);
-    const float M = wave_max(m);
-    float l = 0.0f;
+    // Lane t holds split t / 4, channel quarter t % 4 (its max, sum and 32
+    // outputs loaded together); splits beyond 64 are read in later passes.
+    const int cq = tid & 3;
+    const int s_first = tid >> 2;
+    float m0 = -INFINITY, l0 = 0.0f;
     float acc[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) acc[i] = 0.0f;
-    for (int sp = lane; sp < a.splits; sp += 64) {
-        const float *pt = base + sp * split_stride;
-        const float ms = pt[0];
-        const float w = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
-        l = __builtin_fmaf(pt[1], w, l);
-        // rows of 130 floats: the outputs are 8-byte aligned
-        const float2 *po = (const float2 *)(pt + 2 + 32 * cq);
+    if (s_first < a.splits) {
+        const float *pt = base + s_first * split_stride;
+        m0 = pt[0];
+        l0 = pt[1];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float2 v = po[i];
-            acc[2 * i] = __builtin_fmaf(v.x, w, acc[2 * i]);
-            acc[2 * i + 1] = __builtin_fmaf(v.y, w, acc[2 * i + 1]);
+        for (int i = 0; i < 32; i += 2) {
+            const float2 v = *(const float2 *)(pt + 2 + 32 * cq + i);
+            acc[i] = v.x;
+            acc[i + 1] = v.y;
         }
     }
-#pragma unroll
-    for (int i = 0; i < 32; ++i) s_acc[i][lane] = acc[i];
-    s_l[lane] = l;
+    float m = m0;
+    for (int s = s_first + kAttnThreads / 4; s < a.splits; s += kAttnThreads / 4)
+        m = fmaxf(m, base[s * split_stride]);
+    m = wave_max(m);
+    if ((tid & 63) == 0) s_red[0][wave] = m;
     __syncthreads();
-    if (lane < 32) {
-        float y = 0.0f, lt = 0.0f;
-#pragma unroll 8
-        for (int k = 0; k < 64; ++k) {
-            y += s_acc[lane][k];
-            lt += s_l[k];
+    const float M = fmaxf(fmaxf(s_red[0][0], s_red[0][1]), fmaxf(s_red[0][2], s_red[0][3]));
+
+    const float w0 = m0 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m0 - M);
+    float l = cq == 0 ? l0 * w0 : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) acc[i] *= w0;
+    for (int s = s_first + kAttnThreads / 4; s < a.splits; s += kAttnThreads / 4) {
+        const float *pt = base + s * split_stride;
+        const float ms = pt[0];
+        const float w = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
+        if (cq == 0) l = __builtin_fmaf(pt[1], w, l);
+#pragma unroll
+        for (int i = 0; i < 32; i += 2) {
+            const float2 v = *(const float2 *)(pt + 2 + 32 * cq + i);
+            acc[i] = __builtin_fmaf(v.x, w, acc[i]);
+            acc[i + 1] = __builtin_fmaf(v.y, w, acc[i + 1]);
         }
+    }
+    l = wave_sum(l);
+    if ((tid & 63) == 0) s_red[1][wave] = l;
+
+#pragma unroll
+    for (int i = 0; i < 32; ++i) s_acc[tid >> 2][cq * 33 + i] = acc[i];
+    __syncthreads();
+    const int c = tid & (kHead - 1), half = tid >> 7;
+    float y = 0.0f;
+    for (int k = half; k < 64; k += 2) y += s_acc[k][(c >> 5) * 33 + (c & 31)];
+    __syncthreads();
+    if (half == 1) s_acc[0][c] = y;
+    __syncthreads();
+    if (half == 0) {
+        y += s_acc[0][c];
+        const float lt = s_red[1][0] + s_red[1][1] + s_red[1][2] + s_red[1][3];
         const float o = lt > 0.0f ? y / lt : 0.0f;
         const int r = h / a.group;
         const int qh = kvh * a.group + h % a.group;
-        const int64_t at = ((int64_t)r * a.n_qh + qh) * kHead + 32 * cq + lane;
+        const int64_t at = ((int64_t)r * a.n_qh + qh) * kHead + c;
         if (a.out_f32)
             ((float *)a.out)[at] = o;
         else
@@ -903,8 +932,8 @@ hipError_t launch_decode(const AttnArgs &a, const DequantTab &tab, hipStream_t s
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(a.n_kvh * a.rows * 4)),
-                       dim3(kCombineThreads), 0, stream, a);
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(a.n_kvh * a.rows)),
+                       dim3(kAttnThreads), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -915,8 +944,8 @@ hipError_t launch_tiles(const AttnArgs &a, const DequantTab &tab, hipStream_t st
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(a.n_kvh * a.rows * 4)),
-                       dim3(kCombineThreads), 0, stream, a);
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(a.n_kvh * a.rows)),
+                       dim3(kAttnThreads), 0, stream, a);
     return hipGetLastError();
 }
 
