@@ -51,6 +51,7 @@ and QK + PV flops per second.
     python bench.py --profile-run      # the codec steps only, for rocprofv3
     python bench.py --attention-only [--attention-case NAME]   # attention calls only
     python bench.py --large-only       # the 23.5 GiB set's three kernels only
+    python bench.py --transfer-only packed|separate   # the codec steps, then one layout's transfer
     python bench.py --copy-probe       # plain 1 GiB copy, PMC scale factor
     python bench.py --hbm-probe        # plain streaming ceilings (torch + csrc/stream_ceiling.hip)
 """
@@ -646,6 +647,7 @@ def main():
     ap.add_argument("--no-large", action="store_true")
     ap.add_argument("--attention-only", action="store_true")
     ap.add_argument("--large-only", action="store_true")
+    ap.add_argument("--transfer-only", choices=["packed", "separate"], default=None)
     ap.add_argument("--attention-calls", type=int, default=50)
     ap.add_argument("--attention-case", default=None,
                     choices=[c[0] for c in ATTENTION_CASES])
@@ -658,7 +660,7 @@ def main():
     if args.copy_probe or args.hbm_probe:
         copy_probe(timed=args.hbm_probe)
         return
-    if args.profile_run:  # the timed steps only (same steps and warm-up)
+    if args.profile_run or args.transfer_only:  # the timed steps only (same steps and warm-up)
         args.no_cpu_baseline = True
 
     import torch
@@ -765,6 +767,12 @@ def main():
                      if dom == "quantize" else None},
         "kernels": kern,
     }
+    if args.transfer_only:  # the codec steps, then one layout's transfer alone
+        kms = {n: kern[n]["ms"] for n in names}
+        layout = lynx.LAYOUT_PACKED if args.transfer_only == "packed" else lynx.LAYOUT_SEPARATE
+        print(json.dumps({"transfer": measure_transfer(torch, lynx, kv, codes, out_a, out_f, kms,
+                                                       layout)}), flush=True)
+        return
     if not args.no_transfer and not args.profile_run:
         kms = {n: kern[n]["ms"] for n in names}
         # the pages' transmission buffer (anchor + scalars per block, one copy
