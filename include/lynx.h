@@ -311,8 +311,11 @@ size_t lynx_attn_workspace_bytes(int t_q, int num_q_heads, int num_kv_heads,
  *   workspace    >= lynx_attn_workspace_bytes(...) bytes of device memory,
  *                overwritten (split partials).
  * Scores, the softmax and the accumulation are binary32 (bf16 x bf16
- * products are exact).  t_q * g must be <= 64; the field widths must be
- * 4 + 4.  Errors as above.
+ * products are exact).  g must be <= 64 and the field widths 4 + 4.  The
+ * kernels take at most 64 query rows (t_q * g) per KV head: a call with
+ * more query tokens runs in passes of floor(64 / g) tokens (each reading
+ * the codes again), one after the other on `stream`, sharing the workspace,
+ * whose size is that of the first pass.  Errors as above.
  */
 int lynx_decode_attn_dequant(const void *q, int t_q, int num_q_heads,
                              const uint8_t *k_anchor, const uint8_t *k_residual,

@@ -384,8 +384,14 @@ int dequant_common(const uint8_t *anchor, const uint8_t *residual, lynx_meta met
 // workspace of their partials.  Up to 16 rows the decode kernel takes runs
 // of 32-token chunks (a multiple of its 8 waves), beyond that the tile
 // kernel runs of 128-token steps.
+// Launch plan of one attention pass.  The kernels take at most 64 query
+// rows (t_q * g) per KV head; more query tokens go through the kernels in
+// passes of tq_pass = floor(64 / g) tokens, one after the other on the
+// stream, each over the whole context.  The plan below is that of a pass of
+// t_q tokens (the first, largest pass when called with the call's t_q: its
+// workspace serves every pass).
 struct AttnPlan {
-    int rows, pages, splits, sps, cps;
+    int tq_pass, rows, pages, splits, sps, cps;
     size_t ws_bytes;
 };
 
@@ -394,9 +400,11 @@ int attn_plan(int t_q, int n_qh, int n_kvh, int64_t ctx, AttnPlan *pl) {
         return LYNX_EINVAL;
     if (ctx % kPage || ctx / kPage > INT32_MAX)
         return LYNX_ESHAPE;
-    const int64_t rows = (int64_t)t_q * (n_qh / n_kvh);
-    if (rows > 64)
+    const int group = n_qh / n_kvh;
+    if (group > 64)
         return LYNX_EINVAL;
+    pl->tq_pass = t_q < 64 / group ? t_q : 64 / group;
+    const int64_t rows = (int64_t)pl->tq_pass * group;
     pl->rows = (int)rows;
     pl->pages = (int)(ctx / kPage);
     const int64_t target_wgs = 512;
@@ -700,15 +708,30 @@ int attn_common(const void *q, int t_q, int num_q_heads, const uint8_t *k_anchor
     a.n_qh = num_q_heads;
     a.n_kvh = num_kv_heads;
     a.group = num_q_heads / num_kv_heads;
-    a.t_q = t_q;
-    a.rows = pl.rows;
     a.pages = pl.pages;
-    a.splits = pl.splits;
-    a.steps_per_split = pl.sps;
-    a.chunks_per_split = pl.cps;
     a.causal = causal_tail ? 1 : 0;
     a.qk_scale_log2 = (float)((double)scale * 1.4426950408889634);
-    return hip_status(launch_attention(a, tab, stream));
+    // Passes of at most tq_pass query tokens; token r of the call sees keys
+    // 0 .. ctx_len - t_q + r under the causal tail.
+    const size_t out_elem = a.out_f32 ? sizeof(float) : sizeof(uint16_t);
+    for (int tok0 = 0; tok0 < t_q; tok0 += pl.tq_pass) {
+        const int n = t_q - tok0 < pl.tq_pass ? t_q - tok0 : pl.tq_pass;
+        AttnPlan pp;
+        if ((rc = attn_plan(n, num_q_heads, num_kv_heads, ctx_len, &pp)))
+            return rc;
+        const int64_t row0 = (int64_t)tok0 * num_q_heads * kHead;  // elements of q / out
+        a.q = (const uint16_t *)q + row0;
+        a.out = (char *)out + row0 * out_elem;
+        a.t_q = n;
+        a.causal_base = ctx_len - t_q + tok0;
+        a.rows = pp.rows;
+        a.splits = pp.splits;
+        a.steps_per_split = pp.sps;
+        a.chunks_per_split = pp.cps;
+        if ((rc = hip_status(launch_attention(a, tab, stream))))
+            return rc;
+    }
+    return LYNX_OK;
 }
 
 }  // namespace

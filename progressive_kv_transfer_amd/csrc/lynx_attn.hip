@@ -300,7 +300,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(AttnArgs 
     }
     // Last visible position of this lane's row.
     const int64_t limit =
-        a.causal ? a.ctx - a.t_q + (live ? h / a.group : a.t_q - 1) : a.ctx - 1;
+        a.causal ? a.causal_base + (live ? h / a.group : a.t_q - 1) : a.ctx - 1;
     const float cs = a.qk_scale_log2;
     const float lazy = kLazyLog2 / cs;
 
@@ -337,7 +337,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(AttnArgs 
         step_sync<RT>();
 
         const int64_t tok0 = (int64_t)st * kStep;
-        const bool need_mask = tok0 + kStep - 1 > a.ctx - a.t_q;  // uniform
+        const bool need_mask = tok0 + kStep - 1 > a.causal_base;  // uniform
 #pragma unroll
         for (int ci = 0; ci < RT; ++ci) {
             const int c = wave / RT + kWavesPerTile * ci;
@@ -641,7 +641,7 @@ attn_decode_kernel(AttnArgs a, const DequantTab tab) {
         }
     }
     const int64_t limit =
-        a.causal ? a.ctx - a.t_q + (live ? h / a.group : a.t_q - 1) : a.ctx - 1;
+        a.causal ? a.causal_base + (live ? h / a.group : a.t_q - 1) : a.ctx - 1;
     const float cs = a.qk_scale_log2;
     const float lazy = kLazyLog2 / cs;
 
@@ -710,7 +710,7 @@ attn_decode_kernel(AttnArgs a, const DequantTab tab) {
         if constexpr (KF && VF)  // both full: V codes after the scores (registers)
             dec_load_v<KF, VF>(a, b, j, lane, cd);
         const int64_t tok0 = c * kChunk;
-        if (tok0 + kChunk - 1 > a.ctx - a.t_q) {  // uniform
+        if (tok0 + kChunk - 1 > a.causal_base) {  // uniform
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll

@@ -28,8 +28,11 @@ constexpr int code_max_of(int a, int b) {
 }
 constexpr int kMaxBuckets = 1792;  // 7 KiB of SH16 table words in LDS and in the kernel argument
 
-// Compander tables, built once per (alpha, code_scale) on the host and
-// passed by value as a kernel argument.
+// Compander tables, built once per (alpha, code_scale, field widths) on the
+// host and passed by value as a kernel argument: 9.5 KB, within the kernel
+// argument size HIP passes on gfx950 (12 KB launches checked with ROCm 7;
+// a runtime that refused it would fail the launch with an error, not
+// change a code).
 //
 // thr[k] (k = 1..120) is the smallest binary32 x >= 0 whose Eq. (3) value
 // Y(x) reaches k - 1/2, i.e. the code of |x| is #{k : |x| >= thr[k]};
@@ -106,6 +109,7 @@ struct AttnArgs {
     int64_t astride, gstride, cstride;  // per-block strides of K and V codes
     void *out;      // [t_q][n_qh][128], bf16 or binary32
     int64_t ctx;    // context tokens (multiple of 256)
+    int64_t causal_base;  // causal tail: the last key query token 0 of the launch sees
     int n_qh, n_kvh, group, t_q;
     int rows;       // t_q * group
     int pages, splits;

@@ -206,8 +206,14 @@ def test_attention_workspace_sizes():
     assert ws(5, 8, 4, 1024) == 4 * per(4, 10)
     # 17 rows and more: the tile kernel's steps, one per split
     assert ws(3, 24, 4, 1024) == 8 * per(4, 18)
+    # more than 64 rows per KV head: passes of floor(64 / g) query tokens,
+    # the workspace of the first (largest) pass serves them all
+    assert ws(9, 64, 8, 32768) == ws(8, 64, 8, 32768) == 64 * per(8, 64)  # 72 rows: 64 + 8
+    assert ws(64, 64, 8, 131072) == ws(8, 64, 8, 131072)                  # 8 passes of 64
+    assert ws(5, 32, 2, 1024) == ws(4, 32, 2, 1024)                       # g = 16: 64 + 16
+    assert ws(1, 64, 1, 1024) == 8 * per(1, 64)                           # g = 64: one row a token
     # invalid plans report 0
-    assert ws(9, 64, 8, 32768) == 0      # 72 rows per KV head
+    assert ws(1, 130, 2, 1024) == 0      # 65 query heads per KV head
     assert ws(1, 6, 4, 1024) == 0        # not grouped-query
     assert ws(1, 8, 8, 1000) == 0        # context not whole pages
     assert ws(0, 8, 8, 1024) == 0
@@ -229,8 +235,8 @@ def test_attention_argument_errors(case, expect):
         q = None
     elif case == "group":
         nqh = 7
-    elif case == "rows":
-        t_q = 17
+    elif case == "rows":  # a group of more than 64 query heads per KV head
+        nqh, nkvh = 130, 2
     elif case == "ctx":
         ctx = 1000
     elif case == "head_dim":
@@ -305,7 +311,7 @@ def test_noalloc_attention_refuses_beyond_its_scratch():
     rc = L.lynx_decode_attn_dequant_noalloc(*args(8, 8192, 1024, 256))
     assert rc == -4 and "scratch" in L.lynx_status_string(rc).decode()
     assert L.lynx_decode_attn_dequant_noalloc(*args(1, 64, 8, 300)) == -2
-    assert L.lynx_decode_attn_dequant_noalloc(*args(9, 64, 8, 256)) == -1  # 72 rows
+    assert L.lynx_decode_attn_dequant_noalloc(*args(1, 130, 2, 256)) == -1  # g = 65
     a = list(args(1, 64, 8, 256))
     a[15] = None  # out
     assert L.lynx_decode_attn_dequant_noalloc(*a) == -1

@@ -109,6 +109,22 @@ def test_decode_kernel_group_16_one_head():
     run_case(kv, q, 1, 1, False, False, False)
 
 
+@pytest.mark.parametrize("t_q,n_qh,n_kvh,ctx,full", [
+    (9, 16, 2, 2048, True),    # g = 8, 72 rows: 8 tokens (tile kernel) + 1 (decode kernel)
+    (9, 16, 2, 2048, False),
+    (5, 16, 1, 1024, True),    # g = 16, 80 rows: 4 tokens + 1 token of 16 rows
+    (20, 8, 2, 1280, True)])   # g = 4, 80 rows: 16 tokens + 4 tokens
+def test_more_than_64_rows(t_q, n_qh, n_kvh, ctx, full):
+    """Query tokens beyond 64 rows per KV head run in passes of floor(64 / g)
+    tokens, each with its own causal offset: every row against the oracle."""
+    announce(f"passes t_q={t_q} n_qh={n_qh} n_kvh={n_kvh} ctx={ctx} full={full}")
+    kv = torch.stack([kvgen.kv_tensor(750 + i, ctx, 128 * n_kvh, [3], True, DEV)
+                      for i in range(2)])
+    q = kvgen.queries(751, t_q, n_qh, device=DEV)
+    got, ref = run_case(kv, q, n_kvh, t_q, full, full, True)
+    assert not np.allclose(ref[0], ref[t_q - 1])
+
+
 def test_attention_argument_errors():
     # two tensors of 256 tokens x 2 KV heads: 2 page blocks each
     kv = torch.stack([kvgen.kv_tensor(730 + i, 256, 256, [], True, DEV) for i in range(2)])
