@@ -827,101 +827,82 @@ attn_decode_kernel(AttnArgs a, const DequantTab tab) {
 
 }
 
-// Sum / max over the 64 lanes of a wave.
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int d = 32; d > 0; d >>= 1) x = fmaxf(x, __shfl_xor(x, d, 64));
-    return x;
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int d = 32; d > 0; d >>= 1) x += __shfl_xor(x, d, 64);
-    return x;
-}
-
-// One workgroup of 256 lanes per (kv head, live row) merges the split
-// partials: the maximum M over the splits, then lane t takes the items
-// (split s, channel quarter t % 4) for s = t / 4, t / 4 + 64, ... (up to 64
-// splits this is a single round of loads), weights them by 2^(m_s - M), and
-// the 64 lanes of each quarter are summed through LDS.
+// One workgroup of 256 lanes per (KV head, live row) merges the split
+// partials in one pass: wave w takes the splits w, w + 4, ... (8 at a time,
+// all their loads issued together; a split's max and sum are wave-uniform
+// loads), lane l channel pair l of them, with a running maximum per wave;
+// the 4 waves then meet once in LDS, where 64 lanes rescale and add their
+// (max, sum, pair) results and write the row.
 __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(AttnArgs a) {
-    __shared__ float s_red[2][kAttnThreads / 64];
-    __shared__ float s_acc[64][4 * 33];
+    constexpr int kW = kAttnThreads / 64;
+    constexpr int kU = 8;
+    __shared__ float4 s_part[kW][64];  // pair sums (2), row sum, wave max
     const int wg = (int)__builtin_amdgcn_workgroup_id_x();
     const int kvh = wg % a.n_kvh;
     const int h = wg / a.n_kvh;
     const int tid = (int)__builtin_amdgcn_workitem_id_x();
-    const int wave = tid >> 6;
-    const int64_t split_stride = (int64_t)a.n_kvh * a.rows * kPartial;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int64_t ss = (int64_t)a.n_kvh * a.rows * kPartial;
     const float *base = a.ws + ((int64_t)kvh * a.rows + h) * kPartial;
 
-    // Lane t holds split t / 4, channel quarter t % 4 (its max, sum and 32
-    // outputs loaded together); splits beyond 64 are read in later passes.
-    const int cq = tid & 3;
-    const int s_first = tid >> 2;
-    float m0 = -INFINITY, l0 = 0.0f;
-    float acc[32];
+    float mw = -INFINITY, l = 0.0f;
+    float2 acc = make_float2(0.0f, 0.0f);
+    for (int s0 = wave; s0 < a.splits; s0 += kW * kU) {
+        float ms[kU], ls[kU];
+        float2 v[kU];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) acc[i] = 0.0f;
-    if (s_first < a.splits) {
-        const float *pt = base + s_first * split_stride;
-        m0 = pt[0];
-        l0 = pt[1];
-#pragma unroll
-        for (int i = 0; i < 32; i += 2) {
-            const float2 v = *(const float2 *)(pt + 2 + 32 * cq + i);
-            acc[i] = v.x;
-            acc[i + 1] = v.y;
+        for (int u = 0; u < kU; ++u) {  // splits past the end re-read the last one, weight 0
+            const int sp = min(s0 + kW * u, a.splits - 1);
+            const float *pt = base + sp * ss;
+            ms[u] = pt[0];
+            ls[u] = pt[1];
+            v[u] = *(const float2 *)(pt + 2 + 2 * lane);
         }
-    }
-    float m = m0;
-    for (int s = s_first + kAttnThreads / 4; s < a.splits; s += kAttnThreads / 4)
-        m = fmaxf(m, base[s * split_stride]);
-    m = wave_max(m);
-    if ((tid & 63) == 0) s_red[0][wave] = m;
-    __syncthreads();
-    const float M = fmaxf(fmaxf(s_red[0][0], s_red[0][1]), fmaxf(s_red[0][2], s_red[0][3]));
-
-    const float w0 = m0 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m0 - M);
-    float l = cq == 0 ? l0 * w0 : 0.0f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) acc[i] *= w0;
-    for (int s = s_first + kAttnThreads / 4; s < a.splits; s += kAttnThreads / 4) {
-        const float *pt = base + s * split_stride;
-        const float ms = pt[0];
-        const float w = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
-        if (cq == 0) l = __builtin_fmaf(pt[1], w, l);
+        for (int u = 0; u < kU; ++u)
+            if (s0 + kW * u >= a.splits)
+                ms[u] = -INFINITY;
+        float mn = mw;
 #pragma unroll
-        for (int i = 0; i < 32; i += 2) {
-            const float2 v = *(const float2 *)(pt + 2 + 32 * cq + i);
-            acc[i] = __builtin_fmaf(v.x, w, acc[i]);
-            acc[i + 1] = __builtin_fmaf(v.y, w, acc[i + 1]);
+        for (int u = 0; u < kU; ++u) mn = fmaxf(mn, ms[u]);
+        const float c = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - mn);
+        l *= c;
+        acc.x *= c;
+        acc.y *= c;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const float w = ms[u] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms[u] - mn);
+            l = __builtin_fmaf(ls[u], w, l);
+            acc.x = __builtin_fmaf(v[u].x, w, acc.x);
+            acc.y = __builtin_fmaf(v[u].y, w, acc.y);
         }
+        mw = mn;
     }
-    l = wave_sum(l);
-    if ((tid & 63) == 0) s_red[1][wave] = l;
-
+    s_part[wave][lane] = make_float4(acc.x, acc.y, l, mw);
+    __syncthreads();
+    if (tid < 64) {
+        float M = s_part[0][lane].w;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) s_acc[tid >> 2][cq * 33 + i] = acc[i];
-    __syncthreads();
-    const int c = tid & (kHead - 1), half = tid >> 7;
-    float y = 0.0f;
-    for (int k = half; k < 64; k += 2) y += s_acc[k][(c >> 5) * 33 + (c & 31)];
-    __syncthreads();
-    if (half == 1) s_acc[0][c] = y;
-    __syncthreads();
-    if (half == 0) {
-        y += s_acc[0][c];
-        const float lt = s_red[1][0] + s_red[1][1] + s_red[1][2] + s_red[1][3];
-        const float o = lt > 0.0f ? y / lt : 0.0f;
+        for (int k = 1; k < kW; ++k) M = fmaxf(M, s_part[k][lane].w);
+        float y0 = 0.0f, y1 = 0.0f, lt = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kW; ++k) {
+            const float4 t = s_part[k][lane];
+            const float w = t.w == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(t.w - M);
+            y0 = __builtin_fmaf(t.x, w, y0);
+            y1 = __builtin_fmaf(t.y, w, y1);
+            lt = __builtin_fmaf(t.z, w, lt);
+        }
+        const float o0 = lt > 0.0f ? y0 / lt : 0.0f;
+        const float o1 = lt > 0.0f ? y1 / lt : 0.0f;
         const int r = h / a.group;
         const int qh = kvh * a.group + h % a.group;
-        const int64_t at = ((int64_t)r * a.n_qh + qh) * kHead + c;
+        const int64_t at = ((int64_t)r * a.n_qh + qh) * kHead + 2 * lane;
         if (a.out_f32)
-            ((float *)a.out)[at] = o;
+            *(float2 *)((float *)a.out + at) = make_float2(o0, o1);
         else
-            ((uint16_t *)a.out)[at] = (uint16_t)(pack_bf16(o, 0.0f) & 0xffffu);
+            *(uint32_t *)((uint16_t *)a.out + at) = pack_bf16(o0, o1);
     }
 }
 
