@@ -14,6 +14,7 @@
 #include <utility>
 #include <vector>
 
+#include "lynx_attn_args.h"
 #include "lynx_internal.h"
 
 namespace lynx {

@@ -33,6 +33,7 @@
 // split in the workspace; attn_combine_kernel merges the splits.
 #include <mutex>
 
+#include "lynx_attn_args.h"
 #include "lynx_recon.h"
 
 namespace lynx {

@@ -22,7 +22,7 @@
 //                         sums), then the token inside the run.
 // Ratios and sums are binary64, so a decision can only differ from a
 // sequential evaluation within ~1e-15 of its threshold.
-#include "lynx_internal.h"
+#include "lynx_attn_args.h"
 
 namespace lynx {
 namespace {
