@@ -560,6 +560,7 @@ def measure_large(torch, kvgen, lynx, reps: int = 10):
 
 TRANSFER_OBJECT_BLOCKS = 4096  # 256 MiB of bf16 KV per transfer object (16 objects)
 TRANSFER_REPS = 9              # alternating link-only / pipeline runs (medians reported)
+TRANSFER_RESERVED_CUS = 16     # compute units the codec streams leave to copy kernels
 
 
 def measure_transfer(torch, lynx, kv, codes, out_a, out_f, kern_ms, layout):
@@ -568,7 +569,9 @@ def measure_transfer(torch, lynx, kv, codes, out_a, out_f, kern_ms, layout):
     two link streams, rebuild from anchor, refine).  layout: the code
     layout (packed = the pages' transmission buffer, one copy per hop for an
     object's anchor + metadata; separate = stream and four metadata arrays,
-    five copies)."""
+    five copies).  The sender and receiver run on codec streams that leave
+    TRANSFER_RESERVED_CUS compute units to the runtime's copy kernels; the
+    same measurement on four plain streams is reported beside it."""
     shape = lynx.shape_of(kv)
     nb = lynx.num_blocks(shape)
     p = lynx.params(layout=layout)
@@ -576,7 +579,13 @@ def measure_transfer(torch, lynx, kv, codes, out_a, out_f, kern_ms, layout):
         codes = lynx.quantize_pages(kv, p)
     rx = lynx.alloc_codes(nb, "cuda", layout=layout)
     wire = lynx.alloc_codes(nb, "cpu", pin_memory=True, layout=layout)
-    streams = tuple(torch.cuda.Stream() for _ in range(4))
+    # Sender and receiver: codec streams leaving TRANSFER_RESERVED_CUS compute
+    # units to the runtime's device-to-host copy kernels; the same run with
+    # four plain streams follows for comparison.
+    sender, receiver = lynx.CodecStream(TRANSFER_RESERVED_CUS), lynx.CodecStream(
+        TRANSFER_RESERVED_CUS)
+    streams = (sender.stream, torch.cuda.Stream(), torch.cuda.Stream(), receiver.stream)
+    plain = tuple(torch.cuda.Stream() for _ in range(4))
     # Raw PCIe rates of one 1 GiB pinned copy each way (the link's floor).
     pcie = {}
     for name, src, dst in (("d2h", codes.residual, wire.residual),
@@ -590,23 +599,38 @@ def measure_transfer(torch, lynx, kv, codes, out_a, out_f, kern_ms, layout):
         streams[1].synchronize()
         pcie[name] = src.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
     ob = TRANSFER_OBJECT_BLOCKS
-    lynx.split_stream_transfer(None, shape, ob, codes, wire, rx, copies_only=True, p=p,
-                               streams=streams)  # warm-up
-    # Pinned copies of ~90 ms vary by a few ms from run to run, more than the
-    # codec time whose hiding is measured: alternate link-only and pipeline
-    # runs and take the median of each time.
-    links, pipes = [], []
-    for _ in range(TRANSFER_REPS):
-        links.append(lynx.split_stream_transfer(None, shape, ob, codes, wire, rx,
-                                                copies_only=True, p=p, streams=streams))
-        pipes.append(lynx.split_stream_transfer(kv, shape, ob, codes, wire, rx, out_a, out_f,
-                                                p=p, streams=streams))
-    link = {k: statistics.median(r[k] for r in links) for k in links[0]}
-    pipe = {k: statistics.median(r[k] for r in pipes) for k in pipes[0]}
+    codec_ms = kern_ms["quantize"] + kern_ms["dequant_anchor"]
+
+    def runs(sts):
+        lynx.split_stream_transfer(None, shape, ob, codes, wire, rx, copies_only=True, p=p,
+                                   streams=sts)  # warm-up
+        # Pinned copies of ~90 ms vary by a few ms from run to run, more than
+        # the codec time whose hiding is measured: alternate link-only and
+        # pipeline runs and take the median of each time.
+        links, pipes = [], []
+        for _ in range(TRANSFER_REPS):
+            links.append(lynx.split_stream_transfer(None, shape, ob, codes, wire, rx,
+                                                    copies_only=True, p=p, streams=sts))
+            pipes.append(lynx.split_stream_transfer(kv, shape, ob, codes, wire, rx, out_a,
+                                                    out_f, p=p, streams=sts))
+        link = {k: statistics.median(r[k] for r in links) for k in links[0]}
+        pipe = {k: statistics.median(r[k] for r in pipes) for k in pipes[0]}
+        return links, pipes, link, pipe
+
+    def hidden(exposed_ms):
+        # share of quantize + anchor rebuild time that does not show up after
+        # the link (1 when the pipeline is no slower than the link)
+        return round(min(1.0, max(0.0, 1.0 - max(exposed_ms, 0.0) / codec_ms)), 4)
+
+    links, pipes, link, pipe = runs(streams)
+    _, _, link_p, pipe_p = runs(plain)
+    sender.close()
+    receiver.close()
     anchor_bytes = nb * (16384 + 9216)
     residual_bytes = nb * 16384
     serial_anchor = kern_ms["quantize"] + link["anchor_arrived"] + kern_ms["dequant_anchor"]
     exposed = pipe["anchor_ready"] - link["anchor_arrived"]
+    exposed_p = pipe_p["anchor_ready"] - link_p["anchor_arrived"]
     del rx, wire
     return {
         "workload": WORKLOAD, "object_blocks": ob, "objects": -(-nb // ob),
@@ -624,11 +648,14 @@ def measure_transfer(torch, lynx, kv, codes, out_a, out_f, kern_ms, layout):
                                  "pipeline": [round(r["anchor_ready"], 2) for r in pipes]},
         "link_anchor_GBps": round(anchor_bytes / (link["anchor_arrived"] * 1e-3) / 1e9, 2),
         "serial_anchor_ready_ms": round(serial_anchor, 3),
+        "codec_streams_reserved_cus": TRANSFER_RESERVED_CUS,
         "exposed_anchor_overhead_ms": round(exposed, 3),
-        # share of quantize + anchor rebuild time that does not show up
-        # after the link (1 when the pipeline is no slower than the link)
-        "hidden_fraction_of_codec_time": round(min(1.0, max(0.0, 1.0 - max(exposed, 0.0) / (
-            kern_ms["quantize"] + kern_ms["dequant_anchor"]))), 4),
+        "hidden_fraction_of_codec_time": hidden(exposed),
+        "plain_streams": {"link_anchor_arrived_ms": round(link_p["anchor_arrived"], 3),
+                          "pipeline_anchor_ready_ms": round(pipe_p["anchor_ready"], 3),
+                          "pipeline_full_ready_ms": round(pipe_p["full_ready"], 3),
+                          "exposed_anchor_overhead_ms": round(exposed_p, 3),
+                          "hidden_fraction_of_codec_time": hidden(exposed_p)},
     }
 
 

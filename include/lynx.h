@@ -424,6 +424,25 @@ int lynx_split_stream_transfer(const void *kv, const lynx_kv_shape *shape,
                                hipStream_t link_in, hipStream_t receiver,
                                lynx_transfer_times *times);
 
+/*
+ * A stream for the codec kernels of a transfer (the sender and receiver
+ * streams of lynx_split_stream_transfer) that leaves reserved_cus compute
+ * units of the current device to other work: its kernels run only on the
+ * remaining units (a CU mask; the reserved units are spread evenly over the
+ * unit numbering, so over the XCDs).  The runtime runs most device-to-
+ * pinned-host copies as shader copy kernels; on streams without such a
+ * reserve those kernels wait until the quantize or rebuild kernels' own
+ * workgroups drain, which stalls the link by up to a kernel's duration per
+ * object.  reserved_cus = 0 gives a plain stream.  The stream is a blocking
+ * stream (ordered with the NULL stream, as hipStreamCreate's) of the
+ * current device; release it with lynx_stream_destroy.
+ *   reserved_cus  0 .. (compute units of the device) - 1, else LYNX_EINVAL;
+ *   stream        out: the new stream (NULL: LYNX_EINVAL).
+ * Host only; LYNX_EHIP if the runtime refuses the stream.
+ */
+int lynx_codec_stream_create(int reserved_cus, hipStream_t *stream);
+int lynx_stream_destroy(hipStream_t stream);
+
 /* Workspace bytes of lynx_spec_verify (0 for invalid sizes).  Host only. */
 size_t lynx_spec_verify_workspace_bytes(int t_draft, int vocab);
 

@@ -776,6 +776,40 @@ int lynx_block_stats(const void *kv, const lynx_kv_shape *shape, const lynx_para
                            (float *)gamma_scale, mu, sigma, kModeBlockStats, stream);
 }
 
+int lynx_codec_stream_create(int reserved_cus, hipStream_t *stream) {
+    if (!stream || reserved_cus < 0)
+        return LYNX_EINVAL;
+    *stream = nullptr;
+    int dev = 0, ncu = 0;
+    int rc = hip_status(hipGetDevice(&dev));
+    if (rc)
+        return rc;
+    if ((rc = hip_status(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev))))
+        return rc;
+    if (reserved_cus >= ncu)
+        return LYNX_EINVAL;
+    if (reserved_cus == 0)
+        return hip_status(hipStreamCreate(stream));
+    // Unit u is reserved when it is the last of its share: u = floor((k + 1)
+    // ncu / reserved_cus) - 1 for k = 0 .. reserved_cus - 1.
+    std::vector<uint32_t> mask((size_t)(ncu + 31) / 32, 0u);
+    for (int u = 0, k = 0; u < ncu; ++u) {
+        const bool reserved = k < reserved_cus &&
+                              u == (int)((int64_t)(k + 1) * ncu / reserved_cus) - 1;
+        if (reserved)
+            ++k;
+        else
+            mask[(size_t)u / 32] |= 1u << (u % 32);
+    }
+    return hip_status(hipExtStreamCreateWithCUMask(stream, (uint32_t)mask.size(), mask.data()));
+}
+
+int lynx_stream_destroy(hipStream_t stream) {
+    if (!stream)
+        return LYNX_EINVAL;
+    return hip_status(hipStreamDestroy(stream));
+}
+
 int lynx_split_stream_transfer(const void *kv, const lynx_kv_shape *shape,
                                const lynx_params *params, int64_t object_blocks, lynx_codes tx,
                                lynx_codes wire, lynx_codes rx, void *kv_anchor, void *kv_full,

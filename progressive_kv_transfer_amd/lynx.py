@@ -73,8 +73,8 @@ EXPORTS = ["lynx_default_params", "lynx_num_blocks", "lynx_stream_bytes",
            "lynx_dequant_full", "lynx_page_stats", "lynx_block_stats",
            "lynx_attn_workspace_bytes", "lynx_decode_attn_dequant",
            "lynx_decode_attn_dequant_noalloc",
-           "lynx_split_stream_transfer", "lynx_spec_verify_workspace_bytes",
-           "lynx_spec_verify"]
+           "lynx_split_stream_transfer", "lynx_codec_stream_create", "lynx_stream_destroy",
+           "lynx_spec_verify_workspace_bytes", "lynx_spec_verify"]
 
 _lib = None
 
@@ -128,6 +128,8 @@ def lib():
         L.lynx_split_stream_transfer.argtypes = [vp, P(lynx_kv_shape), P(lynx_params), i64,
                                                  lynx_codes, lynx_codes, lynx_codes, vp, vp,
                                                  i32, vp, vp, vp, vp, P(lynx_transfer_times)]
+        L.lynx_codec_stream_create.argtypes = [i32, P(vp)]
+        L.lynx_stream_destroy.argtypes = [vp]
         L.lynx_spec_verify_workspace_bytes.argtypes = [i32, i32]
         L.lynx_spec_verify_workspace_bytes.restype = ctypes.c_size_t
         L.lynx_spec_verify.argtypes = [vp, vp, vp, vp, ctypes.c_double, i32, i32, vp, vp,
@@ -135,7 +137,8 @@ def lib():
         for f in ("lynx_quantize_pages", "lynx_dequant_anchor", "lynx_dequant_full",
                   "lynx_page_stats", "lynx_block_stats", "lynx_decode_attn_dequant",
                   "lynx_decode_attn_dequant_noalloc",
-                  "lynx_split_stream_transfer", "lynx_spec_verify"):
+                  "lynx_split_stream_transfer", "lynx_spec_verify",
+                  "lynx_codec_stream_create", "lynx_stream_destroy"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -565,6 +568,34 @@ def decode_attn_dequant_noalloc(q: torch.Tensor, k: CodeView, v: CodeView, ctx_l
         v.meta(), ctx_len, num_kv_heads, hd, scale, int(causal_tail),
         ctypes.byref(p) if p else None, out.data_ptr(), code, _stream(stream)))
     return out
+
+
+class CodecStream:
+    """lynx_codec_stream_create: a stream of the current device whose kernels
+    leave `reserved_cus` compute units free (for the runtime's copy kernels
+    during a transfer); `.stream` is the torch view of it.  Destroyed by
+    close() or when the object goes away (after the caller has synchronized
+    it)."""
+
+    def __init__(self, reserved_cus: int = 16):
+        h = ctypes.c_void_p()
+        _check("lynx_codec_stream_create",
+               lib().lynx_codec_stream_create(int(reserved_cus), ctypes.byref(h)))
+        self.handle = h.value
+        self.reserved_cus = int(reserved_cus)
+        self.stream = torch.cuda.ExternalStream(self.handle)
+
+    def close(self):
+        if self.handle:
+            self.stream.synchronize()
+            h, self.handle = self.handle, None
+            _check("lynx_stream_destroy", lib().lynx_stream_destroy(h))
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def split_stream_transfer(kv: torch.Tensor | None, shape: lynx_kv_shape, object_blocks: int,

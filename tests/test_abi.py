@@ -503,3 +503,14 @@ def test_table_cache_is_bounded_and_stable():
     for a in (10.0, 10.0 + 7.25 * 149):
         assert np.array_equal(seen[a].view(np.uint32),
                               lynx.compander_thresholds(lynx.params(alpha=a)).view(np.uint32))
+
+
+def test_codec_stream_argument_errors():
+    """lynx_codec_stream_create / lynx_stream_destroy refuse a NULL output,
+    a negative reserve and a NULL stream before any HIP call."""
+    L = lynx.lib()
+    h = ctypes.c_void_p()
+    assert L.lynx_codec_stream_create(16, None) == -1
+    assert L.lynx_codec_stream_create(-1, ctypes.byref(h)) == -1
+    assert h.value is None
+    assert L.lynx_stream_destroy(None) == -1

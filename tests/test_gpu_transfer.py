@@ -99,3 +99,37 @@ def test_transfer_copies_only():
     for where, c in (("wire", wire), ("rx", rx)):
         assert_codes_match_oracle(c, ref, where)
     assert times["quantized"] >= 0.0 and times["full_ready"] >= times["residual_arrived"] - 1e-3
+
+
+@pytest.mark.parametrize("reserved", [8, 16, 0])
+def test_transfer_on_codec_streams_matches_oracle(kv_set, reserved):
+    """Sender and receiver on lynx_codec_stream_create streams (kernels kept
+    off `reserved` compute units; 0 = a plain stream): the codes on every hop
+    and both rebuilds still equal the oracle's."""
+    kv, (ref, ra, rf) = kv_set
+    announce(f"transfer on codec streams reserved={reserved}")
+    shape = lynx.shape_of(kv)
+    nb = lynx.num_blocks(shape)
+    tx, rx = lynx.alloc_codes(nb, DEV), lynx.alloc_codes(nb, DEV)
+    wire = lynx.alloc_codes(nb, "cpu", pin_memory=True)
+    out_a = torch.full_like(kv, 7.0)
+    out_f = torch.full_like(kv, 7.0)
+    sender, receiver = lynx.CodecStream(reserved), lynx.CodecStream(reserved)
+    torch.cuda.synchronize()
+    streams = (sender.stream, torch.cuda.Stream(), torch.cuda.Stream(), receiver.stream)
+    lynx.split_stream_transfer(kv, shape, 7, tx, wire, rx, out_a, out_f, streams=streams)
+    sender.close()
+    receiver.close()
+    for where, c in (("tx", tx), ("wire", wire), ("rx", rx)):
+        assert_codes_match_oracle(c, ref, where)
+    np.testing.assert_array_equal(kvgen.bf16_bits(out_a), ra)
+    np.testing.assert_array_equal(kvgen.bf16_bits(out_f), rf)
+
+
+def test_codec_stream_errors():
+    """A reserve of every compute unit (or more) and a negative reserve are
+    refused before any stream is made."""
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    for bad in (ncu, ncu + 5, -1):
+        with pytest.raises(lynx.LynxError):
+            lynx.CodecStream(bad)
