@@ -12,6 +12,17 @@
 // (w % 8) * (tiles / 8) + w / 8 and each XCD streams one contiguous eighth).
 // Each direction moves at most 4 GiB, far above the 256 MB last-level cache.
 // Output: one JSON object per line and variant, then one "best" line per mix.
+//
+// Page-block patterns (the quantize kernel's access shape without its
+// arithmetic): one 512-lane workgroup per page block of 256 rows x 256 bytes
+// at a 2 KiB row pitch (8 blocks side by side, as 8 KV heads), 16 bytes per
+// lane (16 lanes per row, 8 loads per lane), then 40 KiB of writes:
+//   early stores   each store depends on two of the lane's own loads, so
+//                  stores go out while later loads are still in flight;
+//   stores after   every store waits for all of the block's loads (a
+//   all loads      block-wide statistic through LDS first, as the page
+//                  minimum / maximum of Algorithm 1 forces).
+// Workgroups in XCD-contiguous order; 4 GiB of blocks.
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -78,6 +89,70 @@ __global__ __launch_bounds__(kLanes) void tile_kernel(const u32x4 *__restrict__ 
         if (x.x == 0x12345678u)
             b[base] = x;
     }
+}
+
+constexpr unsigned kBlockLanes = 512;
+constexpr unsigned kBlocks = 65536;  // 4 GiB of 64 KiB page blocks
+
+template <bool AFTER>  // stores after all of the block's loads
+__global__ __launch_bounds__(kBlockLanes) void block_kernel(const u32x4 *__restrict__ a,
+                                                            u32x4 *__restrict__ b) {
+    __shared__ unsigned s_x[kBlockLanes];
+    const unsigned tid = threadIdx.x;
+    const unsigned q = kBlocks / 8;
+    const size_t blk = (size_t)(blockIdx.x % 8) * q + blockIdx.x / 8;
+    const size_t page = blk >> 3, head = blk & 7;
+    // 16-byte words: a page is 256 rows x 128 words, a block 16 words of a row
+    const u32x4 *src = a + page * (256 * 128) + head * 16 + (tid >> 4) * 128 + (tid & 15);
+    u32x4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = src[(size_t)i * 32 * 128];
+    unsigned h = 0;
+    if (AFTER) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) h ^= (v[i].x + v[i].y * 3u) ^ (v[i].z * 5u + v[i].w);
+        s_x[tid] = h;
+        __syncthreads();
+        h ^= s_x[tid ^ 64];
+        __syncthreads();
+    }
+    u32x4 *dst = b + blk * 2560 + tid;  // 40 KiB per block
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+        u32x4 x = v[(8 * i) / 5] ^ (v[7 - (8 * i) / 5] * 3u);
+        x.x ^= h;
+        __builtin_nontemporal_store(x, dst + (size_t)i * kBlockLanes);
+    }
+}
+
+template <bool AFTER>
+void run_block(const char *name, const u32x4 *a, u32x4 *b, int reps) {
+    const double bytes = (double)kBlocks * (65536.0 + 40960.0);
+    hipEvent_t e0, e1;
+    CK(hipEventCreate(&e0));
+    CK(hipEventCreate(&e1));
+    block_kernel<AFTER><<<kBlocks, kBlockLanes>>>(a, b);
+    CK(hipGetLastError());
+    CK(hipDeviceSynchronize());
+    float ms_best = 1e30f;
+    for (int rep = 0; rep < 3; ++rep) {
+        CK(hipEventRecord(e0));
+        for (int r = 0; r < reps; ++r)
+            block_kernel<AFTER><<<kBlocks, kBlockLanes>>>(a, b);
+        CK(hipEventRecord(e1));
+        CK(hipEventSynchronize(e1));
+        float ms = 0.0f;
+        CK(hipEventElapsedTime(&ms, e0, e1));
+        if (ms < ms_best)
+            ms_best = ms;
+    }
+    const double gbps = bytes / (ms_best / reps * 1e-3) / 1e9;
+    printf("{\"block\": \"%s\", \"bytes_per_launch\": %.0f, \"GBps\": %.1f, "
+           "\"of_8TBps\": %.4f}\n",
+           name, bytes, gbps, gbps / 8000.0);
+    fflush(stdout);
+    CK(hipEventDestroy(e0));
+    CK(hipEventDestroy(e1));
 }
 
 struct Best {
@@ -169,6 +244,10 @@ int main() {
     run_mix<2, 1>("read 2 : write 1", a, b, reps);
     run_mix<1, 2>("read 1 : write 2", a, b, reps);
     run_mix<1, 3>("read 1 : write 3", a, b, reps);
+    static_assert((size_t)kBlocks * 65536 <= kDirBytes, "page blocks fit the read buffer");
+    static_assert((size_t)kBlocks * 40960 <= kDirBytes, "block writes fit the write buffer");
+    run_block<false>("page blocks, early stores", a, b, reps);
+    run_block<true>("page blocks, stores after all loads", a, b, reps);
     CK(hipFree(a));
     CK(hipFree(b));
     return 0;
