@@ -57,9 +57,19 @@ constexpr int kStep = 128;               // tokens per step (half a page)
 constexpr int kRowDw = 68;               // dwords per LDS row: 64 + 4 pad
 constexpr int kKDw = kStep * kRowDw;     // K^ [128 tokens][128 channels]
 constexpr int kVDw = kHead * kRowDw;     // V^ [128 channel rows][128 tokens]
-constexpr int kPartial = 2 + kHead;      // max, sum, output
 constexpr int kMergeRow = 132;           // floats per row in the LDS merge area
 constexpr float kLazyLog2 = 8.0f;        // move the max only beyond 2^8
+
+// Split partials in the workspace: the 128 outputs of (split, KV head, row)
+// as one 512-byte row (whole cache lines), all of them first, then the
+// (max, sum) pair of each.
+__device__ __forceinline__ float *partial_out(const AttnArgs &a, int64_t split, int kvh, int r) {
+    return a.ws + ((split * a.n_kvh + kvh) * a.rows + r) * kHead;
+}
+__device__ __forceinline__ float *partial_ml(const AttnArgs &a, int64_t split, int kvh, int r) {
+    return a.ws + (int64_t)a.splits * a.n_kvh * a.rows * kHead +
+           ((split * a.n_kvh + kvh) * a.rows + r) * 2;
+}
 
 // Codes and metadata of one tensor for one lane's 32 tokens x channel pair.
 struct LaneCodes {
@@ -419,7 +429,6 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(AttnArgs 
             for (int e = 0; e < 4; ++e) row[4 + v_row_channel(16 * mt + 4 * g + e)] = o[mt][e];
     }
     __syncthreads();
-    float *part = a.ws + ((int64_t)split * a.n_kvh + kvh) * a.rows * kPartial;
     for (int idx = tid; idx < a.rows * kHead; idx += kAttnThreads) {
         const int hr = idx >> 7, ch = idx & (kHead - 1);
         const int t = hr >> 4, rr = hr & 15;
@@ -435,12 +444,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(AttnArgs 
             l = __builtin_fmaf(row[1], w, l);
             acc = __builtin_fmaf(row[4 + ch], w, acc);
         }
-        float *dst = part + hr * kPartial;
-        if (ch == 0) {
-            dst[0] = M;
-            dst[1] = l;
-        }
-        dst[2 + ch] = acc;
+        if (ch == 0)
+            *(float2 *)partial_ml(a, split, kvh, hr) = make_float2(M, l);
+        partial_out(a, split, kvh, hr)[ch] = acc;
     }
 }
 
@@ -804,7 +810,6 @@ attn_decode_kernel(AttnArgs a, const DequantTab tab) {
                 row[4 + 2 * (16 * (mt >> 1) + 4 * g + e) + (mt & 1)] = o[mt][e];
     }
     __syncthreads();
-    float *part = a.ws + ((int64_t)split * a.n_kvh + kvh) * a.rows * kPartial;
     for (int idx = tid; idx < a.rows * kHead; idx += kDecThreads) {
         const int hr = idx >> 7, ch = idx & (kHead - 1);
         float M = -INFINITY;
@@ -818,12 +823,9 @@ attn_decode_kernel(AttnArgs a, const DequantTab tab) {
             l = __builtin_fmaf(row[1], w, l);
             acc = __builtin_fmaf(row[4 + ch], w, acc);
         }
-        float *dst = part + hr * kPartial;
-        if (ch == 0) {
-            dst[0] = M;
-            dst[1] = l;
-        }
-        dst[2 + ch] = acc;
+        if (ch == 0)
+            *(float2 *)partial_ml(a, split, kvh, hr) = make_float2(M, l);
+        partial_out(a, split, kvh, hr)[ch] = acc;
     }
 
 }
@@ -844,8 +846,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(AttnArgs a) 
     const int tid = (int)__builtin_amdgcn_workitem_id_x();
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
-    const int64_t ss = (int64_t)a.n_kvh * a.rows * kPartial;
-    const float *base = a.ws + ((int64_t)kvh * a.rows + h) * kPartial;
+    const int64_t so = (int64_t)a.n_kvh * a.rows * kHead;  // split strides
+    const int64_t sm = (int64_t)a.n_kvh * a.rows * 2;
+    const float *ob = partial_out(a, 0, kvh, h);
+    const float *mb = partial_ml(a, 0, kvh, h);
 
     float mw = -INFINITY, l = 0.0f;
     float2 acc = make_float2(0.0f, 0.0f);
@@ -855,10 +859,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(AttnArgs a) 
 #pragma unroll
         for (int u = 0; u < kU; ++u) {  // splits past the end re-read the last one, weight 0
             const int sp = min(s0 + kW * u, a.splits - 1);
-            const float *pt = base + sp * ss;
-            ms[u] = pt[0];
-            ls[u] = pt[1];
-            v[u] = *(const float2 *)(pt + 2 + 2 * lane);
+            ms[u] = mb[sp * sm];
+            ls[u] = mb[sp * sm + 1];
+            v[u] = *(const float2 *)(ob + sp * so + 2 * lane);
         }
 #pragma unroll
         for (int u = 0; u < kU; ++u)

@@ -14,7 +14,7 @@ struct AttnArgs {
     const uint8_t *k_anc, *k_res, *v_anc, *v_res;
     const float *k_gmin, *k_gsc, *k_mu, *k_sg;
     const float *v_gmin, *v_gsc, *v_mu, *v_sg;
-    float *ws;      // partials [split][kv head][row][2 + 128]
+    float *ws;      // partials: [split][kv head][row][128] outputs, then [split][kv head][row][2] (max, sum)
     int64_t astride, gstride, cstride;  // per-block strides of K and V codes
     void *out;      // [t_q][n_qh][128], bf16 or binary32
     int64_t ctx;    // context tokens (multiple of 256)
