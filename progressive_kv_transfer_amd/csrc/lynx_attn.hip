@@ -830,14 +830,16 @@ attn_decode_kernel(AttnArgs a, const DequantTab tab) {
 
 }
 
-// One workgroup of 256 lanes per (KV head, live row) merges the split
-// partials in one pass: wave w takes the splits w, w + 4, ... (8 at a time,
-// all their loads issued together; a split's max and sum are wave-uniform
-// loads), lane l channel pair l of them, with a running maximum per wave;
-// the 4 waves then meet once in LDS, where 64 lanes rescale and add their
-// (max, sum, pair) results and write the row.
-__global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(AttnArgs a) {
-    constexpr int kW = kAttnThreads / 64;
+// One workgroup of 512 lanes per (KV head, live row) merges the split
+// partials in one pass: wave w takes the splits w, w + 8, ... (8 at a time,
+// all their loads issued together, so 64 splits cost one round trip; a
+// split's max and sum are wave-uniform loads), lane l channel pair l of
+// them, with a running maximum per wave; the 8 waves then meet once in LDS,
+// where 64 lanes rescale and add their (max, sum, pair) results and write
+// the row.
+constexpr int kCombineThreads = 512;
+__global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs a) {
+    constexpr int kW = kCombineThreads / 64;
     constexpr int kU = 8;
     __shared__ float4 s_part[kW][64];  // pair sums (2), row sum, wave max
     const int wg = (int)__builtin_amdgcn_workgroup_id_x();
@@ -918,7 +920,7 @@ hipError_t launch_decode(const AttnArgs &a, const DequantTab &tab, hipStream_t s
     if (e != hipSuccess)
         return e;
     hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(a.n_kvh * a.rows)),
-                       dim3(kAttnThreads), 0, stream, a);
+                       dim3(kCombineThreads), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -930,7 +932,7 @@ hipError_t launch_tiles(const AttnArgs &a, const DequantTab &tab, hipStream_t st
     if (e != hipSuccess)
         return e;
     hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(a.n_kvh * a.rows)),
-                       dim3(kAttnThreads), 0, stream, a);
+                       dim3(kCombineThreads), 0, stream, a);
     return hipGetLastError();
 }
 
