@@ -125,6 +125,37 @@ def test_more_than_64_rows(t_q, n_qh, n_kvh, ctx, full):
     assert not np.allclose(ref[0], ref[t_q - 1])
 
 
+def edge_context(k_names, v_names, n_kvh):
+    """K and V [ctx][n_kvh * 128] bf16 from the adversarial edge pages, one
+    page block per (page, KV head) slot, page-major."""
+    pages = kvgen.edge_pages()
+    def build(names):
+        slots = [pages[n] for n in names]
+        rows = [torch.cat(slots[p * n_kvh:(p + 1) * n_kvh], dim=1)
+                for p in range(len(slots) // n_kvh)]
+        return torch.cat(rows, dim=0)
+    return torch.stack([build(k_names), build(v_names)]).to(DEV)
+
+
+EDGE_K = ["constant_channels", "constant_chunks", "spike", "two_valued", "signed_zeros",
+          "subnormals", "all_negative", "zeros", "mixed_sign_zeros", "two_valued"]
+EDGE_V = ["two_valued", "signed_zeros", "huge_range", "all_negative", "zeros",
+          "mixed_sign_zeros", "constant_channels", "constant_chunks", "spike", "subnormals"]
+
+
+@pytest.mark.parametrize("t_q,full", [(1, False), (1, True), (8, True), (8, False)])
+def test_edge_pages_as_context(t_q, full):
+    """A context of 5 pages x 2 KV heads built from the codec's adversarial
+    pages: constant channels and chunks (zero scales), a 5e4 spike (a
+    one-hot softmax), two-valued chunks, signed zeros, bf16 subnormals and
+    all-zero pages in K and V; in V also values of 1e30 beside 1e-30.  Decode
+    (1 query token) and verify (8 tokens, causal) rows against the oracle."""
+    announce(f"edge-page context t_q={t_q} full={full}")
+    kv = edge_context(EDGE_K, EDGE_V, 2)
+    q = kvgen.queries(761, t_q, 16, device=DEV)
+    run_case(kv, q, 2, t_q, full, full, t_q > 1)
+
+
 def test_attention_argument_errors():
     # two tensors of 256 tokens x 2 KV heads: 2 page blocks each
     kv = torch.stack([kvgen.kv_tensor(730 + i, 256, 256, [], True, DEV) for i in range(2)])
