@@ -66,16 +66,83 @@ __device__ __forceinline__ double exp_d(double x) {
     return __builtin_ldexp(p, (int)k);
 }
 
-__device__ __forceinline__ double wave_max_d(double x) {
-#pragma unroll
-    for (int d = 32; d > 0; d >>= 1) x = fmax(x, __shfl_xor(x, d, 64));
-    return x;
+// Cross-lane moves without LDS round trips: DPP within rows of 16 lanes
+// (quad permutes, the mirrored lane of the half row and of the row; row
+// shifts for the scan), v_readlane across the four rows.  A binary64 value
+// moves as its two halves.
+template <int CTRL, bool ZERO_OUT = false>  // ZERO_OUT: lanes without a source read 0
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, ZERO_OUT);
+}
+template <int CTRL, bool ZERO_OUT = false>
+__device__ __forceinline__ double dpp_d(double x) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint64_t lo = dpp_u<CTRL, ZERO_OUT>((uint32_t)u);
+    const uint64_t hi = dpp_u<CTRL, ZERO_OUT>((uint32_t)(u >> 32));
+    return __builtin_bit_cast(double, (hi << 32) | lo);
+}
+__device__ __forceinline__ double readlane_d(double x, int l) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+    return __builtin_bit_cast(double, (hi << 32) | lo);
+}
+constexpr int kQuadSwap1 = 0xb1, kQuadSwap2 = 0x4e, kHalfMirror = 0x141, kRowMirror = 0x140;
+
+// Every lane of a group of 8 (lanes 8 g .. 8 g + 7) gets the group's
+// maximum / sum.
+__device__ __forceinline__ double group_max8(double x) {
+    x = fmax(x, dpp_d<kQuadSwap1>(x));
+    x = fmax(x, dpp_d<kQuadSwap2>(x));
+    return fmax(x, dpp_d<kHalfMirror>(x));
+}
+__device__ __forceinline__ double group_sum8(double x) {
+    x += dpp_d<kQuadSwap1>(x);
+    x += dpp_d<kQuadSwap2>(x);
+    return x + dpp_d<kHalfMirror>(x);
 }
 
+// Wave reductions, the same value in every lane.
+__device__ __forceinline__ double wave_max_d(double x) {
+    x = group_max8(x);
+    x = fmax(x, dpp_d<kRowMirror>(x));
+    return fmax(fmax(readlane_d(x, 0), readlane_d(x, 16)),
+                fmax(readlane_d(x, 32), readlane_d(x, 48)));
+}
 __device__ __forceinline__ double wave_sum_d(double x) {
-#pragma unroll
-    for (int d = 32; d > 0; d >>= 1) x += __shfl_xor(x, d, 64);
-    return x;
+    x = group_sum8(x);
+    x += dpp_d<kRowMirror>(x);
+    return (readlane_d(x, 0) + readlane_d(x, 16)) + (readlane_d(x, 32) + readlane_d(x, 48));
+}
+__device__ __forceinline__ int wave_min_i(int x) {
+    x = min(x, (int)dpp_u<kQuadSwap1>((uint32_t)x));
+    x = min(x, (int)dpp_u<kQuadSwap2>((uint32_t)x));
+    x = min(x, (int)dpp_u<kHalfMirror>((uint32_t)x));
+    x = min(x, (int)dpp_u<kRowMirror>((uint32_t)x));
+    return min(min(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+               min(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
+}
+__device__ __forceinline__ int wave_max_i(int x) {
+    x = max(x, (int)dpp_u<kQuadSwap1>((uint32_t)x));
+    x = max(x, (int)dpp_u<kQuadSwap2>((uint32_t)x));
+    x = max(x, (int)dpp_u<kHalfMirror>((uint32_t)x));
+    x = max(x, (int)dpp_u<kRowMirror>((uint32_t)x));
+    return max(max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+               max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
+}
+
+// Inclusive prefix sum over the wave in lane order: row shifts by 1, 2, 4
+// and 8 (lanes before the row's start read 0), then the totals of the rows
+// before.
+__device__ __forceinline__ double wave_incl_scan_d(double x, int lane) {
+    x += dpp_d<0x111, true>(x);  // row_shr:1
+    x += dpp_d<0x112, true>(x);  // row_shr:2
+    x += dpp_d<0x114, true>(x);  // row_shr:4
+    x += dpp_d<0x118, true>(x);  // row_shr:8
+    const double t0 = readlane_d(x, 15), t1 = readlane_d(x, 31), t2 = readlane_d(x, 47);
+    const int row = lane >> 4;
+    const double off = row == 0 ? 0.0 : row == 1 ? t0 : row == 2 ? t0 + t1 : (t0 + t1) + t2;
+    return x + off;
 }
 
 // Block-wide (256 lanes = 4 waves) reductions; every lane gets the result.
@@ -98,8 +165,7 @@ __device__ double block_sum_d(double x, double *s_red) {
 }
 
 __device__ int block_min_i(int x, int *s_int) {
-#pragma unroll
-    for (int d = 32; d > 0; d >>= 1) x = min(x, __shfl_xor(x, d, 64));
+    x = wave_min_i(x);
     const int tid = (int)__builtin_amdgcn_workitem_id_x();
     __syncthreads();
     if ((tid & 63) == 0) s_int[tid >> 6] = x;
@@ -108,8 +174,7 @@ __device__ int block_min_i(int x, int *s_int) {
 }
 
 __device__ int block_max_i(int x, int *s_int) {
-#pragma unroll
-    for (int d = 32; d > 0; d >>= 1) x = max(x, __shfl_xor(x, d, 64));
+    x = wave_max_i(x);
     const int tid = (int)__builtin_amdgcn_workitem_id_x();
     __syncthreads();
     if ((tid & 63) == 0) s_int[tid >> 6] = x;
@@ -125,12 +190,7 @@ __device__ void block_intervals(double x, double *s_pre, double *s_wsum, double 
                                 double *hi, double *total) {
     const int tid = (int)__builtin_amdgcn_workitem_id_x();
     const int lane = tid & 63, wave = tid >> 6;
-    double incl = x;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const double y = __shfl_up(incl, d, 64);
-        if (lane >= d) incl += y;
-    }
+    const double incl = wave_incl_scan_d(x, lane);
     __syncthreads();
     if (lane == 63) s_wsum[wave] = incl;
     __syncthreads();
@@ -198,19 +258,6 @@ struct Choice {
     double mp, rp, mq, rq;
 };
 
-// Max / sum over the 16 lanes of a lane group (lanes 16 g .. 16 g + 15).
-__device__ __forceinline__ double group_max16(double x) {
-#pragma unroll
-    for (int d = 8; d > 0; d >>= 1) x = fmax(x, __shfl_xor(x, d, 16));
-    return x;
-}
-
-__device__ __forceinline__ double group_sum16(double x) {
-#pragma unroll
-    for (int d = 8; d > 0; d >>= 1) x += __shfl_xor(x, d, 16);
-    return x;
-}
-
 // The decision, computed by every lane of the block: row statistics merged
 // from the chunk statistics, then Eq. (10) per draft.
 __device__ Choice decide(const VerifyArgs &a, double *s_m, double *s_s, int *s_int) {
@@ -228,28 +275,29 @@ __device__ Choice decide(const VerifyArgs &a, double *s_m, double *s_s, int *s_i
         ua = a.u_accept[tid];
     }
     // Row statistics (max, sum of exp_d(l - max)) merged from the chunks: a
-    // group of 16 lanes per row, 16 rows at a time.  Up to 8 x 16 chunks a
-    // lane holds its chunks' statistics in registers (all loads in flight at
-    // once, independent exponentials); beyond that it streams them twice.
-    constexpr int kHeld = 8;
-    const int grp = tid >> 4, sub = tid & 15;
-    for (int r0 = 0; r0 < 2 * a.t + 1; r0 += kThreads / 16) {
+    // group of 8 lanes per row, 32 rows at a time (the 17 rows of 8 drafts
+    // in one pass).  Up to 16 x 8 chunks a lane holds its chunks'
+    // statistics in registers (all loads in flight at once, independent
+    // exponentials); beyond that it streams them twice.
+    constexpr int kG = 8, kHeld = 16;
+    const int grp = tid / kG, sub = tid % kG;
+    for (int r0 = 0; r0 < 2 * a.t + 1; r0 += kThreads / kG) {
         const int r = r0 + grp;
         const bool live = r < 2 * a.t + 1;
         const double *st = a.ws + (int64_t)(live ? r : 0) * a.chunks * 2;
         double m = -INFINITY, s = 0.0;
-        if (a.chunks <= 16 * kHeld) {  // uniform
+        if (a.chunks <= kG * kHeld) {  // uniform
             double mm[kHeld], ss[kHeld];
 #pragma unroll
             for (int i = 0; i < kHeld; ++i) {
-                const int c = sub + 16 * i;
+                const int c = sub + kG * i;
                 const bool ok = live && c < a.chunks;
                 mm[i] = ok ? st[2 * c] : -INFINITY;
                 ss[i] = ok ? st[2 * c + 1] : 0.0;
             }
 #pragma unroll
             for (int i = 0; i < kHeld; ++i) m = fmax(m, mm[i]);
-            m = group_max16(m);
+            m = group_max8(m);
             double e[kHeld];
 #pragma unroll
             for (int i = 0; i < kHeld; ++i)
@@ -258,15 +306,15 @@ __device__ Choice decide(const VerifyArgs &a, double *s_m, double *s_s, int *s_i
             for (int i = 0; i < kHeld; ++i) s += e[i];
         } else {
             if (live)
-                for (int c = sub; c < a.chunks; c += 16) m = fmax(m, st[2 * c]);
-            m = group_max16(m);
+                for (int c = sub; c < a.chunks; c += kG) m = fmax(m, st[2 * c]);
+            m = group_max8(m);
             if (live)
-                for (int c = sub; c < a.chunks; c += 16) {
+                for (int c = sub; c < a.chunks; c += kG) {
                     const double mc = st[2 * c];
                     if (mc != -INFINITY) s += st[2 * c + 1] * exp_d(mc - m);
                 }
         }
-        s = group_sum16(s);
+        s = group_sum8(s);
         if (live && sub == 0) {
             s_m[r] = m;
             s_s[r] = s;
