@@ -458,15 +458,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             av[q >> 2][q & 3] = a;
             rv[q >> 2][q & 3] = r;
         }
-        // 32 contiguous bytes per stream: [chunk j][pair][token of chunk]
-        const int64_t toff = j * (kHead / 2 * kChunk) + p * kChunk;
+        // The chunk's 2 KiB of each stream, [chunk j][pair][token of chunk]:
+        // the lane's pair run is 32 bytes, tokens 0-15 in v[0] and 16-31 in
+        // v[1].  One permlane32 swap per dword leaves lane l < 32 the first
+        // halves of the runs of pairs l and l + 32, and lane l + 32 their
+        // second halves, so the first store instruction writes pairs 0-31
+        // (1 KiB, whole cache lines) and the second pairs 32-63; storing
+        // each lane's run as it is would leave every line half written by
+        // each instruction (measured 3% slower on the same access pattern).
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const auto sa = __builtin_amdgcn_permlane32_swap(av[0][k], av[1][k], false, false);
+            av[0][k] = sa[0];
+            av[1][k] = sa[1];
+            const auto sr = __builtin_amdgcn_permlane32_swap(rv[0][k], rv[1][k], false, false);
+            rv[0][k] = sr[0];
+            rv[1][k] = sr[1];
+        }
+        const int64_t toff = j * (kHead / 2 * kChunk) + 32 * (lane & 31) + 16 * (lane >> 5);
         u32x4 *ao = (u32x4 *)(anchor + b * g.astride + toff);
         u32x4 *ro = (u32x4 *)(residual + b * (kPage * kHead / 2) + toff);
         // Nontemporal stores (measured faster than ordinary ones here).
         __builtin_nontemporal_store(av[0], ao);
-        __builtin_nontemporal_store(av[1], ao + 1);
+        __builtin_nontemporal_store(av[1], ao + 64);  // + 1 KiB
         __builtin_nontemporal_store(rv[0], ro);
-        __builtin_nontemporal_store(rv[1], ro + 1);
+        __builtin_nontemporal_store(rv[1], ro + 64);
     } else {
         // Other widths: field 2 i + e (token i, channel 2p + e) of the lane's
         // run at bit w (2 i + e); the anchor field is the magnitude J >> b,
