@@ -11,8 +11,8 @@
 //                         rows p): chunk max and sum of exp_d(l - max) in
 //                         binary64, 8 independent exponentials per lane;
 //   verify_chunk_kernel   one workgroup per chunk of the chosen row: each
-//                         takes the decision (16 lanes per row merge the
-//                         chunk statistics, 16 rows at a time; one lane per
+//                         takes the decision (8 lanes per row merge the
+//                         chunk statistics, 32 rows at a time; one lane per
 //                         draft tests Eq. (10)), workgroup 0 stores it (the
 //                         first rejection k and the statistics of the row to
 //                         sample from), and each sums its chunk's weights;
