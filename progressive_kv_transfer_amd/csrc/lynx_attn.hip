@@ -247,11 +247,6 @@ __device__ __forceinline__ void step_sync() {
         __syncthreads();
 }
 
-// Channel held by LDS V^ row rho.
-__device__ __forceinline__ int v_row_channel(int rho) {
-    return rho < 64 ? 2 * rho : 2 * (rho - 64) + 1;
-}
-
 template <int RT>  // row tiles of 16: 1, 2 or 4
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(AttnArgs a,
                                                                        const DequantTab tab) {
@@ -415,38 +410,49 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(AttnArgs 
 
     // Merge the waves of each row tile in LDS (reusing the K^ area), then
     // write one partial per live row.
+    // A lane holds channels 32 m + 8 g .. + 7 of its row in o[m] (the even
+    // ones: V^ row rho < 64 is channel 2 rho) and o[m + 4] (the odd ones:
+    // row 64 + rho is channel 2 rho + 1): two 16-byte LDS writes per m; a
+    // merging lane takes 4 channels of a row.
     const float l_row = row_sum4(l_run);
     float *sm = (float *)sK;  // [wave][16 rows][kMergeRow]: max, sum, -, -, 128 outputs
-    {
+    if (live) {  // dead rows are never read
         float *row = sm + (wave * 16 + r16) * kMergeRow;
         if (g == 0) {
             row[0] = m_run == -INFINITY ? -INFINITY : m_run * cs;
             row[1] = l_row;
         }
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) row[4 + v_row_channel(16 * mt + 4 * g + e)] = o[mt][e];
+        for (int m = 0; m < 4; ++m) {
+            float4 *dst = (float4 *)(row + 4 + 32 * m + 8 * g);
+            dst[0] = make_float4(o[m][0], o[m + 4][0], o[m][1], o[m + 4][1]);
+            dst[1] = make_float4(o[m][2], o[m + 4][2], o[m][3], o[m + 4][3]);
+        }
     }
     __syncthreads();
-    for (int idx = tid; idx < a.rows * kHead; idx += kAttnThreads) {
-        const int hr = idx >> 7, ch = idx & (kHead - 1);
+    for (int idx = tid; idx < a.rows * (kHead / 4); idx += kAttnThreads) {
+        const int hr = idx >> 5, c4 = 4 * (idx & (kHead / 4 - 1));
         const int t = hr >> 4, rr = hr & 15;
         float M = -INFINITY;
 #pragma unroll
         for (int k = 0; k < kWavesPerTile; ++k)
             M = fmaxf(M, sm[((t + RT * k) * 16 + rr) * kMergeRow]);
-        float l = 0.0f, acc = 0.0f;
+        float l = 0.0f;
+        float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
         for (int k = 0; k < kWavesPerTile; ++k) {
             const float *row = sm + ((t + RT * k) * 16 + rr) * kMergeRow;
             const float w = row[0] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(row[0] - M);
+            const float4 v = *(const float4 *)(row + 4 + c4);
             l = __builtin_fmaf(row[1], w, l);
-            acc = __builtin_fmaf(row[4 + ch], w, acc);
+            acc.x = __builtin_fmaf(v.x, w, acc.x);
+            acc.y = __builtin_fmaf(v.y, w, acc.y);
+            acc.z = __builtin_fmaf(v.z, w, acc.z);
+            acc.w = __builtin_fmaf(v.w, w, acc.w);
         }
-        if (ch == 0)
+        if (c4 == 0)
             *(float2 *)partial_ml(a, split, kvh, hr) = make_float2(M, l);
-        partial_out(a, split, kvh, hr)[ch] = acc;
+        *(float4 *)(partial_out(a, split, kvh, hr) + c4) = acc;
     }
 }
 
@@ -794,38 +800,47 @@ attn_decode_kernel(AttnArgs a, const DequantTab tab) {
     }
     __syncthreads();  // the merge area overlaps every wave's region
 
-    // Merge the 8 waves in LDS, then one partial per live row.
+    // Merge the 8 waves in LDS, then one partial per live row.  A lane
+    // holds channels 32 m + 8 g .. + 7 of its row in o[2 m] (even) and
+    // o[2 m + 1] (odd): two 16-byte LDS writes per m; a merging lane takes 4
+    // channels of a row.
     const float l_row = row_sum4(l_run);
     float *sm = lds.u.merge;
-    {
+    if (r16 < a.rows) {  // dead rows are never read
         float *row = sm + (wave * 16 + r16) * kMergeRow;
         if (g == 0) {
             row[0] = m_run == -INFINITY ? -INFINITY : m_run * cs;
             row[1] = l_row;
         }
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                row[4 + 2 * (16 * (mt >> 1) + 4 * g + e) + (mt & 1)] = o[mt][e];
+        for (int m = 0; m < 4; ++m) {
+            float4 *dst = (float4 *)(row + 4 + 32 * m + 8 * g);
+            dst[0] = make_float4(o[2 * m][0], o[2 * m + 1][0], o[2 * m][1], o[2 * m + 1][1]);
+            dst[1] = make_float4(o[2 * m][2], o[2 * m + 1][2], o[2 * m][3], o[2 * m + 1][3]);
+        }
     }
     __syncthreads();
-    for (int idx = tid; idx < a.rows * kHead; idx += kDecThreads) {
-        const int hr = idx >> 7, ch = idx & (kHead - 1);
+    for (int idx = tid; idx < a.rows * (kHead / 4); idx += kDecThreads) {
+        const int hr = idx >> 5, c4 = 4 * (idx & (kHead / 4 - 1));
         float M = -INFINITY;
 #pragma unroll
         for (int k = 0; k < kDecWaves; ++k) M = fmaxf(M, sm[(k * 16 + hr) * kMergeRow]);
-        float l = 0.0f, acc = 0.0f;
+        float l = 0.0f;
+        float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
         for (int k = 0; k < kDecWaves; ++k) {
             const float *row = sm + (k * 16 + hr) * kMergeRow;
             const float w = row[0] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(row[0] - M);
+            const float4 v = *(const float4 *)(row + 4 + c4);
             l = __builtin_fmaf(row[1], w, l);
-            acc = __builtin_fmaf(row[4 + ch], w, acc);
+            acc.x = __builtin_fmaf(v.x, w, acc.x);
+            acc.y = __builtin_fmaf(v.y, w, acc.y);
+            acc.z = __builtin_fmaf(v.z, w, acc.z);
+            acc.w = __builtin_fmaf(v.w, w, acc.w);
         }
-        if (ch == 0)
+        if (c4 == 0)
             *(float2 *)partial_ml(a, split, kvh, hr) = make_float2(M, l);
-        partial_out(a, split, kvh, hr)[ch] = acc;
+        *(float4 *)(partial_out(a, split, kvh, hr) + c4) = acc;
     }
 
 }
