@@ -194,17 +194,19 @@ __device__ __forceinline__ void store_k(const LaneCodes &L, float eps, const Lut
 
 // V^ rows: row p holds channel 2p, row 64 + p channel 2p + 1, each as 128
 // tokens of bf16; the lane writes tokens 32c .. 32c + 31 of both rows.
+// Within a chunk's 32 positions the tokens are in the order of the P^T
+// operand: positions 8q .. 8q + 7 hold tokens 4q .. 4q + 3 and
+// 16 + 4q .. 16 + 4q + 3, so a lane's V^ operand is one 16-byte read.
 template <bool FULL>
 __device__ __forceinline__ void store_v(const LaneCodes &L, float eps, const Luts &t, int p,
                                         int c, uint32_t *sV) {
     const u32x4 a[2] = {L.a0, L.a1}, r[2] = {L.r0, L.r1};
     const Affine f = fold(L, eps);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 4; ++q) {  // code word w holds tokens 4w .. 4w + 3
         float y0[8], y1[8];
-        rebuild_word<FULL>(a[q >> 1][2 * (q & 1)], r[q >> 1][2 * (q & 1)], f, t, y0, y1);
-        rebuild_word<FULL>(a[q >> 1][2 * (q & 1) + 1], r[q >> 1][2 * (q & 1) + 1], f, t,
-                           y0 + 4, y1 + 4);
+        rebuild_word<FULL>(a[0][q], r[0][q], f, t, y0, y1);
+        rebuild_word<FULL>(a[1][q], r[1][q], f, t, y0 + 4, y1 + 4);
         const u32x4 e = {pack_bf16(y0[0], y0[1]), pack_bf16(y0[2], y0[3]),
                          pack_bf16(y0[4], y0[5]), pack_bf16(y0[6], y0[7])};
         const u32x4 o = {pack_bf16(y1[0], y1[1]), pack_bf16(y1[2], y1[3]),
@@ -394,12 +396,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(AttnArgs 
                                   pr[2 * i + 1] - __uint_as_float(hw & 0xffff0000u));
             }
             const bf16x8 phi = as_bf16x8(hi), plo = as_bf16x8(lo);
-            const uint32_t *vr = sV + r16 * kRowDw + 16 * c + 2 * g;
+            const uint32_t *vr = sV + r16 * kRowDw + 16 * c + 4 * g;
 #pragma unroll
             for (int mt = 0; mt < 8; ++mt) {
-                const u32x2 t0 = *(const u32x2 *)(vr + 16 * mt * kRowDw);
-                const u32x2 t1 = *(const u32x2 *)(vr + 16 * mt * kRowDw + 8);
-                const bf16x8 av = as_bf16x8(u32x4{t0[0], t0[1], t1[0], t1[1]});
+                const bf16x8 av = as_bf16x8(*(const u32x4 *)(vr + 16 * mt * kRowDw));
                 o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, phi, o[mt], 0, 0, 0);
                 o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, plo, o[mt], 0, 0, 0);
             }
