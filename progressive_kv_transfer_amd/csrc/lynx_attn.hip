@@ -632,12 +632,15 @@ attn_decode_kernel(AttnArgs a, const DequantTab tab) {
     // quad-transpose selectors of this lane
     const uint32_t sel1 = qi < 2 ? 0x05040100u : 0x03020706u;
     const uint32_t sel2 = (qi & 1) ? 0x03070105u : 0x06020400u;
-    // K stage: this lane's pair row (halves swapped for pair bit 2), and
-    // the dword it reads for k-block m, token half tt: pair 16 m + 4 g + qi,
-    // dword (4 tt + qa) ^ (4 (g & 1)) (pair bit 2 = g & 1)
+    // K stage: this lane's pair row holds dwords 0-7 of the pair's run
+    // (tokens 4d .. 4d + 3) in the order 0, 4, 1, 5, 2, 6, 3, 7, so that
+    // dwords qa and 4 + qa (token halves tt = 0, 1) are one 8-byte read, with
+    // the row's two 16-byte halves swapped for pairs with bit 2 set (the
+    // writes then hit distinct banks).  For k-block m the lane reads pair
+    // 16 m + 4 g + qi at position 2 qa ^ 4 (g & 1) (pair bit 2 = g & 1).
     const int kw_lo = lane * 8 + 4 * ((lane >> 2) & 1);
     const int kw_hi = lane * 8 + 4 * (((lane >> 2) & 1) ^ 1);
-    const int kr_base = (4 * g + qi) * 8 + qa;
+    const int kr_base = (4 * g + qi) * 8 + ((2 * qa) ^ (4 * (g & 1)));
 
     // Query row h = r16 of this lane (both products), dead rows are zero.
     const int h = r16;
@@ -681,11 +684,11 @@ attn_decode_kernel(AttnArgs a, const DequantTab tab) {
         // program order): affine tables and the K stage of the chunk.
         pw.affk[lane] = dec_affine(cd.kgm, cd.kgs, cd.kmu, cd.ksg, tab.eps);
         pw.affv[lane] = dec_affine(cd.vgm, cd.vgs, cd.vmu, cd.vsg, tab.eps);
-        *(u32x4 *)&pw.ka[kw_lo] = cd.ka[0];
-        *(u32x4 *)&pw.ka[kw_hi] = cd.ka[1];
+        *(u32x4 *)&pw.ka[kw_lo] = u32x4{cd.ka[0][0], cd.ka[1][0], cd.ka[0][1], cd.ka[1][1]};
+        *(u32x4 *)&pw.ka[kw_hi] = u32x4{cd.ka[0][2], cd.ka[1][2], cd.ka[0][3], cd.ka[1][3]};
         if constexpr (KF) {
-            *(u32x4 *)&pw.kr[kw_lo] = cd.kr[0];
-            *(u32x4 *)&pw.kr[kw_hi] = cd.kr[1];
+            *(u32x4 *)&pw.kr[kw_lo] = u32x4{cd.kr[0][0], cd.kr[1][0], cd.kr[0][1], cd.kr[1][1]};
+            *(u32x4 *)&pw.kr[kw_hi] = u32x4{cd.kr[0][2], cd.kr[1][2], cd.kr[0][3], cd.kr[1][3]};
         }
         asm volatile("" ::: "memory");
 
@@ -694,12 +697,15 @@ attn_decode_kernel(AttnArgs a, const DequantTab tab) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             uint32_t A[2], X[2] = {0u, 0u}, Y[2] = {0u, 0u};
+            const u32x2 kw = *(const u32x2 *)&pw.ka[m * 128 + kr_base];
+            u32x2 rw = {0u, 0u};
+            if constexpr (KF)
+                rw = *(const u32x2 *)&pw.kr[m * 128 + kr_base];
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
-                const int idx = m * 128 + kr_base + ((4 * tt) ^ (4 * (g & 1)));
-                A[tt] = quad_transpose(pw.ka[idx], sel1, sel2);
+                A[tt] = quad_transpose(kw[tt], sel1, sel2);
                 if constexpr (KF) {
-                    const uint32_t R = quad_transpose(pw.kr[idx], sel1, sel2);
+                    const uint32_t R = quad_transpose(rw[tt], sel1, sel2);
                     X[tt] = ((A[tt] << 4) & 0xf0f0f0f0u) | (R & 0x0f0f0f0fu);
                     Y[tt] = (A[tt] & 0xf0f0f0f0u) | ((R >> 4) & 0x0f0f0f0fu);
                 }
