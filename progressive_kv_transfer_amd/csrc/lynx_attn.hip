@@ -462,11 +462,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_partial_kernel(AttnArgs 
 // loads the 32 code bytes of channel pair `lane` of each stream (two 16-byte
 // loads) and the MFMA operands are rebuilt in registers:
 //   K^ (A of S^T = K^ Q^T, 8 channels of one token per lane): the codes go
-//     through a 2 KiB LDS stage per stream ([pair][8 dwords], the two
-//     halves of a pair's row swapped for pairs with bit 2 set, so that the
-//     reads below hit distinct banks); lane (r16 = 4 qa + qi, g) reads, per
-//     k-block m and token half tt, the dword of pair 16 m + 4 g + qi at
-//     tokens 16 tt + 4 qa .. + 3, and a 4 x 4 byte transpose across the
+//     through a 2 KiB LDS stage per stream ([pair][8 dwords], the dwords
+//     of both token halves of a k-block side by side, the two 16-byte
+//     halves of a pair's row swapped for pairs with bit 2 set so that the
+//     writes hit distinct banks); lane (r16 = 4 qa + qi, g) reads, per
+//     k-block m, one 8-byte pair of dwords of pair 16 m + 4 g + qi: tokens
+//     4 qa .. + 3 and 16 + 4 qa .. + 3, and a 4 x 4 byte transpose across the
 //     lanes of a quad (two DPP moves, two v_perm) leaves it the 4 pairs
 //     16 m + 4 g .. + 3 (channels 32 m + 8 g .. + 7) of token 16 tt + r16.
 //   V^ (A of O^T += V^T P^T, 8 tokens of one channel per lane): a 4 x 4
