@@ -219,7 +219,7 @@ __device__ __forceinline__ double *choice_slots(const VerifyArgs &a) {
 }
 
 __global__ __launch_bounds__(kThreads) void verify_stats_kernel(VerifyArgs a) {
-    __shared__ double s_red[4];
+    __shared__ double s_max[4], s_sum[4];  // one slot per wave, each written once
     const int tid = (int)__builtin_amdgcn_workitem_id_x();
     const int wg = (int)__builtin_amdgcn_workgroup_id_x();
     const int r = wg / a.chunks, c = wg % a.chunks;
@@ -234,7 +234,10 @@ __global__ __launch_bounds__(kThreads) void verify_stats_kernel(VerifyArgs a) {
     double m = v[0];
 #pragma unroll
     for (int i = 1; i < kPer; ++i) m = fmax(m, v[i]);
-    m = block_max_d(m, s_red);
+    m = wave_max_d(m);
+    if ((tid & 63) == 0) s_max[tid >> 6] = m;
+    __syncthreads();
+    m = fmax(fmax(s_max[0], s_max[1]), fmax(s_max[2], s_max[3]));
     double s = 0.0;
     if (m != -INFINITY) {  // a chunk of -inf logits holds no mass
         double e[kPer];
@@ -243,7 +246,10 @@ __global__ __launch_bounds__(kThreads) void verify_stats_kernel(VerifyArgs a) {
 #pragma unroll
         for (int i = 0; i < kPer; ++i) s += e[i];
     }
-    s = block_sum_d(s, s_red);
+    s = wave_sum_d(s);
+    if ((tid & 63) == 0) s_sum[tid >> 6] = s;
+    __syncthreads();
+    s = (s_sum[0] + s_sum[1]) + (s_sum[2] + s_sum[3]);
     if (tid == 0) {
         a.ws[(int64_t)wg * 2] = m;
         a.ws[(int64_t)wg * 2 + 1] = s;
