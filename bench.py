@@ -114,8 +114,8 @@ def load_counters():
     return t.get("quantize")
 
 
-# Host threads of one GPU's share of a GPU machine (the box runs one job per GPU
-# and gives each 16 host threads, whatever os.cpu_count() reports).
+# Host threads of one GPU's share of the host (one job runs per GPU and each
+# is given 16 host threads, whatever os.cpu_count() reports).
 CPU_SHARE = 16
 
 

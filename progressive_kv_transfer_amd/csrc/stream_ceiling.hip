@@ -1,7 +1,7 @@
 // Streaming-ceiling probe: a stand-alone program (not part of liblynx.so)
 // that times plain HBM streams on the GPU it runs on, so that a kernel's
 // fraction of the 8 TB/s peak can be read against what a simple stream of
-// the same read / write mix reaches on the same box.
+// the same read / write mix reaches on the same machine.
 //
 // Pattern R : W = every 256-lane workgroup owns one tile of U x 4 KiB in each
 // of R read planes and W write planes (16 bytes per lane and plane per

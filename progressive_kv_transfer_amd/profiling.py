@@ -117,7 +117,7 @@ def traffic(fetch_db, write_db, copy_fetch_db, copy_write_db, elements: int,
             "copy_probe": {"bytes": COPY_BYTES, "fetch_size_kib": cf, "write_size_kib": cw},
             "kernels": kern}
     out = [f"# HBM traffic per launch: {title}", "",
-           "Commands (on the MI355X box, repository root `$R`, one counter per pass):", "",
+           "Commands (on an MI355X, repository root `$R`, one counter per pass):", "",
            *("    " + line for line in command.strip().splitlines()), "",
            f"Scale factors from a plain 1 GiB device copy (`bench.py --copy-probe`): "
            f"FETCH_SIZE reads {cf:.0f} KiB for 1 GiB fetched (x{fscale:.3f}); WRITE_SIZE "
