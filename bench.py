@@ -560,18 +560,19 @@ def measure_large(torch, kvgen, lynx, reps: int = 10):
 
 TRANSFER_OBJECT_BLOCKS = 4096  # 256 MiB of bf16 KV per transfer object (16 objects)
 TRANSFER_REPS = 9              # alternating link-only / pipeline runs (medians reported)
-TRANSFER_RESERVED_CUS = 16     # compute units the codec streams leave to copy kernels
+TRANSFER_RESERVED_CUS = 32     # compute units the codec streams leave to copy kernels
 
 
-def measure_transfer(torch, lynx, kv, codes, out_a, out_f, kern_ms, layout):
+def measure_transfer(torch, lynx, kv, codes, out_a, out_f, kern_ms, layout,
+                     reserved_cus=TRANSFER_RESERVED_CUS):
     """Split-stream transfer of the whole set through pinned host memory:
     the link alone (codes already made) and the full pipeline (quantize,
     two link streams, rebuild from anchor, refine).  layout: the code
     layout (packed = the pages' transmission buffer, one copy per hop for an
     object's anchor + metadata; separate = stream and four metadata arrays,
     five copies).  The sender and receiver run on codec streams that leave
-    TRANSFER_RESERVED_CUS compute units to the runtime's copy kernels; the
-    same measurement on four plain streams is reported beside it."""
+    reserved_cus compute units to the runtime's copy kernels; the same
+    measurement on four plain streams is reported beside it."""
     shape = lynx.shape_of(kv)
     nb = lynx.num_blocks(shape)
     p = lynx.params(layout=layout)
@@ -582,8 +583,7 @@ def measure_transfer(torch, lynx, kv, codes, out_a, out_f, kern_ms, layout):
     # Sender and receiver: codec streams leaving TRANSFER_RESERVED_CUS compute
     # units to the runtime's device-to-host copy kernels; the same run with
     # four plain streams follows for comparison.
-    sender, receiver = lynx.CodecStream(TRANSFER_RESERVED_CUS), lynx.CodecStream(
-        TRANSFER_RESERVED_CUS)
+    sender, receiver = lynx.CodecStream(reserved_cus), lynx.CodecStream(reserved_cus)
     streams = (sender.stream, torch.cuda.Stream(), torch.cuda.Stream(), receiver.stream)
     plain = tuple(torch.cuda.Stream() for _ in range(4))
     # Raw PCIe rates of one 1 GiB pinned copy each way (the link's floor).
@@ -648,7 +648,7 @@ def measure_transfer(torch, lynx, kv, codes, out_a, out_f, kern_ms, layout):
                                  "pipeline": [round(r["anchor_ready"], 2) for r in pipes]},
         "link_anchor_GBps": round(anchor_bytes / (link["anchor_arrived"] * 1e-3) / 1e9, 2),
         "serial_anchor_ready_ms": round(serial_anchor, 3),
-        "codec_streams_reserved_cus": TRANSFER_RESERVED_CUS,
+        "codec_streams_reserved_cus": reserved_cus,
         "exposed_anchor_overhead_ms": round(exposed, 3),
         "hidden_fraction_of_codec_time": hidden(exposed),
         "plain_streams": {"link_anchor_arrived_ms": round(link_p["anchor_arrived"], 3),
@@ -675,6 +675,7 @@ def main():
     ap.add_argument("--attention-only", action="store_true")
     ap.add_argument("--large-only", action="store_true")
     ap.add_argument("--transfer-only", choices=["packed", "separate"], default=None)
+    ap.add_argument("--transfer-reserved-cus", type=int, default=TRANSFER_RESERVED_CUS)
     ap.add_argument("--attention-calls", type=int, default=50)
     ap.add_argument("--attention-case", default=None,
                     choices=[c[0] for c in ATTENTION_CASES])
@@ -798,16 +799,18 @@ def main():
         kms = {n: kern[n]["ms"] for n in names}
         layout = lynx.LAYOUT_PACKED if args.transfer_only == "packed" else lynx.LAYOUT_SEPARATE
         print(json.dumps({"transfer": measure_transfer(torch, lynx, kv, codes, out_a, out_f, kms,
-                                                       layout)}), flush=True)
+                                                       layout, args.transfer_reserved_cus)}),
+              flush=True)
         return
     if not args.no_transfer and not args.profile_run:
         kms = {n: kern[n]["ms"] for n in names}
         # the pages' transmission buffer (anchor + scalars per block, one copy
         # per hop and object), then the separate arrays for comparison
         out["transfer"] = measure_transfer(torch, lynx, kv, codes, out_a, out_f, kms,
-                                           lynx.LAYOUT_PACKED)
+                                           lynx.LAYOUT_PACKED, args.transfer_reserved_cus)
         out["transfer_separate"] = measure_transfer(torch, lynx, kv, codes, out_a, out_f, kms,
-                                                    lynx.LAYOUT_SEPARATE)
+                                                    lynx.LAYOUT_SEPARATE,
+                                                    args.transfer_reserved_cus)
     if not args.profile_run:
         out["split_variants"] = measure_splits(torch, lynx, kv, out_a)
     if not args.no_attention and not args.profile_run:

@@ -429,7 +429,7 @@ int lynx_split_stream_transfer(const void *kv, const lynx_kv_shape *shape,
  * streams of lynx_split_stream_transfer) that leaves reserved_cus compute
  * units of the current device to other work: its kernels run only on the
  * remaining units (a CU mask; the reserved units are spread evenly over the
- * unit numbering, so over the XCDs).  The runtime runs most device-to-
+ * XCDs, whether the mask's bits go to the XCDs in turn or XCD after XCD).  The runtime runs most device-to-
  * pinned-host copies as shader copy kernels; on streams without such a
  * reserve those kernels wait until the quantize or rebuild kernels' own
  * workgroups drain, which stalls the link by up to a kernel's duration per

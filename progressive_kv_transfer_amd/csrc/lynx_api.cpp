@@ -776,6 +776,22 @@ int lynx_block_stats(const void *kv, const lynx_kv_shape *shape, const lynx_para
                            (float *)gamma_scale, mu, sigma, kModeBlockStats, stream);
 }
 
+// The k-th compute unit a codec stream leaves free, as a bit of the stream's
+// CU mask.  On a part of 8 XCDs the driver hands mask bit u to XCD u % 8
+// (unit u / 8 there); the k-th reserved unit is unit 4 x + m of XCD x, for
+// x = k % 8, m = k / 8, so the reserve is spread evenly over the XCDs, and
+// in a numbering of whole XCDs one after another (bit u on XCD u / (ncu / 8))
+// it would be spread evenly too.  Distinct for k < ncu; other unit counts
+// take every (ncu / reserved)-th bit.
+static int reserved_unit(int k, int ncu) {
+    constexpr int kXcds = 8;
+    const int per = ncu / kXcds;
+    if (ncu % kXcds || per % kXcds)
+        return k;
+    const int x = k % kXcds, m = k / kXcds;
+    return x + kXcds * ((per / kXcds * x + m) % per);
+}
+
 int lynx_codec_stream_create(int reserved_cus, hipStream_t *stream) {
     if (!stream || reserved_cus < 0)
         return LYNX_EINVAL;
@@ -790,16 +806,12 @@ int lynx_codec_stream_create(int reserved_cus, hipStream_t *stream) {
         return LYNX_EINVAL;
     if (reserved_cus == 0)
         return hip_status(hipStreamCreate(stream));
-    // Unit u is reserved when it is the last of its share: u = floor((k + 1)
-    // ncu / reserved_cus) - 1 for k = 0 .. reserved_cus - 1.
-    std::vector<uint32_t> mask((size_t)(ncu + 31) / 32, 0u);
-    for (int u = 0, k = 0; u < ncu; ++u) {
-        const bool reserved = k < reserved_cus &&
-                              u == (int)((int64_t)(k + 1) * ncu / reserved_cus) - 1;
-        if (reserved)
-            ++k;
-        else
-            mask[(size_t)u / 32] |= 1u << (u % 32);
+    std::vector<uint32_t> mask((size_t)(ncu + 31) / 32, ~0u);
+    if (ncu % 32)
+        mask.back() = (1u << (ncu % 32)) - 1u;
+    for (int k = 0; k < reserved_cus; ++k) {
+        const int u = reserved_unit(k, ncu);
+        mask[(size_t)u / 32] &= ~(1u << (u % 32));
     }
     return hip_status(hipExtStreamCreateWithCUMask(stream, (uint32_t)mask.size(), mask.data()));
 }

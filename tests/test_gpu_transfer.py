@@ -101,7 +101,7 @@ def test_transfer_copies_only():
     assert times["quantized"] >= 0.0 and times["full_ready"] >= times["residual_arrived"] - 1e-3
 
 
-@pytest.mark.parametrize("reserved", [8, 16, 0])
+@pytest.mark.parametrize("reserved", [8, 16, 32, 64, 0])
 def test_transfer_on_codec_streams_matches_oracle(kv_set, reserved):
     """Sender and receiver on lynx_codec_stream_create streams (kernels kept
     off `reserved` compute units; 0 = a plain stream): the codes on every hop
